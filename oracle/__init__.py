@@ -1,0 +1,6 @@
+"""fp64 CPU oracle of the gpt-oss MoE MLP layer -- TEST INFRASTRUCTURE.
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline
+leg may import this package.  The HIP product path never calls it.
+"""
+from . import moe_oracle  # noqa: F401

@@ -1,0 +1,277 @@
+"""Plain fp64 CPU oracle of the gpt-oss mixture-of-experts MLP layer.
+
+TEST INFRASTRUCTURE.  Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import this module.  The product path (the
+HIP library and its Python binding) never calls it and shares no code with it.
+
+Everything is computed in float64 from exactly the arrays the GPU receives
+(bf16 bit patterns, fp32 biases, raw MXFP4 nibbles and E8M0 scale bytes).
+
+Sources (web pages on gpt-oss; cited by page title and section):
+  [A] "OpenAI 最新开源模型 gpt-oss 架构与训练解析" (dtcms.com/a/486625):
+      section 模型架构, MoE item (top-4 routing, softmax weighting of the
+      selected experts, gated-SwiGLU FFN with clamp and residual);
+      权重量化 item (MoE weights in MXFP4, 4.25 bits per weight);
+      Swish/SwiGLU 替换 GELU (Swish(x) = x * sigmoid(x));
+      RMSNorm 替换 LayerNorm (divide by the root mean square, no bias).
+  [B] "【LLM】GPT-OSS架构变化详解" (dtcms.com/a/386406.html):
+      2.4.1 MoE 的核心原理 (a router scores the experts of each token;
+      the unselected experts do nothing for that token).
+  [C] Xin Zhiyuan's translation of Raschka's "From GPT-2 to gpt-oss"
+      (dreamgost.com/a/xinwen/gongsixinwen/564.html): the GLU variant has
+      three linear layers (gate, up, and the down projection).
+
+Readings where the pages leave a step open (each one is plain and is the one
+the rest of the pages support):
+  * MXFP4 = OCP microscaling FP4: E2M1 element codes, one E8M0 scale byte
+    per 32 consecutive elements of a row, scale 2^(s-127), byte 0xFF = NaN;
+    two codes per byte, the low nibble holds the even element.
+  * Top-k ties go to the lower expert index; slots are ordered by
+    descending logit.
+  * The softmax runs over the k selected logits only.
+  * The clamp limit c applies symmetrically to gate and up, before the
+    sigmoid and before the +1; h = clamp(g) * sigmoid(clamp(g)) * (clamp(u) + 1).
+  * The fused gate/up weight holds the gate rows first ([0, I)) and the up
+    rows second ([I, 2I)); both expert biases live inside the expert, so the
+    down bias is weighted by the gate weight of its slot.
+  * RMSNorm uses eps = 1e-5 and unit gain; in the layer stack the residual
+    stream and each layer's normalised input are stored as bf16.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# storage formats
+# ---------------------------------------------------------------------------
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64.  bf16 is the upper half of an
+    IEEE binary32, so the value is exact in float64."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(v: np.ndarray) -> np.ndarray:
+    """float64 -> nearest bf16 value (ties to even), returned as float64.
+    Exact for normal results (8 significant bits); NaN/inf pass through."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)                      # v = m * 2^e, 0.5 <= |m| < 1
+    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)   # np.rint: half to even
+    return np.where(np.isfinite(v), r, v)
+
+
+def e2m1_value(code: np.ndarray) -> np.ndarray:
+    """Value of a 4-bit E2M1 code, bits [s e1 e0 m]: exponent bias 1, one
+    mantissa bit, exponent field 0 is subnormal (0 or 0.5).  No inf/NaN."""
+    c = np.asarray(code, dtype=np.int64)
+    s = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, e - 1))
+    return np.where(s == 1, -mag, mag)
+
+
+def e8m0_value(byte: np.ndarray) -> np.ndarray:
+    """Value of an E8M0 scale byte: 2^(s-127); 0xFF encodes NaN."""
+    s = np.asarray(byte, dtype=np.int64)
+    return np.where(s == 255, np.nan, np.ldexp(1.0, s - 127))
+
+
+def mxfp4_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP4 rows -> float64 [R, K] ([A] 权重量化; format split per the
+    OCP MX convention).  codes uint8 [R, K/2], scales uint8 [R, K/32]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    R, half = codes.shape
+    K = 2 * half
+    assert scales.shape == (R, K // 32), (scales.shape, R, K)
+    nib = np.empty((R, K), dtype=np.uint8)
+    nib[:, 0::2] = codes & 0x0F          # element 2j: low nibble
+    nib[:, 1::2] = codes >> 4            # element 2j+1: high nibble
+    table = e2m1_value(np.arange(16))
+    w = table[nib]
+    scale = e8m0_value(scales)           # [R, K/32]
+    return w * np.repeat(scale, 32, axis=1)
+
+
+# ---------------------------------------------------------------------------
+# the layer
+# ---------------------------------------------------------------------------
+
+
+def router_logits(x: np.ndarray, router_w: np.ndarray, router_b: np.ndarray) -> np.ndarray:
+    """Router scores l[t, e] = sum_k x[t,k] W_r[e,k] + b_r[e] ([B] 2.4.1: a
+    router scores every expert for each token).  x: float64 [T, d]."""
+    return x @ router_w.T + router_b[None, :]
+
+
+def topk_experts(logits: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest logits per row, descending; ties -> lower
+    index ([A] 模型架构/MoE: top-4 routing).  int64 [T, k]."""
+    T, E = logits.shape
+    out = np.empty((T, k), dtype=np.int64)
+    idx = np.arange(E)
+    for t in range(T):
+        order = np.lexsort((idx, -logits[t]))   # primary: -logit, secondary: index
+        out[t] = order[:k]
+    return out
+
+
+def selected_softmax(sel_logits: np.ndarray) -> np.ndarray:
+    """Softmax over the selected logits of each row ([A] 模型架构/MoE:
+    softmax weighting of the chosen experts)."""
+    m = sel_logits.max(axis=1, keepdims=True)
+    e = np.exp(sel_logits - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def sigmoid(v: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-v))
+
+
+def clamped_swiglu(g: np.ndarray, u: np.ndarray, clamp: float) -> np.ndarray:
+    """h = Swish(clamp(g)) * (clamp(u) + 1): Swish(v) = v*sigmoid(v)
+    ([A] Swish/SwiGLU 替换 GELU); gate-times-up GLU with a clamp and the
+    residual-style +1 on the up branch ([A] 模型架构/MoE)."""
+    gc = np.clip(g, -clamp, clamp)
+    uc = np.clip(u, -clamp, clamp)
+    return gc * sigmoid(gc) * (uc + 1.0)
+
+
+def expert_ffn(xs: np.ndarray, w13: np.ndarray, b13: np.ndarray,
+               w2: np.ndarray, b2: np.ndarray, clamp: float) -> np.ndarray:
+    """One expert on rows xs [n, d] with dequantised weights: the three
+    linear maps of the GLU ([C]): a = xs W13^T + b13, gate = a[:, :I],
+    up = a[:, I:], z = h W2^T + b2."""
+    I = w13.shape[0] // 2
+    a = xs @ w13.T + b13[None, :]
+    h = clamped_swiglu(a[:, :I], a[:, I:], clamp)
+    return h @ w2.T + b2[None, :]
+
+
+class DequantCache:
+    """Dequantises expert e's weights on first use (float64)."""
+
+    def __init__(self, experts: dict):
+        self.ex = experts
+        self._c: dict[int, tuple] = {}
+
+    def __call__(self, e: int):
+        if e not in self._c:
+            ex = self.ex
+            self._c[e] = (
+                mxfp4_dequant(ex["w13_codes"][e], ex["w13_scales"][e]),
+                np.asarray(ex["b13"][e], dtype=np.float64),
+                mxfp4_dequant(ex["w2_codes"][e], ex["w2_scales"][e]),
+                np.asarray(ex["b2"][e], dtype=np.float64),
+            )
+        return self._c[e]
+
+
+def route(x_bits: np.ndarray, router_w_bits: np.ndarray, router_b: np.ndarray, k: int):
+    """Router, top-k and selected softmax.  Returns (logits, ids [T,k],
+    weights [T,k])."""
+    x = bf16_bits_to_f64(x_bits)
+    wr = bf16_bits_to_f64(router_w_bits)
+    logits = router_logits(x, wr, np.asarray(router_b, dtype=np.float64))
+    ids = topk_experts(logits, k)
+    w = selected_softmax(np.take_along_axis(logits, ids, axis=1))
+    return logits, ids, w
+
+
+def moe_layer(x_bits: np.ndarray, router_w_bits: np.ndarray, router_b: np.ndarray,
+              experts: dict, k: int, clamp: float, cache: DequantCache | None = None):
+    """Sparse MoE layer: y[t] = sum_j w[t,j] * FFN_{S_t[j]}(x[t]).
+
+    Each expert runs only on the tokens routed to it ([B] 2.4.1).  Returns a
+    dict with y (float64 [T, d]), logits, ids, w and per-expert counts.
+    """
+    x = bf16_bits_to_f64(x_bits)
+    logits, ids, w = route(x_bits, router_w_bits, router_b, k)
+    T = x.shape[0]
+    E = router_w_bits.shape[0]
+    d = x.shape[1]
+    cache = cache or DequantCache(experts)
+    y = np.zeros((T, d), dtype=np.float64)
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    for e in range(E):
+        tok, slot = np.nonzero(ids == e)
+        if tok.size == 0:
+            continue
+        w13, b13, w2, b2 = cache(e)
+        z = expert_ffn(x[tok], w13, b13, w2, b2, clamp)
+        y[tok] += w[tok, slot][:, None] * z
+    return dict(y=y, logits=logits, ids=ids, w=w, counts=counts)
+
+
+def moe_layer_dense_masked(x_bits: np.ndarray, router_w_bits: np.ndarray, router_b: np.ndarray,
+                           experts: dict, k: int, clamp: float) -> np.ndarray:
+    """Brute-force form of the same layer for tiny inputs: run every expert
+    on every token, then mix with a mask that is w[t,e] on the selected
+    experts and 0 elsewhere.  Written independently of moe_layer (no shared
+    routing helper): the mask comes from a full sort and a full softmax
+    renormalised over the selected set."""
+    x = bf16_bits_to_f64(x_bits)
+    wr = bf16_bits_to_f64(router_w_bits)
+    b = np.asarray(router_b, dtype=np.float64)
+    T, d = x.shape
+    E = wr.shape[0]
+    y = np.zeros((T, d))
+    for t in range(T):
+        l = np.array([float(np.dot(x[t], wr[e])) + b[e] for e in range(E)])
+        ranked = sorted(range(E), key=lambda e: (-l[e], e))
+        chosen = set(ranked[:k])
+        p = np.exp(l - l.max())
+        p = p / p.sum()
+        zsum = sum(p[e] for e in chosen)
+        for e in range(E):
+            mask = p[e] / zsum if e in chosen else 0.0
+            w13 = mxfp4_dequant(experts["w13_codes"][e], experts["w13_scales"][e])
+            w2 = mxfp4_dequant(experts["w2_codes"][e], experts["w2_scales"][e])
+            I = w13.shape[0] // 2
+            g = np.array([np.dot(w13[i], x[t]) for i in range(I)]) + experts["b13"][e][:I]
+            u = np.array([np.dot(w13[I + i], x[t]) for i in range(I)]) + experts["b13"][e][I:]
+            gc = np.minimum(np.maximum(g, -clamp), clamp)
+            uc = np.minimum(np.maximum(u, -clamp), clamp)
+            h = gc / (1.0 + np.exp(-gc)) * (1.0 + uc)
+            z = np.array([np.dot(w2[r], h) for r in range(d)]) + experts["b2"][e]
+            y[t] += mask * z
+    return y
+
+
+def rmsnorm(v: np.ndarray, eps: float = 1e-5) -> np.ndarray:
+    """v / sqrt(mean(v^2) + eps) over the last axis, unit gain, no bias
+    ([A] RMSNorm 替换 LayerNorm)."""
+    return v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)
+
+
+def stack_forward(x0_bits: np.ndarray, layers: list, k: int, clamp: float, eps: float = 1e-5):
+    """Pre-norm residual stack of MoE layers: n = bf16(RMSNorm(x)),
+    x <- bf16(x + MoE(n)).  ``layers`` is a list of dicts with router_w,
+    router_b and the expert arrays.  Returns the final residual stream
+    (float64 holding bf16 values) and the per-layer ids."""
+    x = bf16_bits_to_f64(x0_bits)
+    all_ids = []
+    for L in layers:
+        n = round_to_bf16(rmsnorm(x, eps))
+        n_bits = _f64_bf16_to_bits(n)
+        r = moe_layer(n_bits, L["router_w"], L["router_b"], L, k, clamp)
+        all_ids.append(r["ids"])
+        x = round_to_bf16(x + r["y"])
+    return x, all_ids
+
+
+def _f64_bf16_to_bits(v: np.ndarray) -> np.ndarray:
+    """Bit pattern of float64 values that are already bf16-representable."""
+    f = np.asarray(v, dtype=np.float32)          # exact for bf16 values
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def topk_gap(logits: np.ndarray, k: int) -> np.ndarray:
+    """Gap between the k-th and (k+1)-th largest logit of each row (inf when
+    k equals the number of experts)."""
+    s = -np.sort(-logits, axis=1)
+    if s.shape[1] <= k:
+        return np.full(s.shape[0], np.inf)
+    return s[:, k - 1] - s[:, k]

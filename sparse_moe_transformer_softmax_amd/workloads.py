@@ -1,0 +1,46 @@
+"""Workload shapes of the gpt-oss-shaped MoE MLP layer.
+
+Sizes follow the gpt-oss architecture summaries: 32 experts for the 20b model
+and 128 for the 120b model, top-4 routing, hidden size and expert width 2880
+(dtcms.com "GPT-OSS 与 Qwen3" comparison, p5 model-architecture list), 36
+blocks for the 120b stack.  Each workload carries its seed.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int
+    d: int
+    I: int
+    E: int
+    k: int
+    seed: int
+    routing: str = "random"   # "random" | "zipf"
+    layers: int = 1
+    clamp: float = 7.0
+
+    @property
+    def pairs(self) -> int:
+        return self.T * self.k
+
+
+# Zipf exponent s = 1.2 for the load-imbalance workload, realised through the
+# router bias b(e) = -beta * ln(rank(e)).  beta is the value for which the
+# least-squares slope of log(load) against log(rank) is -1.2 on the seeded
+# 120b prefill inputs (loads capped at T by construction); it was written by
+# oracle/zipf_beta.py.
+ZIPF_BETA = 0.559362
+
+WORKLOADS = {
+    "tiny": Workload("tiny", T=16, d=128, I=128, E=8, k=4, seed=0x5EED0000),
+    "20b_decode": Workload("20b_decode", T=32, d=2880, I=2880, E=32, k=4, seed=0x5EED0001),
+    "20b_prefill": Workload("20b_prefill", T=4096, d=2880, I=2880, E=32, k=4, seed=0x5EED0002),
+    "120b_prefill_zipf": Workload("120b_prefill_zipf", T=8192, d=2880, I=2880, E=128, k=4,
+                                  seed=0x5EED0003, routing="zipf"),
+    "120b_stack36": Workload("120b_stack36", T=2048, d=2880, I=2880, E=128, k=4,
+                             seed=0x5EED1000, layers=36),
+}
