@@ -1,0 +1,151 @@
+/*
+ * moe_mi355x.h -- C ABI of the MI355X (gfx950) gpt-oss mixture-of-experts
+ * MLP layer.
+ *
+ * The layer (gpt-oss pages: "OpenAI 最新开源模型 gpt-oss 架构与训练解析",
+ * 模型架构 section, MoE item; "【LLM】GPT-OSS架构变化详解", 2.4.1):
+ *   logits[t, e] = x[t] . W_r[e] + b_r[e]                       (router)
+ *   S_t          = the k experts with the largest logits         (top-k)
+ *   w[t, j]      = softmax over the k selected logits            (gate weights)
+ *   a            = W13_e x[t] + b13_e ; g = a[0:I], u = a[I:2I]
+ *   h            = clamp(g) * sigmoid(clamp(g)) * (clamp(u) + 1) (clamped SwiGLU)
+ *   z            = W2_e h + b2_e                                 (down projection)
+ *   out[t]       = sum_j w[t, j] * z_{S_t[j]}                    (combine)
+ * clamp(v) limits v to [-clamp, clamp].  The expert weights are MXFP4
+ * (same page, 权重量化 item: 4.25 bits per weight): E2M1 codes, two per byte
+ * with the low nibble holding the even element, and one E8M0 scale byte
+ * (value 2^(s-127), 0xFF = NaN) per 32 consecutive elements of a row.
+ *
+ * Conventions shared by every entry point:
+ *  - All array arguments are DEVICE pointers on the current HIP device,
+ *    row-major and contiguous.  bf16 arrays are passed as raw 16-bit
+ *    patterns.  x, router_w, out and the code arrays must be 16-byte
+ *    aligned; fp32 arrays 4-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *    enqueued asynchronously; the library never synchronises the stream,
+ *    so device faults surface at the caller's next synchronisation.
+ *  - The caller owns every buffer it passes; the library keeps no pointer
+ *    after a call returns.
+ *  - Return value: MOE_OK (0) or a negative moe_status.  No C++ exception
+ *    crosses the boundary and the library prints nothing.
+ *  - Shapes: T >= 0 tokens (T == 0 is a successful no-op); d (model width)
+ *    and I (expert width) positive multiples of 32; 1 <= E <= 256 experts;
+ *    1 <= k <= min(E, 8); T * max(k, E) < 2^31; clamp > 0 (+inf disables
+ *    the clamp).
+ *  - Entry points without a workspace argument use a library-owned device
+ *    workspace per GPU that grows on demand (a growth allocates and
+ *    synchronises the device).  Calls that share it must be ordered on one
+ *    stream; concurrent callers pass their own workspace to
+ *    moe_layer_forward_ws.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MI355X_VERSION 10000 /* 1.0.0 */
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL_PTR = -1,    /* a required pointer is NULL */
+  MOE_ERR_BAD_SHAPE = -2,   /* a size is out of range or inconsistent */
+  MOE_ERR_UNSUPPORTED = -3, /* no gfx950 device is current */
+  MOE_ERR_MISALIGNED = -4,  /* a pointer breaks the alignment rules above */
+  MOE_ERR_NOMEM = -5,       /* workspace allocation failed */
+  MOE_ERR_HIP = -6,         /* a HIP launch or runtime call failed */
+  MOE_ERR_ALIAS = -7,       /* the output overlaps an input */
+  MOE_ERR_WORKSPACE = -8    /* caller workspace too small */
+} moe_status;
+
+/* Full MoE layer.
+ *   x          bf16 [T, d]            token activations
+ *   router_w   bf16 [E, d]            router weight
+ *   router_b   fp32 [E]               router bias
+ *   w13_codes  uint8 [E, 2I, d/2]     fused gate/up weight, E2M1 nibbles;
+ *                                     rows [0, I) gate, rows [I, 2I) up
+ *   w13_scales uint8 [E, 2I, d/32]    E8M0 scales of w13
+ *   b13        fp32 [E, 2I]           gate/up bias
+ *   w2_codes   uint8 [E, d, I/2]      down weight, E2M1 nibbles
+ *   w2_scales  uint8 [E, d, I/32]     E8M0 scales of w2
+ *   b2         fp32 [E, d]            down bias (inside the expert, so it
+ *                                     is weighted by the gate weight)
+ *   out        bf16 [T, d]            written; must not overlap any input
+ * Top-k ties go to the lower expert index. */
+int moe_layer_forward(const void* x, const void* router_w, const float* router_b,
+                      const uint8_t* w13_codes, const uint8_t* w13_scales, const float* b13,
+                      const uint8_t* w2_codes, const uint8_t* w2_scales, const float* b2,
+                      int T, int d, int I, int E, int k, float clamp, void* out, void* stream);
+
+/* Same kernels as moe_layer_forward, with the intermediate results exposed.
+ *   out      bf16 [T, d] or NULL
+ *   out_f32  fp32 [T, d] or NULL: the combine result before bf16 rounding
+ *            (out == round-to-nearest-even(out_f32) element by element)
+ *   topk_id  int32 [T, k]  selected experts, descending logit
+ *   topk_w   fp32 [T, k]   their softmax weights
+ *   counts   int32 [E]     number of (token, slot) pairs per expert
+ * topk_id, topk_w and counts are required. */
+int moe_layer_forward_dbg(const void* x, const void* router_w, const float* router_b,
+                          const uint8_t* w13_codes, const uint8_t* w13_scales, const float* b13,
+                          const uint8_t* w2_codes, const uint8_t* w2_scales, const float* b2,
+                          int T, int d, int I, int E, int k, float clamp, void* out, float* out_f32,
+                          int32_t* topk_id, float* topk_w, int32_t* counts, void* stream);
+
+/* Router, top-k and selected softmax only ("【LLM】GPT-OSS架构变化详解",
+ * 2.4.1; "OpenAI 最新开源模型 gpt-oss 架构与训练解析", MoE item).  Outputs as
+ * in moe_layer_forward_dbg. */
+int moe_route(const void* x, const void* router_w, const float* router_b, int T, int d, int E,
+              int k, int32_t* topk_id, float* topk_w, int32_t* counts, void* stream);
+
+/* Bytes of device workspace moe_layer_forward_ws needs for these sizes
+ * (0 if the sizes are invalid). */
+size_t moe_workspace_bytes(int T, int d, int I, int E, int k);
+
+/* Prepares a caller-owned workspace (256-byte aligned, at least
+ * moe_workspace_bytes) for first use by clearing its counter block with a
+ * kernel on `stream`.  Every completed call leaves the block cleared again. */
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* moe_layer_forward with a caller-owned workspace: allocates nothing.
+ * Concurrent calls need distinct workspaces. */
+int moe_layer_forward_ws(const void* x, const void* router_w, const float* router_b,
+                         const uint8_t* w13_codes, const uint8_t* w13_scales, const float* b13,
+                         const uint8_t* w2_codes, const uint8_t* w2_scales, const float* b2,
+                         int T, int d, int I, int E, int k, float clamp, void* out, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* out = bf16(x / sqrt(mean(x^2) + eps)) per row, unit gain, no bias
+ * ("OpenAI 最新开源模型 gpt-oss 架构与训练解析", RMSNorm 替换 LayerNorm).
+ * x, out bf16 [T, d]; d a multiple of 32; eps >= 0.  out may equal x. */
+int moe_rmsnorm(const void* x, void* out, int T, int d, float eps, void* stream);
+
+/* Pre-norm residual stack of n_layers MoE layers on one GPU:
+ *   n = bf16(RMSNorm(x)); x = bf16(x + MoE_l(n))   for l = 0 .. n_layers-1
+ * Each per-layer argument is a HOST array of n_layers device pointers with
+ * the layouts of moe_layer_forward.  x0 bf16 [T, d] is read; out bf16 [T, d]
+ * receives the final residual stream and must not overlap x0. */
+int moe_stack_forward(const void* x0, int n_layers, const void* const* router_w,
+                      const float* const* router_b, const uint8_t* const* w13_codes,
+                      const uint8_t* const* w13_scales, const float* const* b13,
+                      const uint8_t* const* w2_codes, const uint8_t* const* w2_scales,
+                      const float* const* b2, int T, int d, int I, int E, int k, float clamp,
+                      float eps, void* out, void* stream);
+
+/* Frees the library-owned workspaces (waits for the device first). */
+void moe_release(void);
+
+/* Static description of a status code. */
+const char* moe_status_string(int status);
+
+/* MOE_MI355X_VERSION of the loaded library. */
+int moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

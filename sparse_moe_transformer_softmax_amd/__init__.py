@@ -1,0 +1,220 @@
+"""Python binding of libmoe_mi355x.so, the MI355X (gfx950) gpt-oss MoE MLP layer.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  Tensors are torch CUDA tensors (torch supplies device memory and the
+current stream); bf16 tensors are passed as raw 16-bit patterns.  If the
+library has not been built the functions raise -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "MoeError", "lib", "moe_layer_forward", "moe_layer_forward_dbg", "moe_route",
+    "moe_workspace_bytes", "moe_workspace_init", "moe_layer_forward_ws", "moe_rmsnorm",
+    "moe_stack_forward", "moe_release", "moe_status_string", "moe_version", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SIGS = {
+    "moe_layer_forward": (_I, [_P] * 9 + [_I] * 5 + [_F, _P, _P]),
+    "moe_layer_forward_dbg": (_I, [_P] * 9 + [_I] * 5 + [_F] + [_P] * 6),
+    "moe_route": (_I, [_P] * 3 + [_I] * 4 + [_P] * 4),
+    "moe_workspace_bytes": (ctypes.c_size_t, [_I] * 5),
+    "moe_workspace_init": (_I, [_P, ctypes.c_size_t, _P]),
+    "moe_layer_forward_ws": (_I, [_P] * 9 + [_I] * 5 + [_F, _P, _P, ctypes.c_size_t, _P]),
+    "moe_rmsnorm": (_I, [_P, _P, _I, _I, _F, _P]),
+    "moe_stack_forward": (_I, [_P, _I] + [_P] * 8 + [_I] * 5 + [_F, _F, _P, _P]),
+    "moe_release": (None, []),
+    "moe_status_string": (ctypes.c_char_p, [_I]),
+    "moe_version": (_I, []),
+}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({moe_status_string(status)})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Loads the HIP library (raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run python -m sparse_moe_transformer_softmax_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def moe_version() -> int:
+    return lib().moe_version()
+
+
+def moe_release() -> None:
+    lib().moe_release()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(t, name, dtype, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _ok(fn, st):
+    if st != 0:
+        raise MoeError(fn, st)
+
+
+def _layer_ptrs(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2):
+    torch = _torch()
+    T, d = x.shape
+    E = router_w.shape[0]
+    I = w2_codes.shape[2] * 2
+    ptrs = [
+        _check(x, "x", torch.bfloat16, (T, d)),
+        _check(router_w, "router_w", torch.bfloat16, (E, d)),
+        _check(router_b, "router_b", torch.float32, (E,)),
+        _check(w13_codes, "w13_codes", torch.uint8, (E, 2 * I, d // 2)),
+        _check(w13_scales, "w13_scales", torch.uint8, (E, 2 * I, d // 32)),
+        _check(b13, "b13", torch.float32, (E, 2 * I)),
+        _check(w2_codes, "w2_codes", torch.uint8, (E, d, I // 2)),
+        _check(w2_scales, "w2_scales", torch.uint8, (E, d, I // 32)),
+        _check(b2, "b2", torch.float32, (E, d)),
+    ]
+    return ptrs, T, d, I, E
+
+
+def moe_layer_forward(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
+                      k: int = 4, clamp: float = 7.0, out=None, stream=None):
+    """out = MoE(x) in bf16 [T, d]; see include/moe_mi355x.h."""
+    torch = _torch()
+    ptrs, T, d, I, E = _layer_ptrs(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2)
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.bfloat16, device=x.device)
+    po = _check(out, "out", torch.bfloat16, (T, d))
+    _ok("moe_layer_forward", lib().moe_layer_forward(*ptrs, T, d, I, E, k, clamp, po, _stream(stream)))
+    return out
+
+
+def moe_layer_forward_dbg(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
+                          k: int = 4, clamp: float = 7.0, stream=None):
+    """Returns (out bf16, out_f32, topk_id int32 [T,k], topk_w fp32 [T,k], counts int32 [E])."""
+    torch = _torch()
+    ptrs, T, d, I, E = _layer_ptrs(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2)
+    dev = x.device
+    out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    out_f32 = torch.empty((T, d), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    _ok("moe_layer_forward_dbg", lib().moe_layer_forward_dbg(
+        *ptrs, T, d, I, E, k, clamp, _check(out, "out", torch.bfloat16), _check(out_f32, "out_f32", torch.float32),
+        _check(ids, "ids", torch.int32), _check(w, "w", torch.float32), _check(counts, "counts", torch.int32),
+        _stream(stream)))
+    return out, out_f32, ids, w, counts
+
+
+def moe_route(x, router_w, router_b, k: int = 4, stream=None):
+    """Returns (topk_id int32 [T,k], topk_w fp32 [T,k], counts int32 [E])."""
+    torch = _torch()
+    T, d = x.shape
+    E = router_w.shape[0]
+    px = _check(x, "x", torch.bfloat16, (T, d))
+    pw = _check(router_w, "router_w", torch.bfloat16, (E, d))
+    pb = _check(router_b, "router_b", torch.float32, (E,))
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    counts = torch.empty((E,), dtype=torch.int32, device=x.device)
+    _ok("moe_route", lib().moe_route(px, pw, pb, T, d, E, k, _check(ids, "ids", torch.int32),
+                                     _check(w, "w", torch.float32), _check(counts, "counts", torch.int32),
+                                     _stream(stream)))
+    return ids, w, counts
+
+
+def moe_workspace_bytes(T: int, d: int, I: int, E: int, k: int) -> int:
+    return int(lib().moe_workspace_bytes(T, d, I, E, k))
+
+
+def moe_workspace_init(ws, stream=None) -> None:
+    torch = _torch()
+    _ok("moe_workspace_init", lib().moe_workspace_init(_check(ws, "ws", torch.uint8), ws.numel(), _stream(stream)))
+
+
+def moe_layer_forward_ws(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, ws,
+                         k: int = 4, clamp: float = 7.0, out=None, stream=None):
+    torch = _torch()
+    ptrs, T, d, I, E = _layer_ptrs(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2)
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.bfloat16, device=x.device)
+    po = _check(out, "out", torch.bfloat16, (T, d))
+    pws = _check(ws, "ws", torch.uint8)
+    _ok("moe_layer_forward_ws", lib().moe_layer_forward_ws(*ptrs, T, d, I, E, k, clamp, po, pws, ws.numel(),
+                                                           _stream(stream)))
+    return out
+
+
+def moe_rmsnorm(x, eps: float = 1e-5, out=None, stream=None):
+    torch = _torch()
+    T, d = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _ok("moe_rmsnorm", lib().moe_rmsnorm(_check(x, "x", torch.bfloat16, (T, d)),
+                                         _check(out, "out", torch.bfloat16, (T, d)), T, d, eps, _stream(stream)))
+    return out
+
+
+def moe_stack_forward(x0, layers, k: int = 4, clamp: float = 7.0, eps: float = 1e-5, out=None, stream=None):
+    """layers: list of dicts with router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2."""
+    torch = _torch()
+    T, d = x0.shape
+    n = len(layers)
+    keys = ["router_w", "router_b", "w13_codes", "w13_scales", "b13", "w2_codes", "w2_scales", "b2"]
+    arrays = {kk: (ctypes.c_void_p * n)() for kk in keys}
+    I = E = None
+    for l, L in enumerate(layers):
+        ptrs, _, _, I, E = _layer_ptrs(x0, *[L[kk] for kk in keys])
+        for kk, p in zip(keys, ptrs[1:]):
+            arrays[kk][l] = p.value
+    if out is None:
+        out = torch.empty_like(x0)
+    _ok("moe_stack_forward", lib().moe_stack_forward(
+        _check(x0, "x0", torch.bfloat16, (T, d)), n, *[ctypes.cast(arrays[kk], ctypes.c_void_p) for kk in keys],
+        T, d, I, E, k, clamp, eps, _check(out, "out", torch.bfloat16, (T, d)), _stream(stream)))
+    return out

@@ -1,0 +1,375 @@
+// C ABI of the MoE layer: argument validation, workspace layout and the
+// launch sequence router -> gate/up GEMM -> down GEMM -> combine.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "moe_common.h"
+#include "moe_kernels.h"
+#include "moe_mi355x.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kHeaderInts = 512;  // done counter at [0], expert cursors at [64, 320)
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t topk_id, topk_w, rel_pos, counts, offsets, n_tiles, tiles, expert_rows, xq, hq, y, total;
+  int max_tiles;
+};
+
+int max_tiles_for(int P, int E, int mt) { return (P + mt - 1) / mt + (E < P ? E : P); }
+
+Layout layout(int T, int d, int I, int E, int k) {
+  Layout L;
+  const size_t P = (size_t)T * k;
+  L.max_tiles = max_tiles_for((int)P, E, MT_SMALL);
+  size_t o = up(kHeaderInts * sizeof(int));
+  L.topk_id = o; o = up(o + P * 4);
+  L.topk_w = o; o = up(o + P * 4);
+  L.rel_pos = o; o = up(o + P * 4);
+  L.counts = o; o = up(o + (size_t)E * 4);
+  L.offsets = o; o = up(o + (size_t)(E + 1) * 4);
+  L.n_tiles = o; o = up(o + 4);
+  L.tiles = o; o = up(o + (size_t)L.max_tiles * 8);
+  L.expert_rows = o; o = up(o + (size_t)E * T * 4);
+  L.xq = o; o = up(o + (size_t)T * (d / 32) * MX6_BLOCK_BYTES);
+  L.hq = o; o = up(o + P * (I / 32) * MX6_BLOCK_BYTES);
+  L.y = o; o = up(o + P * d * 4);
+  L.total = o;
+  return L;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_shape(int T, int d, int I, int E, int k) {
+  if (T < 0 || d <= 0 || I <= 0 || (d % 32) || (I % 32)) return MOE_ERR_BAD_SHAPE;
+  if (E < 1 || E > 256 || k < 1 || k > 8 || k > E) return MOE_ERR_BAD_SHAPE;
+  const long long big = (long long)T * (k > E ? k : E);
+  if (big >= (long long)INT_MAX) return MOE_ERR_BAD_SHAPE;
+  if ((long long)d * 2 * I >= (long long)INT_MAX * 16) return MOE_ERR_BAD_SHAPE;
+  return MOE_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_UNSUPPORTED;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_UNSUPPORTED;
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+struct LayerArgs {
+  const void* x; const void* router_w; const float* router_b;
+  const uint8_t* w13c; const uint8_t* w13s; const float* b13;
+  const uint8_t* w2c; const uint8_t* w2s; const float* b2;
+  int T, d, I, E, k; float clamp;
+};
+
+int check_layer(const LayerArgs& a, const void* out) {
+  int st = check_shape(a.T, a.d, a.I, a.E, a.k);
+  if (st) return st;
+  if (!(a.clamp > 0.0f)) return MOE_ERR_BAD_SHAPE;
+  if (a.T == 0) return MOE_OK;  // no-op: nothing is read or written
+  if (!a.x || !a.router_w || !a.router_b || !a.w13c || !a.w13s || !a.b13 || !a.w2c || !a.w2s || !a.b2)
+    return MOE_ERR_NULL_PTR;
+  if (!aligned(a.x, 16) || !aligned(a.router_w, 16) || !aligned(a.w13c, 16) || !aligned(a.w2c, 16) ||
+      !aligned(a.router_b, 4) || !aligned(a.b13, 4) || !aligned(a.b2, 4))
+    return MOE_ERR_MISALIGNED;
+  if (out) {
+    if (!aligned(out, 16)) return MOE_ERR_MISALIGNED;
+    const size_t no = (size_t)a.T * a.d * 2;
+    const size_t E = a.E, d = a.d, I = a.I;
+    if (overlap(out, no, a.x, no) || overlap(out, no, a.router_w, E * d * 2) ||
+        overlap(out, no, a.router_b, E * 4) || overlap(out, no, a.w13c, E * 2 * I * d / 2) ||
+        overlap(out, no, a.w13s, E * 2 * I * d / 32) || overlap(out, no, a.b13, E * 2 * I * 4) ||
+        overlap(out, no, a.w2c, E * d * I / 2) || overlap(out, no, a.w2s, E * d * I / 32) ||
+        overlap(out, no, a.b2, E * d * 4))
+      return MOE_ERR_ALIAS;
+  }
+  return MOE_OK;
+}
+
+// library-owned workspaces, one per device
+struct OwnedWs { void* p = nullptr; size_t n = 0; };
+std::mutex g_mu;
+OwnedWs g_ws[64];
+
+int owned_workspace(size_t need, hipStream_t s, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  OwnedWs& w = g_ws[dev];
+  if (w.n < need) {
+    if (w.p) {
+      if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
+      (void)hipFree(w.p);
+      w.p = nullptr;
+      w.n = 0;
+    }
+    void* p = nullptr;
+    const size_t n = need + need / 8;  // headroom against small growths
+    if (hipMalloc(&p, n) != hipSuccess) {
+      (void)hipGetLastError();
+      return MOE_ERR_NOMEM;
+    }
+    if (launch_zero_ints((int*)p, kHeaderInts, s)) return MOE_ERR_HIP;
+    w.p = p;
+    w.n = n;
+  }
+  *out = w.p;
+  return MOE_OK;
+}
+
+// Enqueues the layer on `s` using workspace `ws` (layout L).  Optional
+// debug outputs replace the workspace copies of the routing results.
+int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float* out_f32,
+              int32_t* topk_id, float* topk_w, int32_t* counts, bool route_only, hipStream_t s,
+              const uint16_t* resid_in = nullptr, uint16_t* resid_out = nullptr,
+              uint16_t* norm_out = nullptr, float eps = 0.f) {
+  const int P = a.T * a.k;
+  const bool small_m = (long long)P <= 16LL * a.E;
+  const int mt = small_m ? MT_SMALL : MT_LARGE;
+  const int max_tiles = max_tiles_for(P, a.E, mt);
+  int* hdr = (int*)ws;
+
+  RouteParams rp;
+  rp.x = (const uint16_t*)a.x;
+  rp.router_w = (const uint16_t*)a.router_w;
+  rp.router_b = a.router_b;
+  rp.T = a.T; rp.d = a.d; rp.E = a.E; rp.k = a.k; rp.mt = mt;
+  rp.topk_id = topk_id ? topk_id : (int*)(ws + L.topk_id);
+  rp.topk_w = topk_w ? topk_w : (float*)(ws + L.topk_w);
+  rp.rel_pos = (int*)(ws + L.rel_pos);
+  rp.expert_rows = (int*)(ws + L.expert_rows);
+  rp.cursor = hdr + 64;
+  rp.done = hdr;
+  rp.counts = counts ? counts : (int*)(ws + L.counts);
+  rp.offsets = (int*)(ws + L.offsets);
+  rp.n_tiles = (int*)(ws + L.n_tiles);
+  rp.tiles = (int2*)(ws + L.tiles);
+  rp.xq = ws + L.xq;
+  if (launch_route(rp, s)) return MOE_ERR_HIP;
+  if (route_only) return MOE_OK;
+
+  GemmParams gp;
+  gp.n_tiles = rp.n_tiles;
+  gp.tiles = rp.tiles;
+  gp.counts = rp.counts;
+  gp.offsets = rp.offsets;
+  gp.expert_rows = rp.expert_rows;
+  gp.T = a.T; gp.k = a.k;
+  gp.a = rp.xq;
+  gp.b_codes = a.w13c; gp.b_scales = a.w13s; gp.bias = a.b13;
+  gp.N = 2 * a.I; gp.K = a.d; gp.I = a.I;
+  gp.clamp = a.clamp;
+  gp.hq = ws + L.hq;
+  gp.y = nullptr;
+  if (launch_gemm_gateup(gp, max_tiles, small_m, s)) return MOE_ERR_HIP;
+
+  gp.a = gp.hq;
+  gp.b_codes = a.w2c; gp.b_scales = a.w2s; gp.bias = a.b2;
+  gp.N = a.d; gp.K = a.I;
+  gp.hq = nullptr;
+  gp.y = (float*)(ws + L.y);
+  if (launch_gemm_down(gp, max_tiles, small_m, s)) return MOE_ERR_HIP;
+
+  CombineParams cp;
+  cp.y = gp.y;
+  cp.topk_id = rp.topk_id;
+  cp.topk_w = rp.topk_w;
+  cp.rel_pos = rp.rel_pos;
+  cp.offsets = rp.offsets;
+  cp.T = a.T; cp.d = a.d; cp.k = a.k;
+  cp.out = (uint16_t*)out;
+  cp.out_f32 = out_f32;
+  cp.resid_in = resid_in;
+  cp.resid_out = resid_out;
+  cp.norm_out = norm_out;
+  cp.eps = eps;
+  if (launch_combine(cp, s)) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_version(void) { return MOE_MI355X_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL_PTR: return "a required pointer is NULL";
+    case MOE_ERR_BAD_SHAPE: return "a size is out of range or inconsistent";
+    case MOE_ERR_UNSUPPORTED: return "the current device is not gfx950";
+    case MOE_ERR_MISALIGNED: return "a pointer breaks the alignment rules";
+    case MOE_ERR_NOMEM: return "workspace allocation failed";
+    case MOE_ERR_HIP: return "a HIP launch or runtime call failed";
+    case MOE_ERR_ALIAS: return "the output overlaps an input";
+    case MOE_ERR_WORKSPACE: return "the workspace is too small";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_bytes(int T, int d, int I, int E, int k) {
+  if (check_shape(T, d, I, E, k)) return 0;
+  return layout(T, d, I, E, k).total;
+}
+
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return MOE_ERR_NULL_PTR;
+  if (!aligned(ws, kAlign)) return MOE_ERR_MISALIGNED;
+  if (ws_bytes < kHeaderInts * sizeof(int)) return MOE_ERR_WORKSPACE;
+  if (int st = check_device()) return st;
+  return launch_zero_ints((int*)ws, kHeaderInts, (hipStream_t)stream) ? MOE_ERR_HIP : MOE_OK;
+}
+
+int moe_layer_forward_ws(const void* x, const void* router_w, const float* router_b,
+                         const uint8_t* w13_codes, const uint8_t* w13_scales, const float* b13,
+                         const uint8_t* w2_codes, const uint8_t* w2_scales, const float* b2, int T, int d,
+                         int I, int E, int k, float clamp, void* out, void* ws, size_t ws_bytes,
+                         void* stream) {
+  LayerArgs a{x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, d, I, E, k, clamp};
+  if (int st = check_layer(a, out)) return st;
+  if (T == 0) return MOE_OK;
+  if (!out || !ws) return MOE_ERR_NULL_PTR;
+  if (!aligned(ws, kAlign)) return MOE_ERR_MISALIGNED;
+  const Layout L = layout(T, d, I, E, k);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (int st = check_device()) return st;
+  return run_layer(a, L, (uint8_t*)ws, out, nullptr, nullptr, nullptr, nullptr, false, (hipStream_t)stream);
+}
+
+int moe_layer_forward(const void* x, const void* router_w, const float* router_b, const uint8_t* w13_codes,
+                      const uint8_t* w13_scales, const float* b13, const uint8_t* w2_codes,
+                      const uint8_t* w2_scales, const float* b2, int T, int d, int I, int E, int k, float clamp,
+                      void* out, void* stream) {
+  LayerArgs a{x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, d, I, E, k, clamp};
+  if (int st = check_layer(a, out)) return st;
+  if (T == 0) return MOE_OK;
+  if (!out) return MOE_ERR_NULL_PTR;
+  if (int st = check_device()) return st;
+  const Layout L = layout(T, d, I, E, k);
+  void* ws = nullptr;
+  if (int st = owned_workspace(L.total, (hipStream_t)stream, &ws)) return st;
+  return run_layer(a, L, (uint8_t*)ws, out, nullptr, nullptr, nullptr, nullptr, false, (hipStream_t)stream);
+}
+
+int moe_layer_forward_dbg(const void* x, const void* router_w, const float* router_b, const uint8_t* w13_codes,
+                          const uint8_t* w13_scales, const float* b13, const uint8_t* w2_codes,
+                          const uint8_t* w2_scales, const float* b2, int T, int d, int I, int E, int k,
+                          float clamp, void* out, float* out_f32, int32_t* topk_id, float* topk_w,
+                          int32_t* counts, void* stream) {
+  LayerArgs a{x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, d, I, E, k, clamp};
+  if (int st = check_layer(a, out)) return st;
+  if (T == 0) return MOE_OK;
+  if (!topk_id || !topk_w || !counts) return MOE_ERR_NULL_PTR;
+  if (!aligned(topk_id, 4) || !aligned(topk_w, 4) || !aligned(counts, 4) || (out_f32 && !aligned(out_f32, 16)))
+    return MOE_ERR_MISALIGNED;
+  if (int st = check_device()) return st;
+  const Layout L = layout(T, d, I, E, k);
+  void* ws = nullptr;
+  if (int st = owned_workspace(L.total, (hipStream_t)stream, &ws)) return st;
+  return run_layer(a, L, (uint8_t*)ws, out, out_f32, topk_id, topk_w, counts, false, (hipStream_t)stream);
+}
+
+int moe_route(const void* x, const void* router_w, const float* router_b, int T, int d, int E, int k,
+              int32_t* topk_id, float* topk_w, int32_t* counts, void* stream) {
+  if (int st = check_shape(T, d, 32, E, k)) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !router_w || !router_b || !topk_id || !topk_w || !counts) return MOE_ERR_NULL_PTR;
+  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(router_b, 4) || !aligned(topk_id, 4) ||
+      !aligned(topk_w, 4) || !aligned(counts, 4))
+    return MOE_ERR_MISALIGNED;
+  if (T == 0) return MOE_OK;
+  if (int st = check_device()) return st;
+  const Layout L = layout(T, d, 32, E, k);
+  void* ws = nullptr;
+  if (int st = owned_workspace(L.total, (hipStream_t)stream, &ws)) return st;
+  LayerArgs a{x, router_w, router_b, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, T, d, 32, E, k, 1.0f};
+  return run_layer(a, L, (uint8_t*)ws, nullptr, nullptr, topk_id, topk_w, counts, true, (hipStream_t)stream);
+}
+
+int moe_rmsnorm(const void* x, void* out, int T, int d, float eps, void* stream) {
+  if (T < 0 || d <= 0 || (d % 32) || !(eps >= 0.0f)) return MOE_ERR_BAD_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !out) return MOE_ERR_NULL_PTR;
+  if (!aligned(x, 16) || !aligned(out, 16)) return MOE_ERR_MISALIGNED;
+  if (T == 0) return MOE_OK;
+  if (int st = check_device()) return st;
+  return launch_rmsnorm((const uint16_t*)x, (uint16_t*)out, T, d, eps, (hipStream_t)stream) ? MOE_ERR_HIP : MOE_OK;
+}
+
+int moe_stack_forward(const void* x0, int n_layers, const void* const* router_w, const float* const* router_b,
+                      const uint8_t* const* w13_codes, const uint8_t* const* w13_scales, const float* const* b13,
+                      const uint8_t* const* w2_codes, const uint8_t* const* w2_scales, const float* const* b2,
+                      int T, int d, int I, int E, int k, float clamp, float eps, void* out, void* stream) {
+  if (n_layers < 1) return MOE_ERR_BAD_SHAPE;
+  if (!x0 || !out || !router_w || !router_b || !w13_codes || !w13_scales || !b13 || !w2_codes || !w2_scales || !b2)
+    return MOE_ERR_NULL_PTR;
+  if (!(eps >= 0.0f)) return MOE_ERR_BAD_SHAPE;
+  for (int l = 0; l < n_layers; ++l) {
+    LayerArgs a{x0, router_w[l], router_b[l], w13_codes[l], w13_scales[l], b13[l], w2_codes[l], w2_scales[l],
+                b2[l], T, d, I, E, k, clamp};
+    if (int st = check_layer(a, out)) return st;
+  }
+  if (T == 0) return MOE_OK;
+  if (int st = check_device()) return st;
+  const Layout L = layout(T, d, I, E, k);
+  const size_t act = up((size_t)T * d * 2);
+  void* wsv = nullptr;
+  if (int st = owned_workspace(L.total + 2 * act, (hipStream_t)stream, &wsv)) return st;
+  uint8_t* ws = (uint8_t*)wsv;
+  uint16_t* norm = (uint16_t*)(ws + L.total);
+  uint16_t* spare = (uint16_t*)(ws + L.total + act);
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_rmsnorm((const uint16_t*)x0, norm, T, d, eps, s)) return MOE_ERR_HIP;
+  // ping-pong the residual stream so that the last layer writes `out`
+  uint16_t* bufs[2] = {(uint16_t*)out, spare};
+  int cur = (n_layers % 2 == 1) ? 0 : 1;
+  const uint16_t* resid = (const uint16_t*)x0;
+  for (int l = 0; l < n_layers; ++l) {
+    LayerArgs a{norm, router_w[l], router_b[l], w13_codes[l], w13_scales[l], b13[l], w2_codes[l], w2_scales[l],
+                b2[l], T, d, I, E, k, clamp};
+    uint16_t* dst = bufs[cur];
+    const bool last = (l == n_layers - 1);
+    if (int st = run_layer(a, L, ws, nullptr, nullptr, nullptr, nullptr, nullptr, false, s, resid, dst,
+                           last ? nullptr : norm, eps))
+      return st;
+    resid = dst;
+    cur ^= 1;
+  }
+  return MOE_OK;
+}
+
+void moe_release(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  for (int dev = 0; dev < 64; ++dev) {
+    OwnedWs& w = g_ws[dev];
+    if (!w.p) continue;
+    (void)hipSetDevice(dev);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(w.p);
+    w.p = nullptr;
+    w.n = 0;
+  }
+  (void)hipSetDevice(cur);
+}
+
+}  // extern "C"

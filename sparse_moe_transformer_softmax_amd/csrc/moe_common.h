@@ -1,0 +1,124 @@
+// Device-side building blocks shared by the MoE kernels (gfx950 / CDNA4).
+//
+// Operand encodings used inside the library:
+//  * MXFP4 weights are consumed raw: E2M1 nibbles (low nibble = even
+//    element) with one E8M0 scale byte per 32 elements, the microscaling
+//    format the gpt-oss pages give for the expert weights ("OpenAI 最新开源
+//    模型 gpt-oss 架构与训练解析", 权重量化 item).
+//  * Activations that feed the block-scaled MFMA (the token rows x of the
+//    gate/up projection and the SwiGLU output h of the down projection) are
+//    stored as "MX6x3" rows: every 32-element block becomes three FP6 (E2M3)
+//    terms, each with its own E8M0 scale, such that the sum of the terms
+//    reproduces the value to about 2^-13 of the block maximum.  One block
+//    occupies 80 bytes: term0 codes [0,24), term1 [24,48), term2 [48,72)
+//    (32 six-bit codes packed little-endian), scale bytes at 72,73,74, zero
+//    padding to 80.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int MX6_BLOCK_BYTES = 80;
+constexpr int MX6_TERMS = 3;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// float -> bf16, round to nearest even (NaN kept quiet)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// E8M0 byte k+127 of the smallest power of two 2^k with 7.5 * 2^k >= amax
+// (7.5 is the largest E2M3 magnitude), so that amax / 2^k never saturates.
+// amax == 0 gives 127.  Non-finite amax gives 0xFF (NaN scale).
+__device__ __forceinline__ int mx6_scale_exp(float amax) {
+  if (!(amax <= 3.0e38f)) return 255;
+  if (amax == 0.0f) return 127;
+  int e;
+  float m = frexpf(amax, &e);  // amax = m * 2^e, m in [0.5, 1)
+  int k = (m <= 0.9375f) ? e - 3 : e - 2;
+  k = k < -127 ? -127 : (k > 127 ? 127 : k);
+  return k + 127;
+}
+
+__device__ __forceinline__ float exp2i(int k) {  // 2^k for k in [-126, 127]
+  return __uint_as_float((uint32_t)(k + 127) << 23);
+}
+
+// Round v (|v| <= 7.5) to the nearest E2M3 value, ties to even; returns the
+// 6-bit code and writes the rounded value.  E2M3: sign, 2 exponent bits
+// (bias 1), 3 mantissa bits; exponent field 0 is subnormal (step 1/8).
+__device__ __forceinline__ uint32_t e2m3_round(float v, float& q) {
+  float a = fabsf(v);
+  float step = a < 2.0f ? 0.125f : (a < 4.0f ? 0.25f : 0.5f);
+  float r = __builtin_rintf(a / step) * step;  // exact: step is a power of two
+  r = fminf(r, 7.5f);
+  uint32_t code;
+  if (r < 1.0f) {
+    code = (uint32_t)(r * 8.0f);                         // e = 0
+  } else if (r < 2.0f) {
+    code = (1u << 3) | (uint32_t)((r - 1.0f) * 8.0f);    // e = 1
+  } else if (r < 4.0f) {
+    code = (2u << 3) | (uint32_t)((r * 0.5f - 1.0f) * 8.0f);
+  } else {
+    code = (3u << 3) | (uint32_t)((r * 0.25f - 1.0f) * 8.0f);
+  }
+  uint32_t s = (__float_as_uint(v) >> 31) & 1u;
+  q = s ? -r : r;
+  return code | (s << 5);
+}
+
+// Pack 32 six-bit codes (one per byte of `c`) little-endian into 6 dwords.
+__device__ __forceinline__ void pack6x32(const uint8_t* c, uint32_t out[6]) {
+#pragma unroll
+  for (int w = 0; w < 6; ++w) out[w] = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int bit = 6 * i;
+    const uint32_t v = c[i] & 63u;
+    out[bit >> 5] |= v << (bit & 31);
+    if ((bit & 31) > 26) out[(bit >> 5) + 1] |= v >> (32 - (bit & 31));
+  }
+}
+
+// Splits one 32-element block (values in registers, v[32]) into three E2M3
+// terms with their own scales.  codes[t][i] gets the 6-bit code of element
+// i of term t; sc[t] the E8M0 byte.
+__device__ __forceinline__ void mx6x3_split(float (&v)[32], uint8_t (&codes)[3][32], int (&sc)[3]) {
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    if (amax != amax) amax = __builtin_inff();
+    int se = mx6_scale_exp(amax);
+    sc[t] = se;
+    if (se == 255) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) codes[t][i] = 0;
+      continue;
+    }
+    const int k = se - 127;
+    // scale by 2^-k in two steps so that neither factor leaves the normal range
+    const float inv_hi = exp2i(-(k >> 1)), inv_lo = exp2i(-(k - (k >> 1)));
+    const float s_hi = exp2i(k >> 1), s_lo = exp2i(k - (k >> 1));
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float q;
+      codes[t][i] = (uint8_t)e2m3_round((v[i] * inv_hi) * inv_lo, q);
+      v[i] -= (q * s_hi) * s_lo;  // exact residual
+    }
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,71 @@
+// Kernel parameter blocks and host-side launchers of the MoE layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouteParams {
+  const uint16_t* x;         // bf16 [T, d]
+  const uint16_t* router_w;  // bf16 [E, d]
+  const float* router_b;     // fp32 [E]
+  int T, d, E, k, mt;        // mt: rows per GEMM tile
+  int* topk_id;              // [T, k]
+  float* topk_w;             // [T, k]
+  int* rel_pos;              // [T, k] row of the pair inside its expert's list
+  int* expert_rows;          // [E, T] pair ids (t*k + j) per expert
+  int* cursor;               // [256] zero between calls
+  int* done;                 // zero between calls
+  int* counts;               // [E]
+  int* offsets;              // [E + 1]
+  int* n_tiles;              // [1]
+  int2* tiles;               // [max_tiles] (expert, first row)
+  uint8_t* xq;               // MX6x3 rows [T, d/32, 80]
+};
+
+struct GemmParams {
+  const int* n_tiles;
+  const int2* tiles;
+  const int* counts;
+  const int* offsets;
+  const int* expert_rows;    // gate/up only: [E, T]
+  int T, k;
+  const uint8_t* a;          // MX6x3 rows: token rows (gate/up) or permuted pair rows (down)
+  const uint8_t* b_codes;    // [E, N, K/2]
+  const uint8_t* b_scales;   // [E, N, K/32]
+  const float* bias;         // [E, N]
+  int N, K, I;
+  float clamp;
+  uint8_t* hq;               // gate/up output: MX6x3 rows [P, I/32, 80]
+  float* y;                  // down output: fp32 [P, N]
+};
+
+struct CombineParams {
+  const float* y;            // [P, d] permuted expert outputs (bias included)
+  const int* topk_id;
+  const float* topk_w;
+  const int* rel_pos;
+  const int* offsets;
+  int T, d, k;
+  uint16_t* out;             // bf16 [T, d] or null
+  float* out_f32;            // fp32 [T, d] or null
+  // residual stack variant (all null otherwise)
+  const uint16_t* resid_in;  // bf16 [T, d]
+  uint16_t* resid_out;       // bf16 [T, d]  = bf16(resid_in + sum)
+  uint16_t* norm_out;        // bf16 [T, d]  = bf16(rmsnorm(resid_out))
+  float eps;
+};
+
+int launch_route(const RouteParams& p, hipStream_t s);
+int launch_gemm_gateup(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s);
+int launch_gemm_down(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s);
+int launch_combine(const CombineParams& p, hipStream_t s);
+int launch_rmsnorm(const uint16_t* x, uint16_t* out, int T, int d, float eps, hipStream_t s);
+int launch_zero_ints(int* p, int n, hipStream_t s);
+
+// rows per GEMM tile of the two configurations
+constexpr int MT_SMALL = 16;
+constexpr int MT_LARGE = 64;
+
+}  // namespace moe
