@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Throughput of the MI355X MoE layer (gpt-oss MoE MLP) on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the whole layer -- router + top-k + softmax, expert
+row lists, gate/up GEMM with the clamped-SwiGLU epilogue, down GEMM, weighted
+combine -- on one batch of synthetic inputs already resident in HBM (for the
+36-layer stack workload, one pass through all layers).  Steps rotate over
+several independently seeded weight sets so that HBM, not the 256 MB
+Infinity Cache, serves the weights.  Prints one JSON line.
+
+Per-kernel durations come from HIP events the library records around each
+kernel on the launch stream (moe_timing_enable); the dominant kernel's
+algorithmic bytes (decode) or FLOPs (prefill) divided by its mean duration
+give the roofline fraction.  The CPU baseline times the fp64 oracle on a
+bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + % roofline (HBM GB/s decode, MFMA TFLOPS prefill)"
+HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+MFMA_FP6_FP4_PEAK = 10.1e15  # MI355X dense FP6/FP4 MFMA, FLOP/s
+KEYS = ["x", "router_w", "router_b", "w13_codes", "w13_scales", "b13", "w2_codes", "w2_scales", "b2"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def mxfp4_bytes(rows: int, cols: int) -> int:
+    return rows * cols // 2 + rows * cols // 32
+
+
+def gen_layer(wl, seed, torch):
+    import numpy as np
+    from sparse_moe_transformer_softmax_amd import synth
+    from sparse_moe_transformer_softmax_amd.workloads import ZIPF_BETA
+    x = synth.gen_x(seed, wl.T, wl.d)
+    wr, br = synth.gen_router(seed, wl.E, wl.d)
+    if wl.routing == "zipf":
+        br = synth.zipf_router_bias(seed, wl.E, ZIPF_BETA)
+    inp = dict(x=x, router_w=wr, router_b=br, **synth.gen_experts(seed, wl.E, wl.d, wl.I))
+    out = {}
+    for k in KEYS:
+        a = np.ascontiguousarray(inp[k])
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 else torch.from_numpy(a)
+        out[k] = t.to("cuda:0")
+    return out, inp
+
+
+def src_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_moe_transformer_softmax_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the summary is missing or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("src_sha") != src_sha():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, inp, budget_s: float):
+    """The fp64 oracle on a bounded sample of the workload's tokens, on this
+    host: the sample doubles until one run takes a quarter of the budget."""
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    n, spent = 1, 0.0
+    while True:
+        t0 = time.perf_counter()
+        O.moe_layer(inp["x"][:n], inp["router_w"], inp["router_b"], inp, wl.k, wl.clamp)
+        spent = time.perf_counter() - t0
+        if spent > budget_s / 4 or n >= wl.T:
+            break
+        n = min(wl.T, 2 * n)
+    tok_s = n / (spent * wl.layers)
+    note = "; stack rate = one layer's rate / 36" if wl.layers > 1 else ""
+    return {"value": tok_s, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"first {n} tokens of weight set 0 through one layer, fp64 numpy oracle, "
+                      f"{spent:.1f} s{note}"}
+
+
+def main():
+    from sparse_moe_transformer_softmax_amd.workloads import WORKLOADS
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="20b_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--sets", type=int, default=0, help="weight sets to rotate over (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 256 MiB device copy first (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the MoE layer here is built and measured on a single MI355X, "
+              f"and no multi-GPU path exists (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import sparse_moe_transformer_softmax_amd as moe
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    moe.lib()
+    wl = WORKLOADS[args.workload]
+    if args.copy_calibration:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    expert_bytes = mxfp4_bytes(2 * wl.I, wl.d) + mxfp4_bytes(wl.d, wl.I) + 4 * (2 * wl.I + wl.d)
+    layer_weight_bytes = wl.E * expert_bytes
+    if args.sets:
+        nsets = args.sets
+    elif wl.layers > 1:
+        nsets = 1
+    else:
+        nsets = max(1, min(4, int(np.ceil(1.1e9 / layer_weight_bytes))))
+    log(f"workload {wl.name}: T={wl.T} d={wl.d} I={wl.I} E={wl.E} k={wl.k} layers={wl.layers} sets={nsets}")
+
+    t0 = time.perf_counter()
+    sets, host0 = [], None
+    nlay = wl.layers
+    for s in range(nsets if nlay == 1 else nlay):
+        g, h = gen_layer(wl, wl.seed + 1000 * s if nlay == 1 else wl.seed + s, torch)
+        sets.append(g)
+        if host0 is None:
+            host0 = h
+        else:
+            del h
+    torch.cuda.synchronize()
+    log(f"inputs generated and uploaded in {time.perf_counter() - t0:.1f} s")
+
+    # routing of every set, for the algorithmic byte and FLOP counts
+    n_sel = []
+    for g in sets:
+        _, _, counts = moe.moe_route(g["x"], g["router_w"], g["router_b"], k=wl.k)
+        n_sel.append(int((counts > 0).sum().item()))
+    P = wl.T * wl.k
+    x_bytes = wl.T * wl.d * 2
+
+    if nlay == 1:
+        def step(i):
+            g = sets[i % nsets]
+            return moe.moe_layer_forward(*[g[k] for k in KEYS], k=wl.k, clamp=wl.clamp, out=outs[i % nsets])
+        outs = [torch.empty((wl.T, wl.d), dtype=torch.bfloat16, device="cuda:0") for _ in range(nsets)]
+        layers_per_step = 1
+    else:
+        x0 = sets[0]["x"]
+        out = torch.empty_like(x0)
+
+        def step(i):
+            return moe.moe_stack_forward(x0, sets, k=wl.k, clamp=wl.clamp, eps=1e-5, out=out)
+        layers_per_step = nlay
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-kernel HIP events recorded by the library
+    moe.moe_timing_read(reset=True)
+    moe.moe_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    moe.moe_timing_enable(False)
+    kt = moe.moe_timing_read(reset=True)
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    tok_s = wl.T / (ms_step * 1e-3)
+    log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (host wall {wall / args.steps * 1e6:.1f} us/step)")
+    for kname, (ms, n) in kt.items():
+        if n:
+            log(f"  {kname:12s} {ms / n * 1e3:9.1f} us/launch  x{n}")
+
+    # algorithmic work
+    if nlay == 1:
+        sel = [n_sel[i % nsets] for i in range(args.steps)]
+        nsel_mean = float(np.mean(sel))
+    else:
+        nsel_mean = float(np.mean(n_sel))
+    layer_bytes = nsel_mean * expert_bytes + wl.E * wl.d * 2 + wl.E * 4 + 2 * x_bytes
+    step_bytes = layer_bytes * layers_per_step
+    step_flops = 2.0 * P * 3 * wl.d * wl.I * layers_per_step
+    gu_ms, gu_n = kt["gateup_gemm"]
+    gu_us = gu_ms / max(gu_n, 1) * 1e3
+    decode_like = (P <= 16 * wl.E)
+    gu_unit_bytes = mxfp4_bytes(2 * wl.I, wl.d) + 4 * 2 * wl.I
+    if decode_like:
+        achieved = (nsel_mean * gu_unit_bytes + x_bytes) / (gu_us * 1e-6)
+        traffic = read_traffic("gateup_gemm", wl.name)
+        roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK, "traffic": traffic, "kernel": "gateup_gemm",
+                "kernel_us": gu_us}
+    else:
+        achieved = (2.0 * P * wl.d * 2 * wl.I) / (gu_us * 1e-6)
+        traffic = read_traffic("gateup_gemm", wl.name)
+        roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": MFMA_FP6_FP4_PEAK / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / MFMA_FP6_FP4_PEAK, "traffic": traffic,
+                "kernel": "gateup_gemm", "kernel_us": gu_us}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, host0, args.cpu_budget)
+        log(f"cpu baseline: {cpu}")
+
+    rec = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "T": wl.T, "d": wl.d, "I": wl.I, "E": wl.E, "k": wl.k, "layers": wl.layers,
+            "routing": wl.routing, "weight_sets": nsets if nlay == 1 else 1,
+            "experts_hit_mean": nsel_mean,
+            "hbm_bytes_per_step": step_bytes, "hbm_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
+            "hbm_frac": step_bytes / (ms_step * 1e-3) / HBM_PEAK,
+            "flops_per_step": step_flops, "TFLOPs": step_flops / (ms_step * 1e-3) / 1e12,
+            "mxfp4_mfma_frac": step_flops / (ms_step * 1e-3) / MFMA_FP6_FP4_PEAK,
+            "kernel_us": {k: (v[0] / v[1] * 1e3 if v[1] else None) for k, v in kt.items()},
+            "parallelism": "single-gpu",
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

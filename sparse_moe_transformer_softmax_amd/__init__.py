@@ -14,6 +14,7 @@ __all__ = [
     "MoeError", "lib", "moe_layer_forward", "moe_layer_forward_dbg", "moe_route",
     "moe_workspace_bytes", "moe_workspace_init", "moe_layer_forward_ws", "moe_rmsnorm",
     "moe_stack_forward", "moe_release", "moe_status_string", "moe_version", "LIB_PATH",
+    "moe_timing_enable", "moe_timing_read", "KERNELS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
@@ -32,6 +33,8 @@ _SIGS = {
     "moe_rmsnorm": (_I, [_P, _P, _I, _I, _F, _P]),
     "moe_stack_forward": (_I, [_P, _I] + [_P] * 8 + [_I] * 5 + [_F, _F, _P, _P]),
     "moe_release": (None, []),
+    "moe_timing_enable": (_I, [_I]),
+    "moe_timing_read": (_I, [_P, _P, _I]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_version": (_I, []),
 }
@@ -68,6 +71,21 @@ def moe_version() -> int:
 
 def moe_release() -> None:
     lib().moe_release()
+
+
+KERNELS = ("route", "gateup_gemm", "down_gemm", "combine", "split_x")
+
+
+def moe_timing_enable(on: bool = True) -> None:
+    _ok("moe_timing_enable", lib().moe_timing_enable(1 if on else 0))
+
+
+def moe_timing_read(reset: bool = True) -> dict:
+    """{kernel: (total_ms, launches)} since the last reset."""
+    ms = (ctypes.c_double * 5)()
+    n = (ctypes.c_int * 5)()
+    _ok("moe_timing_read", lib().moe_timing_read(ctypes.cast(ms, _P), ctypes.cast(n, _P), 1 if reset else 0))
+    return {k: (ms[i], n[i]) for i, k in enumerate(KERNELS)}
 
 
 def _torch():

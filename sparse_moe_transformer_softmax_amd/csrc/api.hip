@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <vector>
 
 #include "moe_common.h"
 #include "moe_kernels.h"
@@ -134,6 +135,36 @@ int owned_workspace(size_t need, hipStream_t s, void** out) {
   return MOE_OK;
 }
 
+// optional per-kernel event timing
+struct Timing {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  struct Rec { int kind; hipEvent_t a, b; };
+  std::vector<Rec> pending;
+  double ms[5] = {0, 0, 0, 0, 0};
+  int n[5] = {0, 0, 0, 0, 0};
+  hipEvent_t get() {
+    if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+} g_t;
+
+struct Timed {
+  int kind; hipStream_t s; hipEvent_t a = nullptr, b = nullptr;
+  Timed(int k, hipStream_t st) : kind(k), s(st) {
+    if (!g_t.on) return;
+    a = g_t.get(); b = g_t.get();
+    if (a && b) (void)hipEventRecord(a, s);
+  }
+  ~Timed() {
+    if (!a || !b) return;
+    (void)hipEventRecord(b, s);
+    g_t.pending.push_back({kind, a, b});
+  }
+};
+
 // Enqueues the layer on `s` using workspace `ws` (layout L).  Optional
 // debug outputs replace the workspace copies of the routing results.
 int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float* out_f32,
@@ -161,9 +192,15 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   rp.offsets = (int*)(ws + L.offsets);
   rp.n_tiles = (int*)(ws + L.n_tiles);
   rp.tiles = (int2*)(ws + L.tiles);
-  rp.xq = ws + L.xq;
-  if (launch_route(rp, s)) return MOE_ERR_HIP;
+  {
+    Timed tm(0, s);
+    if (launch_route(rp, s)) return MOE_ERR_HIP;
+  }
   if (route_only) return MOE_OK;
+  {
+    Timed tm(4, s);
+    if (launch_split_x((const uint16_t*)a.x, ws + L.xq, a.T, a.d, s)) return MOE_ERR_HIP;
+  }
 
   GemmParams gp;
   gp.n_tiles = rp.n_tiles;
@@ -172,20 +209,26 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   gp.offsets = rp.offsets;
   gp.expert_rows = rp.expert_rows;
   gp.T = a.T; gp.k = a.k;
-  gp.a = rp.xq;
+  gp.a = ws + L.xq;
   gp.b_codes = a.w13c; gp.b_scales = a.w13s; gp.bias = a.b13;
   gp.N = 2 * a.I; gp.K = a.d; gp.I = a.I;
   gp.clamp = a.clamp;
   gp.hq = ws + L.hq;
   gp.y = nullptr;
-  if (launch_gemm_gateup(gp, max_tiles, small_m, s)) return MOE_ERR_HIP;
+  {
+    Timed tm(1, s);
+    if (launch_gemm_gateup(gp, max_tiles, small_m, s)) return MOE_ERR_HIP;
+  }
 
   gp.a = gp.hq;
   gp.b_codes = a.w2c; gp.b_scales = a.w2s; gp.bias = a.b2;
   gp.N = a.d; gp.K = a.I;
   gp.hq = nullptr;
   gp.y = (float*)(ws + L.y);
-  if (launch_gemm_down(gp, max_tiles, small_m, s)) return MOE_ERR_HIP;
+  {
+    Timed tm(2, s);
+    if (launch_gemm_down(gp, max_tiles, small_m, s)) return MOE_ERR_HIP;
+  }
 
   CombineParams cp;
   cp.y = gp.y;
@@ -200,7 +243,10 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   cp.resid_out = resid_out;
   cp.norm_out = norm_out;
   cp.eps = eps;
-  if (launch_combine(cp, s)) return MOE_ERR_HIP;
+  {
+    Timed tm(3, s);
+    if (launch_combine(cp, s)) return MOE_ERR_HIP;
+  }
   return MOE_OK;
 }
 
@@ -352,6 +398,29 @@ int moe_stack_forward(const void* x0, int n_layers, const void* const* router_w,
       return st;
     resid = dst;
     cur ^= 1;
+  }
+  return MOE_OK;
+}
+
+int moe_timing_enable(int on) {
+  g_t.on = on != 0;
+  return MOE_OK;
+}
+
+int moe_timing_read(double* ms, int* launches, int reset) {
+  for (auto& r : g_t.pending) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return MOE_ERR_HIP;
+    g_t.ms[r.kind] += t;
+    g_t.n[r.kind] += 1;
+    g_t.pool.push_back(r.a);
+    g_t.pool.push_back(r.b);
+  }
+  g_t.pending.clear();
+  for (int i = 0; i < 5; ++i) {
+    if (ms) ms[i] = g_t.ms[i];
+    if (launches) launches[i] = g_t.n[i];
+    if (reset) { g_t.ms[i] = 0; g_t.n[i] = 0; }
   }
   return MOE_OK;
 }

@@ -72,6 +72,27 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   }
 }
 
+// Plain combine: one thread per float4 column group of one token, so that a
+// small batch still spreads over many workgroups.
+__global__ __launch_bounds__(256) void combine_cols_kernel(CombineParams p) {
+  const int t = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int k = p.k, d = p.d;
+  if (c >= (d >> 2)) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const int pair = t * k + j;
+    const float w = p.topk_w[pair];
+    const float4 v = ((const float4*)(p.y + (size_t)(p.offsets[p.topk_id[pair]] + p.rel_pos[pair]) * d))[c];
+    acc.x = fmaf(w, v.x, acc.x);
+    acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z);
+    acc.w = fmaf(w, v.w, acc.w);
+  }
+  if (p.out_f32) ((float4*)(p.out_f32 + (size_t)t * d))[c] = acc;
+  if (p.out) ((uint2*)(p.out + (size_t)t * d))[c] = pack_bf16x4(acc);
+}
+
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* x, uint16_t* out, int T, int d, float eps) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -98,7 +119,11 @@ __global__ void zero_ints_kernel(int* p, int n) {
 }
 
 int launch_combine(const CombineParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3((p.T + 3) / 4), dim3(256), 0, s, p);
+  if (p.resid_out == nullptr) {
+    hipLaunchKernelGGL(combine_cols_kernel, dim3((p.d / 4 + 255) / 256, p.T), dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(combine_kernel, dim3((p.T + 3) / 4), dim3(256), 0, s, p);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

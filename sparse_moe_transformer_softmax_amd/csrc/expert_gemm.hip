@@ -23,10 +23,26 @@
 // by the router; grid.x walks spans of output columns; each wave owns 16*MB
 // rows and NCB 16-column blocks.  Gate/up waves own matching gate and up
 // columns, so the epilogue has both halves of h in the same lane.
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_kernels.h"
 
 namespace moe {
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1: array indices
+// stay compile-time constants, so register arrays never fall back to
+// private memory.
+template <int I, int N>
+struct StaticFor {
+  template <class F>
+  __device__ __forceinline__ static void run(F&& f) {
+    if constexpr (I < N) {
+      f(std::integral_constant<int, I>{});
+      StaticFor<I + 1, N>::run(f);
+    }
+  }
+};
 
 __device__ __forceinline__ float clamped_swiglu(float g, float u, float c) {
   const float gc = (g != g) ? g : fminf(fmaxf(g, -c), c);
@@ -34,151 +50,185 @@ __device__ __forceinline__ float clamped_swiglu(float g, float u, float c) {
   return gc / (1.0f + expf(-gc)) * (uc + 1.0f);
 }
 
-template <int MB, int NCB, int NW, bool GATEUP>
-__global__ __launch_bounds__(NW * 64) void expert_gemm_kernel(GemmParams p) {
-  constexpr int HALF = NCB / 2;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tile = blockIdx.y;
-  if (tile >= *p.n_tiles) return;
-  const int2 te = p.tiles[tile];
-  const int e = te.x, m0 = te.y;
-  const int rows = min(16 * MB, p.counts[e] - m0);
-  const int row_base = p.offsets[e] + m0;
-  const int K = p.K, N = p.N, I = p.I;
-  const int nblk = K >> 5;
-  const int g = lane >> 4, r = lane & 15;
-  const int unit = blockIdx.x * NW + wave;
+template <int MB, int NCB>
+struct Stage {
+  uint4 a[MB][5];  // MX6x3 block of each 16-row block (3 x 24 B codes, 3 scale bytes)
+  uint4 bc[NCB];   // 32 E2M1 codes of each weight column block
+  int bs[NCB];     // E8M0 scale of each weight column block
+};
 
-  // ---- output columns of this wave ---------------------------------------
-  int col0;  // first gate column (gate/up) or first output column (down)
-  int brow[NCB];
-  bool bok[NCB];
-  if (GATEUP) {
-    col0 = unit * HALF * 16;
-#pragma unroll
-    for (int j = 0; j < HALF; ++j) {
-      bok[j] = bok[HALF + j] = (col0 + 16 * j) < I;
-      brow[j] = col0 + 16 * j + r;
-      brow[HALF + j] = I + col0 + 16 * j + r;
-    }
-  } else {
-    col0 = unit * NCB * 16;
-#pragma unroll
-    for (int j = 0; j < NCB; ++j) {
-      bok[j] = (col0 + 16 * j) < N;
-      brow[j] = col0 + 16 * j + r;
-    }
-  }
-  if (!bok[0]) return;
-
+// Operand addressing of one wave: NCB weight column blocks and MB 16-row
+// blocks of A.  Rows and columns outside the tile read row 0 / column block
+// 0 of the tile (their results are never stored), so every lane always
+// issues the same loads.
+template <int MB, int NCB, bool GATEUP>
+struct WaveOperands {
+  int col0;            // first gate column (gate/up) or output column (down)
+  bool bok[NCB];       // column block exists
   const uint8_t* bcode[NCB];
   const uint8_t* bscale[NCB];
-#pragma unroll
-  for (int j = 0; j < NCB; ++j) {
-    const size_t rr = (size_t)e * N + (bok[j] ? brow[j] : 0);
-    bcode[j] = p.b_codes + rr * (size_t)(K >> 1) + 16 * g;
-    bscale[j] = p.b_scales + rr * (size_t)nblk + g;
-  }
   const uint8_t* arow[MB];
-  bool aok[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int m = 16 * mb + r;
-    aok[mb] = m < rows;
-    size_t ar = 0;
-    if (aok[mb]) {
-      if (GATEUP) ar = (size_t)(p.expert_rows[(size_t)e * p.T + m0 + m] / p.k);
-      else ar = (size_t)(row_base + m);
-    }
-    arow[mb] = p.a + (ar * nblk + g) * MX6_BLOCK_BYTES;
-  }
 
-  v4f acc[MB][NCB];
+  __device__ __forceinline__ bool init(const GemmParams& p, int e, int m0, int rows, int row_base, int unit,
+                                       int r) {
+    constexpr int HALF = NCB / 2;
+    const int K = p.K, N = p.N, I = p.I, nblk = K >> 5;
+    int brow[NCB];
+    if (GATEUP) {
+      col0 = unit * HALF * 16;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int j = 0; j < NCB; ++j) acc[mb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-  const int nchunk = (nblk + 3) >> 2;
-  uint4 A[MB][5], Bc[NCB];
-  int Bs[NCB];
-  auto load = [&](int c, uint4 (&a)[MB][5], uint4 (&bc)[NCB], int (&bs)[NCB]) {
-    const bool inb = (4 * c + g) < nblk;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      if (aok[mb] && inb) {
-        const uint4* src = (const uint4*)(arow[mb] + (size_t)(4 * c) * MX6_BLOCK_BYTES);
-#pragma unroll
-        for (int q = 0; q < 5; ++q) a[mb][q] = src[q];
-      } else {
-#pragma unroll
-        for (int q = 0; q < 5; ++q) a[mb][q] = make_uint4(0, 0, 0, 0);
-        a[mb][4].z = 0x007f7f7fu;
+      for (int j = 0; j < HALF; ++j) {
+        bok[j] = bok[HALF + j] = (col0 + 16 * j) < I;
+        brow[j] = col0 + 16 * j + r;
+        brow[HALF + j] = I + col0 + 16 * j + r;
       }
-    }
-#pragma unroll
-    for (int j = 0; j < NCB; ++j) {
-      if (bok[j] && inb) {
-        bc[j] = *(const uint4*)(bcode[j] + (size_t)(4 * c) * 16);
-        bs[j] = bscale[j][4 * c];
-      } else {
-        bc[j] = make_uint4(0, 0, 0, 0);
-        bs[j] = 127;
-      }
-    }
-  };
-  load(0, A, Bc, Bs);
-  for (int c = 0; c < nchunk; ++c) {
-    uint4 An[MB][5], Bn[NCB];
-    int Bsn[NCB];
-    if (c + 1 < nchunk) load(c + 1, An, Bn, Bsn);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const uint32_t* aw = (const uint32_t*)&A[mb][0];
-      const v8i a0 = {(int)aw[0], (int)aw[1], (int)aw[2], (int)aw[3], (int)aw[4], (int)aw[5], 0, 0};
-      const v8i a1 = {(int)aw[6], (int)aw[7], (int)aw[8], (int)aw[9], (int)aw[10], (int)aw[11], 0, 0};
-      const v8i a2 = {(int)aw[12], (int)aw[13], (int)aw[14], (int)aw[15], (int)aw[16], (int)aw[17], 0, 0};
-      const int sw = (int)aw[18];
-      const int s0 = sw & 0xff, s1 = (sw >> 8) & 0xff, s2 = (sw >> 16) & 0xff;
+    } else {
+      col0 = unit * NCB * 16;
 #pragma unroll
       for (int j = 0; j < NCB; ++j) {
-        const v8i b = {(int)Bc[j].x, (int)Bc[j].y, (int)Bc[j].z, (int)Bc[j].w, 0, 0, 0, 0};
-        acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, b, acc[mb][j], 2, 4, 0, s0, 0, Bs[j]);
-        acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, b, acc[mb][j], 2, 4, 0, s1, 0, Bs[j]);
-        acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a2, b, acc[mb][j], 2, 4, 0, s2, 0, Bs[j]);
+        bok[j] = (col0 + 16 * j) < N;
+        brow[j] = col0 + 16 * j + r;
       }
     }
-    if (c + 1 < nchunk) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int q = 0; q < 5; ++q) A[mb][q] = An[mb][q];
-#pragma unroll
-      for (int j = 0; j < NCB; ++j) { Bc[j] = Bn[j]; Bs[j] = Bsn[j]; }
-    }
-  }
-
-  if (!GATEUP) {
-    // ---- down epilogue: + b2, fp32 rows in permuted order ------------------
+    if (!bok[0]) return false;
 #pragma unroll
     for (int j = 0; j < NCB; ++j) {
-      if (!bok[j]) continue;
-      const int col = col0 + 16 * j + r;
-      const float bias = p.bias[(size_t)e * N + col];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = 16 * mb + 4 * g + q;
-          if (row < rows) p.y[(size_t)(row_base + row) * N + col] = acc[mb][j][q] + bias;
-        }
+      const size_t rr = (size_t)e * N + (bok[j] ? brow[j] : brow[0]);
+      bcode[j] = p.b_codes + rr * (size_t)(K >> 1);
+      bscale[j] = p.b_scales + rr * (size_t)nblk;
     }
-    return;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = (16 * mb + r) < rows ? 16 * mb + r : 0;
+      const size_t ar = GATEUP ? (size_t)(p.expert_rows[(size_t)e * p.T + m0 + m] / p.k) : (size_t)(row_base + m);
+      arow[mb] = p.a + ar * nblk * MX6_BLOCK_BYTES;
+    }
+    return true;
   }
 
-  // ---- gate/up epilogue: + b13, clamped SwiGLU, MX6x3 split of h ----------
-  __shared__ uint8_t s_codes[NW][16][3][32];
-  __shared__ uint32_t s_sc[NW][16];
+  // loads chunk c (K blocks 4c .. 4c+3; lane group g takes block 4c+g,
+  // clamped to the last block)
+  __device__ __forceinline__ void load(int c, int g, int nblk, Stage<MB, NCB>& st) const {
+    const int blk = min(4 * c + g, nblk - 1);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const uint4* src = (const uint4*)(arow[mb] + (size_t)blk * MX6_BLOCK_BYTES);
+#pragma unroll
+      for (int q = 0; q < 5; ++q) st.a[mb][q] = src[q];
+    }
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) {
+      st.bc[j] = *(const uint4*)(bcode[j] + (size_t)blk * 16);
+      st.bs[j] = bscale[j][blk];
+    }
+  }
+};
+
+// One 128-wide K step for every (row block, column block): three MFMAs,
+// one per FP6 term of A.  keep = 0 on lanes whose K block does not take
+// part (past the end of K or outside the wave's share): they contribute
+// zero codes with a unit scale.
+template <int MB, int NCB>
+__device__ __forceinline__ uint32_t keep_mask(bool in) { return in ? 0xffffffffu : 0u; }
+
+template <int MB, int NCB>
+__device__ __forceinline__ void mma_stage(v4f (&acc)[MB][NCB], const Stage<MB, NCB>& st, uint32_t keep) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const uint32_t* aw = (const uint32_t*)&st.a[mb][0];
+    const v8i a0 = {(int)aw[0], (int)aw[1], (int)aw[2], (int)aw[3], (int)aw[4], (int)aw[5], 0, 0};
+    const v8i a1 = {(int)aw[6], (int)aw[7], (int)aw[8], (int)aw[9], (int)aw[10], (int)aw[11], 0, 0};
+    const v8i a2 = {(int)aw[12], (int)aw[13], (int)aw[14], (int)aw[15], (int)aw[16], (int)aw[17], 0, 0};
+    const int sw = (int)aw[18];
+    const int s0 = sw & 0xff, s1 = (sw >> 8) & 0xff, s2 = (sw >> 16) & 0xff;
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) {
+      const v8i b = {(int)(st.bc[j].x & keep), (int)(st.bc[j].y & keep), (int)(st.bc[j].z & keep),
+                     (int)(st.bc[j].w & keep), 0, 0, 0, 0};
+      const int bsc = (int)(((uint32_t)st.bs[j] & keep) | (127u & ~keep));
+      acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, b, acc[mb][j], 2, 4, 0, s0, 0, bsc);
+      acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, b, acc[mb][j], 2, 4, 0, s1, 0, bsc);
+      acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a2, b, acc[mb][j], 2, 4, 0, s2, 0, bsc);
+    }
+  }
+}
+
+// Down epilogue: + b2, fp32 rows in expert-grouped order.
+template <int MB, int NCB>
+__device__ __forceinline__ void epilogue_down(const GemmParams& p, const v4f (&acc)[MB][NCB], const bool (&bok)[NCB],
+                                              int e, int rows, int row_base, int col0, int lane) {
+  const int g = lane >> 4, r = lane & 15, N = p.N;
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) {
+    if (!bok[j]) continue;
+    const int col = col0 + 16 * j + r;
+    const float bias = p.bias[(size_t)e * N + col];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = 16 * mb + 4 * g + q;
+        if (row < rows) p.y[(size_t)(row_base + row) * N + col] = acc[mb][j][q] + bias;
+      }
+  }
+}
+
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Maximum over the 16 lanes of a DPP row (lanes 16g .. 16g+15): rotations
+// by 8, 4, 2, 1 within the row leave every lane holding the row maximum.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false)));
+  return v;
+}
+
+// MX6x3 split of one 32-column block of h held as two values per lane by
+// the 16 lanes of a DPP row (columns r and 16 + r): writes the row's codes
+// to LDS s_codes_row[3][32] and returns the packed scale word.
+__device__ __forceinline__ uint32_t split_h_row(float h0, float h1, int r, uint8_t (*s_codes_row)[32]) {
+  uint32_t scw = 0;
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    float amax = fmaxf(fabsf(h0), fabsf(h1));
+    if (h0 != h0 || h1 != h1) amax = __builtin_inff();
+    amax = row16_max(amax);
+    const int se = mx6_scale_exp(amax);
+    scw |= (uint32_t)se << (8 * t);
+    uint32_t k0 = 0, k1 = 0;
+    if (se != 255) {
+      const int kk = se - 127;
+      const float ih = exp2i(-(kk >> 1)), il = exp2i(-(kk - (kk >> 1)));
+      const float sh = exp2i(kk >> 1), sl = exp2i(kk - (kk >> 1));
+      float q0, q1;
+      k0 = e2m3_round((h0 * ih) * il, q0);
+      k1 = e2m3_round((h1 * ih) * il, q1);
+      h0 -= (q0 * sh) * sl;
+      h1 -= (q1 * sh) * sl;
+    }
+    s_codes_row[t][r] = (uint8_t)k0;
+    s_codes_row[t][16 + r] = (uint8_t)k1;
+  }
+  return scw;
+}
+
+// Gate/up epilogue: + b13, clamped SwiGLU, MX6x3 split of h.  Gate column
+// block j pairs with up column block HALF + j; each 32-column group
+// (blocks 2pp, 2pp+1) is one MX block of h.  The amax of a row's 32 values
+// is reduced over the 16 lanes that hold that row; codes go through the
+// wave's LDS scratch (s_codes[16][3][32], s_sc[16]) to be packed.
+template <int MB, int NCB>
+__device__ __forceinline__ void epilogue_gateup(const GemmParams& p, const v4f (&acc)[MB][NCB],
+                                                const bool (&bok)[NCB], int e, int rows, int row_base, int col0,
+                                                int lane, uint8_t (*s_codes)[3][32], uint32_t* s_sc) {
+  constexpr int HALF = NCB / 2;
+  const int g = lane >> 4, r = lane & 15, N = p.N, I = p.I;
   const int iblocks = I >> 5;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -213,24 +263,20 @@ __global__ __launch_bounds__(NW * 64) void expert_gemm_kernel(GemmParams p) {
             h0 -= (q0 * sh) * sl;
             h1 -= (q1 * sh) * sl;
           }
-          s_codes[wave][row][t][r] = (uint8_t)k0;
-          s_codes[wave][row][t][16 + r] = (uint8_t)k1;
+          s_codes[row][t][r] = (uint8_t)k0;
+          s_codes[row][t][16 + r] = (uint8_t)k1;
         }
-        if (r == 0) s_sc[wave][row] = scw;
+        if (r == 0) s_sc[row] = scw;
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      lds_wave_sync();
       const int blk = (col0 >> 5) + pp;
       if (lane < 48) {
         const int row = lane / 3, t = lane - 3 * (lane / 3);
         if (16 * mb + row < rows) {
-          uint8_t cc[32];
-#pragma unroll
-          for (int i = 0; i < 32; ++i) cc[i] = s_codes[wave][row][t][i];
           uint32_t pk[6];
-          pack6x32(cc, pk);
-          uint2* dst = (uint2*)(p.hq + ((size_t)(row_base + 16 * mb + row) * iblocks + blk) * MX6_BLOCK_BYTES + 24 * t);
+          pack6x32(s_codes[row][t], pk);
+          uint2* dst =
+              (uint2*)(p.hq + ((size_t)(row_base + 16 * mb + row) * iblocks + blk) * MX6_BLOCK_BYTES + 24 * t);
           dst[0] = make_uint2(pk[0], pk[1]);
           dst[1] = make_uint2(pk[2], pk[3]);
           dst[2] = make_uint2(pk[4], pk[5]);
@@ -239,46 +285,320 @@ __global__ __launch_bounds__(NW * 64) void expert_gemm_kernel(GemmParams p) {
         const int row = lane - 48;
         if (16 * mb + row < rows) {
           uint2* dst = (uint2*)(p.hq + ((size_t)(row_base + 16 * mb + row) * iblocks + blk) * MX6_BLOCK_BYTES + 72);
-          dst[0] = make_uint2(s_sc[wave][row], 0u);
+          dst[0] = make_uint2(s_sc[row], 0u);
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      lds_wave_sync();
     }
   }
 }
 
-// configurations: (MB, NCB, NW)
-//   small-M (about 16 rows per expert, decode): one 16-row block per wave,
-//     many narrow column spans so that every CU streams weights;
-//   large-M (prefill): four 16-row blocks per wave.
+// ---------------------------------------------------------------------------
+// Decode ("skinny") kernel: tiles of at most 16 rows.  The KS waves of a
+// workgroup share one set of NCB column blocks and split K between them, so
+// that many waves stream weights concurrently while each keeps a batch of D
+// chunks of loads in flight.  Wave 0 sums the K-slice partials from LDS in
+// a fixed order and runs the epilogue.
+template <int NCB, int KS, int D, bool GATEUP>
+__global__ __launch_bounds__(KS * 64) void expert_gemm_skinny(GemmParams p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tile = blockIdx.y;
+  if (tile >= *p.n_tiles) return;
+  const int2 te = p.tiles[tile];
+  const int e = te.x, m0 = te.y;
+  const int rows = min(16, p.counts[e] - m0);
+  const int row_base = p.offsets[e] + m0;
+  const int nblk = p.K >> 5;
+  const int g = lane >> 4, r = lane & 15;
+  WaveOperands<1, NCB, GATEUP> op;
+  if (!op.init(p, e, m0, rows, row_base, blockIdx.x, r)) return;  // uniform over the workgroup
+
+  v4f acc[1][NCB];
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) acc[0][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  const int nchunk = (nblk + 3) >> 2, nfull = nblk >> 2;
+  const int cbeg = wave * nchunk / KS, cend = (wave + 1) * nchunk / KS;
+  for (int c0 = cbeg; c0 < cend; c0 += D) {
+    Stage<1, NCB> st[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) op.load(min(c0 + i, cend - 1), g, nblk, st[i]);
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+      if (c0 + i < cend) mma_stage(acc, st[i], keep_mask<1, NCB>(4 * (c0 + i) + g < nblk));
+  }
+
+  __shared__ v4f s_acc[KS][NCB][64];
+  __shared__ uint8_t s_codes[16][3][32];
+  __shared__ uint32_t s_sc[16];
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) s_acc[wave][j][lane] = acc[0][j];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) {
+    v4f t = s_acc[0][j][lane];
+#pragma unroll
+    for (int w = 1; w < KS; ++w) t += s_acc[w][j][lane];
+    acc[0][j] = t;
+  }
+  if (GATEUP)
+    epilogue_gateup<1, NCB>(p, acc, op.bok, e, rows, row_base, op.col0, lane, s_codes, s_sc);
+  else
+    epilogue_down<1, NCB>(p, acc, op.bok, e, rows, row_base, op.col0, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel: tiles of at most 16 rows, so the kernel is bound by the
+// weight stream.  A workgroup owns 64 weight rows (gate/up: 32 gate + the
+// matching 32 up rows; down: 64 output rows) and walks K in phases of 32
+// blocks.  Wave w copies the phase's code and scale segments of column
+// block w (16 consecutive weight rows) from HBM straight to LDS with
+// buffer_load ... lds -- no register staging, and every instruction reads
+// 1 KB of lane-consecutive addresses, so whole cache lines are fetched (the
+// scale bytes land one per LDS dword, the layout of byte loads to LDS).
+// Within a row the 32 blocks of a phase are stored XOR-swizzled (logical
+// block b of row j at slot b ^ (j & 15)), so the MFMA operand reads -- 16
+// rows x one block per lane group -- hit distinct LDS banks.  A rows come
+// from the MX6x3 buffer through a buffer resource: lanes of rows past the
+// tile read at an offset beyond the resource, which returns zero without
+// touching memory.  The four waves split each phase's blocks; wave 0 sums
+// their partials in a fixed order and runs the epilogue.  With 36 KB of
+// LDS and at most 128 VGPRs, four workgroups share a CU, so about 136 KB
+// of weights per CU are in flight.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int DEC_KPH = 32;                // K blocks per phase
+constexpr int DEC_NW = 4;                  // waves per workgroup
+constexpr int DEC_WB = DEC_KPH / DEC_NW;   // blocks per wave per phase (8)
+constexpr int DEC_CH = DEC_WB / 4;         // 4-block chunks per wave per phase (2)
+
+template <bool GATEUP>
+__global__ __launch_bounds__(DEC_NW * 64, 3) void expert_gemm_decode(GemmParams p) {
+  constexpr int NCB = 4, NW = DEC_NW;
+  // readfirstlane: the wave index is uniform, so the buffer resources and
+  // LDS bases derived from it live in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = blockIdx.y;
+  if (tile >= *p.n_tiles) return;
+  const int2 te = p.tiles[tile];
+  const int e = te.x, m0 = te.y;
+  const int rows = min(16, p.counts[e] - m0);
+  const int row_base = p.offsets[e] + m0;
+  const int K = p.K, N = p.N, I = p.I, nblk = K >> 5;
+  const int g = lane >> 4, r = lane & 15;
+
+  // columns of the workgroup
+  int col0;
+  bool bok[NCB];
+  if (GATEUP) {
+    col0 = blockIdx.x * 32;
+    bok[0] = bok[2] = col0 < I;
+    bok[1] = bok[3] = col0 + 16 < I;
+  } else {
+    col0 = blockIdx.x * 64;
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) bok[j] = col0 + 16 * j < N;
+  }
+  if (!bok[0]) return;  // uniform over the workgroup
+  // first weight row of this wave's column block (a missing block copies
+  // block 0); its 16 rows are consecutive weight rows
+  size_t my_row;
+  {
+    const int cbv = bok[wave] ? wave : 0;
+    const int n = GATEUP ? (cbv < 2 ? 0 : I) + col0 + 16 * (cbv & 1) : col0 + 16 * cbv;
+    my_row = (size_t)e * N + n;
+  }
+  const __amdgpu_buffer_rsrc_t crsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_codes + my_row * (size_t)(K >> 1)), 0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t srsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_scales + my_row * (size_t)nblk), 0, 0x7fffffff, 0x00020000);
+
+  __shared__ __align__(16) uint8_t s_code[64 * DEC_KPH * 16];
+  __shared__ __align__(16) uint32_t s_scl[64 * DEC_KPH];  // byte loads to LDS land one per dword
+  __shared__ uint8_t s_codes[16][3][32];
+  __shared__ uint32_t s_sc[16];
+
+  // A rows through a buffer resource over the whole MX6x3 buffer (the decode
+  // path keeps it far below 2 GiB); a lane's offset selects row and block
+  const int arow_bytes = nblk * MX6_BLOCK_BYTES;
+  int a_first;
+  {
+    const int m = r < rows ? r : 0;
+    a_first = GATEUP ? p.expert_rows[(size_t)e * p.T + m0 + m] / p.k : row_base + m;
+  }
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.a, 0, 0x7ffffff0, 0x00020000);
+  const bool arow_ok = r < rows;
+
+  v4f acc[1][NCB];
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) acc[0][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  const int half = lane >> 5, slot = lane & 31;
+  const int nph = (nblk + DEC_KPH - 1) / DEC_KPH;
+  for (int ph = 0; ph < nph; ++ph) {
+    const int pb0 = ph * DEC_KPH, npb = min(DEC_KPH, nblk - pb0);
+    // ---- copy: instruction q moves rows 2q, 2q+1 of this wave's block ----
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int rr = 2 * q + half;                 // row within the column block
+      const int b = min(slot ^ rr, npb - 1);       // logical block stored at `slot`
+      const int lds_off = (wave * 16 + 2 * q) * DEC_KPH * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(crsrc, (lds_void_t*)(s_code + lds_off), 16,
+                                               rr * (K >> 1) + (pb0 + b) * 16, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, (lds_void_t*)(s_scl + (wave * 16 + 2 * q) * DEC_KPH), 1,
+                                               rr * nblk + pb0 + min(slot, npb - 1), 0, 0, 0);
+    }
+    uint4 av[DEC_CH][5];
+#pragma unroll
+    for (int c = 0; c < DEC_CH; ++c) {
+      const int blk = pb0 + min(wave * DEC_WB + 4 * c + g, npb - 1);
+      const int off = arow_ok ? a_first * arow_bytes + blk * MX6_BLOCK_BYTES : 0x7ffffff0;
+#pragma unroll
+      for (int q = 0; q < 5; ++q) {
+        const auto t4 = __builtin_amdgcn_raw_buffer_load_b128(arsrc, off + 16 * q, 0, 0);
+        av[c][q] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
+      }
+    }
+    // the copies write LDS behind the compiler's back: wait for all of this
+    // wave's loads before the barrier publishes the phase to the other waves
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt not waited on
+    __syncthreads();
+    // ---- MFMA over this wave's blocks ----
+#pragma unroll
+    for (int c = 0; c < DEC_CH; ++c) {
+      const int bl = wave * DEC_WB + 4 * c + g;  // logical block within the phase
+      Stage<1, NCB> st;
+#pragma unroll
+      for (int q = 0; q < 5; ++q) st.a[0][q] = av[c][q];
+#pragma unroll
+      for (int j = 0; j < NCB; ++j) {
+        const int jj = 16 * j + r;
+        st.bc[j] = *(const uint4*)(s_code + (jj * DEC_KPH + (bl ^ r)) * 16);
+        st.bs[j] = (int)(s_scl[jj * DEC_KPH + bl] & 0xffu);
+      }
+      mma_stage(acc, st, keep_mask<1, NCB>(bl < npb));
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: wave w takes accumulator element w, i.e. tile rows
+  // 4g + w; it sums the four waves' partials in a fixed order ----
+  float* s_acc = (float*)s_code;  // [NW][NCB][4][64], reuses the code buffer
+#pragma unroll
+  for (int j = 0; j < NCB; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s_acc[((wave * NCB + j) * 4 + q) * 64 + lane] = acc[0][j][q];
+  __syncthreads();
+  float v[NCB];
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) {
+    float t = s_acc[((0 * NCB + j) * 4 + wave) * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) t += s_acc[((w * NCB + j) * 4 + wave) * 64 + lane];
+    v[j] = t;
+  }
+  const int row = 4 * g + wave;  // tile row of this lane's values
+  if (!GATEUP) {
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) {
+      if (!bok[j]) continue;
+      const int col = col0 + 16 * j + r;
+      if (row < rows) p.y[(size_t)(row_base + row) * N + col] = v[j] + p.bias[(size_t)e * N + col];
+    }
+    return;
+  }
+  const int c0 = col0 + r;
+  const float h0 = clamped_swiglu(v[0] + p.bias[(size_t)e * N + c0], v[2] + p.bias[(size_t)e * N + I + c0], p.clamp);
+  const float h1 = clamped_swiglu(v[1] + p.bias[(size_t)e * N + c0 + 16], v[3] + p.bias[(size_t)e * N + I + c0 + 16],
+                                  p.clamp);
+  const uint32_t scw = split_h_row(h0, h1, r, s_codes[row]);
+  if (r == 0) s_sc[row] = scw;
+  lds_wave_sync();
+  const int blk = col0 >> 5;
+  if (lane < 12) {
+    const int rw = 4 * (lane / 3) + wave, t = lane % 3;
+    if (rw < rows) {
+      uint32_t pk[6];
+      pack6x32(s_codes[rw][t], pk);
+      uint2* dst = (uint2*)(p.hq + ((size_t)(row_base + rw) * (I >> 5) + blk) * MX6_BLOCK_BYTES + 24 * t);
+      dst[0] = make_uint2(pk[0], pk[1]);
+      dst[1] = make_uint2(pk[2], pk[3]);
+      dst[2] = make_uint2(pk[4], pk[5]);
+    }
+  } else if (lane < 16) {
+    const int rw = 4 * (lane - 12) + wave;
+    if (rw < rows) {
+      uint2* dst = (uint2*)(p.hq + ((size_t)(row_base + rw) * (I >> 5) + blk) * MX6_BLOCK_BYTES + 72);
+      dst[0] = make_uint2(s_sc[rw], 0u);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// General kernel (tiles of 16*MB rows): each of the NW waves owns NCB column
+// blocks over the whole K range.
+template <int MB, int NCB, int NW, int D, bool GATEUP>
+__global__ __launch_bounds__(NW * 64) void expert_gemm_kernel(GemmParams p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tile = blockIdx.y;
+  if (tile >= *p.n_tiles) return;
+  const int2 te = p.tiles[tile];
+  const int e = te.x, m0 = te.y;
+  const int rows = min(16 * MB, p.counts[e] - m0);
+  const int row_base = p.offsets[e] + m0;
+  const int nblk = p.K >> 5;
+  const int g = lane >> 4, r = lane & 15;
+  WaveOperands<MB, NCB, GATEUP> op;
+  if (!op.init(p, e, m0, rows, row_base, blockIdx.x * NW + wave, r)) return;
+
+  v4f acc[MB][NCB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) acc[mb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  const int nchunk = (nblk + 3) >> 2, nfull = nblk >> 2;
+  for (int c0 = 0; c0 < nchunk; c0 += D) {
+    Stage<MB, NCB> st[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) op.load(min(c0 + i, nchunk - 1), g, nblk, st[i]);
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+      if (c0 + i < nchunk) mma_stage(acc, st[i], keep_mask<MB, NCB>(4 * (c0 + i) + g < nblk));
+  }
+  __shared__ uint8_t s_codes[NW][16][3][32];
+  __shared__ uint32_t s_sc[NW][16];
+  if (GATEUP)
+    epilogue_gateup<MB, NCB>(p, acc, op.bok, e, rows, row_base, op.col0, lane, s_codes[wave], s_sc[wave]);
+  else
+    epilogue_down<MB, NCB>(p, acc, op.bok, e, rows, row_base, op.col0, lane);
+}
+
+// Launch configurations.
+//   small-M (tiles of 16 rows, decode): skinny kernel, 4 waves split K over
+//     one 64-column span (gate/up: 32 gate + 32 up columns);
+//   large-M (prefill): four 16-row blocks per wave, four waves per span.
 int launch_gemm_gateup(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s) {
   if (small_m) {
-    constexpr int MB = 1, NCB = 4, NW = 3;
-    const int span = NW * (NCB / 2) * 16;
-    dim3 grid((p.I + span - 1) / span, max_tiles);
-    hipLaunchKernelGGL((expert_gemm_kernel<MB, NCB, NW, true>), grid, dim3(NW * 64), 0, s, p);
+    dim3 grid((p.I + 31) / 32, max_tiles);
+    hipLaunchKernelGGL((expert_gemm_decode<true>), grid, dim3(DEC_NW * 64), 0, s, p);
   } else {
-    constexpr int MB = 4, NCB = 4, NW = 4;
+    constexpr int MB = 4, NCB = 4, NW = 4, D = 2;
     const int span = NW * (NCB / 2) * 16;
     dim3 grid((p.I + span - 1) / span, max_tiles);
-    hipLaunchKernelGGL((expert_gemm_kernel<MB, NCB, NW, true>), grid, dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((expert_gemm_kernel<MB, NCB, NW, D, true>), grid, dim3(NW * 64), 0, s, p);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_gemm_down(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s) {
   if (small_m) {
-    constexpr int MB = 1, NCB = 2, NW = 3;
-    const int span = NW * NCB * 16;
-    dim3 grid((p.N + span - 1) / span, max_tiles);
-    hipLaunchKernelGGL((expert_gemm_kernel<MB, NCB, NW, false>), grid, dim3(NW * 64), 0, s, p);
+    dim3 grid((p.N + 63) / 64, max_tiles);
+    hipLaunchKernelGGL((expert_gemm_decode<false>), grid, dim3(DEC_NW * 64), 0, s, p);
   } else {
-    constexpr int MB = 4, NCB = 4, NW = 4;
+    constexpr int MB = 4, NCB = 4, NW = 4, D = 2;
     const int span = NW * NCB * 16;
     dim3 grid((p.N + span - 1) / span, max_tiles);
-    hipLaunchKernelGGL((expert_gemm_kernel<MB, NCB, NW, false>), grid, dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((expert_gemm_kernel<MB, NCB, NW, D, false>), grid, dim3(NW * 64), 0, s, p);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

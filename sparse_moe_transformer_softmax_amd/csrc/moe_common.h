@@ -22,6 +22,7 @@ namespace moe {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr int MX6_BLOCK_BYTES = 80;
 constexpr int MX6_TERMS = 3;
@@ -44,9 +45,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 __device__ __forceinline__ int mx6_scale_exp(float amax) {
   if (!(amax <= 3.0e38f)) return 255;
   if (amax == 0.0f) return 127;
-  int e;
-  float m = frexpf(amax, &e);  // amax = m * 2^e, m in [0.5, 1)
-  int k = (m <= 0.9375f) ? e - 3 : e - 2;
+  const uint32_t bits = __float_as_uint(amax);
+  const int ex = (int)((bits >> 23) & 0xffu);
+  if (ex == 0) return 0;  // subnormal amax: 2^-127 * 7.5 covers it
+  // amax = 1.m * 2^(ex-127) and 7.5 = 1.875 * 2^2: k = ex - 129 when
+  // 1.m <= 1.875 (mantissa field <= 0x700000), else ex - 128
+  int k = ((bits & 0x7fffffu) <= 0x700000u) ? ex - 129 : ex - 128;
   k = k < -127 ? -127 : (k > 127 ? 127 : k);
   return k + 127;
 }
@@ -57,23 +61,19 @@ __device__ __forceinline__ float exp2i(int k) {  // 2^k for k in [-126, 127]
 
 // Round v (|v| <= 7.5) to the nearest E2M3 value, ties to even; returns the
 // 6-bit code and writes the rounded value.  E2M3: sign, 2 exponent bits
-// (bias 1), 3 mantissa bits; exponent field 0 is subnormal (step 1/8).
+// (bias 1), 3 mantissa bits; exponent field 0 is subnormal.  The grid step
+// is 1/8 on [0, 2), 1/4 on [2, 4), 1/2 on [4, 7.5]; with n the rounded
+// multiple of the step, the code is n, n + 8 and n + 16 on the three ranges.
 __device__ __forceinline__ uint32_t e2m3_round(float v, float& q) {
-  float a = fabsf(v);
-  float step = a < 2.0f ? 0.125f : (a < 4.0f ? 0.25f : 0.5f);
-  float r = __builtin_rintf(a / step) * step;  // exact: step is a power of two
-  r = fminf(r, 7.5f);
-  uint32_t code;
-  if (r < 1.0f) {
-    code = (uint32_t)(r * 8.0f);                         // e = 0
-  } else if (r < 2.0f) {
-    code = (1u << 3) | (uint32_t)((r - 1.0f) * 8.0f);    // e = 1
-  } else if (r < 4.0f) {
-    code = (2u << 3) | (uint32_t)((r * 0.5f - 1.0f) * 8.0f);
-  } else {
-    code = (3u << 3) | (uint32_t)((r * 0.25f - 1.0f) * 8.0f);
-  }
-  uint32_t s = (__float_as_uint(v) >> 31) & 1u;
+  const float a = fabsf(v);
+  const bool lo = a < 2.0f, mid = a < 4.0f;
+  const float inv = lo ? 8.0f : (mid ? 4.0f : 2.0f);
+  const float step = lo ? 0.125f : (mid ? 0.25f : 0.5f);
+  float n = __builtin_rintf(a * inv);  // exact scaling by a power of two
+  n = fminf(n, lo ? 16.0f : (mid ? 16.0f : 15.0f));
+  const float r = n * step;
+  const uint32_t code = (uint32_t)n + (lo ? 0u : (mid ? 8u : 16u));
+  const uint32_t s = (__float_as_uint(v) >> 31) & 1u;
   q = s ? -r : r;
   return code | (s << 5);
 }
@@ -92,22 +92,22 @@ __device__ __forceinline__ void pack6x32(const uint8_t* c, uint32_t out[6]) {
 }
 
 // Splits one 32-element block (values in registers, v[32]) into three E2M3
-// terms with their own scales.  codes[t][i] gets the 6-bit code of element
-// i of term t; sc[t] the E8M0 byte.
-__device__ __forceinline__ void mx6x3_split(float (&v)[32], uint8_t (&codes)[3][32], int (&sc)[3]) {
+// terms with their own scales: pk[t] receives the 32 six-bit codes of term t
+// packed little-endian, sc[t] its E8M0 byte.  On return v holds the residual.
+__device__ __forceinline__ void mx6x3_split(float (&v)[32], uint32_t (&pk)[3][6], int (&sc)[3]) {
 #pragma unroll
   for (int t = 0; t < 3; ++t) {
+#pragma unroll
+    for (int w = 0; w < 6; ++w) pk[t][w] = 0;
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    if (amax != amax) amax = __builtin_inff();
-    int se = mx6_scale_exp(amax);
-    sc[t] = se;
-    if (se == 255) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) codes[t][i] = 0;
-      continue;
-    }
+    for (int i = 0; i < 32; ++i)
+      if (v[i] != v[i]) amax = __builtin_inff();
+    const int se = mx6_scale_exp(amax);
+    sc[t] = se;
+    if (se == 255) continue;
     const int k = se - 127;
     // scale by 2^-k in two steps so that neither factor leaves the normal range
     const float inv_hi = exp2i(-(k >> 1)), inv_lo = exp2i(-(k - (k >> 1)));
@@ -115,8 +115,49 @@ __device__ __forceinline__ void mx6x3_split(float (&v)[32], uint8_t (&codes)[3][
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       float q;
-      codes[t][i] = (uint8_t)e2m3_round((v[i] * inv_hi) * inv_lo, q);
+      const uint32_t c = e2m3_round((v[i] * inv_hi) * inv_lo, q);
       v[i] -= (q * s_hi) * s_lo;  // exact residual
+      const int bit = 6 * i;
+      pk[t][bit >> 5] |= c << (bit & 31);
+      if ((bit & 31) > 26) pk[t][(bit >> 5) + 1] |= c >> (32 - (bit & 31));
+    }
+  }
+}
+
+// Four-lane form of mx6x3_split: the 32 elements of a block live in four
+// lanes whose ids differ by X1 and X2 (lane group q holds elements
+// 8q .. 8q+7).  The block
+// maximum of every term is reduced across the four lanes; each lane returns
+// the 48 bits of its 8 codes per term (bits[t] low 48 bits = elements
+// 8q..8q+7 of term t, 6 bits each, little-endian), to be stored at byte
+// 6q of that term's 24-byte code field.
+template <int X1 = 1, int X2 = 2>
+__device__ __forceinline__ void mx6x3_split_quad(float (&v)[8], uint64_t (&bits)[3], int (&sc)[3]) {
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    bits[t] = 0;
+    float amax = 0.0f;
+    bool nan = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      amax = fmaxf(amax, fabsf(v[i]));
+      nan |= (v[i] != v[i]);
+    }
+    if (nan) amax = __builtin_inff();
+    amax = fmaxf(amax, __shfl_xor(amax, X1));
+    amax = fmaxf(amax, __shfl_xor(amax, X2));
+    const int se = mx6_scale_exp(amax);
+    sc[t] = se;
+    if (se == 255) continue;
+    const int k = se - 127;
+    const float inv_hi = exp2i(-(k >> 1)), inv_lo = exp2i(-(k - (k >> 1)));
+    const float s_hi = exp2i(k >> 1), s_lo = exp2i(k - (k >> 1));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float q;
+      const uint32_t c = e2m3_round((v[i] * inv_hi) * inv_lo, q);
+      v[i] -= (q * s_hi) * s_lo;  // exact residual
+      bits[t] |= (uint64_t)c << (6 * i);
     }
   }
 }

@@ -21,7 +21,6 @@ struct RouteParams {
   int* offsets;              // [E + 1]
   int* n_tiles;              // [1]
   int2* tiles;               // [max_tiles] (expert, first row)
-  uint8_t* xq;               // MX6x3 rows [T, d/32, 80]
 };
 
 struct GemmParams {
@@ -58,6 +57,7 @@ struct CombineParams {
 };
 
 int launch_route(const RouteParams& p, hipStream_t s);
+int launch_split_x(const uint16_t* x, uint8_t* xq, int T, int d, hipStream_t s);
 int launch_gemm_gateup(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s);
 int launch_gemm_down(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s);
 int launch_combine(const CombineParams& p, hipStream_t s);
