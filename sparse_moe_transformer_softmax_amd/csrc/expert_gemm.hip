@@ -367,10 +367,20 @@ __global__ __launch_bounds__(KS * 64) void expert_gemm_skinny(GemmParams p) {
 // of weights per CU are in flight.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int DEC_KPH = 32;                // K blocks per phase
+constexpr int DEC_KPH = 16;                // K blocks per phase
 constexpr int DEC_NW = 4;                  // waves per workgroup
-constexpr int DEC_WB = DEC_KPH / DEC_NW;   // blocks per wave per phase (8)
-constexpr int DEC_CH = DEC_WB / 4;         // 4-block chunks per wave per phase (2)
+constexpr int DEC_Q = DEC_KPH / 4;         // copy instructions per wave per phase (codes; same for scales)
+constexpr int DEC_WB = DEC_KPH / DEC_NW;   // blocks per wave per phase (4 = one chunk)
+constexpr int DEC_VM = 2 * DEC_Q + 5;      // vector-memory instructions per wave per phase
+static_assert(DEC_WB == 4, "one 4-block chunk per wave per phase");
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt[3:0] bits 3:0, vmcnt[5:4] bits
+// 15:14; expcnt and lgkmcnt left at their maxima, i.e. not waited on)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 template <bool GATEUP>
 __global__ __launch_bounds__(DEC_NW * 64, 3) void expert_gemm_decode(GemmParams p) {
@@ -413,8 +423,9 @@ __global__ __launch_bounds__(DEC_NW * 64, 3) void expert_gemm_decode(GemmParams 
   const __amdgpu_buffer_rsrc_t srsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_scales + my_row * (size_t)nblk), 0, 0x7fffffff, 0x00020000);
 
-  __shared__ __align__(16) uint8_t s_code[64 * DEC_KPH * 16];
-  __shared__ __align__(16) uint32_t s_scl[64 * DEC_KPH];  // byte loads to LDS land one per dword
+  // two phase buffers: codes [64 rows][16 slots][16 B], scales one per dword
+  __shared__ __align__(16) uint8_t s_code[2][64 * DEC_KPH * 16];
+  __shared__ __align__(16) uint32_t s_scl[2][64 * DEC_KPH];
   __shared__ uint8_t s_codes[16][3][32];
   __shared__ uint32_t s_sc[16];
 
@@ -433,57 +444,104 @@ __global__ __launch_bounds__(DEC_NW * 64, 3) void expert_gemm_decode(GemmParams 
 #pragma unroll
   for (int j = 0; j < NCB; ++j) acc[0][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  const int half = lane >> 5, slot = lane & 31;
-  const int nph = (nblk + DEC_KPH - 1) / DEC_KPH;
-  for (int ph = 0; ph < nph; ++ph) {
+  // issue every load of phase ph: this wave's column block into LDS buffer
+  // `buf` (instruction q moves rows 4q .. 4q+3), this wave's A block into av
+  const int sub = lane / DEC_KPH, slot = lane % DEC_KPH;
+  auto issue = [&](int ph, int buf, uint4 (&av)[5]) {
     const int pb0 = ph * DEC_KPH, npb = min(DEC_KPH, nblk - pb0);
-    // ---- copy: instruction q moves rows 2q, 2q+1 of this wave's block ----
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int rr = 2 * q + half;                 // row within the column block
+    for (int q = 0; q < DEC_Q; ++q) {
+      const int rr = 4 * q + sub;                  // row within the column block
       const int b = min(slot ^ rr, npb - 1);       // logical block stored at `slot`
-      const int lds_off = (wave * 16 + 2 * q) * DEC_KPH * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(crsrc, (lds_void_t*)(s_code + lds_off), 16,
+      const int row_off = (wave * 16 + 4 * q) * DEC_KPH;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(crsrc, (lds_void_t*)(s_code[buf] + row_off * 16), 16,
                                                rr * (K >> 1) + (pb0 + b) * 16, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, (lds_void_t*)(s_scl + (wave * 16 + 2 * q) * DEC_KPH), 1,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, (lds_void_t*)(s_scl[buf] + row_off), 1,
                                                rr * nblk + pb0 + min(slot, npb - 1), 0, 0, 0);
     }
-    uint4 av[DEC_CH][5];
+    const int blk = pb0 + min(wave * DEC_WB + g, npb - 1);
+    const int off = arow_ok ? a_first * arow_bytes + blk * MX6_BLOCK_BYTES : 0x7ffffff0;
 #pragma unroll
-    for (int c = 0; c < DEC_CH; ++c) {
-      const int blk = pb0 + min(wave * DEC_WB + 4 * c + g, npb - 1);
-      const int off = arow_ok ? a_first * arow_bytes + blk * MX6_BLOCK_BYTES : 0x7ffffff0;
-#pragma unroll
-      for (int q = 0; q < 5; ++q) {
-        const auto t4 = __builtin_amdgcn_raw_buffer_load_b128(arsrc, off + 16 * q, 0, 0);
-        av[c][q] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
-      }
+    for (int q = 0; q < 5; ++q) {
+      const auto t4 = __builtin_amdgcn_raw_buffer_load_b128(arsrc, off + 16 * q, 0, 0);
+      av[q] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
     }
-    // the copies write LDS behind the compiler's back: wait for all of this
-    // wave's loads before the barrier publishes the phase to the other waves
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt not waited on
-    __syncthreads();
-    // ---- MFMA over this wave's blocks ----
+  };
+  auto consume = [&](int ph, int buf, const uint4 (&av)[5]) {
+    const int npb = min(DEC_KPH, nblk - ph * DEC_KPH);
+    const int bl = wave * DEC_WB + g;  // logical block within the phase
+    Stage<1, NCB> st;
 #pragma unroll
-    for (int c = 0; c < DEC_CH; ++c) {
-      const int bl = wave * DEC_WB + 4 * c + g;  // logical block within the phase
-      Stage<1, NCB> st;
-#pragma unroll
-      for (int q = 0; q < 5; ++q) st.a[0][q] = av[c][q];
-#pragma unroll
-      for (int j = 0; j < NCB; ++j) {
-        const int jj = 16 * j + r;
-        st.bc[j] = *(const uint4*)(s_code + (jj * DEC_KPH + (bl ^ r)) * 16);
-        st.bs[j] = (int)(s_scl[jj * DEC_KPH + bl] & 0xffu);
-      }
-      mma_stage(acc, st, keep_mask<1, NCB>(bl < npb));
+    for (int q = 0; q < 5; ++q) st.a[0][q] = av[q];
+    // The LDS reads are written as one asm block that waits for its own
+    // results: the compiler cannot tell the two phase buffers apart, and
+    // would otherwise wait for every copy in flight (the next phase's too)
+    // before reading.  The barriers and explicit vmcnt waits order them.
+    const uint32_t cb_addr = (uint32_t)(uintptr_t)(s_code[buf]) + (uint32_t)((r * DEC_KPH + (bl ^ r)) * 16);
+    const uint32_t sb_addr = (uint32_t)(uintptr_t)(s_scl[buf]) + (uint32_t)((r * DEC_KPH + bl) * 4);
+    v4u b0, b1, b2, b3;
+    uint32_t s0, s1, s2, s3;
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:%10\n\t"
+        "ds_read_b128 %2, %8 offset:%11\n\t"
+        "ds_read_b128 %3, %8 offset:%12\n\t"
+        "ds_read_b32 %4, %9\n\t"
+        "ds_read_b32 %5, %9 offset:%13\n\t"
+        "ds_read_b32 %6, %9 offset:%14\n\t"
+        "ds_read_b32 %7, %9 offset:%15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
+        : "v"(cb_addr), "v"(sb_addr), "i"(16 * DEC_KPH * 16), "i"(32 * DEC_KPH * 16), "i"(48 * DEC_KPH * 16),
+          "i"(16 * DEC_KPH * 4), "i"(32 * DEC_KPH * 4), "i"(48 * DEC_KPH * 4));
+    st.bc[0] = make_uint4(b0.x, b0.y, b0.z, b0.w);
+    st.bc[1] = make_uint4(b1.x, b1.y, b1.z, b1.w);
+    st.bc[2] = make_uint4(b2.x, b2.y, b2.z, b2.w);
+    st.bc[3] = make_uint4(b3.x, b3.y, b3.z, b3.w);
+    st.bs[0] = (int)(s0 & 0xffu);
+    st.bs[1] = (int)(s1 & 0xffu);
+    st.bs[2] = (int)(s2 & 0xffu);
+    st.bs[3] = (int)(s3 & 0xffu);
+    mma_stage(acc, st, keep_mask<1, NCB>(bl < npb));
+  };
+
+  // double-buffered phases: the loads of phase ph+1 are in flight while
+  // phase ph is consumed.  The copies write LDS behind the compiler's back,
+  // so each wave waits explicitly (vmcnt counts in issue order) for its own
+  // loads of phase ph, then a bare s_barrier publishes the phase: a
+  // __syncthreads() would make the compiler drain every copy in flight,
+  // the next phase's included.  The second barrier keeps a buffer from
+  // being refilled while another wave still reads it (the asm reads above
+  // complete before their wave reaches it).
+  const int nph = (nblk + DEC_KPH - 1) / DEC_KPH;
+  uint4 av0[5], av1[5];
+  issue(0, 0, av0);
+  for (int ph = 0; ph < nph; ph += 2) {
+    if (ph + 1 < nph) {
+      issue(ph + 1, 1, av1);
+      wait_vmcnt<DEC_VM>();
+    } else {
+      wait_vmcnt<0>();
     }
-    __syncthreads();
+    __builtin_amdgcn_s_barrier();
+    consume(ph, 0, av0);
+    __builtin_amdgcn_s_barrier();
+    if (ph + 1 >= nph) break;
+    if (ph + 2 < nph) {
+      issue(ph + 2, 0, av0);
+      wait_vmcnt<DEC_VM>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    consume(ph + 1, 1, av1);
+    __builtin_amdgcn_s_barrier();
   }
+  wait_vmcnt<0>();
 
   // ---- epilogue: wave w takes accumulator element w, i.e. tile rows
   // 4g + w; it sums the four waves' partials in a fixed order ----
-  float* s_acc = (float*)s_code;  // [NW][NCB][4][64], reuses the code buffer
+  float* s_acc = (float*)s_code[0];  // [NW][NCB][4][64], reuses the code buffers
 #pragma unroll
   for (int j = 0; j < NCB; ++j)
 #pragma unroll
@@ -535,6 +593,194 @@ __global__ __launch_bounds__(DEC_NW * 64, 3) void expert_gemm_decode(GemmParams 
 }
 
 // ---------------------------------------------------------------------------
+// Prefill kernel: tiles of PF_MT = 128 rows.  A workgroup of four waves
+// computes a 128-row x (16*NCB)-column output tile; wave w owns rows
+// 32w .. 32w+31 (two 16-row blocks) and all NCB column blocks, so its
+// accumulators (2 x NCB 16x16 tiles) sit in the register file and every B
+// fragment read from LDS feeds six MFMAs.  K advances in chunks of four
+// 32-element blocks through two LDS buffers: the global loads of chunk c+1
+// are issued into registers before chunk c is consumed and written to the
+// other buffer afterwards, one barrier per chunk.  A rows are padded to 336
+// bytes in LDS and B rows are stored with their four 16-byte pieces
+// XOR-swizzled by (row >> 2) & 3, so the operand reads are free of LDS bank
+// conflicts.
+constexpr int PF_MT = 128;                  // rows per tile
+constexpr int PF_NWM = 4;                   // waves (each 32 rows)
+constexpr int PF_ARS = 336;                 // LDS row stride of A (4 blocks x 80 B + 16 B pad)
+
+template <bool GATEUP, int NCB>
+struct PfShared {
+  uint8_t a[2][PF_MT * PF_ARS];
+  uint8_t b[2][NCB * 16 * 64];
+  uint8_t bs[2][NCB * 16 * 4];
+  uint8_t codes[PF_NWM][16][3][32];
+  uint32_t sc[PF_NWM][16];
+  int arow[PF_MT];
+};
+
+template <bool GATEUP, int NCB>
+__global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams p) {
+  constexpr int MB = 2;
+  constexpr int NBR = NCB * 16;                        // B rows per tile
+  constexpr int A_PIECES = PF_MT * 20 / (PF_NWM * 64); // 16-B A pieces per thread per chunk (10)
+  constexpr int B_PIECES = NBR * 4 / (PF_NWM * 64);    // 16-B B pieces per thread per chunk
+  constexpr int S_PIECES = NBR * 4 / (PF_NWM * 64);    // scale bytes per thread per chunk
+  static_assert(PF_MT * 20 % (PF_NWM * 64) == 0 && NBR * 4 % (PF_NWM * 64) == 0, "even staging split");
+  __shared__ __align__(16) PfShared<GATEUP, NCB> sh;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = blockIdx.y;
+  if (tile >= *p.n_tiles) return;
+  const int2 te = p.tiles[tile];
+  const int e = te.x, m0 = te.y;
+  const int rows = min(PF_MT, p.counts[e] - m0);
+  const int row_base = p.offsets[e] + m0;
+  const int K = p.K, N = p.N, I = p.I, nblk = K >> 5;
+  const int g = lane >> 4, r = lane & 15;
+
+  // ---- columns of the tile ----
+  constexpr int HALF = NCB / 2;
+  int col0;
+  bool bok[NCB];
+  if (GATEUP) {
+    col0 = blockIdx.x * HALF * 16;
+#pragma unroll
+    for (int j = 0; j < HALF; ++j) bok[j] = bok[HALF + j] = (col0 + 16 * j) < I;
+  } else {
+    col0 = blockIdx.x * NCB * 16;
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) bok[j] = (col0 + 16 * j) < N;
+  }
+  // weight row of B row n (0 .. NBR-1); missing column blocks read block 0
+  auto brow = [&](int n) -> size_t {
+    const int j = n >> 4, rr = n & 15;
+    int row;
+    if (GATEUP) {
+      const int jj = j < HALF ? j : j - HALF;
+      const int c = (col0 + 16 * jj) < I ? col0 + 16 * jj : col0;
+      row = (j < HALF ? 0 : I) + c + rr;
+    } else {
+      row = ((col0 + 16 * j) < N ? col0 + 16 * j : col0) + rr;
+    }
+    return (size_t)e * N + row;
+  };
+  // A row index of each tile row (rows past the tile read tile row 0)
+  if (tid < PF_MT) {
+    const int m = tid < rows ? tid : 0;
+    sh.arow[tid] = GATEUP ? p.expert_rows[(size_t)e * p.T + m0 + m] / p.k : row_base + m;
+  }
+  __syncthreads();
+
+  // ---- staging: global -> registers -> LDS ----
+  v4u ra[A_PIECES], rb[B_PIECES];
+  uint32_t rs[S_PIECES];
+  const size_t a_rowbytes = (size_t)nblk * MX6_BLOCK_BYTES;
+  auto stage_load = [&](int c) {
+    StaticFor<0, A_PIECES>::run([&](auto ic) {
+      constexpr int q = decltype(ic)::value;
+      const int pc = tid + PF_NWM * 64 * q;
+      const int row = pc / 20, piece = pc - 20 * (pc / 20);
+      const int blk = min(4 * c + piece / 5, nblk - 1);
+      ra[q] = *(const v4u*)(p.a + (size_t)sh.arow[row] * a_rowbytes + (size_t)blk * MX6_BLOCK_BYTES +
+                             (piece % 5) * 16);
+    });
+    StaticFor<0, B_PIECES>::run([&](auto ic) {
+      constexpr int q = decltype(ic)::value;
+      const int pc = tid + PF_NWM * 64 * q;
+      const int n = pc >> 2, piece = pc & 3;
+      const int blk = min(4 * c + piece, nblk - 1);
+      rb[q] = *(const v4u*)(p.b_codes + brow(n) * (size_t)(K >> 1) + (size_t)blk * 16);
+    });
+    StaticFor<0, S_PIECES>::run([&](auto ic) {
+      constexpr int q = decltype(ic)::value;
+      const int pc = tid + PF_NWM * 64 * q;
+      const int n = pc >> 2, piece = pc & 3;
+      const int blk = min(4 * c + piece, nblk - 1);
+      rs[q] = p.b_scales[brow(n) * (size_t)nblk + blk];
+    });
+  };
+  auto stage_store = [&](int buf) {
+    StaticFor<0, A_PIECES>::run([&](auto ic) {
+      constexpr int q = decltype(ic)::value;
+      const int pc = tid + PF_NWM * 64 * q;
+      const int row = pc / 20, piece = pc - 20 * (pc / 20);
+      *(v4u*)(sh.a[buf] + row * PF_ARS + piece * 16) = ra[q];
+    });
+    StaticFor<0, B_PIECES>::run([&](auto ic) {
+      constexpr int q = decltype(ic)::value;
+      const int pc = tid + PF_NWM * 64 * q;
+      const int n = pc >> 2, piece = pc & 3;
+      *(v4u*)(sh.b[buf] + n * 64 + ((piece ^ ((n >> 2) & 3)) * 16)) = rb[q];
+    });
+    StaticFor<0, S_PIECES>::run([&](auto ic) {
+      constexpr int q = decltype(ic)::value;
+      const int pc = tid + PF_NWM * 64 * q;
+      sh.bs[buf][pc] = (uint8_t)rs[q];
+    });
+  };
+
+  v4f acc[MB][NCB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) acc[mb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int c, int buf) {
+    const uint32_t keep = (4 * c + g) < nblk ? 0xffffffffu : 0u;
+    v8i a[MB][3];
+    int as[MB][3];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const uint8_t* src = sh.a[buf] + (32 * wave + 16 * mb + r) * PF_ARS + g * MX6_BLOCK_BYTES;
+      uint32_t w[20];
+#pragma unroll
+      for (int q = 0; q < 5; ++q) {
+        const v4u t = *(const v4u*)(src + 16 * q);
+        w[4 * q] = t.x; w[4 * q + 1] = t.y; w[4 * q + 2] = t.z; w[4 * q + 3] = t.w;
+      }
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        a[mb][t] = (v8i){(int)w[6 * t], (int)w[6 * t + 1], (int)w[6 * t + 2], (int)w[6 * t + 3], (int)w[6 * t + 4],
+                         (int)w[6 * t + 5], 0, 0};
+        as[mb][t] = (int)((w[18] >> (8 * t)) & 0xffu);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) {
+      const int n = 16 * j + r;
+      const v4u bq = *(const v4u*)(sh.b[buf] + n * 64 + ((g ^ ((n >> 2) & 3)) * 16));
+      const int bsc = (int)(((uint32_t)sh.bs[buf][n * 4 + g] & keep) | (127u & ~keep));
+      const v8i b = {(int)(bq.x & keep), (int)(bq.y & keep), (int)(bq.z & keep), (int)(bq.w & keep), 0, 0, 0, 0};
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+          acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[mb][t], b, acc[mb][j], 2, 4, 0, as[mb][t],
+                                                                        0, bsc);
+    }
+  };
+
+  const int nchunk = (nblk + 3) >> 2;
+  stage_load(0);
+  stage_store(0);
+  __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    const bool more = c + 1 < nchunk;
+    if (more) stage_load(c + 1);
+    compute(c, c & 1);
+    if (more) stage_store((c + 1) & 1);
+    __syncthreads();
+  }
+
+  const int rows_w = rows - 32 * wave;
+  const int row_base_w = row_base + 32 * wave;
+  if (GATEUP)
+    epilogue_gateup<MB, NCB>(p, acc, bok, e, rows_w, row_base_w, col0, lane, sh.codes[wave], sh.sc[wave]);
+  else
+    epilogue_down<MB, NCB>(p, acc, bok, e, rows_w, row_base_w, col0, lane);
+}
+
+// ---------------------------------------------------------------------------
 // General kernel (tiles of 16*MB rows): each of the NW waves owns NCB column
 // blocks over the whole K range.
 template <int MB, int NCB, int NW, int D, bool GATEUP>
@@ -582,10 +828,9 @@ int launch_gemm_gateup(const GemmParams& p, int max_tiles, bool small_m, hipStre
     dim3 grid((p.I + 31) / 32, max_tiles);
     hipLaunchKernelGGL((expert_gemm_decode<true>), grid, dim3(DEC_NW * 64), 0, s, p);
   } else {
-    constexpr int MB = 4, NCB = 4, NW = 4, D = 2;
-    const int span = NW * (NCB / 2) * 16;
-    dim3 grid((p.I + span - 1) / span, max_tiles);
-    hipLaunchKernelGGL((expert_gemm_kernel<MB, NCB, NW, D, true>), grid, dim3(NW * 64), 0, s, p);
+    constexpr int NCB = 20;  // 160 gate + 160 up columns
+    dim3 grid((p.I + NCB * 8 - 1) / (NCB * 8), max_tiles);
+    hipLaunchKernelGGL((expert_gemm_prefill<true, NCB>), grid, dim3(PF_NWM * 64), 0, s, p);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
@@ -595,10 +840,9 @@ int launch_gemm_down(const GemmParams& p, int max_tiles, bool small_m, hipStream
     dim3 grid((p.N + 63) / 64, max_tiles);
     hipLaunchKernelGGL((expert_gemm_decode<false>), grid, dim3(DEC_NW * 64), 0, s, p);
   } else {
-    constexpr int MB = 4, NCB = 4, NW = 4, D = 2;
-    const int span = NW * NCB * 16;
-    dim3 grid((p.N + span - 1) / span, max_tiles);
-    hipLaunchKernelGGL((expert_gemm_kernel<MB, NCB, NW, D, false>), grid, dim3(NW * 64), 0, s, p);
+    constexpr int NCB = 20;  // 320 output columns
+    dim3 grid((p.N + NCB * 16 - 1) / (NCB * 16), max_tiles);
+    hipLaunchKernelGGL((expert_gemm_prefill<false, NCB>), grid, dim3(PF_NWM * 64), 0, s, p);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

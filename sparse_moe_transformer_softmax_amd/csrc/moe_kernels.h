@@ -66,6 +66,6 @@ int launch_zero_ints(int* p, int n, hipStream_t s);
 
 // rows per GEMM tile of the two configurations
 constexpr int MT_SMALL = 16;
-constexpr int MT_LARGE = 64;
+constexpr int MT_LARGE = 128;
 
 }  // namespace moe
