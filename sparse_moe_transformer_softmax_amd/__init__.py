@@ -76,8 +76,17 @@ def moe_release() -> None:
 KERNELS = ("route", "gateup_gemm", "down_gemm", "combine", "split_x")
 
 
-def moe_timing_enable(on: bool = True) -> None:
-    _ok("moe_timing_enable", lib().moe_timing_enable(1 if on else 0))
+def moe_timing_enable(on=True) -> None:
+    """on: True (every kernel), False (off), or an iterable of names from KERNELS."""
+    if on is True:
+        mask = (1 << len(KERNELS)) - 1
+    elif not on:
+        mask = 0
+    else:
+        mask = 0
+        for k in on:
+            mask |= 1 << KERNELS.index(k)
+    _ok("moe_timing_enable", lib().moe_timing_enable(mask))
 
 
 def moe_timing_read(reset: bool = True) -> dict:

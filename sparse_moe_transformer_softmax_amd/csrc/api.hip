@@ -17,7 +17,9 @@ using namespace moe;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kHeaderInts = 512;  // done counter at [0], expert cursors at [64, 320)
+// done counter at [0]; expert e's cursor at 64 + CURSOR_STRIDE * e, one cache
+// line per expert so that the atomics of different experts do not serialize
+constexpr int kHeaderInts = 64 + CURSOR_STRIDE * 256;
 
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -137,7 +139,7 @@ int owned_workspace(size_t need, hipStream_t s, void** out) {
 
 // optional per-kernel event timing
 struct Timing {
-  bool on = false;
+  int mask = 0;  // bit i: time kernel kind i
   std::vector<hipEvent_t> pool;
   struct Rec { int kind; hipEvent_t a, b; };
   std::vector<Rec> pending;
@@ -154,7 +156,7 @@ struct Timing {
 struct Timed {
   int kind; hipStream_t s; hipEvent_t a = nullptr, b = nullptr;
   Timed(int k, hipStream_t st) : kind(k), s(st) {
-    if (!g_t.on) return;
+    if (!((g_t.mask >> k) & 1)) return;
     a = g_t.get(); b = g_t.get();
     if (a && b) (void)hipEventRecord(a, s);
   }
@@ -402,8 +404,8 @@ int moe_stack_forward(const void* x0, int n_layers, const void* const* router_w,
   return MOE_OK;
 }
 
-int moe_timing_enable(int on) {
-  g_t.on = on != 0;
+int moe_timing_enable(int mask) {
+  g_t.mask = mask & 0x1f;
   return MOE_OK;
 }
 

@@ -15,7 +15,7 @@ struct RouteParams {
   float* topk_w;             // [T, k]
   int* rel_pos;              // [T, k] row of the pair inside its expert's list
   int* expert_rows;          // [E, T] pair ids (t*k + j) per expert
-  int* cursor;               // [256] zero between calls
+  int* cursor;               // [256 * CURSOR_STRIDE], expert e at e * CURSOR_STRIDE; zero between calls
   int* done;                 // zero between calls
   int* counts;               // [E]
   int* offsets;              // [E + 1]
@@ -63,6 +63,9 @@ int launch_gemm_down(const GemmParams& p, int max_tiles, bool small_m, hipStream
 int launch_combine(const CombineParams& p, hipStream_t s);
 int launch_rmsnorm(const uint16_t* x, uint16_t* out, int T, int d, float eps, hipStream_t s);
 int launch_zero_ints(int* p, int n, hipStream_t s);
+
+// ints between consecutive expert cursors (one 128-byte cache line)
+constexpr int CURSOR_STRIDE = 32;
 
 // rows per GEMM tile of the two configurations
 constexpr int MT_SMALL = 16;

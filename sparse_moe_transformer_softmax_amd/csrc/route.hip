@@ -36,7 +36,7 @@ constexpr int RT_THREADS = 1024;  // 16 waves
 template <int NCBW, int MBR>
 __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
   constexpr int MT = 16 * MBR;
-  constexpr int BATCH = (8 / (MBR + NCBW)) > 2 ? 8 / (MBR + NCBW) : 2;  // K steps in flight
+  constexpr int BATCH = (18 / (MBR + NCBW)) > 2 ? 18 / (MBR + NCBW) : 2;  // K steps in flight (<= 18 b128 loads)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * MT;
   const int T = p.T, d = p.d, E = p.E, k = p.k;
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
   // atomicAdd returns, so each reservation is performed before the barrier
   for (int e = tid; e < E; e += RT_THREADS) {
     const int c = __popcll(s_mask[e]);
-    s_base[e] = c ? atomicAdd(&p.cursor[e], c) : 0;
+    s_base[e] = c ? atomicAdd(&p.cursor[e * CURSOR_STRIDE], c) : 0;
   }
   __syncthreads();
   const int ntok = min(MT, T - t0);
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
   const int e = tid;
   int cnt = 0, nt = 0;
   if (e < E) {
-    cnt = atomicAdd(&p.cursor[e], 0);
+    cnt = atomicAdd(&p.cursor[e * CURSOR_STRIDE], 0);
     nt = (cnt + p.mt - 1) / p.mt;
     p.counts[e] = cnt;
   }
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
     p.offsets[e] = incl[0] - cnt;
     const int tb = incl[1] - nt;
     for (int i = 0; i < nt; ++i) p.tiles[tb + i] = make_int2(e, i * p.mt);
-    atomicExch(&p.cursor[e], 0);
+    atomicExch(&p.cursor[e * CURSOR_STRIDE], 0);
     if (e == E - 1) {
       p.offsets[E] = incl[0];
       *p.n_tiles = incl[1];
@@ -277,19 +277,25 @@ int launch_split_x(const uint16_t* x, uint8_t* xq, int T, int d, hipStream_t str
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// LDS partials of a configuration: KS * MT * ES floats must fit s_part
+static bool route_fits(int ncb, int ncbw, int mbr) {
+  const int eg = (ncb + ncbw - 1) / ncbw, ks = 16 / eg;
+  return ks >= 1 && ks * 16 * mbr * (16 * ncb + 1) <= 16 * 1032;
+}
+
 int launch_route(const RouteParams& p, hipStream_t stream) {
   const int ncb = (p.E + 15) / 16;
   const bool big = p.T >= 2048 && ncb <= 8;
   const int grid = (p.T + (big ? 31 : 15)) / (big ? 32 : 16);
+  const int ncbw = big ? (ncb <= 4 ? 1 : 2) : (ncb <= 8 ? 2 : 4);
+  if (!route_fits(ncb, ncbw, big ? 2 : 1)) return -1;
   if (big) {
     if (ncb <= 4)
       hipLaunchKernelGGL((route_kernel<1, 2>), dim3(grid), dim3(RT_THREADS), 0, stream, p);
     else
       hipLaunchKernelGGL((route_kernel<2, 2>), dim3(grid), dim3(RT_THREADS), 0, stream, p);
   } else {
-    if (ncb <= 4)
-      hipLaunchKernelGGL((route_kernel<1, 1>), dim3(grid), dim3(RT_THREADS), 0, stream, p);
-    else if (ncb <= 8)
+    if (ncb <= 8)
       hipLaunchKernelGGL((route_kernel<2, 1>), dim3(grid), dim3(RT_THREADS), 0, stream, p);
     else
       hipLaunchKernelGGL((route_kernel<4, 1>), dim3(grid), dim3(RT_THREADS), 0, stream, p);

@@ -1,0 +1,118 @@
+"""Short text summaries of rocprofv3 CSV output, for the committed profiles.
+
+    python -m sparse_moe_transformer_softmax_amd.profsum stats KERNEL_STATS_CSV [--cmd CMD]
+    python -m sparse_moe_transformer_softmax_amd.profsum traffic --fetch CSV --write CSV \
+        --kernel SUBSTR --copy-kernel SUBSTR --copy-bytes BYTES [--cmd CMD]
+
+`stats` prints the per-kernel call count and mean/min/max duration from a
+`--kernel-trace --stats --output-format csv` run.  `traffic` reads two
+`--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` counter-collection files (KiB per
+dispatch), scales each counter by what it reads for a reference copy kernel
+that moves a known number of bytes each way, and prints the HBM bytes per
+launch of the kernel whose name contains SUBSTR, as `key: value` lines that
+bench.py reads back (with the hash of the kernel sources they belong to).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def src_sha() -> str:
+    """Hash of the HIP sources; a counter summary is valid only for these."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_moe_transformer_softmax_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(n: str) -> str:
+    n = n.strip('"')
+    if n.startswith("void "):
+        n = n[5:]
+    return n if len(n) <= 90 else n[:87] + "..."
+
+
+def cmd_stats(args) -> None:
+    rows = list(csv.DictReader(open(args.csv)))
+    print(f"# rocprofv3 kernel statistics")
+    if args.cmd:
+        print(f"# command: {args.cmd}")
+    print(f"{'kernel':90s} {'calls':>6s} {'mean_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}")
+    for r in rows:
+        print(f"{short_name(r['Name']):90s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+              f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}")
+
+
+def per_dispatch(path: str, counter: str, substr: str):
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter or substr not in r["Kernel_Name"]:
+            continue
+        did = r["Dispatch_Id"]
+        vals[did] = vals.get(did, 0.0) + float(r["Counter_Value"])
+    return list(vals.values())
+
+
+def cmd_traffic(args) -> None:
+    f_k = per_dispatch(args.fetch, "FETCH_SIZE", args.kernel)
+    w_k = per_dispatch(args.write, "WRITE_SIZE", args.kernel)
+    f_c = per_dispatch(args.fetch, "FETCH_SIZE", args.copy_kernel)
+    w_c = per_dispatch(args.write, "WRITE_SIZE", args.copy_kernel)
+    if not (f_k and w_k and f_c and w_c):
+        sys.exit(f"missing dispatches: kernel fetch {len(f_k)} write {len(w_k)}, copy fetch {len(f_c)} write {len(w_c)}")
+    kib = 1024.0
+    # the copy reads and writes copy_bytes: counter KiB -> true bytes
+    f_scale = args.copy_bytes / (max(f_c) * kib)
+    w_scale = args.copy_bytes / (max(w_c) * kib)
+    fetch = statistics.mean(f_k) * kib * f_scale
+    write = statistics.mean(w_k) * kib * w_scale
+    print("# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
+    if args.cmd:
+        for c in args.cmd:
+            print(f"# command: {c}")
+    print(f"kernel: {args.kernel}")
+    print(f"dispatches: {len(f_k)} fetch, {len(w_k)} write")
+    print(f"copy_reference: {args.copy_kernel} moving {args.copy_bytes} bytes each way")
+    print(f"copy_fetch_KiB: {max(f_c):.1f}")
+    print(f"copy_write_KiB: {max(w_c):.1f}")
+    print(f"fetch_scale: {f_scale:.4f}")
+    print(f"write_scale: {w_scale:.4f}")
+    print(f"fetch_KiB_per_launch_raw: {statistics.mean(f_k):.1f}")
+    print(f"write_KiB_per_launch_raw: {statistics.mean(w_k):.1f}")
+    print(f"fetch_bytes_per_launch: {fetch:.0f}")
+    print(f"write_bytes_per_launch: {write:.0f}")
+    print(f"traffic_bytes_per_launch: {fetch + write:.0f}")
+    print(f"src_sha: {src_sha()}")
+
+
+def main(argv=None) -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd_name", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--cmd", default="")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--copy-kernel", required=True)
+    t.add_argument("--copy-bytes", type=float, required=True)
+    t.add_argument("--cmd", action="append", default=[])
+    args = ap.parse_args(argv)
+    if args.cmd_name == "stats":
+        cmd_stats(args)
+    else:
+        cmd_traffic(args)
+
+
+if __name__ == "__main__":
+    main()
