@@ -17,7 +17,7 @@ from oracle.workload_inputs import make_inputs
 from sparse_moe_transformer_softmax_amd import synth
 from sparse_moe_transformer_softmax_amd.workloads import WORKLOADS, Workload
 import sparse_moe_transformer_softmax_amd as moe
-from tests.parity_util import (TOL, bf16_excess, bf16_tensor_to_f64, check_routing, rel_max_err, to_gpu)
+from tests.parity_util import (TOL, bf16_excess, bf16_half_ulp, bf16_tensor_to_f64, check_routing, rel_max_err, to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -251,7 +251,14 @@ def test_stack_against_oracle(torch):
     """Three seeded layers end to end against the oracle's pre-norm residual
     stack.  Only layer 0's input is conditioned by the gap rule; tokens whose
     oracle gap falls to 1e-3 or below at a later layer are reported and left
-    out of the comparison (their expert set is not pinned)."""
+    out of the comparison (their expert set is not pinned).
+
+    Every layer rounds the residual stream to bf16 on both sides, and a
+    difference far below the tolerance can send an intermediate value to the
+    other neighbouring bf16 value; that step of one ulp is carried to the
+    output by the residual adds.  The allowance is therefore one ulp of each
+    intermediate residual plus half an ulp of the final one, on top of the
+    1e-2 * rms(ref) budget for arithmetic error."""
     x0, layers = _stack_inputs()
     say(f"stack vs oracle T={STACK.T} d={STACK.d} L={STACK.layers}")
     gl = [to_gpu(L) for L in layers]
@@ -260,7 +267,10 @@ def test_stack_against_oracle(torch):
     torch.cuda.synchronize()
     x = O.bf16_bits_to_f64(x0)
     min_gap = np.full(STACK.T, np.inf)
-    for L in layers:
+    allow = np.zeros_like(x)
+    for li, L in enumerate(layers):
+        if li > 0:
+            allow += 2.0 * bf16_half_ulp(x)
         n_bits = O._f64_bf16_to_bits(O.round_to_bf16(O.rmsnorm(x, 1e-5)))
         logits, _, _ = O.route(n_bits, L["router_w"], L["router_b"], STACK.k)
         min_gap = np.minimum(min_gap, O.topk_gap(logits, STACK.k))
@@ -269,6 +279,10 @@ def test_stack_against_oracle(torch):
     keep = min_gap > 1e-3
     say(f"stack: {int((~keep).sum())} of {STACK.T} tokens left out (gap <= 1e-3 at a later layer)")
     assert keep.sum() >= STACK.T * 3 // 4
-    ex = bf16_excess(bf16_tensor_to_f64(got)[keep], x[keep])
-    say(f"stack: excess/rms={ex:.3e}")
+    g64 = bf16_tensor_to_f64(got)[keep]
+    ref = x[keep]
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    ex = float(np.max(np.abs(g64 - ref) - bf16_half_ulp(ref) - allow[keep]) / rms)
+    say(f"stack: excess/rms={ex:.3e} (beyond the rounding allowance); final-rounding-only excess/rms="
+        f"{bf16_excess(g64, ref):.3e}")
     assert ex <= TOL
