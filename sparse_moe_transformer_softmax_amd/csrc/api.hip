@@ -213,7 +213,7 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   gp.T = a.T; gp.k = a.k;
   gp.a = ws + L.xq;
   gp.b_codes = a.w13c; gp.b_scales = a.w13s; gp.bias = a.b13;
-  gp.N = 2 * a.I; gp.K = a.d; gp.I = a.I;
+  gp.N = 2 * a.I; gp.K = a.d; gp.I = a.I; gp.E = a.E;
   gp.clamp = a.clamp;
   gp.hq = ws + L.hq;
   gp.y = nullptr;

@@ -600,13 +600,20 @@ __global__ __launch_bounds__(DEC_NW * 64, 3) void expert_gemm_decode(GemmParams 
 // fragment read from LDS feeds six MFMAs.  K advances in chunks of four
 // 32-element blocks through two LDS buffers: the global loads of chunk c+1
 // are issued into registers before chunk c is consumed and written to the
-// other buffer afterwards, one barrier per chunk.  A rows are padded to 336
-// bytes in LDS and B rows are stored with their four 16-byte pieces
-// XOR-swizzled by (row >> 2) & 3, so the operand reads are free of LDS bank
-// conflicts.
+// other buffer after its MFMAs have been issued, one barrier per chunk.
+// Inside a chunk the B fragment of column block j+1 is read from LDS while
+// the MFMAs of block j run.  A rows are padded to 336 bytes in LDS and B
+// rows are stored with their four 16-byte pieces XOR-swizzled by
+// (row >> 2) & 3, so the operand reads are free of LDS bank conflicts.
+//
+// Work items (tile, column span) are numbered tile-major and dealt to the
+// eight XCDs in contiguous ranges (workgroup i runs on XCD i mod 8), so the
+// column spans of one tile -- which share its A rows -- and the tiles of
+// one expert -- which share its weights -- meet in the same L2.
 constexpr int PF_MT = 128;                  // rows per tile
 constexpr int PF_NWM = 4;                   // waves (each 32 rows)
 constexpr int PF_ARS = 336;                 // LDS row stride of A (4 blocks x 80 B + 16 B pad)
+constexpr int PF_XCD = 8;                   // XCDs of the device
 
 template <bool GATEUP, int NCB>
 struct PfShared {
@@ -615,11 +622,10 @@ struct PfShared {
   uint8_t bs[2][NCB * 16 * 4];
   uint8_t codes[PF_NWM][16][3][32];
   uint32_t sc[PF_NWM][16];
-  int arow[PF_MT];
 };
 
 template <bool GATEUP, int NCB>
-__global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams p) {
+__global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams p, int spans) {
   constexpr int MB = 2;
   constexpr int NBR = NCB * 16;                        // B rows per tile
   constexpr int A_PIECES = PF_MT * 20 / (PF_NWM * 64); // 16-B A pieces per thread per chunk (10)
@@ -628,9 +634,15 @@ __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams
   static_assert(PF_MT * 20 % (PF_NWM * 64) == 0 && NBR * 4 % (PF_NWM * 64) == 0, "even staging split");
   __shared__ __align__(16) PfShared<GATEUP, NCB> sh;
 
+  // ---- work item ----
+  const int total = *p.n_tiles * spans;
+  const int per = (total + PF_XCD - 1) / PF_XCD;
+  const int lin = blockIdx.x;
+  const int item = (lin % PF_XCD) * per + lin / PF_XCD;
+  if (lin / PF_XCD >= per || item >= total) return;
+  const int tile = item / spans, span = item - tile * spans;
+
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tile = blockIdx.y;
-  if (tile >= *p.n_tiles) return;
   const int2 te = p.tiles[tile];
   const int e = te.x, m0 = te.y;
   const int rows = min(PF_MT, p.counts[e] - m0);
@@ -643,16 +655,37 @@ __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams
   int col0;
   bool bok[NCB];
   if (GATEUP) {
-    col0 = blockIdx.x * HALF * 16;
+    col0 = span * HALF * 16;
 #pragma unroll
     for (int j = 0; j < HALF; ++j) bok[j] = bok[HALF + j] = (col0 + 16 * j) < I;
   } else {
-    col0 = blockIdx.x * NCB * 16;
+    col0 = span * NCB * 16;
 #pragma unroll
     for (int j = 0; j < NCB; ++j) bok[j] = (col0 + 16 * j) < N;
   }
-  // weight row of B row n (0 .. NBR-1); missing column blocks read block 0
-  auto brow = [&](int n) -> size_t {
+
+  // ---- per-thread staging offsets (fixed over K; the launcher checks
+  // that every offset fits 32 bits) ----
+  // A piece q of this thread: tile row (tid + 256q) / 20, piece (tid + 256q) % 20
+  // (block-in-chunk piece / 5, 16-byte part piece % 5); low 2 bits hold the
+  // block-in-chunk, the rest the byte offset of the row's part.
+  const uint32_t a_rowbytes = (uint32_t)nblk * MX6_BLOCK_BYTES;
+  uint32_t a_off[A_PIECES];
+  StaticFor<0, A_PIECES>::run([&](auto ic) {
+    constexpr int q = decltype(ic)::value;
+    const int pc = tid + PF_NWM * 64 * q;
+    const int row = pc / 20, piece = pc - 20 * (pc / 20);
+    const int m = row < rows ? row : 0;  // rows past the tile read tile row 0
+    const uint32_t ar = GATEUP ? (uint32_t)(p.expert_rows[(size_t)e * p.T + m0 + m] / p.k) : (uint32_t)(row_base + m);
+    a_off[q] = ar * a_rowbytes + (uint32_t)((piece % 5) * 16) + (uint32_t)(piece / 5);
+  });
+  // B piece q: weight row n = tid/4 + 64q of the tile, 16-byte piece tid % 4
+  // of each chunk; missing column blocks read block 0
+  const int bpiece = tid & 3;
+  uint32_t b_row[B_PIECES];
+  StaticFor<0, B_PIECES>::run([&](auto ic) {
+    constexpr int q = decltype(ic)::value;
+    const int n = (tid >> 2) + PF_NWM * 16 * q;
     const int j = n >> 4, rr = n & 15;
     int row;
     if (GATEUP) {
@@ -662,41 +695,26 @@ __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams
     } else {
       row = ((col0 + 16 * j) < N ? col0 + 16 * j : col0) + rr;
     }
-    return (size_t)e * N + row;
-  };
-  // A row index of each tile row (rows past the tile read tile row 0)
-  if (tid < PF_MT) {
-    const int m = tid < rows ? tid : 0;
-    sh.arow[tid] = GATEUP ? p.expert_rows[(size_t)e * p.T + m0 + m] / p.k : row_base + m;
-  }
-  __syncthreads();
+    b_row[q] = (uint32_t)e * (uint32_t)N + (uint32_t)row;
+  });
 
   // ---- staging: global -> registers -> LDS ----
   v4u ra[A_PIECES], rb[B_PIECES];
   uint32_t rs[S_PIECES];
-  const size_t a_rowbytes = (size_t)nblk * MX6_BLOCK_BYTES;
   auto stage_load = [&](int c) {
     StaticFor<0, A_PIECES>::run([&](auto ic) {
       constexpr int q = decltype(ic)::value;
-      const int pc = tid + PF_NWM * 64 * q;
-      const int row = pc / 20, piece = pc - 20 * (pc / 20);
-      const int blk = min(4 * c + piece / 5, nblk - 1);
-      ra[q] = *(const v4u*)(p.a + (size_t)sh.arow[row] * a_rowbytes + (size_t)blk * MX6_BLOCK_BYTES +
-                             (piece % 5) * 16);
+      const int blk = min(4 * c + (int)(a_off[q] & 3u), nblk - 1);
+      ra[q] = *(const v4u*)(p.a + (size_t)((a_off[q] & ~3u) + (uint32_t)blk * MX6_BLOCK_BYTES));
     });
+    const int blk = min(4 * c + bpiece, nblk - 1);
     StaticFor<0, B_PIECES>::run([&](auto ic) {
       constexpr int q = decltype(ic)::value;
-      const int pc = tid + PF_NWM * 64 * q;
-      const int n = pc >> 2, piece = pc & 3;
-      const int blk = min(4 * c + piece, nblk - 1);
-      rb[q] = *(const v4u*)(p.b_codes + brow(n) * (size_t)(K >> 1) + (size_t)blk * 16);
+      rb[q] = *(const v4u*)(p.b_codes + (size_t)(b_row[q] * (uint32_t)(K >> 1) + (uint32_t)blk * 16u));
     });
     StaticFor<0, S_PIECES>::run([&](auto ic) {
       constexpr int q = decltype(ic)::value;
-      const int pc = tid + PF_NWM * 64 * q;
-      const int n = pc >> 2, piece = pc & 3;
-      const int blk = min(4 * c + piece, nblk - 1);
-      rs[q] = p.b_scales[brow(n) * (size_t)nblk + blk];
+      rs[q] = p.b_scales[(size_t)(b_row[q] * (uint32_t)nblk + (uint32_t)blk)];
     });
   };
   auto stage_store = [&](int buf) {
@@ -708,14 +726,12 @@ __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams
     });
     StaticFor<0, B_PIECES>::run([&](auto ic) {
       constexpr int q = decltype(ic)::value;
-      const int pc = tid + PF_NWM * 64 * q;
-      const int n = pc >> 2, piece = pc & 3;
-      *(v4u*)(sh.b[buf] + n * 64 + ((piece ^ ((n >> 2) & 3)) * 16)) = rb[q];
+      const int n = (tid >> 2) + PF_NWM * 16 * q;
+      *(v4u*)(sh.b[buf] + n * 64 + ((bpiece ^ ((n >> 2) & 3)) * 16)) = rb[q];
     });
     StaticFor<0, S_PIECES>::run([&](auto ic) {
       constexpr int q = decltype(ic)::value;
-      const int pc = tid + PF_NWM * 64 * q;
-      sh.bs[buf][pc] = (uint8_t)rs[q];
+      sh.bs[buf][tid + PF_NWM * 64 * q] = (uint8_t)rs[q];
     });
   };
 
@@ -745,30 +761,44 @@ __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams
         as[mb][t] = (int)((w[18] >> (8 * t)) & 0xffu);
       }
     }
-#pragma unroll
-    for (int j = 0; j < NCB; ++j) {
+    // B fragments one column block ahead of the MFMAs that use them
+    v4u bq[2];
+    uint32_t bsb[2];
+    auto read_b = [&](int j, int slot) {
       const int n = 16 * j + r;
-      const v4u bq = *(const v4u*)(sh.b[buf] + n * 64 + ((g ^ ((n >> 2) & 3)) * 16));
-      const int bsc = (int)(((uint32_t)sh.bs[buf][n * 4 + g] & keep) | (127u & ~keep));
-      const v8i b = {(int)(bq.x & keep), (int)(bq.y & keep), (int)(bq.z & keep), (int)(bq.w & keep), 0, 0, 0, 0};
+      bq[slot] = *(const v4u*)(sh.b[buf] + n * 64 + ((g ^ ((n >> 2) & 3)) * 16));
+      bsb[slot] = sh.bs[buf][n * 4 + g];
+    };
+    read_b(0, 0);
+    StaticFor<0, NCB>::run([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j + 1 < NCB) read_b(j + 1, (j + 1) & 1);
+      const v4u b4 = bq[j & 1];
+      const int bsc = (int)((bsb[j & 1] & keep) | (127u & ~keep));
+      const v8i b = {(int)(b4.x & keep), (int)(b4.y & keep), (int)(b4.z & keep), (int)(b4.w & keep), 0, 0, 0, 0};
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int t = 0; t < 3; ++t)
           acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[mb][t], b, acc[mb][j], 2, 4, 0, as[mb][t],
                                                                         0, bsc);
-    }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   const int nchunk = (nblk + 3) >> 2;
   stage_load(0);
   stage_store(0);
   __syncthreads();
+  // The loop body is one basic block (the last iteration reloads the last
+  // chunk into the idle buffer), so the scheduling barriers keep the LDS
+  // stores behind the MFMAs and the global loads' latency behind both.
   for (int c = 0; c < nchunk; ++c) {
-    const bool more = c + 1 < nchunk;
-    if (more) stage_load(c + 1);
+    stage_load(min(c + 1, nchunk - 1));
+    __builtin_amdgcn_sched_barrier(0);
     compute(c, c & 1);
-    if (more) stage_store((c + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_store((c + 1) & 1);
     __syncthreads();
   }
 
@@ -819,6 +849,14 @@ __global__ __launch_bounds__(NW * 64) void expert_gemm_kernel(GemmParams p) {
     epilogue_down<MB, NCB>(p, acc, op.bok, e, rows, row_base, op.col0, lane);
 }
 
+// The prefill kernel addresses operands with 32-bit byte offsets.
+static bool prefill_offsets_fit(const GemmParams& p) {
+  const unsigned long long lim = 1ull << 32;
+  const unsigned long long a_rows = p.hq ? (unsigned long long)p.T : (unsigned long long)p.T * p.k;
+  const unsigned long long e_rows = (unsigned long long)p.E * p.N;
+  return a_rows * (p.K / 32) * MX6_BLOCK_BYTES < lim && e_rows * (p.K / 2) < lim;
+}
+
 // Launch configurations.
 //   small-M (tiles of 16 rows, decode): skinny kernel, 4 waves split K over
 //     one 64-column span (gate/up: 32 gate + 32 up columns);
@@ -829,8 +867,11 @@ int launch_gemm_gateup(const GemmParams& p, int max_tiles, bool small_m, hipStre
     hipLaunchKernelGGL((expert_gemm_decode<true>), grid, dim3(DEC_NW * 64), 0, s, p);
   } else {
     constexpr int NCB = 20;  // 160 gate + 160 up columns
-    dim3 grid((p.I + NCB * 8 - 1) / (NCB * 8), max_tiles);
-    hipLaunchKernelGGL((expert_gemm_prefill<true, NCB>), grid, dim3(PF_NWM * 64), 0, s, p);
+    if (!prefill_offsets_fit(p)) return -1;
+    const int spans = (p.I + NCB * 8 - 1) / (NCB * 8);
+    const long long items = (long long)max_tiles * spans;
+    hipLaunchKernelGGL((expert_gemm_prefill<true, NCB>), dim3((unsigned)((items + PF_XCD - 1) / PF_XCD * PF_XCD)),
+                       dim3(PF_NWM * 64), 0, s, p, spans);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
@@ -841,8 +882,11 @@ int launch_gemm_down(const GemmParams& p, int max_tiles, bool small_m, hipStream
     hipLaunchKernelGGL((expert_gemm_decode<false>), grid, dim3(DEC_NW * 64), 0, s, p);
   } else {
     constexpr int NCB = 20;  // 320 output columns
-    dim3 grid((p.N + NCB * 16 - 1) / (NCB * 16), max_tiles);
-    hipLaunchKernelGGL((expert_gemm_prefill<false, NCB>), grid, dim3(PF_NWM * 64), 0, s, p);
+    if (!prefill_offsets_fit(p)) return -1;
+    const int spans = (p.N + NCB * 16 - 1) / (NCB * 16);
+    const long long items = (long long)max_tiles * spans;
+    hipLaunchKernelGGL((expert_gemm_prefill<false, NCB>), dim3((unsigned)((items + PF_XCD - 1) / PF_XCD * PF_XCD)),
+                       dim3(PF_NWM * 64), 0, s, p, spans);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -34,7 +34,7 @@ struct GemmParams {
   const uint8_t* b_codes;    // [E, N, K/2]
   const uint8_t* b_scales;   // [E, N, K/32]
   const float* bias;         // [E, N]
-  int N, K, I;
+  int N, K, I, E;
   float clamp;
   uint8_t* hq;               // gate/up output: MX6x3 rows [P, I/32, 80]
   float* y;                  // down output: fp32 [P, N]
