@@ -31,7 +31,10 @@
  *  - Shapes: T >= 0 tokens (T == 0 is a successful no-op); d (model width)
  *    and I (expert width) positive multiples of 32; 1 <= E <= 256 experts;
  *    1 <= k <= min(E, 8); T * max(k, E) < 2^31; clamp > 0 (+inf disables
- *    the clamp).
+ *    the clamp).  Larger problems than the kernels address with 32-bit
+ *    offsets return MOE_ERR_UNSUPPORTED: T * k * max(d, I) * 5/2 must stay
+ *    below 2^31 bytes (the activation operand) and E * I * d below 2^32
+ *    (the gate/up weight codes).
  *  - Entry points without a workspace argument use a library-owned device
  *    workspace per GPU that grows on demand (a growth allocates and
  *    synchronises the device).  Calls that share it must be ordered on one
@@ -54,7 +57,7 @@ typedef enum moe_status {
   MOE_OK = 0,
   MOE_ERR_NULL_PTR = -1,    /* a required pointer is NULL */
   MOE_ERR_BAD_SHAPE = -2,   /* a size is out of range or inconsistent */
-  MOE_ERR_UNSUPPORTED = -3, /* no gfx950 device is current */
+  MOE_ERR_UNSUPPORTED = -3, /* no gfx950 device is current, or the problem is too large */
   MOE_ERR_MISALIGNED = -4,  /* a pointer breaks the alignment rules above */
   MOE_ERR_NOMEM = -5,       /* workspace allocation failed */
   MOE_ERR_HIP = -6,         /* a HIP launch or runtime call failed */

@@ -58,6 +58,11 @@ int check_shape(int T, int d, int I, int E, int k) {
   const long long big = (long long)T * (k > E ? k : E);
   if (big >= (long long)INT_MAX) return MOE_ERR_BAD_SHAPE;
   if ((long long)d * 2 * I >= (long long)INT_MAX * 16) return MOE_ERR_BAD_SHAPE;
+  // operands are addressed with 32-bit byte offsets (MX6x3 activations:
+  // 80 bytes per 32 elements)
+  const long long w = d > I ? d : I;
+  if ((long long)T * k * (w / 32) * MX6_BLOCK_BYTES >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if ((long long)E * I * d >= (1ll << 32)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -19,9 +19,8 @@
 // consecutive K values of block l / 16 of the 128-wide step; the result
 // C[4*(l/16) + q][l % 16] sits in accumulator element q of lane l.
 //
-// Work decomposition: grid.y walks the tile list (expert, first row) built
-// by the router; grid.x walks spans of output columns; each wave owns 16*MB
-// rows and NCB 16-column blocks.  Gate/up waves own matching gate and up
+// Work decomposition: the router's tile list (expert, first row) times
+// spans of output columns.  Gate/up workgroups own matching gate and up
 // columns, so the epilogue has both halves of h in the same lane.
 #include <type_traits>
 
@@ -57,73 +56,6 @@ struct Stage {
   int bs[NCB];     // E8M0 scale of each weight column block
 };
 
-// Operand addressing of one wave: NCB weight column blocks and MB 16-row
-// blocks of A.  Rows and columns outside the tile read row 0 / column block
-// 0 of the tile (their results are never stored), so every lane always
-// issues the same loads.
-template <int MB, int NCB, bool GATEUP>
-struct WaveOperands {
-  int col0;            // first gate column (gate/up) or output column (down)
-  bool bok[NCB];       // column block exists
-  const uint8_t* bcode[NCB];
-  const uint8_t* bscale[NCB];
-  const uint8_t* arow[MB];
-
-  __device__ __forceinline__ bool init(const GemmParams& p, int e, int m0, int rows, int row_base, int unit,
-                                       int r) {
-    constexpr int HALF = NCB / 2;
-    const int K = p.K, N = p.N, I = p.I, nblk = K >> 5;
-    int brow[NCB];
-    if (GATEUP) {
-      col0 = unit * HALF * 16;
-#pragma unroll
-      for (int j = 0; j < HALF; ++j) {
-        bok[j] = bok[HALF + j] = (col0 + 16 * j) < I;
-        brow[j] = col0 + 16 * j + r;
-        brow[HALF + j] = I + col0 + 16 * j + r;
-      }
-    } else {
-      col0 = unit * NCB * 16;
-#pragma unroll
-      for (int j = 0; j < NCB; ++j) {
-        bok[j] = (col0 + 16 * j) < N;
-        brow[j] = col0 + 16 * j + r;
-      }
-    }
-    if (!bok[0]) return false;
-#pragma unroll
-    for (int j = 0; j < NCB; ++j) {
-      const size_t rr = (size_t)e * N + (bok[j] ? brow[j] : brow[0]);
-      bcode[j] = p.b_codes + rr * (size_t)(K >> 1);
-      bscale[j] = p.b_scales + rr * (size_t)nblk;
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int m = (16 * mb + r) < rows ? 16 * mb + r : 0;
-      const size_t ar = GATEUP ? (size_t)(p.expert_rows[(size_t)e * p.T + m0 + m] / p.k) : (size_t)(row_base + m);
-      arow[mb] = p.a + ar * nblk * MX6_BLOCK_BYTES;
-    }
-    return true;
-  }
-
-  // loads chunk c (K blocks 4c .. 4c+3; lane group g takes block 4c+g,
-  // clamped to the last block)
-  __device__ __forceinline__ void load(int c, int g, int nblk, Stage<MB, NCB>& st) const {
-    const int blk = min(4 * c + g, nblk - 1);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const uint4* src = (const uint4*)(arow[mb] + (size_t)blk * MX6_BLOCK_BYTES);
-#pragma unroll
-      for (int q = 0; q < 5; ++q) st.a[mb][q] = src[q];
-    }
-#pragma unroll
-    for (int j = 0; j < NCB; ++j) {
-      st.bc[j] = *(const uint4*)(bcode[j] + (size_t)blk * 16);
-      st.bs[j] = bscale[j][blk];
-    }
-  }
-};
-
 // One 128-wide K step for every (row block, column block): three MFMAs,
 // one per FP6 term of A.  keep = 0 on lanes whose K block does not take
 // part (past the end of K or outside the wave's share): they contribute
@@ -150,26 +82,6 @@ __device__ __forceinline__ void mma_stage(v4f (&acc)[MB][NCB], const Stage<MB, N
       acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, b, acc[mb][j], 2, 4, 0, s1, 0, bsc);
       acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a2, b, acc[mb][j], 2, 4, 0, s2, 0, bsc);
     }
-  }
-}
-
-// Down epilogue: + b2, fp32 rows in expert-grouped order.
-template <int MB, int NCB>
-__device__ __forceinline__ void epilogue_down(const GemmParams& p, const v4f (&acc)[MB][NCB], const bool (&bok)[NCB],
-                                              int e, int rows, int row_base, int col0, int lane) {
-  const int g = lane >> 4, r = lane & 15, N = p.N;
-#pragma unroll
-  for (int j = 0; j < NCB; ++j) {
-    if (!bok[j]) continue;
-    const int col = col0 + 16 * j + r;
-    const float bias = p.bias[(size_t)e * N + col];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = 16 * mb + 4 * g + q;
-        if (row < rows) p.y[(size_t)(row_base + row) * N + col] = acc[mb][j][q] + bias;
-      }
   }
 }
 
@@ -216,135 +128,6 @@ __device__ __forceinline__ uint32_t split_h_row(float h0, float h1, int r, uint8
     s_codes_row[t][16 + r] = (uint8_t)k1;
   }
   return scw;
-}
-
-// Gate/up epilogue: + b13, clamped SwiGLU, MX6x3 split of h.  Gate column
-// block j pairs with up column block HALF + j; each 32-column group
-// (blocks 2pp, 2pp+1) is one MX block of h.  The amax of a row's 32 values
-// is reduced over the 16 lanes that hold that row; codes go through the
-// wave's LDS scratch (s_codes[16][3][32], s_sc[16]) to be packed.
-template <int MB, int NCB>
-__device__ __forceinline__ void epilogue_gateup(const GemmParams& p, const v4f (&acc)[MB][NCB],
-                                                const bool (&bok)[NCB], int e, int rows, int row_base, int col0,
-                                                int lane, uint8_t (*s_codes)[3][32], uint32_t* s_sc) {
-  constexpr int HALF = NCB / 2;
-  const int g = lane >> 4, r = lane & 15, N = p.N, I = p.I;
-  const int iblocks = I >> 5;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-    for (int pp = 0; pp < HALF / 2; ++pp) {
-      if (!bok[2 * pp]) continue;
-      const int c0 = col0 + 32 * pp + r;
-      const float bg0 = p.bias[(size_t)e * N + c0], bg1 = p.bias[(size_t)e * N + c0 + 16];
-      const float bu0 = p.bias[(size_t)e * N + I + c0], bu1 = p.bias[(size_t)e * N + I + c0 + 16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float h0 = clamped_swiglu(acc[mb][2 * pp][q] + bg0, acc[mb][HALF + 2 * pp][q] + bu0, p.clamp);
-        float h1 = clamped_swiglu(acc[mb][2 * pp + 1][q] + bg1, acc[mb][HALF + 2 * pp + 1][q] + bu1, p.clamp);
-        const int row = 4 * g + q;
-        uint32_t scw = 0;
-#pragma unroll
-        for (int t = 0; t < 3; ++t) {
-          float amax = fmaxf(fabsf(h0), fabsf(h1));
-          if (h0 != h0 || h1 != h1) amax = __builtin_inff();
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-          const int se = mx6_scale_exp(amax);
-          scw |= (uint32_t)se << (8 * t);
-          uint32_t k0 = 0, k1 = 0;
-          if (se != 255) {
-            const int kk = se - 127;
-            const float ih = exp2i(-(kk >> 1)), il = exp2i(-(kk - (kk >> 1)));
-            const float sh = exp2i(kk >> 1), sl = exp2i(kk - (kk >> 1));
-            float q0, q1;
-            k0 = e2m3_round((h0 * ih) * il, q0);
-            k1 = e2m3_round((h1 * ih) * il, q1);
-            h0 -= (q0 * sh) * sl;
-            h1 -= (q1 * sh) * sl;
-          }
-          s_codes[row][t][r] = (uint8_t)k0;
-          s_codes[row][t][16 + r] = (uint8_t)k1;
-        }
-        if (r == 0) s_sc[row] = scw;
-      }
-      lds_wave_sync();
-      const int blk = (col0 >> 5) + pp;
-      if (lane < 48) {
-        const int row = lane / 3, t = lane - 3 * (lane / 3);
-        if (16 * mb + row < rows) {
-          uint32_t pk[6];
-          pack6x32(s_codes[row][t], pk);
-          uint2* dst =
-              (uint2*)(p.hq + ((size_t)(row_base + 16 * mb + row) * iblocks + blk) * MX6_BLOCK_BYTES + 24 * t);
-          dst[0] = make_uint2(pk[0], pk[1]);
-          dst[1] = make_uint2(pk[2], pk[3]);
-          dst[2] = make_uint2(pk[4], pk[5]);
-        }
-      } else {
-        const int row = lane - 48;
-        if (16 * mb + row < rows) {
-          uint2* dst = (uint2*)(p.hq + ((size_t)(row_base + 16 * mb + row) * iblocks + blk) * MX6_BLOCK_BYTES + 72);
-          dst[0] = make_uint2(s_sc[row], 0u);
-        }
-      }
-      lds_wave_sync();
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Decode ("skinny") kernel: tiles of at most 16 rows.  The KS waves of a
-// workgroup share one set of NCB column blocks and split K between them, so
-// that many waves stream weights concurrently while each keeps a batch of D
-// chunks of loads in flight.  Wave 0 sums the K-slice partials from LDS in
-// a fixed order and runs the epilogue.
-template <int NCB, int KS, int D, bool GATEUP>
-__global__ __launch_bounds__(KS * 64) void expert_gemm_skinny(GemmParams p) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tile = blockIdx.y;
-  if (tile >= *p.n_tiles) return;
-  const int2 te = p.tiles[tile];
-  const int e = te.x, m0 = te.y;
-  const int rows = min(16, p.counts[e] - m0);
-  const int row_base = p.offsets[e] + m0;
-  const int nblk = p.K >> 5;
-  const int g = lane >> 4, r = lane & 15;
-  WaveOperands<1, NCB, GATEUP> op;
-  if (!op.init(p, e, m0, rows, row_base, blockIdx.x, r)) return;  // uniform over the workgroup
-
-  v4f acc[1][NCB];
-#pragma unroll
-  for (int j = 0; j < NCB; ++j) acc[0][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-  const int nchunk = (nblk + 3) >> 2, nfull = nblk >> 2;
-  const int cbeg = wave * nchunk / KS, cend = (wave + 1) * nchunk / KS;
-  for (int c0 = cbeg; c0 < cend; c0 += D) {
-    Stage<1, NCB> st[D];
-#pragma unroll
-    for (int i = 0; i < D; ++i) op.load(min(c0 + i, cend - 1), g, nblk, st[i]);
-#pragma unroll
-    for (int i = 0; i < D; ++i)
-      if (c0 + i < cend) mma_stage(acc, st[i], keep_mask<1, NCB>(4 * (c0 + i) + g < nblk));
-  }
-
-  __shared__ v4f s_acc[KS][NCB][64];
-  __shared__ uint8_t s_codes[16][3][32];
-  __shared__ uint32_t s_sc[16];
-#pragma unroll
-  for (int j = 0; j < NCB; ++j) s_acc[wave][j][lane] = acc[0][j];
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int j = 0; j < NCB; ++j) {
-    v4f t = s_acc[0][j][lane];
-#pragma unroll
-    for (int w = 1; w < KS; ++w) t += s_acc[w][j][lane];
-    acc[0][j] = t;
-  }
-  if (GATEUP)
-    epilogue_gateup<1, NCB>(p, acc, op.bok, e, rows, row_base, op.col0, lane, s_codes, s_sc);
-  else
-    epilogue_down<1, NCB>(p, acc, op.bok, e, rows, row_base, op.col0, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -615,14 +398,115 @@ constexpr int PF_NWM = 4;                   // waves (each 32 rows)
 constexpr int PF_ARS = 336;                 // LDS row stride of A (4 blocks x 80 B + 16 B pad)
 constexpr int PF_XCD = 8;                   // XCDs of the device
 
+// Prefill epilogues.  After the K loop the operand buffers are free; each
+// wave stages its results in its own part of them, 16 rows at a time, so
+// that the global stores are whole 16-byte pieces of consecutive bytes.
+//
+// Gate/up: h = clamped SwiGLU of (gate + b13, up + b13) is written to LDS as
+// fp32 [16][16*HALF + 4]; then four lanes per (row, 32-column block) split
+// the block into its three E2M3 terms (block maximum reduced across the
+// quad with DPP), assemble the 80-byte MX6x3 blocks in LDS, and the wave
+// copies the rows' blocks out.
+template <int NCB>
+__device__ __forceinline__ void pf_epilogue_gateup(const GemmParams& p, const v4f (&acc)[2][NCB], int e, int rows_w,
+                                                   int row_base_w, int col0, int lane, uint8_t* scratch) {
+  constexpr int HALF = NCB / 2;      // gate column blocks
+  constexpr int HS = 16 * HALF + 4;  // row stride of h in floats
+  constexpr int NB = HALF / 2;       // MX blocks of h per row
+  static_assert(HALF % 2 == 0, "gate span is whole 32-column blocks");
+  float* sh_h = (float*)scratch;
+  uint8_t* sh_blk = scratch + 16 * HS * 4;
+  const int g = lane >> 4, r = lane & 15, N = p.N, I = p.I;
+  const int nvalid = min(NB, (I - col0) >> 5);
+  float bg[HALF], bu[HALF];
+#pragma unroll
+  for (int j = 0; j < HALF; ++j) {
+    const int c = min(col0 + 16 * j + r, I - 1);  // columns past I are never stored
+    bg[j] = p.bias[(size_t)e * N + c];
+    bu[j] = p.bias[(size_t)e * N + I + c];
+  }
+  const int row = lane >> 2, q4 = lane & 3;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    if (16 * mb >= rows_w) break;
+#pragma unroll
+    for (int j = 0; j < HALF; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        sh_h[(4 * g + q) * HS + 16 * j + r] = clamped_swiglu(acc[mb][j][q] + bg[j], acc[mb][HALF + j][q] + bu[j], p.clamp);
+    lds_wave_sync();
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float* src = sh_h + row * HS + 32 * b + 8 * q4;
+      const v4f lo = *(const v4f*)src, hi = *(const v4f*)(src + 4);
+      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      uint64_t bits[3];
+      int sc[3];
+      mx6x3_split_quad<1, 2>(v, bits, sc);
+      uint8_t* dst = sh_blk + (row * NB + b) * MX6_BLOCK_BYTES;
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        uint16_t* d16 = (uint16_t*)(dst + 24 * t + 6 * q4);
+        d16[0] = (uint16_t)bits[t];
+        d16[1] = (uint16_t)(bits[t] >> 16);
+        d16[2] = (uint16_t)(bits[t] >> 32);
+      }
+      if (q4 == 0) *(uint2*)(dst + 72) = make_uint2((uint32_t)sc[0] | ((uint32_t)sc[1] << 8) | ((uint32_t)sc[2] << 16), 0u);
+    }
+    lds_wave_sync();
+    const int ppr = nvalid * (MX6_BLOCK_BYTES / 16);  // 16-byte pieces per row
+    const size_t rowbytes = (size_t)(I >> 5) * MX6_BLOCK_BYTES;
+    for (int pi = lane; pi < 16 * ppr; pi += 64) {
+      const int rw = pi / ppr, off = (pi - rw * ppr) * 16;
+      if (16 * mb + rw < rows_w)
+        *(v4u*)(p.hq + (size_t)(row_base_w + 16 * mb + rw) * rowbytes + (size_t)(col0 >> 5) * MX6_BLOCK_BYTES + off) =
+            *(const v4u*)(sh_blk + rw * NB * MX6_BLOCK_BYTES + off);
+    }
+    lds_wave_sync();
+  }
+}
+
+// Down: y = acc + b2 (fp32) is staged as [16][16*NCB + 4] and copied out as
+// float4 pieces of whole rows.
+template <int NCB>
+__device__ __forceinline__ void pf_epilogue_down(const GemmParams& p, const v4f (&acc)[2][NCB], int e, int rows_w,
+                                                 int row_base_w, int col0, int lane, uint8_t* scratch) {
+  constexpr int YS = 16 * NCB + 4;
+  float* sh_y = (float*)scratch;
+  const int g = lane >> 4, r = lane & 15, N = p.N;
+  const int c4n = min(16 * NCB, N - col0) >> 2;  // float4 pieces per row inside N
+  float bias[NCB];
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) bias[j] = p.bias[(size_t)e * N + min(col0 + 16 * j + r, N - 1)];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    if (16 * mb >= rows_w) break;
+#pragma unroll
+    for (int j = 0; j < NCB; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sh_y[(4 * g + q) * YS + 16 * j + r] = acc[mb][j][q] + bias[j];
+    lds_wave_sync();
+    for (int pi = lane; pi < 16 * c4n; pi += 64) {
+      const int rw = pi / c4n, c4 = pi - rw * c4n;
+      if (16 * mb + rw < rows_w)
+        *(v4f*)(p.y + (size_t)(row_base_w + 16 * mb + rw) * N + col0 + 4 * c4) = *(const v4f*)(sh_y + rw * YS + 4 * c4);
+    }
+    lds_wave_sync();
+  }
+}
+
 template <bool GATEUP, int NCB>
 struct PfShared {
   uint8_t a[2][PF_MT * PF_ARS];
   uint8_t b[2][NCB * 16 * 64];
   uint8_t bs[2][NCB * 16 * 4];
-  uint8_t codes[PF_NWM][16][3][32];
-  uint32_t sc[PF_NWM][16];
 };
+// per-wave epilogue scratch inside the A buffers: max of the down staging
+// (16 x (320 + 4) floats) and the gate/up staging (16 x (160 + 4) floats +
+// 16 x 5 MX6x3 blocks)
+constexpr int PF_EPI_BYTES = 16 * (16 * 20 + 4) * 4;
+static_assert(PF_EPI_BYTES >= 16 * (16 * 10 + 4) * 4 + 16 * 5 * MX6_BLOCK_BYTES, "gate/up staging fits");
+static_assert(PF_NWM * PF_EPI_BYTES <= 2 * PF_MT * PF_ARS, "epilogue staging fits the A buffers");
 
 template <bool GATEUP, int NCB>
 __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams p, int spans) {
@@ -632,6 +516,7 @@ __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams
   constexpr int B_PIECES = NBR * 4 / (PF_NWM * 64);    // 16-B B pieces per thread per chunk
   constexpr int S_PIECES = NBR * 4 / (PF_NWM * 64);    // scale bytes per thread per chunk
   static_assert(PF_MT * 20 % (PF_NWM * 64) == 0 && NBR * 4 % (PF_NWM * 64) == 0, "even staging split");
+  static_assert(16 * (16 * NCB + 4) * 4 <= PF_EPI_BYTES, "epilogue staging fits");
   __shared__ __align__(16) PfShared<GATEUP, NCB> sh;
 
   // ---- work item ----
@@ -802,51 +687,14 @@ __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams
     __syncthreads();
   }
 
+  // the loop's last barrier has passed: the operand buffers are free
   const int rows_w = rows - 32 * wave;
   const int row_base_w = row_base + 32 * wave;
+  uint8_t* scratch = &sh.a[0][0] + wave * PF_EPI_BYTES;
   if (GATEUP)
-    epilogue_gateup<MB, NCB>(p, acc, bok, e, rows_w, row_base_w, col0, lane, sh.codes[wave], sh.sc[wave]);
+    pf_epilogue_gateup<NCB>(p, acc, e, rows_w, row_base_w, col0, lane, scratch);
   else
-    epilogue_down<MB, NCB>(p, acc, bok, e, rows_w, row_base_w, col0, lane);
-}
-
-// ---------------------------------------------------------------------------
-// General kernel (tiles of 16*MB rows): each of the NW waves owns NCB column
-// blocks over the whole K range.
-template <int MB, int NCB, int NW, int D, bool GATEUP>
-__global__ __launch_bounds__(NW * 64) void expert_gemm_kernel(GemmParams p) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tile = blockIdx.y;
-  if (tile >= *p.n_tiles) return;
-  const int2 te = p.tiles[tile];
-  const int e = te.x, m0 = te.y;
-  const int rows = min(16 * MB, p.counts[e] - m0);
-  const int row_base = p.offsets[e] + m0;
-  const int nblk = p.K >> 5;
-  const int g = lane >> 4, r = lane & 15;
-  WaveOperands<MB, NCB, GATEUP> op;
-  if (!op.init(p, e, m0, rows, row_base, blockIdx.x * NW + wave, r)) return;
-
-  v4f acc[MB][NCB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int j = 0; j < NCB; ++j) acc[mb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-  const int nchunk = (nblk + 3) >> 2, nfull = nblk >> 2;
-  for (int c0 = 0; c0 < nchunk; c0 += D) {
-    Stage<MB, NCB> st[D];
-#pragma unroll
-    for (int i = 0; i < D; ++i) op.load(min(c0 + i, nchunk - 1), g, nblk, st[i]);
-#pragma unroll
-    for (int i = 0; i < D; ++i)
-      if (c0 + i < nchunk) mma_stage(acc, st[i], keep_mask<MB, NCB>(4 * (c0 + i) + g < nblk));
-  }
-  __shared__ uint8_t s_codes[NW][16][3][32];
-  __shared__ uint32_t s_sc[NW][16];
-  if (GATEUP)
-    epilogue_gateup<MB, NCB>(p, acc, op.bok, e, rows, row_base, op.col0, lane, s_codes[wave], s_sc[wave]);
-  else
-    epilogue_down<MB, NCB>(p, acc, op.bok, e, rows, row_base, op.col0, lane);
+    pf_epilogue_down<NCB>(p, acc, e, rows_w, row_base_w, col0, lane, scratch);
 }
 
 // The prefill kernel addresses operands with 32-bit byte offsets.
@@ -858,9 +706,10 @@ static bool prefill_offsets_fit(const GemmParams& p) {
 }
 
 // Launch configurations.
-//   small-M (tiles of 16 rows, decode): skinny kernel, 4 waves split K over
-//     one 64-column span (gate/up: 32 gate + 32 up columns);
-//   large-M (prefill): four 16-row blocks per wave, four waves per span.
+//   small-M (tiles of 16 rows, decode): grid (64-column spans, tiles), four
+//     waves stream one span's weights through LDS;
+//   large-M (prefill): one workgroup per (128-row tile, 320-column span)
+//     work item, 1-D grid dealt to the XCDs in contiguous ranges.
 int launch_gemm_gateup(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s) {
   if (small_m) {
     dim3 grid((p.I + 31) / 32, max_tiles);

@@ -144,8 +144,14 @@ __device__ __forceinline__ void mx6x3_split_quad(float (&v)[8], uint64_t (&bits)
       nan |= (v[i] != v[i]);
     }
     if (nan) amax = __builtin_inff();
-    amax = fmaxf(amax, __shfl_xor(amax, X1));
-    amax = fmaxf(amax, __shfl_xor(amax, X2));
+    if constexpr (X1 == 1 && X2 == 2) {
+      // lanes of a quad: DPP quad_perm [1,0,3,2] and [2,3,0,1]
+      amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0xB1, 0xf, 0xf, false)));
+      amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x4E, 0xf, 0xf, false)));
+    } else {
+      amax = fmaxf(amax, __shfl_xor(amax, X1));
+      amax = fmaxf(amax, __shfl_xor(amax, X2));
+    }
     const int se = mx6_scale_exp(amax);
     sc[t] = se;
     if (se == 255) continue;
