@@ -73,15 +73,24 @@ __device__ __forceinline__ void mma_stage(v4f (&acc)[MB][NCB], const Stage<MB, N
     const v8i a2 = {(int)aw[12], (int)aw[13], (int)aw[14], (int)aw[15], (int)aw[16], (int)aw[17], 0, 0};
     const int sw = (int)aw[18];
     const int s0 = sw & 0xff, s1 = (sw >> 8) & 0xff, s2 = (sw >> 16) & 0xff;
+    v8i b[NCB];
+    int bsc[NCB];
 #pragma unroll
     for (int j = 0; j < NCB; ++j) {
-      const v8i b = {(int)(st.bc[j].x & keep), (int)(st.bc[j].y & keep), (int)(st.bc[j].z & keep),
-                     (int)(st.bc[j].w & keep), 0, 0, 0, 0};
-      const int bsc = (int)(((uint32_t)st.bs[j] & keep) | (127u & ~keep));
-      acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, b, acc[mb][j], 2, 4, 0, s0, 0, bsc);
-      acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, b, acc[mb][j], 2, 4, 0, s1, 0, bsc);
-      acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a2, b, acc[mb][j], 2, 4, 0, s2, 0, bsc);
+      b[j] = (v8i){(int)(st.bc[j].x & keep), (int)(st.bc[j].y & keep), (int)(st.bc[j].z & keep),
+                   (int)(st.bc[j].w & keep), 0, 0, 0, 0};
+      bsc[j] = (int)(((uint32_t)st.bs[j] & keep) | (127u & ~keep));
     }
+    // term-major order: consecutive MFMAs use different accumulators
+#pragma unroll
+    for (int j = 0; j < NCB; ++j)
+      acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, b[j], acc[mb][j], 2, 4, 0, s0, 0, bsc[j]);
+#pragma unroll
+    for (int j = 0; j < NCB; ++j)
+      acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, b[j], acc[mb][j], 2, 4, 0, s1, 0, bsc[j]);
+#pragma unroll
+    for (int j = 0; j < NCB; ++j)
+      acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a2, b[j], acc[mb][j], 2, 4, 0, s2, 0, bsc[j]);
   }
 }
 
@@ -381,13 +390,15 @@ __global__ __launch_bounds__(DEC_NW * 64, 3) void expert_gemm_decode(GemmParams 
 // 32w .. 32w+31 (two 16-row blocks) and all NCB column blocks, so its
 // accumulators (2 x NCB 16x16 tiles) sit in the register file and every B
 // fragment read from LDS feeds six MFMAs.  K advances in chunks of four
-// 32-element blocks through two LDS buffers: the global loads of chunk c+1
-// are issued into registers before chunk c is consumed and written to the
-// other buffer after its MFMAs have been issued, one barrier per chunk.
-// Inside a chunk the B fragment of column block j+1 is read from LDS while
-// the MFMAs of block j run.  A rows are padded to 336 bytes in LDS and B
-// rows are stored with their four 16-byte pieces XOR-swizzled by
-// (row >> 2) & 3, so the operand reads are free of LDS bank conflicts.
+// 32-element blocks.  A rows are not shared between waves, so each wave
+// loads its own A fragments straight from global memory into registers,
+// one chunk ahead.  The weight tile (shared by the four waves) goes
+// through two LDS buffers: its global loads for chunk c+1 are issued into
+// registers before chunk c is consumed and written to the other buffer
+// after chunk c's MFMAs have been issued, one barrier per chunk.  Inside a
+// chunk, B fragments are read from LDS PF_BPRE column blocks ahead of their
+// MFMAs.  B rows are stored with their four 16-byte pieces XOR-swizzled by
+// (row >> 2) & 3, so the fragment reads are free of LDS bank conflicts.
 //
 // Work items (tile, column span) are numbered tile-major and dealt to the
 // eight XCDs in contiguous ranges (workgroup i runs on XCD i mod 8), so the
@@ -395,8 +406,8 @@ __global__ __launch_bounds__(DEC_NW * 64, 3) void expert_gemm_decode(GemmParams 
 // one expert -- which share its weights -- meet in the same L2.
 constexpr int PF_MT = 128;                  // rows per tile
 constexpr int PF_NWM = 4;                   // waves (each 32 rows)
-constexpr int PF_ARS = 336;                 // LDS row stride of A (4 blocks x 80 B + 16 B pad)
 constexpr int PF_XCD = 8;                   // XCDs of the device
+constexpr int PF_BPRE = 3;                  // B fragments read ahead of their MFMAs
 
 // Prefill epilogues.  After the K loop the operand buffers are free; each
 // wave stages its results in its own part of them, 16 rows at a time, so
@@ -497,27 +508,28 @@ __device__ __forceinline__ void pf_epilogue_down(const GemmParams& p, const v4f 
 
 template <bool GATEUP, int NCB>
 struct PfShared {
-  uint8_t a[2][PF_MT * PF_ARS];
   uint8_t b[2][NCB * 16 * 64];
   uint8_t bs[2][NCB * 16 * 4];
 };
-// per-wave epilogue scratch inside the A buffers: max of the down staging
-// (16 x (320 + 4) floats) and the gate/up staging (16 x (160 + 4) floats +
-// 16 x 5 MX6x3 blocks)
+// per-wave epilogue scratch: max of the down staging (16 x (320 + 4)
+// floats) and the gate/up staging (16 x (160 + 4) floats + 16 x 5 MX6x3
+// blocks); the weight buffers share its first bytes (the epilogue starts
+// after the loop's last barrier)
 constexpr int PF_EPI_BYTES = 16 * (16 * 20 + 4) * 4;
 static_assert(PF_EPI_BYTES >= 16 * (16 * 10 + 4) * 4 + 16 * 5 * MX6_BLOCK_BYTES, "gate/up staging fits");
-static_assert(PF_NWM * PF_EPI_BYTES <= 2 * PF_MT * PF_ARS, "epilogue staging fits the A buffers");
 
 template <bool GATEUP, int NCB>
 __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams p, int spans) {
   constexpr int MB = 2;
   constexpr int NBR = NCB * 16;                        // B rows per tile
-  constexpr int A_PIECES = PF_MT * 20 / (PF_NWM * 64); // 16-B A pieces per thread per chunk (10)
   constexpr int B_PIECES = NBR * 4 / (PF_NWM * 64);    // 16-B B pieces per thread per chunk
   constexpr int S_PIECES = NBR * 4 / (PF_NWM * 64);    // scale bytes per thread per chunk
-  static_assert(PF_MT * 20 % (PF_NWM * 64) == 0 && NBR * 4 % (PF_NWM * 64) == 0, "even staging split");
+  static_assert(NBR * 4 % (PF_NWM * 64) == 0, "even staging split");
   static_assert(16 * (16 * NCB + 4) * 4 <= PF_EPI_BYTES, "epilogue staging fits");
-  __shared__ __align__(16) PfShared<GATEUP, NCB> sh;
+  static_assert(NCB % 4 == 0, "scales are packed four column blocks per dword");
+  static_assert(sizeof(PfShared<GATEUP, NCB>) <= PF_NWM * PF_EPI_BYTES, "weight buffers fit the scratch");
+  __shared__ __align__(16) uint8_t smem[PF_NWM * PF_EPI_BYTES];
+  PfShared<GATEUP, NCB>& sh = *reinterpret_cast<PfShared<GATEUP, NCB>*>(smem);
 
   // ---- work item ----
   const int total = *p.n_tiles * spans;
@@ -538,36 +550,38 @@ __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams
   // ---- columns of the tile ----
   constexpr int HALF = NCB / 2;
   int col0;
-  bool bok[NCB];
   if (GATEUP) {
     col0 = span * HALF * 16;
-#pragma unroll
-    for (int j = 0; j < HALF; ++j) bok[j] = bok[HALF + j] = (col0 + 16 * j) < I;
   } else {
     col0 = span * NCB * 16;
-#pragma unroll
-    for (int j = 0; j < NCB; ++j) bok[j] = (col0 + 16 * j) < N;
   }
 
-  // ---- per-thread staging offsets (fixed over K; the launcher checks
-  // that every offset fits 32 bits) ----
-  // A piece q of this thread: tile row (tid + 256q) / 20, piece (tid + 256q) % 20
-  // (block-in-chunk piece / 5, 16-byte part piece % 5); low 2 bits hold the
-  // block-in-chunk, the rest the byte offset of the row's part.
+  // ---- operand addressing: buffer resources over the whole A, code and
+  // scale arrays (their sizes fit 32 bits; the launcher checks); each
+  // lane's offsets are fixed over K and the chunk advance is a uniform
+  // scalar offset.  Lanes past the end of K read the next row or past the
+  // array (zero), and are masked off in the MFMAs.
   const uint32_t a_rowbytes = (uint32_t)nblk * MX6_BLOCK_BYTES;
-  uint32_t a_off[A_PIECES];
-  StaticFor<0, A_PIECES>::run([&](auto ic) {
-    constexpr int q = decltype(ic)::value;
-    const int pc = tid + PF_NWM * 64 * q;
-    const int row = pc / 20, piece = pc - 20 * (pc / 20);
-    const int m = row < rows ? row : 0;  // rows past the tile read tile row 0
-    const uint32_t ar = GATEUP ? (uint32_t)(p.expert_rows[(size_t)e * p.T + m0 + m] / p.k) : (uint32_t)(row_base + m);
-    a_off[q] = ar * a_rowbytes + (uint32_t)((piece % 5) * 16) + (uint32_t)(piece / 5);
-  });
+  const uint32_t a_rows_total = GATEUP ? (uint32_t)p.T : (uint32_t)(p.T * p.k);
+  const __amdgpu_buffer_rsrc_t arsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.a, 0, (int)(a_rows_total * a_rowbytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.b_codes, 0, (int)((uint32_t)p.E * (uint32_t)N * (uint32_t)(K >> 1)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.b_scales, 0, (int)((uint32_t)p.E * (uint32_t)N * (uint32_t)nblk), 0x00020000);
+  // A: tile rows 32w + 16mb + r (rows past the tile read tile row 0), block g of the chunk
+  uint32_t a_off[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int row = 32 * wave + 16 * mb + r;
+    const int m = row < rows ? row : 0;
+    a_off[mb] = (GATEUP ? (uint32_t)(p.expert_rows[(size_t)e * p.T + m0 + m] / p.k) : (uint32_t)(row_base + m)) *
+                    a_rowbytes + (uint32_t)g * MX6_BLOCK_BYTES;
+  }
   // B piece q: weight row n = tid/4 + 64q of the tile, 16-byte piece tid % 4
   // of each chunk; missing column blocks read block 0
   const int bpiece = tid & 3;
-  uint32_t b_row[B_PIECES];
+  uint32_t b_off[B_PIECES], s_off[S_PIECES];
   StaticFor<0, B_PIECES>::run([&](auto ic) {
     constexpr int q = decltype(ic)::value;
     const int n = (tid >> 2) + PF_NWM * 16 * q;
@@ -580,43 +594,46 @@ __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams
     } else {
       row = ((col0 + 16 * j) < N ? col0 + 16 * j : col0) + rr;
     }
-    b_row[q] = (uint32_t)e * (uint32_t)N + (uint32_t)row;
+    const uint32_t brow = (uint32_t)e * (uint32_t)N + (uint32_t)row;
+    b_off[q] = brow * (uint32_t)(K >> 1) + (uint32_t)bpiece * 16u;
+    s_off[q] = brow * (uint32_t)nblk + (uint32_t)bpiece;
   });
 
-  // ---- staging: global -> registers -> LDS ----
-  v4u ra[A_PIECES], rb[B_PIECES];
+  // ---- A: global -> registers ----
+  auto load_a = [&](int c, v4u (&av)[MB][5]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int q = 0; q < 5; ++q)
+        av[mb][q] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(arsrc, a_off[mb] + 16 * q,
+                                                                                  c * 4 * MX6_BLOCK_BYTES, 0));
+  };
+  // ---- B: global -> registers -> LDS ----
+  v4u rb[B_PIECES];
   uint32_t rs[S_PIECES];
   auto stage_load = [&](int c) {
-    StaticFor<0, A_PIECES>::run([&](auto ic) {
-      constexpr int q = decltype(ic)::value;
-      const int blk = min(4 * c + (int)(a_off[q] & 3u), nblk - 1);
-      ra[q] = *(const v4u*)(p.a + (size_t)((a_off[q] & ~3u) + (uint32_t)blk * MX6_BLOCK_BYTES));
-    });
-    const int blk = min(4 * c + bpiece, nblk - 1);
     StaticFor<0, B_PIECES>::run([&](auto ic) {
       constexpr int q = decltype(ic)::value;
-      rb[q] = *(const v4u*)(p.b_codes + (size_t)(b_row[q] * (uint32_t)(K >> 1) + (uint32_t)blk * 16u));
+      rb[q] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(crsrc, b_off[q], c * 64, 0));
     });
     StaticFor<0, S_PIECES>::run([&](auto ic) {
       constexpr int q = decltype(ic)::value;
-      rs[q] = p.b_scales[(size_t)(b_row[q] * (uint32_t)nblk + (uint32_t)blk)];
+      rs[q] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, s_off[q], c * 4, 0);
     });
   };
   auto stage_store = [&](int buf) {
-    StaticFor<0, A_PIECES>::run([&](auto ic) {
-      constexpr int q = decltype(ic)::value;
-      const int pc = tid + PF_NWM * 64 * q;
-      const int row = pc / 20, piece = pc - 20 * (pc / 20);
-      *(v4u*)(sh.a[buf] + row * PF_ARS + piece * 16) = ra[q];
-    });
     StaticFor<0, B_PIECES>::run([&](auto ic) {
       constexpr int q = decltype(ic)::value;
       const int n = (tid >> 2) + PF_NWM * 16 * q;
       *(v4u*)(sh.b[buf] + n * 64 + ((bpiece ^ ((n >> 2) & 3)) * 16)) = rb[q];
     });
+    // scale of (column n = 16j + r, block g) at byte ((j/4 * 4 + g) * 16 + r) * 4 + j % 4:
+    // one dword read gives a lane the scales of four column blocks
     StaticFor<0, S_PIECES>::run([&](auto ic) {
       constexpr int q = decltype(ic)::value;
-      sh.bs[buf][tid + PF_NWM * 64 * q] = (uint8_t)rs[q];
+      const int n = (tid >> 2) + PF_NWM * 16 * q;
+      const int j = n >> 4, rr = n & 15;
+      sh.bs[buf][(((j >> 2) * 4 + bpiece) * 16 + rr) * 4 + (j & 3)] = (uint8_t)rs[q];
     });
   };
 
@@ -626,71 +643,78 @@ __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams
 #pragma unroll
     for (int j = 0; j < NCB; ++j) acc[mb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int c, int buf) {
+  // One chunk: A fragments are taken out of the load registers, which are
+  // refilled at once with the next chunk (as are the weight staging
+  // registers); then the B fragments are read from LDS PF_BPRE column blocks
+  // ahead of their MFMAs.  Lanes whose K block lies past the end of K
+  // contribute zero codes with unit scales on both operands.  The body is
+  // one basic block (the last iteration reloads the last chunk), so the
+  // scheduling barriers keep the LDS stores behind the MFMAs and the global
+  // loads' latency behind both.
+  const int nchunk = (nblk + 3) >> 2;
+  v4u av[MB][5];
+  load_a(0, av);
+  stage_load(0);
+  stage_store(0);
+  __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    const int buf = c & 1;
     const uint32_t keep = (4 * c + g) < nblk ? 0xffffffffu : 0u;
     v8i a[MB][3];
     int as[MB][3];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const uint8_t* src = sh.a[buf] + (32 * wave + 16 * mb + r) * PF_ARS + g * MX6_BLOCK_BYTES;
       uint32_t w[20];
 #pragma unroll
       for (int q = 0; q < 5; ++q) {
-        const v4u t = *(const v4u*)(src + 16 * q);
-        w[4 * q] = t.x; w[4 * q + 1] = t.y; w[4 * q + 2] = t.z; w[4 * q + 3] = t.w;
+        w[4 * q] = av[mb][q].x & keep; w[4 * q + 1] = av[mb][q].y & keep;
+        w[4 * q + 2] = av[mb][q].z & keep; w[4 * q + 3] = av[mb][q].w & keep;
       }
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
         a[mb][t] = (v8i){(int)w[6 * t], (int)w[6 * t + 1], (int)w[6 * t + 2], (int)w[6 * t + 3], (int)w[6 * t + 4],
                          (int)w[6 * t + 5], 0, 0};
-        as[mb][t] = (int)((w[18] >> (8 * t)) & 0xffu);
+        as[mb][t] = (int)(((w[18] >> (8 * t)) & 0xffu) | (127u & ~keep));
       }
     }
-    // B fragments one column block ahead of the MFMAs that use them
-    v4u bq[2];
-    uint32_t bsb[2];
-    auto read_b = [&](int j, int slot) {
+    const int cn = min(c + 1, nchunk - 1);
+    load_a(cn, av);
+    stage_load(cn);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t bsw[NCB / 4];
+#pragma unroll
+    for (int jj = 0; jj < NCB / 4; ++jj) bsw[jj] = *(const uint32_t*)(sh.bs[buf] + ((jj * 4 + g) * 16 + r) * 4);
+    v4u bq[PF_BPRE + 1];
+    auto read_b = [&](int j) {
       const int n = 16 * j + r;
-      bq[slot] = *(const v4u*)(sh.b[buf] + n * 64 + ((g ^ ((n >> 2) & 3)) * 16));
-      bsb[slot] = sh.bs[buf][n * 4 + g];
+      bq[j % (PF_BPRE + 1)] = *(const v4u*)(sh.b[buf] + n * 64 + ((g ^ ((n >> 2) & 3)) * 16));
     };
-    read_b(0, 0);
+    StaticFor<0, PF_BPRE>::run([&](auto jc) { read_b(decltype(jc)::value); });
     StaticFor<0, NCB>::run([&](auto jc) {
       constexpr int j = decltype(jc)::value;
-      if constexpr (j + 1 < NCB) read_b(j + 1, (j + 1) & 1);
-      const v4u b4 = bq[j & 1];
-      const int bsc = (int)((bsb[j & 1] & keep) | (127u & ~keep));
+      if constexpr (j + PF_BPRE < NCB) read_b(j + PF_BPRE);
+      const v4u b4 = bq[j % (PF_BPRE + 1)];
+      const uint32_t braw = (bsw[j >> 2] >> (8 * (j & 3))) & 0xffu;
+      const int bsc = (int)((braw & keep) | (127u & ~keep));
       const v8i b = {(int)(b4.x & keep), (int)(b4.y & keep), (int)(b4.z & keep), (int)(b4.w & keep), 0, 0, 0, 0};
+      // the two row blocks alternate, so consecutive MFMAs never depend on
+      // each other
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int t = 0; t < 3; ++t)
 #pragma unroll
-        for (int t = 0; t < 3; ++t)
+        for (int mb = 0; mb < MB; ++mb)
           acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[mb][t], b, acc[mb][j], 2, 4, 0, as[mb][t],
                                                                         0, bsc);
       __builtin_amdgcn_sched_barrier(0);
     });
-  };
-
-  const int nchunk = (nblk + 3) >> 2;
-  stage_load(0);
-  stage_store(0);
-  __syncthreads();
-  // The loop body is one basic block (the last iteration reloads the last
-  // chunk into the idle buffer), so the scheduling barriers keep the LDS
-  // stores behind the MFMAs and the global loads' latency behind both.
-  for (int c = 0; c < nchunk; ++c) {
-    stage_load(min(c + 1, nchunk - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    compute(c, c & 1);
-    __builtin_amdgcn_sched_barrier(0);
     stage_store((c + 1) & 1);
     __syncthreads();
   }
 
-  // the loop's last barrier has passed: the operand buffers are free
+  // the loop's last barrier has passed: the weight buffers are free
   const int rows_w = rows - 32 * wave;
   const int row_base_w = row_base + 32 * wave;
-  uint8_t* scratch = &sh.a[0][0] + wave * PF_EPI_BYTES;
+  uint8_t* scratch = smem + wave * PF_EPI_BYTES;
   if (GATEUP)
     pf_epilogue_gateup<NCB>(p, acc, e, rows_w, row_base_w, col0, lane, scratch);
   else
