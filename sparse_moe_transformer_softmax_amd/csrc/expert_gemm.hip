@@ -385,27 +385,33 @@ __global__ __launch_bounds__(DEC_NW * 64, 3) void expert_gemm_decode(GemmParams 
 }
 
 // ---------------------------------------------------------------------------
-// Prefill kernel: tiles of PF_MT = 128 rows.  A workgroup of four waves
-// computes a 128-row x (16*NCB)-column output tile; wave w owns rows
-// 32w .. 32w+31 (two 16-row blocks) and all NCB column blocks, so its
-// accumulators (2 x NCB 16x16 tiles) sit in the register file and every B
-// fragment read from LDS feeds six MFMAs.  K advances in chunks of four
-// 32-element blocks.  A rows are not shared between waves, so each wave
-// loads its own A fragments straight from global memory into registers,
-// one chunk ahead.  The weight tile (shared by the four waves) goes
-// through two LDS buffers: its global loads for chunk c+1 are issued into
-// registers before chunk c is consumed and written to the other buffer
-// after chunk c's MFMAs have been issued, one barrier per chunk.  Inside a
-// chunk, B fragments are read from LDS PF_BPRE column blocks ahead of their
-// MFMAs.  B rows are stored with their four 16-byte pieces XOR-swizzled by
-// (row >> 2) & 3, so the fragment reads are free of LDS bank conflicts.
+// Prefill kernel: tiles of PF_MT = 64 rows x 256 output columns (gate/up:
+// 128 gate + the matching 128 up columns).  A workgroup has four waves and
+// two workgroups share a CU, so every SIMD runs two waves (a single wave per
+// SIMD issues the block-scaled MFMAs at only about 60% of the pipe's rate)
+// and one workgroup's start and epilogue overlap the other's K loop.  Wave
+// (wm, wn) owns rows 32wm .. 32wm+31 (two 16-row blocks) and column half wn
+// (gate/up: 64 gate + 64 up columns, i.e. two whole MX blocks of h), eight
+// 16-column blocks in all, so every B fragment read from LDS feeds six
+// MFMAs.  K advances in
+// chunks of four 32-element blocks.  Each wave loads its A fragments
+// straight from global memory into registers, one chunk ahead.  The weight
+// tile goes through two LDS buffers: its global loads for chunk c+1 are
+// issued into registers before chunk c is consumed and written to the
+// other buffer after chunk c's MFMAs have been issued, one barrier per
+// chunk.  Inside a chunk, B fragments are read from LDS PF_BPRE column
+// blocks ahead of their MFMAs.  B rows are stored with their four 16-byte
+// pieces XOR-swizzled by (row >> 2) & 3, so the fragment reads are free of
+// LDS bank conflicts.
 //
 // Work items (tile, column span) are numbered tile-major and dealt to the
 // eight XCDs in contiguous ranges (workgroup i runs on XCD i mod 8), so the
 // column spans of one tile -- which share its A rows -- and the tiles of
 // one expert -- which share its weights -- meet in the same L2.
-constexpr int PF_MT = 128;                  // rows per tile
-constexpr int PF_NWM = 4;                   // waves (each 32 rows)
+constexpr int PF_MT = 64;                   // rows per tile
+constexpr int PF_NT = 256;                  // weight rows (output columns) per tile
+constexpr int PF_NW = 4;                    // waves: 2 row halves x 2 column halves
+constexpr int PF_NCB = 8;                   // 16-column blocks per wave
 constexpr int PF_XCD = 8;                   // XCDs of the device
 constexpr int PF_BPRE = 3;                  // B fragments read ahead of their MFMAs
 
@@ -419,23 +425,17 @@ constexpr int PF_BPRE = 3;                  // B fragments read ahead of their M
 // quad with DPP), assemble the 80-byte MX6x3 blocks in LDS, and the wave
 // copies the rows' blocks out.
 template <int NCB>
-__device__ __forceinline__ void pf_epilogue_gateup(const GemmParams& p, const v4f (&acc)[2][NCB], int e, int rows_w,
-                                                   int row_base_w, int col0, int lane, uint8_t* scratch) {
+__device__ __forceinline__ void pf_epilogue_gateup(const GemmParams& p, const v4f (&acc)[2][NCB],
+                                                   const float (&bias)[NCB], int rows_w, int row_base_w, int col0,
+                                                   int lane, uint8_t* scratch) {
   constexpr int HALF = NCB / 2;      // gate column blocks
   constexpr int HS = 16 * HALF + 4;  // row stride of h in floats
   constexpr int NB = HALF / 2;       // MX blocks of h per row
   static_assert(HALF % 2 == 0, "gate span is whole 32-column blocks");
   float* sh_h = (float*)scratch;
   uint8_t* sh_blk = scratch + 16 * HS * 4;
-  const int g = lane >> 4, r = lane & 15, N = p.N, I = p.I;
+  const int g = lane >> 4, r = lane & 15, I = p.I;
   const int nvalid = min(NB, (I - col0) >> 5);
-  float bg[HALF], bu[HALF];
-#pragma unroll
-  for (int j = 0; j < HALF; ++j) {
-    const int c = min(col0 + 16 * j + r, I - 1);  // columns past I are never stored
-    bg[j] = p.bias[(size_t)e * N + c];
-    bu[j] = p.bias[(size_t)e * N + I + c];
-  }
   const int row = lane >> 2, q4 = lane & 3;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
@@ -444,7 +444,8 @@ __device__ __forceinline__ void pf_epilogue_gateup(const GemmParams& p, const v4
     for (int j = 0; j < HALF; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        sh_h[(4 * g + q) * HS + 16 * j + r] = clamped_swiglu(acc[mb][j][q] + bg[j], acc[mb][HALF + j][q] + bu[j], p.clamp);
+        sh_h[(4 * g + q) * HS + 16 * j + r] =
+            clamped_swiglu(acc[mb][j][q] + bias[j], acc[mb][HALF + j][q] + bias[HALF + j], p.clamp);
     lds_wave_sync();
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -480,15 +481,13 @@ __device__ __forceinline__ void pf_epilogue_gateup(const GemmParams& p, const v4
 // Down: y = acc + b2 (fp32) is staged as [16][16*NCB + 4] and copied out as
 // float4 pieces of whole rows.
 template <int NCB>
-__device__ __forceinline__ void pf_epilogue_down(const GemmParams& p, const v4f (&acc)[2][NCB], int e, int rows_w,
-                                                 int row_base_w, int col0, int lane, uint8_t* scratch) {
+__device__ __forceinline__ void pf_epilogue_down(const GemmParams& p, const v4f (&acc)[2][NCB],
+                                                 const float (&bias)[NCB], int rows_w, int row_base_w, int col0,
+                                                 int lane, uint8_t* scratch) {
   constexpr int YS = 16 * NCB + 4;
   float* sh_y = (float*)scratch;
   const int g = lane >> 4, r = lane & 15, N = p.N;
   const int c4n = min(16 * NCB, N - col0) >> 2;  // float4 pieces per row inside N
-  float bias[NCB];
-#pragma unroll
-  for (int j = 0; j < NCB; ++j) bias[j] = p.bias[(size_t)e * N + min(col0 + 16 * j + r, N - 1)];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     if (16 * mb >= rows_w) break;
@@ -506,30 +505,25 @@ __device__ __forceinline__ void pf_epilogue_down(const GemmParams& p, const v4f 
   }
 }
 
-template <bool GATEUP, int NCB>
 struct PfShared {
-  uint8_t b[2][NCB * 16 * 64];
-  uint8_t bs[2][NCB * 16 * 4];
+  uint8_t b[2][PF_NT * 64];
+  uint8_t bs[2][PF_NT * 4];
 };
-// per-wave epilogue scratch: max of the down staging (16 x (320 + 4)
-// floats) and the gate/up staging (16 x (160 + 4) floats + 16 x 5 MX6x3
-// blocks); the weight buffers share its first bytes (the epilogue starts
+// per-wave epilogue scratch: max of the down staging (16 x (128 + 4)
+// floats) and the gate/up staging (16 x (64 + 4) floats + 16 x 2 MX6x3
+// blocks); the weight buffers share the same bytes (the epilogue starts
 // after the loop's last barrier)
-constexpr int PF_EPI_BYTES = 16 * (16 * 20 + 4) * 4;
-static_assert(PF_EPI_BYTES >= 16 * (16 * 10 + 4) * 4 + 16 * 5 * MX6_BLOCK_BYTES, "gate/up staging fits");
+constexpr int PF_EPI_BYTES = 16 * (16 * PF_NCB + 4) * 4;
+static_assert(PF_EPI_BYTES >= 16 * (8 * PF_NCB + 4) * 4 + 16 * (PF_NCB / 4) * MX6_BLOCK_BYTES, "gate/up staging fits");
+constexpr int PF_SMEM = (int)sizeof(PfShared) > PF_NW * PF_EPI_BYTES ? (int)sizeof(PfShared) : PF_NW * PF_EPI_BYTES;
 
-template <bool GATEUP, int NCB>
-__global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams p, int spans) {
-  constexpr int MB = 2;
-  constexpr int NBR = NCB * 16;                        // B rows per tile
-  constexpr int B_PIECES = NBR * 4 / (PF_NWM * 64);    // 16-B B pieces per thread per chunk
-  constexpr int S_PIECES = NBR * 4 / (PF_NWM * 64);    // scale bytes per thread per chunk
-  static_assert(NBR * 4 % (PF_NWM * 64) == 0, "even staging split");
-  static_assert(16 * (16 * NCB + 4) * 4 <= PF_EPI_BYTES, "epilogue staging fits");
-  static_assert(NCB % 4 == 0, "scales are packed four column blocks per dword");
-  static_assert(sizeof(PfShared<GATEUP, NCB>) <= PF_NWM * PF_EPI_BYTES, "weight buffers fit the scratch");
-  __shared__ __align__(16) uint8_t smem[PF_NWM * PF_EPI_BYTES];
-  PfShared<GATEUP, NCB>& sh = *reinterpret_cast<PfShared<GATEUP, NCB>*>(smem);
+template <bool GATEUP>
+__global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams p, int spans) {
+  constexpr int MB = 2, NCB = PF_NCB;
+  constexpr int B_PIECES = PF_NT * 4 / (PF_NW * 64);  // 16-B weight pieces per thread per chunk
+  static_assert(PF_NT * 4 % (PF_NW * 64) == 0, "even staging split");
+  __shared__ __align__(16) uint8_t smem[PF_SMEM];
+  PfShared& sh = *reinterpret_cast<PfShared*>(smem);
 
   // ---- work item ----
   const int total = *p.n_tiles * spans;
@@ -540,6 +534,7 @@ __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams
   const int tile = item / spans, span = item - tile * spans;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
   const int2 te = p.tiles[tile];
   const int e = te.x, m0 = te.y;
   const int rows = min(PF_MT, p.counts[e] - m0);
@@ -547,13 +542,26 @@ __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams
   const int K = p.K, N = p.N, I = p.I, nblk = K >> 5;
   const int g = lane >> 4, r = lane & 15;
 
-  // ---- columns of the tile ----
-  constexpr int HALF = NCB / 2;
-  int col0;
-  if (GATEUP) {
-    col0 = span * HALF * 16;
-  } else {
-    col0 = span * NCB * 16;
+  // tile columns: gate/up -- gate columns span*128 .. +127 (LDS rows 0..127)
+  // and the same up columns (LDS rows 128..255); down -- span*256 .. +255
+  const int tcol0 = GATEUP ? span * (PF_NT / 2) : span * PF_NT;
+  // LDS row of the wave's column block j
+  auto lds_row = [&](int j) -> int {
+    if (GATEUP) return (j < NCB / 2 ? 0 : PF_NT / 2) + wn * (8 * NCB) + 16 * (j % (NCB / 2));
+    return wn * (16 * NCB) + 16 * j;
+  };
+
+  // epilogue biases, loaded now so that they arrive during the K loop
+  const int wcol0 = GATEUP ? tcol0 + wn * (8 * NCB) : tcol0 + wn * (16 * NCB);
+  float bias[NCB];
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) {
+    if (GATEUP) {
+      const int c = min(wcol0 + 16 * (j % (NCB / 2)) + r, I - 1);  // columns past I are never stored
+      bias[j] = p.bias[(size_t)e * N + (j < NCB / 2 ? 0 : I) + c];
+    } else {
+      bias[j] = p.bias[(size_t)e * N + min(wcol0 + 16 * j + r, N - 1)];
+    }
   }
 
   // ---- operand addressing: buffer resources over the whole A, code and
@@ -569,37 +577,35 @@ __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams
       (void*)p.b_codes, 0, (int)((uint32_t)p.E * (uint32_t)N * (uint32_t)(K >> 1)), 0x00020000);
   const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.b_scales, 0, (int)((uint32_t)p.E * (uint32_t)N * (uint32_t)nblk), 0x00020000);
-  // A: tile rows 32w + 16mb + r (rows past the tile read tile row 0), block g of the chunk
+  // A: tile rows 32wm + 16mb + r (rows past the tile read tile row 0), block g of the chunk
   uint32_t a_off[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const int row = 32 * wave + 16 * mb + r;
+    const int row = 32 * wm + 16 * mb + r;
     const int m = row < rows ? row : 0;
     a_off[mb] = (GATEUP ? (uint32_t)(p.expert_rows[(size_t)e * p.T + m0 + m] / p.k) : (uint32_t)(row_base + m)) *
                     a_rowbytes + (uint32_t)g * MX6_BLOCK_BYTES;
   }
-  // B piece q: weight row n = tid/4 + 64q of the tile, 16-byte piece tid % 4
-  // of each chunk; missing column blocks read block 0
+  // weight piece q of this thread: LDS row n = tid/4 + 128q, 16-byte piece
+  // tid % 4 of each chunk; columns past the end read the span's first block
   const int bpiece = tid & 3;
-  uint32_t b_off[B_PIECES], s_off[S_PIECES];
+  uint32_t b_off[B_PIECES], s_off[B_PIECES];
   StaticFor<0, B_PIECES>::run([&](auto ic) {
     constexpr int q = decltype(ic)::value;
-    const int n = (tid >> 2) + PF_NWM * 16 * q;
-    const int j = n >> 4, rr = n & 15;
+    const int n = (tid >> 2) + (PF_NW * 16) * q;
     int row;
     if (GATEUP) {
-      const int jj = j < HALF ? j : j - HALF;
-      const int c = (col0 + 16 * jj) < I ? col0 + 16 * jj : col0;
-      row = (j < HALF ? 0 : I) + c + rr;
+      const int c = tcol0 + (n & (PF_NT / 2 - 1));
+      row = (n < PF_NT / 2 ? 0 : I) + (c < I ? c : tcol0 + (n & 15));
     } else {
-      row = ((col0 + 16 * j) < N ? col0 + 16 * j : col0) + rr;
+      const int c = tcol0 + n;
+      row = c < N ? c : tcol0 + (n & 15);
     }
     const uint32_t brow = (uint32_t)e * (uint32_t)N + (uint32_t)row;
     b_off[q] = brow * (uint32_t)(K >> 1) + (uint32_t)bpiece * 16u;
     s_off[q] = brow * (uint32_t)nblk + (uint32_t)bpiece;
   });
 
-  // ---- A: global -> registers ----
   auto load_a = [&](int c, v4u (&av)[MB][5]) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -608,32 +614,24 @@ __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams
         av[mb][q] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(arsrc, a_off[mb] + 16 * q,
                                                                                   c * 4 * MX6_BLOCK_BYTES, 0));
   };
-  // ---- B: global -> registers -> LDS ----
   v4u rb[B_PIECES];
-  uint32_t rs[S_PIECES];
+  uint32_t rs[B_PIECES];
   auto stage_load = [&](int c) {
     StaticFor<0, B_PIECES>::run([&](auto ic) {
       constexpr int q = decltype(ic)::value;
       rb[q] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(crsrc, b_off[q], c * 64, 0));
-    });
-    StaticFor<0, S_PIECES>::run([&](auto ic) {
-      constexpr int q = decltype(ic)::value;
       rs[q] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, s_off[q], c * 4, 0);
     });
   };
+  // scale of (LDS row n = 16J + r, block g) at byte ((J/4 * 4 + g) * 16 + r) * 4 + J % 4:
+  // one dword read gives a lane the scales of four column blocks
   auto stage_store = [&](int buf) {
     StaticFor<0, B_PIECES>::run([&](auto ic) {
       constexpr int q = decltype(ic)::value;
-      const int n = (tid >> 2) + PF_NWM * 16 * q;
+      const int n = (tid >> 2) + (PF_NW * 16) * q;
       *(v4u*)(sh.b[buf] + n * 64 + ((bpiece ^ ((n >> 2) & 3)) * 16)) = rb[q];
-    });
-    // scale of (column n = 16j + r, block g) at byte ((j/4 * 4 + g) * 16 + r) * 4 + j % 4:
-    // one dword read gives a lane the scales of four column blocks
-    StaticFor<0, S_PIECES>::run([&](auto ic) {
-      constexpr int q = decltype(ic)::value;
-      const int n = (tid >> 2) + PF_NWM * 16 * q;
-      const int j = n >> 4, rr = n & 15;
-      sh.bs[buf][(((j >> 2) * 4 + bpiece) * 16 + rr) * 4 + (j & 3)] = (uint8_t)rs[q];
+      const int J = n >> 4, rr = n & 15;
+      sh.bs[buf][(((J >> 2) * 4 + bpiece) * 16 + rr) * 4 + (J & 3)] = (uint8_t)rs[q];
     });
   };
 
@@ -681,12 +679,17 @@ __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams
     load_a(cn, av);
     stage_load(cn);
     __builtin_amdgcn_sched_barrier(0);
-    uint32_t bsw[NCB / 4];
+    // the wave's eight column blocks form two groups of four consecutive LDS
+    // row blocks, i.e. two scale dwords
+    uint32_t bsw[2];
 #pragma unroll
-    for (int jj = 0; jj < NCB / 4; ++jj) bsw[jj] = *(const uint32_t*)(sh.bs[buf] + ((jj * 4 + g) * 16 + r) * 4);
+    for (int h = 0; h < 2; ++h) {
+      const int J0 = lds_row(4 * h) >> 4;
+      bsw[h] = *(const uint32_t*)(sh.bs[buf] + (((J0 >> 2) * 4 + g) * 16 + r) * 4);
+    }
     v4u bq[PF_BPRE + 1];
     auto read_b = [&](int j) {
-      const int n = 16 * j + r;
+      const int n = lds_row(j) + r;
       bq[j % (PF_BPRE + 1)] = *(const v4u*)(sh.b[buf] + n * 64 + ((g ^ ((n >> 2) & 3)) * 16));
     };
     StaticFor<0, PF_BPRE>::run([&](auto jc) { read_b(decltype(jc)::value); });
@@ -712,13 +715,13 @@ __global__ __launch_bounds__(PF_NWM * 64, 1) void expert_gemm_prefill(GemmParams
   }
 
   // the loop's last barrier has passed: the weight buffers are free
-  const int rows_w = rows - 32 * wave;
-  const int row_base_w = row_base + 32 * wave;
+  const int rows_w = rows - 32 * wm;
+  const int row_base_w = row_base + 32 * wm;
   uint8_t* scratch = smem + wave * PF_EPI_BYTES;
   if (GATEUP)
-    pf_epilogue_gateup<NCB>(p, acc, e, rows_w, row_base_w, col0, lane, scratch);
+    pf_epilogue_gateup<NCB>(p, acc, bias, rows_w, row_base_w, wcol0, lane, scratch);
   else
-    pf_epilogue_down<NCB>(p, acc, e, rows_w, row_base_w, col0, lane, scratch);
+    pf_epilogue_down<NCB>(p, acc, bias, rows_w, row_base_w, wcol0, lane, scratch);
 }
 
 // The prefill kernel addresses operands with 32-bit byte offsets.
@@ -732,19 +735,18 @@ static bool prefill_offsets_fit(const GemmParams& p) {
 // Launch configurations.
 //   small-M (tiles of 16 rows, decode): grid (64-column spans, tiles), four
 //     waves stream one span's weights through LDS;
-//   large-M (prefill): one workgroup per (128-row tile, 320-column span)
+//   large-M (prefill): one workgroup per (128-row tile, 256-column span)
 //     work item, 1-D grid dealt to the XCDs in contiguous ranges.
 int launch_gemm_gateup(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s) {
   if (small_m) {
     dim3 grid((p.I + 31) / 32, max_tiles);
     hipLaunchKernelGGL((expert_gemm_decode<true>), grid, dim3(DEC_NW * 64), 0, s, p);
   } else {
-    constexpr int NCB = 20;  // 160 gate + 160 up columns
     if (!prefill_offsets_fit(p)) return -1;
-    const int spans = (p.I + NCB * 8 - 1) / (NCB * 8);
+    const int spans = (p.I + PF_NT / 2 - 1) / (PF_NT / 2);
     const long long items = (long long)max_tiles * spans;
-    hipLaunchKernelGGL((expert_gemm_prefill<true, NCB>), dim3((unsigned)((items + PF_XCD - 1) / PF_XCD * PF_XCD)),
-                       dim3(PF_NWM * 64), 0, s, p, spans);
+    hipLaunchKernelGGL((expert_gemm_prefill<true>), dim3((unsigned)((items + PF_XCD - 1) / PF_XCD * PF_XCD)),
+                       dim3(PF_NW * 64), 0, s, p, spans);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
@@ -754,12 +756,11 @@ int launch_gemm_down(const GemmParams& p, int max_tiles, bool small_m, hipStream
     dim3 grid((p.N + 63) / 64, max_tiles);
     hipLaunchKernelGGL((expert_gemm_decode<false>), grid, dim3(DEC_NW * 64), 0, s, p);
   } else {
-    constexpr int NCB = 20;  // 320 output columns
     if (!prefill_offsets_fit(p)) return -1;
-    const int spans = (p.N + NCB * 16 - 1) / (NCB * 16);
+    const int spans = (p.N + PF_NT - 1) / PF_NT;
     const long long items = (long long)max_tiles * spans;
-    hipLaunchKernelGGL((expert_gemm_prefill<false, NCB>), dim3((unsigned)((items + PF_XCD - 1) / PF_XCD * PF_XCD)),
-                       dim3(PF_NWM * 64), 0, s, p, spans);
+    hipLaunchKernelGGL((expert_gemm_prefill<false>), dim3((unsigned)((items + PF_XCD - 1) / PF_XCD * PF_XCD)),
+                       dim3(PF_NW * 64), 0, s, p, spans);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -69,6 +69,6 @@ constexpr int CURSOR_STRIDE = 32;
 
 // rows per GEMM tile of the two configurations
 constexpr int MT_SMALL = 16;
-constexpr int MT_LARGE = 128;
+constexpr int MT_LARGE = 64;
 
 }  // namespace moe
