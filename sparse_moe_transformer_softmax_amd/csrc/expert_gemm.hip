@@ -22,6 +22,7 @@
 // Work decomposition: the router's tile list (expert, first row) times
 // spans of output columns.  Gate/up workgroups own matching gate and up
 // columns, so the epilogue has both halves of h in the same lane.
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_common.h"
@@ -141,29 +142,44 @@ __device__ __forceinline__ uint32_t split_h_row(float h0, float h1, int r, uint8
 
 // ---------------------------------------------------------------------------
 // Decode kernel: tiles of at most 16 rows, so the kernel is bound by the
-// weight stream.  A workgroup owns 64 weight rows (gate/up: 32 gate + the
-// matching 32 up rows; down: 64 output rows) and walks K in phases of 32
-// blocks.  Wave w copies the phase's code and scale segments of column
-// block w (16 consecutive weight rows) from HBM straight to LDS with
-// buffer_load ... lds -- no register staging, and every instruction reads
-// 1 KB of lane-consecutive addresses, so whole cache lines are fetched (the
-// scale bytes land one per LDS dword, the layout of byte loads to LDS).
-// Within a row the 32 blocks of a phase are stored XOR-swizzled (logical
-// block b of row j at slot b ^ (j & 15)), so the MFMA operand reads -- 16
-// rows x one block per lane group -- hit distinct LDS banks.  A rows come
-// from the MX6x3 buffer through a buffer resource: lanes of rows past the
-// tile read at an offset beyond the resource, which returns zero without
-// touching memory.  The four waves split each phase's blocks; wave 0 sums
-// their partials in a fixed order and runs the epilogue.  With 36 KB of
-// LDS and at most 128 VGPRs, four workgroups share a CU, so about 136 KB
-// of weights per CU are in flight.
+// weight stream.  Work items are (tile, 64-row weight span) pairs (gate/up:
+// 32 gate + the matching 32 up rows; down: 64 output rows), numbered
+// tile-major; a persistent workgroup walks items blockIdx.x,
+// blockIdx.x + gridDim.x, ... and the phases of consecutive items form one
+// stream: while the last phase of an item is consumed, the first phase of
+// the next item is already being copied, and the item's epilogue runs with
+// that copy in flight.  An item walks K in phases of DEC_KPH blocks.  Wave w
+// copies the phase's code and scale segments of column block w (16
+// consecutive weight rows) from HBM straight to LDS with buffer_load ... lds
+// -- no register staging, and every instruction reads 1 KB of
+// lane-consecutive addresses, so whole cache lines are fetched (the scale
+// bytes land one per LDS dword, the layout of byte loads to LDS).  Within a
+// row the blocks of a phase are stored XOR-swizzled (logical block b of row
+// j at slot b ^ (j & 15)), so the MFMA operand reads -- 16 rows x one block
+// per lane group -- hit distinct LDS banks.  A rows come from the MX6x3
+// buffer through a buffer resource: lanes of rows past the tile read at an
+// offset beyond the resource, which returns zero without touching memory.
+// The four waves split each phase's blocks; the epilogue sums their
+// partials in a fixed order.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int DEC_KPH = 16;                // K blocks per phase
 constexpr int DEC_NW = 4;                  // waves per workgroup
 constexpr int DEC_Q = DEC_KPH / 4;         // copy instructions per wave per phase (codes; same for scales)
 constexpr int DEC_WB = DEC_KPH / DEC_NW;   // blocks per wave per phase (4 = one chunk)
-constexpr int DEC_VM = 2 * DEC_Q + 5;      // vector-memory instructions per wave per phase
+// Scale bytes go to LDS with 2-byte copies when a weight row's scale bytes
+// start 2-byte aligned (K/32 even): lane L's two bytes land in LDS dword L,
+// so a wave moves its 16 rows x 16 blocks in two instructions and a phase
+// buffer holds 8 dwords per weight row; otherwise with 1-byte copies (four
+// instructions, 16 dwords per row).  The smaller buffers let four
+// workgroups share a CU.
+template <bool U16>
+struct DecCfg {
+  static constexpr int SQ = U16 ? 2 : DEC_Q;                // scale copy instructions per wave per phase
+  static constexpr int SROW = U16 ? DEC_KPH / 2 : DEC_KPH;  // scale dwords per weight row
+  static constexpr int VM = DEC_Q + SQ + 5;                 // vector-memory instructions per wave per phase
+  static constexpr int WG_PER_CU = U16 ? 4 : 3;             // resident workgroups per CU
+};
 static_assert(DEC_WB == 4, "one 4-block chunk per wave per phase");
 
 // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt[3:0] bits 3:0, vmcnt[5:4] bits
@@ -174,91 +190,131 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Everything the decode kernel needs to know about one work item.
+struct DecItem {
+  int e, rows, row_base, col0;
+  int ok_mask;                      // bit j: column block j lies inside the output
+  __amdgpu_buffer_rsrc_t crsrc;     // this wave's 16 weight rows: codes
+  __amdgpu_buffer_rsrc_t srsrc;     //   and scales
+  int a_off;                        // this lane's A row offset, or past the A resource
+};
+
 template <bool GATEUP>
-__global__ __launch_bounds__(DEC_NW * 64, 3) void expert_gemm_decode(GemmParams p) {
+__device__ __forceinline__ void dec_load_item(const GemmParams& p, int item, int spans, int wave, int r, DecItem& it) {
+  const int K = p.K, N = p.N, I = p.I, nblk = K >> 5;
+  const int tile = item / spans, span = item - tile * spans;
+  const int2 te = p.tiles[tile];
+  const int e = te.x, m0 = te.y;
+  it.e = e;
+  it.rows = min(16, p.counts[e] - m0);
+  it.row_base = p.offsets[e] + m0;
+  int ok = 0;
+  if (GATEUP) {
+    it.col0 = span * 32;
+    ok = (it.col0 < I ? 0x5 : 0) | (it.col0 + 16 < I ? 0xA : 0);
+  } else {
+    it.col0 = span * 64;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ok |= (it.col0 + 16 * j < N) ? (1 << j) : 0;
+  }
+  it.ok_mask = ok;
+  // first weight row of this wave's column block (a missing block copies
+  // block 0); its 16 rows are consecutive weight rows
+  const int cbv = ((ok >> wave) & 1) ? wave : 0;
+  const int n = GATEUP ? (cbv < 2 ? 0 : I) + it.col0 + 16 * (cbv & 1) : it.col0 + 16 * cbv;
+  const size_t my_row = (size_t)e * N + n;
+  // resources end at the end of the arrays, so that copies past the last
+  // row return zeros instead of reading past the allocation
+  const size_t rows_left = (size_t)p.E * N - my_row;
+  it.crsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_codes + my_row * (size_t)(K >> 1)), 0,
+                                               (int)(rows_left * (size_t)(K >> 1)), 0x00020000);
+  it.srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_scales + my_row * (size_t)nblk), 0,
+                                               (int)(rows_left * (size_t)nblk), 0x00020000);
+  const int m = r < it.rows ? r : 0;
+  const int arow = GATEUP ? p.expert_rows[(size_t)e * p.T + m0 + m] / p.k : it.row_base + m;
+  it.a_off = r < it.rows ? arow * nblk * MX6_BLOCK_BYTES : 0x7ffffff0;
+}
+
+// An item whose copies all fall outside their resources: they return zeros
+// without touching memory (issued after the last real phase so that every
+// step has the same shape).
+__device__ __forceinline__ void dec_null_item(const GemmParams& p, DecItem& it) {
+  it.e = 0; it.rows = 0; it.row_base = 0; it.col0 = 0; it.ok_mask = 0;
+  it.crsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.b_codes, 0, 0, 0x00020000);
+  it.srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.b_scales, 0, 0, 0x00020000);
+  it.a_off = 0x7ffffff0;
+}
+
+template <bool GATEUP, int NPH, bool U16>
+__global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_gemm_decode(GemmParams p, int spans) {
+  using Cfg = DecCfg<U16>;
   constexpr int NCB = 4, NW = DEC_NW;
   // readfirstlane: the wave index is uniform, so the buffer resources and
   // LDS bases derived from it live in scalar registers
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tile = blockIdx.y;
-  if (tile >= *p.n_tiles) return;
-  const int2 te = p.tiles[tile];
-  const int e = te.x, m0 = te.y;
-  const int rows = min(16, p.counts[e] - m0);
-  const int row_base = p.offsets[e] + m0;
+  const int total = *p.n_tiles * spans;
+  int item = blockIdx.x;
+  if (item >= total) return;
   const int K = p.K, N = p.N, I = p.I, nblk = K >> 5;
   const int g = lane >> 4, r = lane & 15;
-
-  // columns of the workgroup
-  int col0;
-  bool bok[NCB];
-  if (GATEUP) {
-    col0 = blockIdx.x * 32;
-    bok[0] = bok[2] = col0 < I;
-    bok[1] = bok[3] = col0 + 16 < I;
-  } else {
-    col0 = blockIdx.x * 64;
-#pragma unroll
-    for (int j = 0; j < NCB; ++j) bok[j] = col0 + 16 * j < N;
-  }
-  if (!bok[0]) return;  // uniform over the workgroup
-  // first weight row of this wave's column block (a missing block copies
-  // block 0); its 16 rows are consecutive weight rows
-  size_t my_row;
-  {
-    const int cbv = bok[wave] ? wave : 0;
-    const int n = GATEUP ? (cbv < 2 ? 0 : I) + col0 + 16 * (cbv & 1) : col0 + 16 * cbv;
-    my_row = (size_t)e * N + n;
-  }
-  const __amdgpu_buffer_rsrc_t crsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_codes + my_row * (size_t)(K >> 1)), 0, 0x7fffffff, 0x00020000);
-  const __amdgpu_buffer_rsrc_t srsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_scales + my_row * (size_t)nblk), 0, 0x7fffffff, 0x00020000);
+  const int nph = (nblk + DEC_KPH - 1) / DEC_KPH;
 
   // two phase buffers: codes [64 rows][16 slots][16 B], scales one per dword
   __shared__ __align__(16) uint8_t s_code[2][64 * DEC_KPH * 16];
-  __shared__ __align__(16) uint32_t s_scl[2][64 * DEC_KPH];
+  __shared__ __align__(16) uint32_t s_scl[2][64 * Cfg::SROW];
   __shared__ uint8_t s_codes[16][3][32];
   __shared__ uint32_t s_sc[16];
 
-  // A rows through a buffer resource over the whole MX6x3 buffer (the decode
-  // path keeps it far below 2 GiB); a lane's offset selects row and block
-  const int arow_bytes = nblk * MX6_BLOCK_BYTES;
-  int a_first;
-  {
-    const int m = r < rows ? r : 0;
-    a_first = GATEUP ? p.expert_rows[(size_t)e * p.T + m0 + m] / p.k : row_base + m;
-  }
+  // A rows through a buffer resource over the whole MX6x3 buffer (the
+  // library keeps it below 2 GiB); a lane's offset selects row and block
   const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.a, 0, 0x7ffffff0, 0x00020000);
-  const bool arow_ok = r < rows;
 
-  v4f acc[1][NCB];
-#pragma unroll
-  for (int j = 0; j < NCB; ++j) acc[0][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-  // issue every load of phase ph: this wave's column block into LDS buffer
-  // `buf` (instruction q moves rows 4q .. 4q+3), this wave's A block into av
+  // issue every load of phase ph of item `it`: this wave's column block
+  // into LDS buffer `buf` (instruction q moves rows 4q .. 4q+3), this wave's
+  // A block into av
   const int sub = lane / DEC_KPH, slot = lane % DEC_KPH;
-  auto issue = [&](int ph, int buf, uint4 (&av)[5]) {
+  auto issue = [&](const DecItem& it, int ph, int buf, uint4 (&av)[5]) {
     const int pb0 = ph * DEC_KPH, npb = min(DEC_KPH, nblk - pb0);
 #pragma unroll
     for (int q = 0; q < DEC_Q; ++q) {
       const int rr = 4 * q + sub;                  // row within the column block
       const int b = min(slot ^ rr, npb - 1);       // logical block stored at `slot`
       const int row_off = (wave * 16 + 4 * q) * DEC_KPH;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(crsrc, (lds_void_t*)(s_code[buf] + row_off * 16), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(it.crsrc, (lds_void_t*)(s_code[buf] + row_off * 16), 16,
                                                rr * (K >> 1) + (pb0 + b) * 16, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, (lds_void_t*)(s_scl[buf] + row_off), 1,
-                                               rr * nblk + pb0 + min(slot, npb - 1), 0, 0, 0);
+      if constexpr (!U16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(it.srsrc, (lds_void_t*)(s_scl[buf] + row_off), 1,
+                                                 rr * nblk + pb0 + min(slot, npb - 1), 0, 0, 0);
+    }
+    if constexpr (U16) {
+      // instruction q moves rows 8q .. 8q+7; lane L holds the block pair
+      // (L % 8) ^ ((row >> 2) & 3) of row 8q + L/8, so that the reads of 16
+      // rows hit 16 banks; pairs past the phase read pair 0 (never used)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int rr = 8 * q + (lane >> 3);
+        const int u = (lane & 7) ^ ((rr >> 2) & 3);
+        const int uc = 2 * u < npb ? u : 0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(it.srsrc,
+                                                 (lds_void_t*)(s_scl[buf] + (wave * 16 + 8 * q) * Cfg::SROW), 2,
+                                                 rr * nblk + pb0 + 2 * uc, 0, 0, 0);
+      }
     }
     const int blk = pb0 + min(wave * DEC_WB + g, npb - 1);
-    const int off = arow_ok ? a_first * arow_bytes + blk * MX6_BLOCK_BYTES : 0x7ffffff0;
+    const int off = it.a_off < 0x7ffffff0 ? it.a_off + blk * MX6_BLOCK_BYTES : 0x7ffffff0;
 #pragma unroll
-    for (int q = 0; q < 5; ++q) {
+    for (int q = 0; q < 4; ++q) {
       const auto t4 = __builtin_amdgcn_raw_buffer_load_b128(arsrc, off + 16 * q, 0, 0);
       av[q] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
     }
+    // bytes 64 .. 75: the last term's codes and the scale bytes (the padding
+    // dword is not loaded: a register that a load in flight writes must not
+    // be dead, or the compiler waits for the load before reusing it)
+    const auto t3 = __builtin_amdgcn_raw_buffer_load_b96(arsrc, off + 64, 0, 0);
+    av[4] = make_uint4(t3[0], t3[1], t3[2], 0u);
   };
+
+  v4f acc[1][NCB];
   auto consume = [&](int ph, int buf, const uint4 (&av)[5]) {
     const int npb = min(DEC_KPH, nblk - ph * DEC_KPH);
     const int bl = wave * DEC_WB + g;  // logical block within the phase
@@ -270,7 +326,9 @@ __global__ __launch_bounds__(DEC_NW * 64, 3) void expert_gemm_decode(GemmParams 
     // would otherwise wait for every copy in flight (the next phase's too)
     // before reading.  The barriers and explicit vmcnt waits order them.
     const uint32_t cb_addr = (uint32_t)(uintptr_t)(s_code[buf]) + (uint32_t)((r * DEC_KPH + (bl ^ r)) * 16);
-    const uint32_t sb_addr = (uint32_t)(uintptr_t)(s_scl[buf]) + (uint32_t)((r * DEC_KPH + bl) * 4);
+    const uint32_t sb_addr =
+        (uint32_t)(uintptr_t)(s_scl[buf]) +
+        (uint32_t)((U16 ? r * Cfg::SROW + ((bl >> 1) ^ ((r >> 2) & 3)) : r * DEC_KPH + bl) * 4);
     v4u b0, b1, b2, b3;
     uint32_t s0, s1, s2, s3;
     asm volatile(
@@ -285,106 +343,123 @@ __global__ __launch_bounds__(DEC_NW * 64, 3) void expert_gemm_decode(GemmParams 
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
         : "v"(cb_addr), "v"(sb_addr), "i"(16 * DEC_KPH * 16), "i"(32 * DEC_KPH * 16), "i"(48 * DEC_KPH * 16),
-          "i"(16 * DEC_KPH * 4), "i"(32 * DEC_KPH * 4), "i"(48 * DEC_KPH * 4));
+          "i"(16 * Cfg::SROW * 4), "i"(32 * Cfg::SROW * 4), "i"(48 * Cfg::SROW * 4));
     st.bc[0] = make_uint4(b0.x, b0.y, b0.z, b0.w);
     st.bc[1] = make_uint4(b1.x, b1.y, b1.z, b1.w);
     st.bc[2] = make_uint4(b2.x, b2.y, b2.z, b2.w);
     st.bc[3] = make_uint4(b3.x, b3.y, b3.z, b3.w);
-    st.bs[0] = (int)(s0 & 0xffu);
-    st.bs[1] = (int)(s1 & 0xffu);
-    st.bs[2] = (int)(s2 & 0xffu);
-    st.bs[3] = (int)(s3 & 0xffu);
+    const int sh = U16 ? 8 * (bl & 1) : 0;  // byte of the block within its pair
+    st.bs[0] = (int)((s0 >> sh) & 0xffu);
+    st.bs[1] = (int)((s1 >> sh) & 0xffu);
+    st.bs[2] = (int)((s2 >> sh) & 0xffu);
+    st.bs[3] = (int)((s3 >> sh) & 0xffu);
     mma_stage(acc, st, keep_mask<1, NCB>(bl < npb));
   };
 
-  // double-buffered phases: the loads of phase ph+1 are in flight while
-  // phase ph is consumed.  The copies write LDS behind the compiler's back,
-  // so each wave waits explicitly (vmcnt counts in issue order) for its own
-  // loads of phase ph, then a bare s_barrier publishes the phase: a
-  // __syncthreads() would make the compiler drain every copy in flight,
-  // the next phase's included.  The second barrier keeps a buffer from
-  // being refilled while another wave still reads it (the asm reads above
-  // complete before their wave reaches it).
-  const int nph = (nblk + DEC_KPH - 1) / DEC_KPH;
-  uint4 av0[5], av1[5];
-  issue(0, 0, av0);
-  for (int ph = 0; ph < nph; ph += 2) {
-    if (ph + 1 < nph) {
-      issue(ph + 1, 1, av1);
-      wait_vmcnt<DEC_VM>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __builtin_amdgcn_s_barrier();
-    consume(ph, 0, av0);
-    __builtin_amdgcn_s_barrier();
-    if (ph + 1 >= nph) break;
-    if (ph + 2 < nph) {
-      issue(ph + 2, 0, av0);
-      wait_vmcnt<DEC_VM>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __builtin_amdgcn_s_barrier();
-    consume(ph + 1, 1, av1);
-    __builtin_amdgcn_s_barrier();
-  }
-  wait_vmcnt<0>();
-
-  // ---- epilogue: wave w takes accumulator element w, i.e. tile rows
-  // 4g + w; it sums the four waves' partials in a fixed order ----
-  float* s_acc = (float*)s_code[0];  // [NW][NCB][4][64], reuses the code buffers
+  // ---- epilogue of item `it`: wave w takes accumulator element w, i.e.
+  // tile rows 4g + w, and sums the four waves' partials in a fixed order.
+  // s_acc is the phase buffer consumed last (free until the next issue).
+  auto epilogue = [&](const DecItem& it, float* s_acc) {
 #pragma unroll
-  for (int j = 0; j < NCB; ++j)
+    for (int j = 0; j < NCB; ++j)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s_acc[((wave * NCB + j) * 4 + q) * 64 + lane] = acc[0][j][q];
-  __syncthreads();
-  float v[NCB];
-#pragma unroll
-  for (int j = 0; j < NCB; ++j) {
-    float t = s_acc[((0 * NCB + j) * 4 + wave) * 64 + lane];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) t += s_acc[((w * NCB + j) * 4 + wave) * 64 + lane];
-    v[j] = t;
-  }
-  const int row = 4 * g + wave;  // tile row of this lane's values
-  if (!GATEUP) {
+      for (int q = 0; q < 4; ++q) s_acc[((wave * NCB + j) * 4 + q) * 64 + lane] = acc[0][j][q];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the partials are in LDS
+    __builtin_amdgcn_s_barrier();
+    float v[NCB];
 #pragma unroll
     for (int j = 0; j < NCB; ++j) {
-      if (!bok[j]) continue;
-      const int col = col0 + 16 * j + r;
-      if (row < rows) p.y[(size_t)(row_base + row) * N + col] = v[j] + p.bias[(size_t)e * N + col];
+      float t = s_acc[((0 * NCB + j) * 4 + wave) * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) t += s_acc[((w * NCB + j) * 4 + wave) * 64 + lane];
+      v[j] = t;
     }
-    return;
+    const int row = 4 * g + wave;  // tile row of this lane's values
+    const int e = it.e, col0 = it.col0, rows = it.rows, row_base = it.row_base;
+    if (!GATEUP) {
+#pragma unroll
+      for (int j = 0; j < NCB; ++j) {
+        if (!((it.ok_mask >> j) & 1)) continue;
+        const int col = col0 + 16 * j + r;
+        if (row < rows) p.y[(size_t)(row_base + row) * N + col] = v[j] + p.bias[(size_t)e * N + col];
+      }
+      return;
+    }
+    const int c0 = min(col0 + r, I - 1), c1 = min(col0 + 16 + r, I - 1);  // columns past I are never stored
+    const float h0 = clamped_swiglu(v[0] + p.bias[(size_t)e * N + c0], v[2] + p.bias[(size_t)e * N + I + c0], p.clamp);
+    const float h1 = clamped_swiglu(v[1] + p.bias[(size_t)e * N + c1], v[3] + p.bias[(size_t)e * N + I + c1], p.clamp);
+    const uint32_t scw = split_h_row(h0, h1, r, s_codes[row]);
+    if (r == 0) s_sc[row] = scw;
+    lds_wave_sync();
+    const int blk = col0 >> 5;
+    if (lane < 12) {
+      const int rw = 4 * (lane / 3) + wave, t = lane % 3;
+      if (rw < rows) {
+        uint32_t pk[6];
+        pack6x32(s_codes[rw][t], pk);
+        uint2* dst = (uint2*)(p.hq + ((size_t)(row_base + rw) * (I >> 5) + blk) * MX6_BLOCK_BYTES + 24 * t);
+        dst[0] = make_uint2(pk[0], pk[1]);
+        dst[1] = make_uint2(pk[2], pk[3]);
+        dst[2] = make_uint2(pk[4], pk[5]);
+      }
+    } else if (lane < 16) {
+      const int rw = 4 * (lane - 12) + wave;
+      if (rw < rows) {
+        uint2* dst = (uint2*)(p.hq + ((size_t)(row_base + rw) * (I >> 5) + blk) * MX6_BLOCK_BYTES + 72);
+        dst[0] = make_uint2(s_sc[rw], 0u);
+      }
+    }
+    lds_wave_sync();
+  };
+
+  // The phase loop.  Each step: issue the copies of the next phase (past the
+  // last phase, of the null item, so that every step has the same shape),
+  // wait for this wave's copies of the current phase (vmcnt counts in issue
+  // order; the next phase's DEC_VM operations may stay in flight), publish
+  // them with a bare s_barrier -- a __syncthreads() would make the compiler
+  // drain every copy in flight -- and consume.  The second barrier keeps a
+  // buffer from being refilled while another wave still reads it.  With the
+  // phase count known at compile time (NPH > 0) the loop is unrolled, so the
+  // A registers of consecutive phases are fixed and no copy of a load in
+  // flight forces an early wait; the scheduling barrier keeps the consume's
+  // register moves behind the wait.
+  DecItem cur, nul;
+  dec_load_item<GATEUP>(p, item, spans, wave, r, cur);
+  dec_null_item(p, nul);
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) acc[0][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  uint4 av0[5], av1[5];
+  issue(cur, 0, 0, av0);
+  auto step = [&](int ph, int buf, const uint4 (&avc)[5], uint4 (&avn)[5]) {
+    const bool more_ph = ph + 1 < nph;
+    issue(more_ph ? cur : nul, more_ph ? ph + 1 : 0, buf ^ 1, avn);
+    wait_vmcnt<Cfg::VM>();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    consume(ph, buf, avc);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (NPH > 0) {
+    StaticFor<0, NPH>::run([&](auto pc) {
+      constexpr int ph = decltype(pc)::value;
+      if constexpr (ph % 2 == 0)
+        step(ph, 0, av0, av1);
+      else
+        step(ph, 1, av1, av0);
+    });
+  } else {
+    for (int ph = 0;;) {
+      step(ph, 0, av0, av1);
+      if (++ph >= nph) break;
+      step(ph, 1, av1, av0);
+      if (++ph >= nph) break;
+    }
   }
-  const int c0 = col0 + r;
-  const float h0 = clamped_swiglu(v[0] + p.bias[(size_t)e * N + c0], v[2] + p.bias[(size_t)e * N + I + c0], p.clamp);
-  const float h1 = clamped_swiglu(v[1] + p.bias[(size_t)e * N + c0 + 16], v[3] + p.bias[(size_t)e * N + I + c0 + 16],
-                                  p.clamp);
-  const uint32_t scw = split_h_row(h0, h1, r, s_codes[row]);
-  if (r == 0) s_sc[row] = scw;
-  lds_wave_sync();
-  const int blk = col0 >> 5;
-  if (lane < 12) {
-    const int rw = 4 * (lane / 3) + wave, t = lane % 3;
-    if (rw < rows) {
-      uint32_t pk[6];
-      pack6x32(s_codes[rw][t], pk);
-      uint2* dst = (uint2*)(p.hq + ((size_t)(row_base + rw) * (I >> 5) + blk) * MX6_BLOCK_BYTES + 24 * t);
-      dst[0] = make_uint2(pk[0], pk[1]);
-      dst[1] = make_uint2(pk[2], pk[3]);
-      dst[2] = make_uint2(pk[4], pk[5]);
-    }
-  } else if (lane < 16) {
-    const int rw = 4 * (lane - 12) + wave;
-    if (rw < rows) {
-      uint2* dst = (uint2*)(p.hq + ((size_t)(row_base + rw) * (I >> 5) + blk) * MX6_BLOCK_BYTES + 72);
-      dst[0] = make_uint2(s_sc[rw], 0u);
-    }
-  }
+  wait_vmcnt<0>();  // the null item's copies
+  epilogue(cur, (float*)s_code[(nph - 1) & 1]);
 }
 
-// ---------------------------------------------------------------------------
 // Prefill kernel: tiles of PF_MT = 64 rows x 256 output columns (gate/up:
 // 128 gate + the matching 128 up columns).  A workgroup has four waves and
 // two workgroups share a CU, so every SIMD runs two waves (a single wave per
@@ -732,15 +807,42 @@ static bool prefill_offsets_fit(const GemmParams& p) {
   return a_rows * (p.K / 32) * MX6_BLOCK_BYTES < lim && e_rows * (p.K / 2) < lim;
 }
 
+// Decode kernel instance for the phase count of K (unrolled up to 8 phases).
+template <bool GATEUP, bool U16>
+static void launch_decode_u(const GemmParams& p, unsigned grid, int spans, hipStream_t s) {
+  const int nph = (p.K / 32 + DEC_KPH - 1) / DEC_KPH;
+  const dim3 g(grid), b(DEC_NW * 64);
+  switch (nph) {
+    case 1: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 1, U16>), g, b, 0, s, p, spans); break;
+    case 2: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 2, U16>), g, b, 0, s, p, spans); break;
+    case 3: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 3, U16>), g, b, 0, s, p, spans); break;
+    case 4: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 4, U16>), g, b, 0, s, p, spans); break;
+    case 5: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 5, U16>), g, b, 0, s, p, spans); break;
+    case 6: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 6, U16>), g, b, 0, s, p, spans); break;
+    case 7: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 7, U16>), g, b, 0, s, p, spans); break;
+    case 8: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 8, U16>), g, b, 0, s, p, spans); break;
+    default: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 0, U16>), g, b, 0, s, p, spans); break;
+  }
+}
+
+template <bool GATEUP>
+static void launch_decode(const GemmParams& p, unsigned grid, int spans, hipStream_t s) {
+  if ((p.K / 32) % 2 == 0)
+    launch_decode_u<GATEUP, true>(p, grid, spans, s);
+  else
+    launch_decode_u<GATEUP, false>(p, grid, spans, s);
+}
+
 // Launch configurations.
-//   small-M (tiles of 16 rows, decode): grid (64-column spans, tiles), four
-//     waves stream one span's weights through LDS;
+//   small-M (tiles of 16 rows, decode): persistent workgroups (three per
+//     CU) walk the (tile, 64-row span) items, four waves stream each span's
+//     weights through LDS;
 //   large-M (prefill): one workgroup per (128-row tile, 256-column span)
 //     work item, 1-D grid dealt to the XCDs in contiguous ranges.
 int launch_gemm_gateup(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s) {
   if (small_m) {
-    dim3 grid((p.I + 31) / 32, max_tiles);
-    hipLaunchKernelGGL((expert_gemm_decode<true>), grid, dim3(DEC_NW * 64), 0, s, p);
+    const int spans = (p.I + 31) / 32;
+    launch_decode<true>(p, (unsigned)((long long)max_tiles * spans), spans, s);
   } else {
     if (!prefill_offsets_fit(p)) return -1;
     const int spans = (p.I + PF_NT / 2 - 1) / (PF_NT / 2);
@@ -753,8 +855,8 @@ int launch_gemm_gateup(const GemmParams& p, int max_tiles, bool small_m, hipStre
 
 int launch_gemm_down(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s) {
   if (small_m) {
-    dim3 grid((p.N + 63) / 64, max_tiles);
-    hipLaunchKernelGGL((expert_gemm_decode<false>), grid, dim3(DEC_NW * 64), 0, s, p);
+    const int spans = (p.N + 63) / 64;
+    launch_decode<false>(p, (unsigned)((long long)max_tiles * spans), spans, s);
   } else {
     if (!prefill_offsets_fit(p)) return -1;
     const int spans = (p.N + PF_NT - 1) / PF_NT;
