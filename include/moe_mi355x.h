@@ -139,14 +139,14 @@ int moe_stack_forward(const void* x0, int n_layers, const void* const* router_w,
                       float eps, void* out, void* stream);
 
 /* Per-kernel timing for profiling.  Bit i of mask selects kernel kind i of
- * {0 route, 1 gate/up GEMM, 2 down GEMM, 3 combine, 4 activation split};
+ * {0 route (including the MX6x3 split of x, done by the same launch),
+ * 1 gate/up GEMM, 2 down GEMM, 3 combine, 4 reserved (never launched)};
  * while a kind is selected, every layer call records a HIP event pair
  * around each launch of that kernel on the call's stream (mask 0 turns
- * timing off; 0x1f times every kernel).  moe_timing_read waits for the recorded events, fills
- * ms[5] with the summed milliseconds and launches[5] with the launch counts
- * of the kernels {route, gate/up GEMM, down GEMM, combine, activation split}
- * since the last reset, and resets the sums when reset != 0.  Not
- * thread-safe. */
+ * timing off; 0x1f times every kernel).  moe_timing_read waits for the
+ * recorded events, fills ms[5] with the summed milliseconds and
+ * launches[5] with the launch counts of the kinds above since the last
+ * reset, and resets the sums when reset != 0.  Not thread-safe. */
 int moe_timing_enable(int mask);
 int moe_timing_read(double* ms, int* launches, int reset);
 

@@ -17,14 +17,17 @@ using namespace moe;
 namespace {
 
 constexpr size_t kAlign = 256;
-// done counter at [0]; expert e's cursor at 64 + CURSOR_STRIDE * e, one cache
-// line per expert so that the atomics of different experts do not serialize
-constexpr int kHeaderInts = 64 + CURSOR_STRIDE * 256;
+// done counter at [0]; expert e's cursor at 64 + CURSOR_STRIDE * e and token
+// block b's K-split counter at 64 + CURSOR_STRIDE * (256 + b), one cache line
+// each so that atomics on different counters do not serialize
+constexpr int kCursor0 = 64;
+constexpr int kTbDone0 = kCursor0 + CURSOR_STRIDE * 256;
+constexpr int kHeaderInts = kTbDone0 + CURSOR_STRIDE * ROUTE_MAX_SPLIT_BLOCKS;
 
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t topk_id, topk_w, rel_pos, counts, offsets, n_tiles, tiles, expert_rows, xq, hq, y, total;
+  size_t topk_id, topk_w, rel_pos, counts, offsets, n_tiles, tiles, expert_rows, part, xq, hq, y, total;
   int max_tiles;
 };
 
@@ -43,6 +46,7 @@ Layout layout(int T, int d, int I, int E, int k) {
   L.n_tiles = o; o = up(o + 4);
   L.tiles = o; o = up(o + (size_t)L.max_tiles * 8);
   L.expert_rows = o; o = up(o + (size_t)E * T * 4);
+  L.part = o; o = up(o + (size_t)ROUTE_MAX_SPLIT_BLOCKS * 16 * E * 4);
   L.xq = o; o = up(o + (size_t)T * (d / 32) * MX6_BLOCK_BYTES);
   L.hq = o; o = up(o + P * (I / 32) * MX6_BLOCK_BYTES);
   L.y = o; o = up(o + P * d * 4);
@@ -193,8 +197,12 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   rp.topk_w = topk_w ? topk_w : (float*)(ws + L.topk_w);
   rp.rel_pos = (int*)(ws + L.rel_pos);
   rp.expert_rows = (int*)(ws + L.expert_rows);
-  rp.cursor = hdr + 64;
+  rp.cursor = hdr + kCursor0;
   rp.done = hdr;
+  rp.tb_done = hdr + kTbDone0;
+  rp.part = (float*)(ws + L.part);
+  rp.xq = route_only ? nullptr : ws + L.xq;
+  rp.n_tb = rp.ks = 0;  // set by launch_route
   rp.counts = counts ? counts : (int*)(ws + L.counts);
   rp.offsets = (int*)(ws + L.offsets);
   rp.n_tiles = (int*)(ws + L.n_tiles);
@@ -204,10 +212,6 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
     if (launch_route(rp, s)) return MOE_ERR_HIP;
   }
   if (route_only) return MOE_OK;
-  {
-    Timed tm(4, s);
-    if (launch_split_x((const uint16_t*)a.x, ws + L.xq, a.T, a.d, s)) return MOE_ERR_HIP;
-  }
 
   GemmParams gp;
   gp.n_tiles = rp.n_tiles;

@@ -21,6 +21,11 @@ struct RouteParams {
   int* offsets;              // [E + 1]
   int* n_tiles;              // [1]
   int2* tiles;               // [max_tiles] (expert, first row)
+  // K split over workgroups (set by launch_route)
+  int n_tb, ks;              // token blocks, workgroups per token block
+  float* part;               // [ROUTE_MAX_SPLIT_BLOCKS][16][E] partial logits
+  int* tb_done;              // [ROUTE_MAX_SPLIT_BLOCKS * CURSOR_STRIDE] zero between calls
+  uint8_t* xq;               // MX6x3 rows of x [T, d/32, 80], or null (no split)
 };
 
 struct GemmParams {
@@ -57,7 +62,7 @@ struct CombineParams {
 };
 
 int launch_route(const RouteParams& p, hipStream_t s);
-int launch_split_x(const uint16_t* x, uint8_t* xq, int T, int d, hipStream_t s);
+int route_kslices(int T, int E);
 int launch_gemm_gateup(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s);
 int launch_gemm_down(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s);
 int launch_combine(const CombineParams& p, hipStream_t s);
@@ -66,6 +71,8 @@ int launch_zero_ints(int* p, int n, hipStream_t s);
 
 // ints between consecutive expert cursors (one 128-byte cache line)
 constexpr int CURSOR_STRIDE = 32;
+// most workgroups in the K-split router mode (token blocks x K slices)
+constexpr int ROUTE_MAX_SPLIT_BLOCKS = 16;
 
 // rows per GEMM tile of the two configurations
 constexpr int MT_SMALL = 16;
