@@ -464,7 +464,8 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
 // 128 gate + the matching 128 up columns).  A workgroup has four waves and
 // two workgroups share a CU, so every SIMD runs two waves (a single wave per
 // SIMD issues the block-scaled MFMAs at only about 60% of the pipe's rate)
-// and one workgroup's start and epilogue overlap the other's K loop.  Wave
+// and one workgroup's start and epilogue overlap the other's K loop (a
+// single 8-wave workgroup with 128 x 384 tiles measured slower).  Wave
 // (wm, wn) owns rows 32wm .. 32wm+31 (two 16-row blocks) and column half wn
 // (gate/up: 64 gate + 64 up columns, i.e. two whole MX blocks of h), eight
 // 16-column blocks in all, so every B fragment read from LDS feeds six
@@ -488,7 +489,7 @@ constexpr int PF_NT = 256;                  // weight rows (output columns) per 
 constexpr int PF_NW = 4;                    // waves: 2 row halves x 2 column halves
 constexpr int PF_NCB = 8;                   // 16-column blocks per wave
 constexpr int PF_XCD = 8;                   // XCDs of the device
-constexpr int PF_BPRE = 3;                  // B fragments read ahead of their MFMAs
+constexpr int PF_BPRE = 2;                  // B fragments read ahead of their MFMAs
 
 // Prefill epilogues.  After the K loop the operand buffers are free; each
 // wave stages its results in its own part of them, 16 rows at a time, so
@@ -626,16 +627,16 @@ __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams 
     return wn * (16 * NCB) + 16 * j;
   };
 
-  // epilogue biases, loaded now so that they arrive during the K loop
+  // the tile's biases (by LDS row), loaded now so that they arrive during
+  // the K loop; columns past the end are never stored
   const int wcol0 = GATEUP ? tcol0 + wn * (8 * NCB) : tcol0 + wn * (16 * NCB);
-  float bias[NCB];
-#pragma unroll
-  for (int j = 0; j < NCB; ++j) {
+  __shared__ float s_bias[PF_NT];
+  for (int n = tid; n < PF_NT; n += PF_NW * 64) {
     if (GATEUP) {
-      const int c = min(wcol0 + 16 * (j % (NCB / 2)) + r, I - 1);  // columns past I are never stored
-      bias[j] = p.bias[(size_t)e * N + (j < NCB / 2 ? 0 : I) + c];
+      const int c = min(tcol0 + (n % (PF_NT / 2)), I - 1);
+      s_bias[n] = p.bias[(size_t)e * N + (n < PF_NT / 2 ? 0 : I) + c];
     } else {
-      bias[j] = p.bias[(size_t)e * N + min(wcol0 + 16 * j + r, N - 1)];
+      s_bias[n] = p.bias[(size_t)e * N + min(tcol0 + n, N - 1)];
     }
   }
 
@@ -670,7 +671,7 @@ __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams 
     const int n = (tid >> 2) + (PF_NW * 16) * q;
     int row;
     if (GATEUP) {
-      const int c = tcol0 + (n & (PF_NT / 2 - 1));
+      const int c = tcol0 + (n % (PF_NT / 2));
       row = (n < PF_NT / 2 ? 0 : I) + (c < I ? c : tcol0 + (n & 15));
     } else {
       const int c = tcol0 + n;
@@ -698,15 +699,25 @@ __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams 
       rs[q] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, s_off[q], c * 4, 0);
     });
   };
-  // scale of (LDS row n = 16J + r, block g) at byte ((J/4 * 4 + g) * 16 + r) * 4 + J % 4:
-  // one dword read gives a lane the scales of four column blocks
+  // scale of (LDS row n, block g): LDS row n is column block j of column
+  // half h (lds_row(j) of wave column h, row r); its byte sits at
+  // (((h * NCB/4 + j/4) * 4 + g) * 16 + r) * 4 + j % 4, so one dword read
+  // gives a lane the scales of four of its column blocks
   auto stage_store = [&](int buf) {
     StaticFor<0, B_PIECES>::run([&](auto ic) {
       constexpr int q = decltype(ic)::value;
       const int n = (tid >> 2) + (PF_NW * 16) * q;
       *(v4u*)(sh.b[buf] + n * 64 + ((bpiece ^ ((n >> 2) & 3)) * 16)) = rb[q];
-      const int J = n >> 4, rr = n & 15;
-      sh.bs[buf][(((J >> 2) * 4 + bpiece) * 16 + rr) * 4 + (J & 3)] = (uint8_t)rs[q];
+      int h, j;
+      if (GATEUP) {
+        const int part = n >= PF_NT / 2, rem = n - part * (PF_NT / 2);
+        h = rem / (8 * NCB);
+        j = part * (NCB / 2) + (rem - h * (8 * NCB)) / 16;
+      } else {
+        h = n / (16 * NCB);
+        j = (n - h * (16 * NCB)) / 16;
+      }
+      sh.bs[buf][(((h * (NCB / 4) + (j >> 2)) * 4 + bpiece) * 16 + (n & 15)) * 4 + (j & 3)] = (uint8_t)rs[q];
     });
   };
 
@@ -754,14 +765,12 @@ __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams 
     load_a(cn, av);
     stage_load(cn);
     __builtin_amdgcn_sched_barrier(0);
-    // the wave's eight column blocks form two groups of four consecutive LDS
-    // row blocks, i.e. two scale dwords
-    uint32_t bsw[2];
+    // the wave's column blocks form groups of four consecutive LDS row
+    // blocks, one scale dword each
+    uint32_t bsw[NCB / 4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int J0 = lds_row(4 * h) >> 4;
-      bsw[h] = *(const uint32_t*)(sh.bs[buf] + (((J0 >> 2) * 4 + g) * 16 + r) * 4);
-    }
+    for (int h = 0; h < NCB / 4; ++h)
+      bsw[h] = *(const uint32_t*)(sh.bs[buf] + (((wn * (NCB / 4) + h) * 4 + g) * 16 + r) * 4);
     v4u bq[PF_BPRE + 1];
     auto read_b = [&](int j) {
       const int n = lds_row(j) + r;
@@ -790,6 +799,9 @@ __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams 
   }
 
   // the loop's last barrier has passed: the weight buffers are free
+  float bias[NCB];
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) bias[j] = s_bias[lds_row(j) + r];
   const int rows_w = rows - 32 * wm;
   const int row_base_w = row_base + 32 * wm;
   uint8_t* scratch = smem + wave * PF_EPI_BYTES;

@@ -16,9 +16,10 @@
 //     (waves in LDS, then workgroups: the last workgroup of the block to
 //     finish adds the others' partials, exchanged through memory), plus the
 //     fp32 bias;
-//  2. per token, each expert's rank among all E logits (ties -> lower
-//     expert id) -- ranks below k are the slots -- and the softmax over the
-//     k selected logits;
+//  2. per token, the k largest logits (ties -> lower expert id): for
+//     E <= 64 each expert's rank among all E logits (ranks below k are the
+//     slots), for larger E k rounds of a wave-wide arg-max; then the softmax
+//     over the k selected logits;
 //  3. per expert, a 64-bit token mask in LDS gives every (token, slot) pair a
 //     stable rank inside the workgroup; one returning atomic per
 //     (workgroup, expert) reserves the workgroup's slice of that expert's row
@@ -215,66 +216,105 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
   for (int u = tid; u < MT * E; u += RT_THREADS) s_logit[u / E][u - (u / E) * E] += p.router_b[u - (u / E) * E];
   __syncthreads();
 
-  // ---- 2. top-k + softmax: one wave per token.  Each lane ranks its
-  // experts against all E logits (ties -> lower id; NaN never wins a slot);
-  // rank j < k takes slot j, so slots follow descending logit ----
+  // ---- 2. top-k + softmax: one wave per token -----------------------------
   for (int tl = wave; tl < MT; tl += RT_THREADS / 64) {
     const int t = t0 + tl;
     if (t >= T) break;
-    // ordering key: the logit's bits made monotone as an unsigned integer
-    // (NaN -> -inf) above the complement of the expert id, so that a larger
-    // key is a larger logit or, on a tie, a lower id
-    auto key_of = [](float x, int e) -> uint64_t {
-      // NaN -> -inf; -0 -> +0 (equal logits tie on the id)
-      const uint32_t b = (x != x) ? 0xff800000u : (x == 0.0f ? 0u : __float_as_uint(x));
-      const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-      return ((uint64_t)o << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
-    };
-    float v[EPL];
-    uint64_t key[EPL];
-    int rank[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
+    if constexpr (EPL == 1) {
+      // E <= 64: each lane ranks its expert against all E logits (ties ->
+      // lower id; NaN never wins a slot); rank j < k takes slot j, so slots
+      // follow descending logit.  Ordering key: the logit's bits made
+      // monotone as an unsigned integer above the complement of the id.
+      auto key_of = [](float x, int e) -> uint64_t {
+        // NaN -> -inf; -0 -> +0 (equal logits tie on the id)
+        const uint32_t b = (x != x) ? 0xff800000u : (x == 0.0f ? 0u : __float_as_uint(x));
+        const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+        return ((uint64_t)o << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+      };
+      const int e = lane;
       const float x = e < E ? s_logit[tl][e] : -__builtin_inff();
-      v[i] = (x != x) ? -__builtin_inff() : x;
-      key[i] = key_of(x, e);
-      rank[i] = 0;
-    }
-    float m = -__builtin_inff();
-    for (int e4 = 0; e4 < E; e4 += 4) {
-      const v4f w4 = *(const v4f*)&s_logit[tl][e4];  // same address on every lane: a broadcast
+      const float v = (x != x) ? -__builtin_inff() : x;
+      const uint64_t key = key_of(x, e);
+      int rank = 0;
+      float m = -__builtin_inff();
+      for (int e4 = 0; e4 < E; e4 += 4) {
+        const v4f w4 = *(const v4f*)&s_logit[tl][e4];  // same address on every lane: a broadcast
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int e2 = e4 + c;
-        const bool in = e2 < E;
-        const uint64_t k2 = key_of(w4[c], e2);
-        m = in ? fmaxf(m, (w4[c] != w4[c]) ? -__builtin_inff() : w4[c]) : m;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) rank[i] += (in && k2 > key[i]) ? 1 : 0;
+        for (int c = 0; c < 4; ++c) {
+          const int e2 = e4 + c;
+          const bool in = e2 < E;
+          m = in ? fmaxf(m, (w4[c] != w4[c]) ? -__builtin_inff() : w4[c]) : m;
+          rank += (in && key_of(w4[c], e2) > key) ? 1 : 0;
+        }
       }
-    }
-    // softmax over the selected logits: e^(l - max) in slot order
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && rank[i] < k) {
-        s_ex[tl][rank[i]] = expf(v[i] - m);
-        s_ids[tl * k + rank[i]] = e;
+      // softmax over the selected logits: e^(l - max), summed in slot order
+      if (e < E && rank < k) {
+        s_ex[tl][rank] = expf(v - m);
+        s_ids[tl * k + rank] = e;
       }
-    }
-    lds_wave_sync_route();
-    if (lane < k) {
-      float den = 0.f;
-      for (int j = 0; j < k; ++j) den += s_ex[tl][j];
-      const int e = s_ids[tl * k + lane];
-      const float raw = s_logit[tl][e];
-      p.topk_id[(size_t)t * k + lane] = e;
-      p.topk_w[(size_t)t * k + lane] = (raw != raw) ? raw : s_ex[tl][lane] / den;
-      atomicOr(&s_mask[e], 1ull << tl);
+      lds_wave_sync_route();
+      if (lane < k) {
+        float den = 0.f;
+        for (int j = 0; j < k; ++j) den += s_ex[tl][j];
+        const int es = s_ids[tl * k + lane];
+        const float raw = s_logit[tl][es];
+        p.topk_id[(size_t)t * k + lane] = es;
+        p.topk_w[(size_t)t * k + lane] = (raw != raw) ? raw : s_ex[tl][lane] / den;
+        atomicOr(&s_mask[es], 1ull << tl);
+      }
+    } else {
+      // E > 64: k rounds of a wave-wide arg-max (ties -> lower id; NaN
+      // never wins a slot); lane j keeps the value and id of slot j
+      float v[EPL];
+      bool taken[EPL];
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        const float x = e < E ? s_logit[tl][e] : -__builtin_inff();
+        v[i] = (x != x) ? -__builtin_inff() : x;
+        taken[i] = e >= E;
+      }
+      float my_v = -__builtin_inff(), m = -__builtin_inff();
+      int my_e = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j >= k) break;
+        float bv = -__builtin_inff();
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          const int e = lane + 64 * i;
+          if (!taken[i] && (v[i] > bv || (v[i] == bv && e < be))) { bv = v[i]; be = e; }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          const float ov = __shfl_xor(bv, off);
+          const int oe = __shfl_xor(be, off);
+          if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+        }
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          if (lane + 64 * i == be) taken[i] = true;
+        if (j == 0) m = bv;
+        if (lane == j) { my_v = bv; my_e = be; }
+      }
+      // softmax over the selected logits (the raw logit, NaN included,
+      // decides the weight)
+      const float ex = (lane < k) ? expf(my_v - m) : 0.f;
+      float den = ex;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+      if (lane < k) {
+        const float raw = s_logit[tl][my_e];
+        p.topk_id[(size_t)t * k + lane] = my_e;
+        p.topk_w[(size_t)t * k + lane] = (raw != raw) ? raw : ex / den;
+        s_ids[tl * k + lane] = my_e;
+        atomicOr(&s_mask[my_e], 1ull << tl);
+      }
     }
   }
   __syncthreads();
+
   // ---- 3. per-expert row lists ---------------------------------------------
   // atomicAdd returns, so each reservation is performed before the barrier
   for (int e = tid; e < E; e += RT_THREADS) {
