@@ -43,4 +43,9 @@ WORKLOADS = {
                                   seed=0x5EED0003, routing="zipf"),
     "120b_stack36": Workload("120b_stack36", T=2048, d=2880, I=2880, E=128, k=4,
                              seed=0x5EED1000, layers=36),
+    # The contrast model of the same page's gpt-oss / Qwen3 comparison
+    # ("OpenAI 最新开源模型 gpt-oss 架构与训练解析", gpt-oss 与 Qwen3 模型对比):
+    # width 2048, expert projection 768, 128 experts with 8 active per token.
+    "qwen3_decode": Workload("qwen3_decode", T=32, d=2048, I=768, E=128, k=8, seed=0x5EED0004),
+    "qwen3_prefill": Workload("qwen3_prefill", T=4096, d=2048, I=768, E=128, k=8, seed=0x5EED0005),
 }

@@ -103,6 +103,19 @@ def test_prefill_120b_zipf_sampled(torch):
     run_and_check(torch, inputs_for("120b_prefill_zipf"), wl.k, wl.clamp, sample=sample, label="120b-prefill-zipf")
 
 
+def test_qwen3_shape_decode(torch):
+    """Second workload: 128 experts, top-8, d=2048, I=768."""
+    wl = WORKLOADS["qwen3_decode"]
+    run_and_check(torch, inputs_for("qwen3_decode"), wl.k, wl.clamp, label="qwen3-decode")
+
+
+def test_qwen3_shape_prefill_sampled(torch):
+    wl = WORKLOADS["qwen3_prefill"]
+    rng = np.random.default_rng(9)
+    sample = np.sort(rng.choice(wl.T, 40, replace=False))
+    run_and_check(torch, inputs_for("qwen3_prefill"), wl.k, wl.clamp, sample=sample, label="qwen3-prefill")
+
+
 RAGGED = [
     # T, d, I, E, k
     (37, 160, 96, 24, 2),
