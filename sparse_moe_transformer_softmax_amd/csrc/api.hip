@@ -47,8 +47,8 @@ Layout layout(int T, int d, int I, int E, int k) {
   L.tiles = o; o = up(o + (size_t)L.max_tiles * 8);
   L.expert_rows = o; o = up(o + (size_t)E * T * 4);
   L.part = o; o = up(o + (size_t)ROUTE_MAX_SPLIT_BLOCKS * 16 * E * 4);
-  L.xq = o; o = up(o + (size_t)T * (d / 32) * MX6_BLOCK_BYTES);
-  L.hq = o; o = up(o + P * (I / 32) * MX6_BLOCK_BYTES);
+  L.xq = o; o = up(o + (size_t)T * mx6_row_bytes(d / 32));
+  L.hq = o; o = up(o + P * mx6_row_bytes(I / 32));
   L.y = o; o = up(o + P * d * 4);
   L.total = o;
   return L;
@@ -65,7 +65,7 @@ int check_shape(int T, int d, int I, int E, int k) {
   // operands are addressed with 32-bit byte offsets (MX6x3 activations:
   // 80 bytes per 32 elements)
   const long long w = d > I ? d : I;
-  if ((long long)T * k * (w / 32) * MX6_BLOCK_BYTES >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * k * mx6_row_bytes((int)(w / 32)) >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
   if ((long long)E * I * d >= (1ll << 32)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }

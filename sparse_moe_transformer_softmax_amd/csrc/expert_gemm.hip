@@ -232,7 +232,7 @@ __device__ __forceinline__ void dec_load_item(const GemmParams& p, int item, int
                                                (int)(rows_left * (size_t)nblk), 0x00020000);
   const int m = r < it.rows ? r : 0;
   const int arow = GATEUP ? p.expert_rows[(size_t)e * p.T + m0 + m] / p.k : it.row_base + m;
-  it.a_off = r < it.rows ? arow * nblk * MX6_BLOCK_BYTES : 0x7ffffff0;
+  it.a_off = r < it.rows ? arow * mx6_row_bytes(nblk) : 0x7ffffff0;
 }
 
 // An item whose copies all fall outside their resources: they return zeros
@@ -300,17 +300,20 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
                                                  rr * nblk + pb0 + 2 * uc, 0, 0, 0);
       }
     }
+    // block pb0 + 4w + g of the phase (blocks past K read the last block;
+    // their products are masked off); piece q of the lanes g = 0..3 is one
+    // 64-byte line of the piece-interleaved row
     const int blk = pb0 + min(wave * DEC_WB + g, npb - 1);
-    const int off = it.a_off < 0x7ffffff0 ? it.a_off + blk * MX6_BLOCK_BYTES : 0x7ffffff0;
+    const int off = it.a_off < 0x7ffffff0 ? it.a_off + mx6_byte_offset(blk, 0) : 0x7ffffff0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const auto t4 = __builtin_amdgcn_raw_buffer_load_b128(arsrc, off + 16 * q, 0, 0);
+      const auto t4 = __builtin_amdgcn_raw_buffer_load_b128(arsrc, off + 64 * q, 0, 0);
       av[q] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
     }
     // bytes 64 .. 75: the last term's codes and the scale bytes (the padding
     // dword is not loaded: a register that a load in flight writes must not
     // be dead, or the compiler waits for the load before reusing it)
-    const auto t3 = __builtin_amdgcn_raw_buffer_load_b96(arsrc, off + 64, 0, 0);
+    const auto t3 = __builtin_amdgcn_raw_buffer_load_b96(arsrc, off + 256, 0, 0);
     av[4] = make_uint4(t3[0], t3[1], t3[2], 0u);
   };
 
@@ -397,16 +400,17 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
       if (rw < rows) {
         uint32_t pk[6];
         pack6x32(s_codes[rw][t], pk);
-        uint2* dst = (uint2*)(p.hq + ((size_t)(row_base + rw) * (I >> 5) + blk) * MX6_BLOCK_BYTES + 24 * t);
-        dst[0] = make_uint2(pk[0], pk[1]);
-        dst[1] = make_uint2(pk[2], pk[3]);
-        dst[2] = make_uint2(pk[4], pk[5]);
+        uint8_t* hrow = p.hq + (size_t)(row_base + rw) * mx6_row_bytes(I >> 5);
+        // 8-byte stores at multiples of 8 never straddle a 16-byte piece
+        *(uint2*)(hrow + mx6_byte_offset(blk, 24 * t)) = make_uint2(pk[0], pk[1]);
+        *(uint2*)(hrow + mx6_byte_offset(blk, 24 * t + 8)) = make_uint2(pk[2], pk[3]);
+        *(uint2*)(hrow + mx6_byte_offset(blk, 24 * t + 16)) = make_uint2(pk[4], pk[5]);
       }
     } else if (lane < 16) {
       const int rw = 4 * (lane - 12) + wave;
       if (rw < rows) {
-        uint2* dst = (uint2*)(p.hq + ((size_t)(row_base + rw) * (I >> 5) + blk) * MX6_BLOCK_BYTES + 72);
-        dst[0] = make_uint2(s_sc[rw], 0u);
+        uint8_t* hrow = p.hq + (size_t)(row_base + rw) * mx6_row_bytes(I >> 5);
+        *(uint2*)(hrow + mx6_byte_offset(blk, 72)) = make_uint2(s_sc[rw], 0u);
       }
     }
     lds_wave_sync();
@@ -543,12 +547,12 @@ __device__ __forceinline__ void pf_epilogue_gateup(const GemmParams& p, const v4
     }
     lds_wave_sync();
     const int ppr = nvalid * (MX6_BLOCK_BYTES / 16);  // 16-byte pieces per row
-    const size_t rowbytes = (size_t)(I >> 5) * MX6_BLOCK_BYTES;
+    const size_t rowbytes = (size_t)mx6_row_bytes(I >> 5);
     for (int pi = lane; pi < 16 * ppr; pi += 64) {
-      const int rw = pi / ppr, off = (pi - rw * ppr) * 16;
+      const int rw = pi / ppr, pc = pi - rw * ppr, bl = pc / 5, q = pc - 5 * bl;
       if (16 * mb + rw < rows_w)
-        *(v4u*)(p.hq + (size_t)(row_base_w + 16 * mb + rw) * rowbytes + (size_t)(col0 >> 5) * MX6_BLOCK_BYTES + off) =
-            *(const v4u*)(sh_blk + rw * NB * MX6_BLOCK_BYTES + off);
+        *(v4u*)(p.hq + (size_t)(row_base_w + 16 * mb + rw) * rowbytes + mx6_byte_offset((col0 >> 5) + bl, 16 * q)) =
+            *(const v4u*)(sh_blk + (rw * NB + bl) * MX6_BLOCK_BYTES + 16 * q);
     }
     lds_wave_sync();
   }
@@ -645,7 +649,7 @@ __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams 
   // lane's offsets are fixed over K and the chunk advance is a uniform
   // scalar offset.  Lanes past the end of K read the next row or past the
   // array (zero), and are masked off in the MFMAs.
-  const uint32_t a_rowbytes = (uint32_t)nblk * MX6_BLOCK_BYTES;
+  const uint32_t a_rowbytes = (uint32_t)mx6_row_bytes(nblk);
   const uint32_t a_rows_total = GATEUP ? (uint32_t)p.T : (uint32_t)(p.T * p.k);
   const __amdgpu_buffer_rsrc_t arsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.a, 0, (int)(a_rows_total * a_rowbytes), 0x00020000);
@@ -660,7 +664,7 @@ __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams 
     const int row = 32 * wm + 16 * mb + r;
     const int m = row < rows ? row : 0;
     a_off[mb] = (GATEUP ? (uint32_t)(p.expert_rows[(size_t)e * p.T + m0 + m] / p.k) : (uint32_t)(row_base + m)) *
-                    a_rowbytes + (uint32_t)g * MX6_BLOCK_BYTES;
+                    a_rowbytes + (uint32_t)g * 16u;
   }
   // weight piece q of this thread: LDS row n = tid/4 + 128q, 16-byte piece
   // tid % 4 of each chunk; columns past the end read the span's first block
@@ -687,8 +691,8 @@ __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams 
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int q = 0; q < 5; ++q)
-        av[mb][q] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(arsrc, a_off[mb] + 16 * q,
-                                                                                  c * 4 * MX6_BLOCK_BYTES, 0));
+        av[mb][q] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(arsrc, a_off[mb] + 64 * q,
+                                                                                  c * MX6_GROUP_BYTES, 0));
   };
   v4u rb[B_PIECES];
   uint32_t rs[B_PIECES];
@@ -816,7 +820,7 @@ static bool prefill_offsets_fit(const GemmParams& p) {
   const unsigned long long lim = 1ull << 32;
   const unsigned long long a_rows = p.hq ? (unsigned long long)p.T : (unsigned long long)p.T * p.k;
   const unsigned long long e_rows = (unsigned long long)p.E * p.N;
-  return a_rows * (p.K / 32) * MX6_BLOCK_BYTES < lim && e_rows * (p.K / 2) < lim;
+  return a_rows * mx6_row_bytes(p.K / 32) < lim && e_rows * (p.K / 2) < lim;
 }
 
 // Decode kernel instance for the phase count of K (unrolled up to 8 phases).

@@ -10,9 +10,14 @@
 //    stored as "MX6x3" rows: every 32-element block becomes three FP6 (E2M3)
 //    terms, each with its own E8M0 scale, such that the sum of the terms
 //    reproduces the value to about 2^-13 of the block maximum.  One block
-//    occupies 80 bytes: term0 codes [0,24), term1 [24,48), term2 [48,72)
-//    (32 six-bit codes packed little-endian), scale bytes at 72,73,74, zero
-//    padding to 80.
+//    has 80 bytes: term0 codes [0,24), term1 [24,48), term2 [48,72) (32
+//    six-bit codes packed little-endian), scale bytes at 72,73,74, padding
+//    to 80.  In a row, blocks are grouped four at a time (one 128-wide MFMA
+//    step, 320 bytes) and the group is stored piece-interleaved: byte i of
+//    block 4c + g sits at 320c + (4 * (i / 16) + g) * 16 + i % 16, so the
+//    four lanes that read the same 16-byte piece of four consecutive blocks
+//    read one 64-byte line.  A row of n blocks occupies ceil(n / 4) * 320
+//    bytes.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -26,6 +31,15 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr int MX6_BLOCK_BYTES = 80;
 constexpr int MX6_TERMS = 3;
+constexpr int MX6_GROUP_BYTES = 4 * MX6_BLOCK_BYTES;  // four blocks, piece-interleaved
+
+// bytes of an MX6x3 row of nblk blocks
+__host__ __device__ constexpr int mx6_row_bytes(int nblk) { return ((nblk + 3) >> 2) * MX6_GROUP_BYTES; }
+
+// offset within a row of byte i (0..79) of block b
+__host__ __device__ __forceinline__ int mx6_byte_offset(int b, int i) {
+  return (b >> 2) * MX6_GROUP_BYTES + (((i >> 4) << 2) + (b & 3)) * 16 + (i & 15);
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);

@@ -43,7 +43,8 @@ __device__ __forceinline__ void lds_wave_sync_route() {
 constexpr int RT_LS = 260;        // LDS row stride of the logits (16-byte aligned rows)
 
 // MX6x3 split of one 32-element block of x by four lanes (q4 = lane % 4
-// holds elements 8q4 .. 8q4+7): the activation operand of the gate/up GEMM.
+// holds elements 8q4 .. 8q4+7): the activation operand of the gate/up GEMM,
+// written in the piece-interleaved row layout.
 __device__ __forceinline__ void split_block(const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, int u, int nblk,
                                             int d, int q4, bool ok) {
   const int uu = ok ? u : 0;  // out-of-range quads compute on block 0 and store nothing
@@ -60,16 +61,16 @@ __device__ __forceinline__ void split_block(const uint16_t* __restrict__ x, uint
   int sc[3];
   mx6x3_split_quad<1, 2>(v, bits, sc);
   if (!ok) return;
-  uint8_t* dst = xq + (size_t)uu * MX6_BLOCK_BYTES;
+  uint8_t* row = xq + (size_t)t * mx6_row_bytes(nblk);
+  // 2-byte stores never straddle a 16-byte piece (even offsets)
 #pragma unroll
-  for (int tt = 0; tt < 3; ++tt) {
-    uint16_t* d16 = (uint16_t*)(dst + 24 * tt + 6 * q4);
-    d16[0] = (uint16_t)bits[tt];
-    d16[1] = (uint16_t)(bits[tt] >> 16);
-    d16[2] = (uint16_t)(bits[tt] >> 32);
-  }
+  for (int tt = 0; tt < 3; ++tt)
+#pragma unroll
+    for (int h = 0; h < 3; ++h)
+      *(uint16_t*)(row + mx6_byte_offset(b, 24 * tt + 6 * q4 + 2 * h)) = (uint16_t)(bits[tt] >> (16 * h));
   if (q4 == 0)
-    *(uint2*)(dst + 72) = make_uint2((uint32_t)sc[0] | ((uint32_t)sc[1] << 8) | ((uint32_t)sc[2] << 16), 0u);
+    *(uint2*)(row + mx6_byte_offset(b, 72)) =
+        make_uint2((uint32_t)sc[0] | ((uint32_t)sc[1] << 8) | ((uint32_t)sc[2] << 16), 0u);
 }
 
 // NCBW: 16-expert column blocks per wave (1 for E <= 64, 2 for E <= 128,
