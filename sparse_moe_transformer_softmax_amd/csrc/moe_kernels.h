@@ -23,7 +23,7 @@ struct RouteParams {
   int2* tiles;               // [max_tiles] (expert, first row)
   // K split over workgroups (set by launch_route)
   int n_tb, ks;              // token blocks, workgroups per token block
-  float* part;               // [ROUTE_MAX_SPLIT_BLOCKS][16][E] partial logits
+  float* part;               // [ROUTE_MAX_SPLIT_BLOCKS * 16][E] partial logits
   int* tb_done;              // [ROUTE_MAX_SPLIT_BLOCKS * CURSOR_STRIDE] zero between calls
   uint8_t* xq;               // MX6x3 rows of x [T, d/32, 80], or null (no split)
 };
@@ -62,7 +62,6 @@ struct CombineParams {
 };
 
 int launch_route(const RouteParams& p, hipStream_t s);
-int route_kslices(int T, int E);
 int launch_gemm_gateup(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s);
 int launch_gemm_down(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s);
 int launch_combine(const CombineParams& p, hipStream_t s);

@@ -21,13 +21,15 @@
 //     slots), for larger E k rounds of a wave-wide arg-max; then the softmax
 //     over the k selected logits;
 //  3. per expert, a 64-bit token mask in LDS gives every (token, slot) pair a
-//     stable rank inside the workgroup; one returning atomic per
-//     (workgroup, expert) reserves the workgroup's slice of that expert's row
-//     list;
-//  4. the last workgroup to finish (device-scope atomic counter; it reads only
-//     atomically updated counters, so no cache-flushing fence is needed)
-//     turns the per-expert counts into offsets and the GEMM tile list, then
-//     clears the counters for the next call.
+//     stable rank inside the workgroup; with several token blocks one
+//     returning atomic per (workgroup, expert) reserves the workgroup's slice
+//     of that expert's row list;
+//  4. the last token block to finish (device-scope atomic counter; it reads
+//     only atomically updated counters, so no cache-flushing fence is
+//     needed) turns the per-expert counts into offsets and the GEMM tile
+//     list with one wave, then clears the counters for the next call.  A
+//     batch that fits one token block (decode) needs neither counter: its
+//     counts are the popcounts of the LDS masks.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -105,13 +107,13 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
   const int eg = wave % EG, ks = wave / EG;  // waves with ks >= KS idle in the GEMM
   const int ES = 16 * ncb + 1;               // row stride of the partials
 
-  __shared__ float s_part[16 * 1032];        // [KS][MT][ES]: KS * MT * ES <= 16 * 1032
+  // [KS][MT][ES]: KS * MT * ES <= 16 * 1032; later the top-k keys
+  __shared__ __align__(16) float s_part[16 * 1032];
   __shared__ __align__(16) float s_logit[MT][RT_LS];
   __shared__ unsigned long long s_mask[256];
   __shared__ int s_base[256];
   __shared__ int s_ids[MT * 8];
   __shared__ float s_ex[MT][8];
-  __shared__ int s_scan[256];
   __shared__ int s_flag;
 
   for (int e = tid; e < 256; e += RT_THREADS) s_mask[e] = 0ull;
@@ -125,45 +127,63 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
 #pragma unroll
       for (int j = 0; j < NCBW; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
     // rows past T and experts past E read row 0 (their logits are never
-    // used), so every load is unconditional
-    const uint16_t* xrow[MBR];
+    // used); K blocks past the wave's range read beyond the buffer, which
+    // returns zeros without memory traffic, so every load and MFMA is
+    // unconditional and no load repeats another
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)p.x, 0, T * d * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void*)p.router_w, 0, E * d * 2, 0x00020000);
+    uint32_t xo[MBR], wo[NCBW];
 #pragma unroll
     for (int i = 0; i < MBR; ++i) {
       const int t = t0 + 16 * i + r;
-      xrow[i] = p.x + (size_t)(t < T ? t : 0) * d + 8 * g;
+      xo[i] = (uint32_t)((t < T ? t : 0) * d + 8 * g) * 2u;
     }
-    const uint16_t* wrow[NCBW];
     bool cbok[NCBW];
 #pragma unroll
     for (int j = 0; j < NCBW; ++j) {
       const int cb = eg + EG * j;
       const int e = cb * 16 + r;
       cbok[j] = cb < ncb;
-      wrow[j] = p.router_w + (size_t)(e < E ? e : 0) * d + 8 * g;
+      wo[j] = (uint32_t)((e < E ? e : 0) * d + 8 * g) * 2u;
     }
     const int s0 = kb0 + ks * (kb1 - kb0) / KS, s1 = kb0 + (ks + 1) * (kb1 - kb0) / KS;
-    for (int sb = s0; sb < s1; sb += BATCH) {
-      uint4 a[BATCH][MBR], b[BATCH][NCBW];
+    // one batch of NB K blocks: every load issued, then the MFMAs
+    auto batch = [&](auto nb_c, int sb) {
+      constexpr int NB = decltype(nb_c)::value;
+      uint4 a[NB][MBR], b[NB][NCBW];
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int kk = min(sb + u, s1 - 1) * 32;
+      for (int u = 0; u < NB; ++u) {
+        const bool in = sb + u < s1;
+        const uint32_t kb = (uint32_t)(sb + u) * 64u;
 #pragma unroll
-        for (int i = 0; i < MBR; ++i) a[u][i] = *(const uint4*)(xrow[i] + kk);
+        for (int i = 0; i < MBR; ++i) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr, in ? xo[i] + kb : 0xffffff00u, 0, 0);
+          a[u][i] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
 #pragma unroll
-        for (int j = 0; j < NCBW; ++j) b[u][j] = *(const uint4*)(wrow[j] + kk);
+        for (int j = 0; j < NCBW; ++j) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, in ? wo[j] + kb : 0xffffff00u, 0, 0);
+          b[u][j] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      // (column blocks past the experts compute on row 0 and are dropped
+      // below: a branch here would let the compiler sink the loads into it)
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        if (sb + u >= s1) break;
+      for (int u = 0; u < NB; ++u)
 #pragma unroll
         for (int j = 0; j < NCBW; ++j)
-          if (cbok[j])
 #pragma unroll
-            for (int i = 0; i < MBR; ++i)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[u][i]),
-                                                                 __builtin_bit_cast(v8bf, b[u][j]), acc[i][j], 0, 0, 0);
-      }
-    }
+          for (int i = 0; i < MBR; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[u][i]),
+                                                               __builtin_bit_cast(v8bf, b[u][j]), acc[i][j], 0, 0, 0);
+    };
+    // full batches, then the remainder two blocks at a time (a short K
+    // range, as at decode, issues no more loads than it needs: each load
+    // instruction costs address-unit time even when it reads nothing)
+    int sb = s0;
+    for (; sb + BATCH <= s1; sb += BATCH) batch(std::integral_constant<int, BATCH>{}, sb);
+    for (; sb < s1; sb += 2) batch(std::integral_constant<int, 2>{}, sb);
 #pragma unroll
     for (int j = 0; j < NCBW; ++j) {
       if (!cbok[j]) continue;
@@ -175,31 +195,37 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
     }
   }
   __syncthreads();
-  // fixed-order sum over the waves' sub-slices
-  for (int u = tid; u < MT * E; u += RT_THREADS) {
-    const int tl = u / E, e = u - tl * E;
-    float v = 0.f;
-    for (int q = 0; q < KS; ++q) v += s_part[(q * MT + tl) * ES + e];
-    s_logit[tl][e] = v;
-  }
 
-  // ---- K-split exchange: every workgroup of the token block writes its
-  // partial logits with stores that reach the device-coherent level, waits
-  // for them, and counts itself in; the last one sums the partials in slice
-  // order (loads from the same level) and carries on alone ----
-  if (p.ks > 1) {
-    __syncthreads();
+  if (p.ks == 1) {
+    // fixed-order sum over the waves' sub-slices, then the bias
+    for (int u = tid; u < MT * E; u += RT_THREADS) {
+      const int tl = u / E, e = u - tl * E;
+      float v = 0.f;
+      for (int q = 0; q < KS; ++q) v += s_part[(q * MT + tl) * ES + e];
+      s_logit[tl][e] = v + p.router_b[e];
+    }
+  } else {
+    // ---- K-split exchange: every workgroup of the token block writes its
+    // partial logits with stores that reach the device-coherent level, waits
+    // for them, and counts itself in; the last one sums the partials in
+    // slice order (loads from the same level), adds the bias and carries on
+    // alone ----
     float* part = p.part + (size_t)tb * p.ks * MT * E;
-    for (int u = tid; u < MT * E; u += RT_THREADS)
-      __hip_atomic_store(part + (size_t)kslice * MT * E + u, s_logit[u / E][u - (u / E) * E], __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    for (int u = tid; u < MT * E; u += RT_THREADS) {
+      const int tl = u / E, e = u - tl * E;
+      float v = 0.f;
+      for (int q = 0; q < KS; ++q) v += s_part[(q * MT + tl) * ES + e];
+      __hip_atomic_store(part + (size_t)kslice * MT * E + u, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the partials have reached memory
     __syncthreads();
     if (tid == 0) s_flag = (atomicAdd(p.tb_done + tb * CURSOR_STRIDE, 1) == p.ks - 1);
     __syncthreads();
     if (!s_flag) return;
     for (int u = tid; u < MT * E; u += RT_THREADS) {
-      // all slices' loads in flight at once, then the sum in slice order
+      // all slices' loads (and the bias) in flight at once, then the sum in
+      // slice order
+      const float bias = p.router_b[u - (u / E) * E];
       float pv[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q)
@@ -209,61 +235,69 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
 #pragma unroll
       for (int q = 0; q < 8; ++q)
         if (q < p.ks) v += pv[q];
-      s_logit[u / E][u - (u / E) * E] = v;
+      s_logit[u / E][u - (u / E) * E] = v + bias;
     }
     if (tid == 0) atomicExch(p.tb_done + tb * CURSOR_STRIDE, 0);
   }
   __syncthreads();
-  for (int u = tid; u < MT * E; u += RT_THREADS) s_logit[u / E][u - (u / E) * E] += p.router_b[u - (u / E) * E];
-  __syncthreads();
 
-  // ---- 2. top-k + softmax: one wave per token -----------------------------
-  for (int tl = wave; tl < MT; tl += RT_THREADS / 64) {
-    const int t = t0 + tl;
-    if (t >= T) break;
-    if constexpr (EPL == 1) {
-      // E <= 64: each lane ranks its expert against all E logits (ties ->
-      // lower id; NaN never wins a slot); rank j < k takes slot j, so slots
-      // follow descending logit.  Ordering key: the logit's bits made
-      // monotone as an unsigned integer above the complement of the id.
-      auto key_of = [](float x, int e) -> uint64_t {
-        // NaN -> -inf; -0 -> +0 (equal logits tie on the id)
-        const uint32_t b = (x != x) ? 0xff800000u : (x == 0.0f ? 0u : __float_as_uint(x));
-        const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-        return ((uint64_t)o << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
-      };
-      const int e = lane;
-      const float x = e < E ? s_logit[tl][e] : -__builtin_inff();
-      const float v = (x != x) ? -__builtin_inff() : x;
-      const uint64_t key = key_of(x, e);
+  // ---- 2. top-k + softmax --------------------------------------------------
+  // Ordering key of a logit: its bits made monotone as an unsigned integer
+  // (NaN -> -inf, -0 -> +0, so equal logits tie on the id) above the
+  // complement of the expert id; a larger key ranks first.
+  auto key_of = [](float x, int e) -> uint64_t {
+    const uint32_t b = (x != x) ? 0xff800000u : (x == 0.0f ? 0u : __float_as_uint(x));
+    const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+  };
+  const int ntok = min(MT, T - t0);
+  if constexpr (EPL == 1) {
+    // E <= 64: every (token, expert) pair is one thread's; its rank among the
+    // token's E keys (ranks below k are the slots, so slots follow
+    // descending logit).  Keys go to LDS once (over the GEMM partials, no
+    // longer needed); padding keys are 0, below every real key.
+    uint64_t* s_key = (uint64_t*)s_part;  // [MT][64]
+    const int EP = (E + 1) & ~1;
+    for (int u = tid; u < ntok * 64; u += RT_THREADS) {
+      const int tl = u >> 6, e = u & 63;
+      if (e < EP) s_key[u] = e < E ? key_of(s_logit[tl][e], e) : 0ull;
+    }
+    __syncthreads();
+    for (int u = tid; u < ntok * E; u += RT_THREADS) {
+      const int tl = u / E, e = u - tl * E;
+      const uint64_t* kr = s_key + tl * 64;
+      const uint64_t key = kr[e];
       int rank = 0;
-      float m = -__builtin_inff();
-      for (int e4 = 0; e4 < E; e4 += 4) {
-        const v4f w4 = *(const v4f*)&s_logit[tl][e4];  // same address on every lane: a broadcast
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int e2 = e4 + c;
-          const bool in = e2 < E;
-          m = in ? fmaxf(m, (w4[c] != w4[c]) ? -__builtin_inff() : w4[c]) : m;
-          rank += (in && key_of(w4[c], e2) > key) ? 1 : 0;
-        }
+      for (int e2 = 0; e2 < EP; e2 += 2) {
+        const ulonglong2 k2 = *(const ulonglong2*)(kr + e2);
+        rank += (k2.x > key) ? 1 : 0;
+        rank += (k2.y > key) ? 1 : 0;
       }
-      // softmax over the selected logits: e^(l - max), summed in slot order
-      if (e < E && rank < k) {
-        s_ex[tl][rank] = expf(v - m);
-        s_ids[tl * k + rank] = e;
-      }
-      lds_wave_sync_route();
-      if (lane < k) {
-        float den = 0.f;
-        for (int j = 0; j < k; ++j) den += s_ex[tl][j];
-        const int es = s_ids[tl * k + lane];
-        const float raw = s_logit[tl][es];
-        p.topk_id[(size_t)t * k + lane] = es;
-        p.topk_w[(size_t)t * k + lane] = (raw != raw) ? raw : s_ex[tl][lane] / den;
-        atomicOr(&s_mask[es], 1ull << tl);
-      }
-    } else {
+      if (rank < k) s_ids[tl * k + rank] = e;
+    }
+    __syncthreads();
+    // softmax over the selected logits: e^(l - max) summed in slot order,
+    // max = the slot-0 logit (NaN counted as -inf); a NaN logit's weight is
+    // that NaN
+    for (int u = tid; u < ntok * k; u += RT_THREADS) {
+      const int tl = u / k, j = u - tl * k;
+      auto val = [&](int jj) {
+        const float x = s_logit[tl][s_ids[tl * k + jj]];
+        return (x != x) ? -__builtin_inff() : x;
+      };
+      const float m = val(0);
+      float den = 0.f;
+      for (int jj = 0; jj < k; ++jj) den += expf(val(jj) - m);
+      const int es = s_ids[tl * k + j];
+      const float raw = s_logit[tl][es];
+      const int t = t0 + tl;
+      p.topk_id[(size_t)t * k + j] = es;
+      p.topk_w[(size_t)t * k + j] = (raw != raw) ? raw : expf(val(j) - m) / den;
+      atomicOr(&s_mask[es], 1ull << tl);
+    }
+  } else {
+    for (int tl = wave; tl < ntok; tl += RT_THREADS / 64) {
+      const int t = t0 + tl;
       // E > 64: k rounds of a wave-wide arg-max (ties -> lower id; NaN
       // never wins a slot); lane j keeps the value and id of slot j
       float v[EPL];
@@ -318,12 +352,12 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
 
   // ---- 3. per-expert row lists ---------------------------------------------
   // atomicAdd returns, so each reservation is performed before the barrier
+  const bool single = p.n_tb == 1;
   for (int e = tid; e < E; e += RT_THREADS) {
     const int c = __popcll(s_mask[e]);
-    s_base[e] = c ? atomicAdd(&p.cursor[e * CURSOR_STRIDE], c) : 0;
+    s_base[e] = (c && !single) ? atomicAdd(&p.cursor[e * CURSOR_STRIDE], c) : 0;
   }
   __syncthreads();
-  const int ntok = min(MT, T - t0);
   for (int q = tid; q < ntok * k; q += RT_THREADS) {
     const int tl = q / k, j = q - tl * k;
     const int e = s_ids[q];
@@ -334,42 +368,47 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
   }
 
   // ---- 4. last token block: offsets, tile list, counter reset -------------
-  if (tid == 0) s_flag = (atomicAdd(p.done, 1) == p.n_tb - 1);
-  __syncthreads();
-  if (!s_flag) return;
-  const int e = tid;
-  int cnt = 0, nt = 0;
-  if (e < E) {
-    cnt = atomicAdd(&p.cursor[e * CURSOR_STRIDE], 0);
-    nt = (cnt + p.mt - 1) / p.mt;
-    p.counts[e] = cnt;
-  }
-  // inclusive scans over E (<= 256) of cnt and nt
-  const int vals[2] = {cnt, nt};
-  int incl[2];
-  for (int s = 0; s < 2; ++s) {
-    if (tid < 256) s_scan[tid] = vals[s];
+  if (!single) {
+    if (tid == 0) s_flag = (atomicAdd(p.done, 1) == p.n_tb - 1);
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int add = (tid < 256 && tid >= off) ? s_scan[tid - off] : 0;
-      __syncthreads();
-      if (tid < 256) s_scan[tid] += add;
-      __syncthreads();
-    }
-    incl[s] = tid < 256 ? s_scan[tid] : 0;
-    __syncthreads();
+    if (!s_flag) return;
   }
-  if (e < E) {
-    p.offsets[e] = incl[0] - cnt;
-    const int tb = incl[1] - nt;
-    for (int i = 0; i < nt; ++i) p.tiles[tb + i] = make_int2(e, i * p.mt);
-    atomicExch(&p.cursor[e * CURSOR_STRIDE], 0);
-    if (e == E - 1) {
-      p.offsets[E] = incl[0];
-      *p.n_tiles = incl[1];
-    }
+  if (wave != 0) return;
+  // one wave: lane L owns experts 4L .. 4L+3 (E <= 256); inclusive scans of
+  // the counts and tile counts across the lanes
+  int c4[4], n4[4], cs = 0, ns = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * lane + i;
+    c4[i] = e >= E ? 0 : single ? __popcll(s_mask[e]) : atomicAdd(&p.cursor[e * CURSOR_STRIDE], 0);
+    n4[i] = (c4[i] + p.mt - 1) / p.mt;
+    cs += c4[i];
+    ns += n4[i];
   }
-  if (tid == 0) atomicExch(p.done, 0);
+  int ci = cs, ni = ns;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ca = __shfl_up(ci, off), na = __shfl_up(ni, off);
+    if (lane >= off) { ci += ca; ni += na; }
+  }
+  int cex = ci - cs, nex = ni - ns;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * lane + i;
+    if (e < E) {
+      p.counts[e] = c4[i];
+      p.offsets[e] = cex;
+      for (int j = 0; j < n4[i]; ++j) p.tiles[nex + j] = make_int2(e, j * p.mt);
+      if (!single) atomicExch(&p.cursor[e * CURSOR_STRIDE], 0);
+    }
+    cex += c4[i];
+    nex += n4[i];
+  }
+  if (lane == 63) {
+    p.offsets[E] = ci;
+    *p.n_tiles = ni;
+    if (!single) atomicExch(p.done, 0);
+  }
 }
 
 // LDS partials of a configuration: KS * MT * ES floats must fit s_part
@@ -378,26 +417,36 @@ static bool route_fits(int ncb, int ncbw, int mbr) {
   return ks >= 1 && ks * 16 * mbr * (16 * ncb + 1) <= 16 * 1032;
 }
 
-// Workgroups per token block: small batches split K over several
-// workgroups so that the router weight streams through more CUs.
-int route_kslices(int T, int E) {
+// Launch shape of the router: token-block height (16 * mbr), column blocks
+// per wave, token blocks and the workgroups per token block.  Small batches
+// split K over several workgroups so that the router weight streams through
+// more CUs; a batch of up to 32 tokens over at most 64 experts is one token
+// block.
+struct RouteShape {
+  int mbr, ncbw, n_tb, ks;
+};
+static bool route_shape(int T, int E, RouteShape& r) {
   const int ncb = (E + 15) / 16;
   const bool big = T >= 2048 && ncb <= 8;
-  const int n_tb = (T + (big ? 31 : 15)) / (big ? 32 : 16);
-  if (n_tb >= ROUTE_MAX_SPLIT_BLOCKS) return 1;
-  const int ks = ROUTE_MAX_SPLIT_BLOCKS / n_tb;
-  return ks < 8 ? ks : 8;
+  const bool one32 = T > 16 && T <= 32 && ncb <= 4 && route_fits(ncb, 1, 2);
+  r.mbr = (big || one32) ? 2 : 1;
+  r.ncbw = big ? (ncb <= 4 ? 1 : 2) : one32 ? 1 : (ncb <= 8 ? 2 : 4);
+  r.n_tb = (T + 16 * r.mbr - 1) / (16 * r.mbr);
+  r.ks = r.n_tb >= ROUTE_MAX_SPLIT_BLOCKS ? 1 : ROUTE_MAX_SPLIT_BLOCKS / r.n_tb;
+  if (r.ks > 8) r.ks = 8;
+  return route_fits(ncb, r.ncbw, r.mbr);
 }
 
 int launch_route(const RouteParams& p0, hipStream_t stream) {
   RouteParams p = p0;
-  const int ncb = (p.E + 15) / 16;
-  const bool big = p.T >= 2048 && ncb <= 8;
-  p.n_tb = (p.T + (big ? 31 : 15)) / (big ? 32 : 16);
-  p.ks = route_kslices(p.T, p.E);
-  const int ncbw = big ? (ncb <= 4 ? 1 : 2) : (ncb <= 8 ? 2 : 4);
-  if (!route_fits(ncb, ncbw, big ? 2 : 1)) return -1;
-  if (p.ks > 1 && (p.part == nullptr || p.tb_done == nullptr || p.n_tb * p.ks > ROUTE_MAX_SPLIT_BLOCKS)) return -1;
+  RouteShape r;
+  if (!route_shape(p.T, p.E, r)) return -1;
+  p.n_tb = r.n_tb;
+  p.ks = r.ks;
+  // the partials of all K slices: n_tb * ks * 16 * mbr rows of E floats
+  if (p.ks > 1 && (p.part == nullptr || p.tb_done == nullptr || p.n_tb * p.ks > ROUTE_MAX_SPLIT_BLOCKS ||
+                   p.n_tb * p.ks * r.mbr > ROUTE_MAX_SPLIT_BLOCKS))
+    return -1;
   const long long quads = p.xq ? (long long)p.T * (p.d / 32) : 0;
   const long long grid = (long long)p.n_tb * p.ks + (quads + RT_THREADS / 4 - 1) / (RT_THREADS / 4);
   const dim3 g((unsigned)grid), b(RT_THREADS);
@@ -411,13 +460,13 @@ int launch_route(const RouteParams& p0, hipStream_t stream) {
     else                                                                                          \
       hipLaunchKernelGGL((route_kernel<NCBW, MBR, 4>), g, b, 0, stream, p);                       \
   } while (0)
-  if (big) {
-    if (ncb <= 4)
+  if (r.mbr == 2) {
+    if (r.ncbw == 1)
       MOE_ROUTE(1, 2);
     else
       MOE_ROUTE(2, 2);
   } else {
-    if (ncb <= 8)
+    if (r.ncbw == 2)
       MOE_ROUTE(2, 1);
     else
       MOE_ROUTE(4, 1);

@@ -29,6 +29,8 @@ def src_sha() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_moe_transformer_softmax_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if not f.endswith((".hip", ".h")):
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
