@@ -144,11 +144,11 @@ __device__ __forceinline__ uint32_t split_h_row(float h0, float h1, int r, uint8
 // Decode kernel: tiles of at most 16 rows, so the kernel is bound by the
 // weight stream.  Work items are (tile, 64-row weight span) pairs (gate/up:
 // 32 gate + the matching 32 up rows; down: 64 output rows), numbered
-// tile-major; a persistent workgroup walks items blockIdx.x,
-// blockIdx.x + gridDim.x, ... and the phases of consecutive items form one
-// stream: while the last phase of an item is consumed, the first phase of
-// the next item is already being copied, and the item's epilogue runs with
-// that copy in flight.  An item walks K in phases of DEC_KPH blocks.  Wave w
+// tile-major, one per workgroup; four workgroups share a CU, so one's
+// start and epilogue overlap the others' streams.  (A persistent variant
+// that walks several items and overlaps each epilogue with the next item's
+// first copies measured slower: it needs more registers per lane.)  An
+// item walks K in phases of DEC_KPH blocks.  Wave w
 // copies the phase's code and scale segments of column block w (16
 // consecutive weight rows) from HBM straight to LDS with buffer_load ... lds
 // -- no register staging, and every instruction reads 1 KB of
@@ -197,17 +197,25 @@ struct DecItem {
   __amdgpu_buffer_rsrc_t crsrc;     // this wave's 16 weight rows: codes
   __amdgpu_buffer_rsrc_t srsrc;     //   and scales
   int a_off;                        // this lane's A row offset, or past the A resource
+  float bias[4];                    // this lane's epilogue bias values (gate/up: gate and up of
+                                    // columns col0 + r and col0 + 16 + r; down: column col0 + 16j + r)
 };
+
+// The tile list, counts, offsets and row lists were written by an earlier
+// launch and are only read here, so they are read as constant memory:
+// scalar loads of uniform values (the expert's 16 row-list entries of the
+// tile too, then picked per lane by a select ladder).
+typedef __attribute__((address_space(4))) const int cint_t;
 
 template <bool GATEUP>
 __device__ __forceinline__ void dec_load_item(const GemmParams& p, int item, int spans, int wave, int r, DecItem& it) {
   const int K = p.K, N = p.N, I = p.I, nblk = K >> 5;
   const int tile = item / spans, span = item - tile * spans;
-  const int2 te = p.tiles[tile];
-  const int e = te.x, m0 = te.y;
+  cint_t* te = (cint_t*)p.tiles + 2 * (size_t)tile;
+  const int e = te[0], m0 = te[1];
   it.e = e;
-  it.rows = min(16, p.counts[e] - m0);
-  it.row_base = p.offsets[e] + m0;
+  it.rows = min(16, ((cint_t*)p.counts)[e] - m0);
+  it.row_base = ((cint_t*)p.offsets)[e] + m0;
   int ok = 0;
   if (GATEUP) {
     it.col0 = span * 32;
@@ -230,9 +238,34 @@ __device__ __forceinline__ void dec_load_item(const GemmParams& p, int item, int
                                                (int)(rows_left * (size_t)(K >> 1)), 0x00020000);
   it.srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_scales + my_row * (size_t)nblk), 0,
                                                (int)(rows_left * (size_t)nblk), 0x00020000);
-  const int m = r < it.rows ? r : 0;
-  const int arow = GATEUP ? p.expert_rows[(size_t)e * p.T + m0 + m] / p.k : it.row_base + m;
+  int arow = it.row_base + r;
+  if (GATEUP) {
+    // entries past the expert's T read on into the next expert's list or
+    // the workspace region after the lists; they are never used
+    cint_t* erow = (cint_t*)p.expert_rows + (size_t)e * p.T + m0;
+    int v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = erow[i];
+    int x = v[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) x = r == i ? v[i] : x;
+    arow = x / p.k;
+  }
   it.a_off = r < it.rows ? arow * mx6_row_bytes(nblk) : 0x7ffffff0;
+  // the epilogue's bias, loaded now so that its latency hides under the
+  // weight stream (columns past the output read the last column, never
+  // stored)
+  const float* bias = p.bias + (size_t)e * N;
+  if (GATEUP) {
+    const int c0 = min(it.col0 + r, I - 1), c1 = min(it.col0 + 16 + r, I - 1);
+    it.bias[0] = bias[c0];
+    it.bias[1] = bias[I + c0];
+    it.bias[2] = bias[c1];
+    it.bias[3] = bias[I + c1];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) it.bias[j] = bias[min(it.col0 + 16 * j + r, N - 1)];
+  }
 }
 
 // An item whose copies all fall outside their resources: they return zeros
@@ -243,6 +276,7 @@ __device__ __forceinline__ void dec_null_item(const GemmParams& p, DecItem& it) 
   it.crsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.b_codes, 0, 0, 0x00020000);
   it.srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.b_scales, 0, 0, 0x00020000);
   it.a_off = 0x7ffffff0;
+  it.bias[0] = it.bias[1] = it.bias[2] = it.bias[3] = 0.f;
 }
 
 template <bool GATEUP, int NPH, bool U16>
@@ -272,19 +306,32 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
   // issue every load of phase ph of item `it`: this wave's column block
   // into LDS buffer `buf` (instruction q moves rows 4q .. 4q+3), this wave's
   // A block into av
-  const int sub = lane / DEC_KPH, slot = lane % DEC_KPH;
+  const int lane_id = lane;
+  // The phase's own offset goes into the instructions' scalar offset (pb0
+  // blocks: 16 B of codes, 1 B of scales, 80 B of A per block), so the lane
+  // offsets are the same for every full phase and need no registers per
+  // phase.  The bounds checks only ever rely on lane offsets: rows past an
+  // item and the null item's copies have lane offsets at or past the
+  // resource's end; every other access lies inside its row.
+  // (with the phase count known, every phase but the last is full: its
+  // offsets are then the same in every phase)
   auto issue = [&](const DecItem& it, int ph, int buf, uint4 (&av)[5]) {
-    const int pb0 = ph * DEC_KPH, npb = min(DEC_KPH, nblk - pb0);
+    // the lane offsets are recomputed at every issue (a few instructions)
+    // rather than held in registers across the item loop
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    const int sub = lane / DEC_KPH, slot = lane % DEC_KPH, g = lane >> 4;
+    const int pb0 = ph * DEC_KPH, npb = (NPH > 0 && ph < NPH - 1) ? DEC_KPH : min(DEC_KPH, nblk - pb0);
 #pragma unroll
     for (int q = 0; q < DEC_Q; ++q) {
       const int rr = 4 * q + sub;                  // row within the column block
       const int b = min(slot ^ rr, npb - 1);       // logical block stored at `slot`
       const int row_off = (wave * 16 + 4 * q) * DEC_KPH;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(it.crsrc, (lds_void_t*)(s_code[buf] + row_off * 16), 16,
-                                               rr * (K >> 1) + (pb0 + b) * 16, 0, 0, 0);
+                                               rr * (K >> 1) + b * 16, pb0 * 16, 0, 0);
       if constexpr (!U16)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(it.srsrc, (lds_void_t*)(s_scl[buf] + row_off), 1,
-                                                 rr * nblk + pb0 + min(slot, npb - 1), 0, 0, 0);
+                                                 rr * nblk + min(slot, npb - 1), pb0, 0, 0);
     }
     if constexpr (U16) {
       // instruction q moves rows 8q .. 8q+7; lane L holds the block pair
@@ -297,29 +344,30 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
         const int uc = 2 * u < npb ? u : 0;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(it.srsrc,
                                                  (lds_void_t*)(s_scl[buf] + (wave * 16 + 8 * q) * Cfg::SROW), 2,
-                                                 rr * nblk + pb0 + 2 * uc, 0, 0, 0);
+                                                 rr * nblk + 2 * uc, pb0, 0, 0);
       }
     }
     // block pb0 + 4w + g of the phase (blocks past K read the last block;
     // their products are masked off); piece q of the lanes g = 0..3 is one
     // 64-byte line of the piece-interleaved row
-    const int blk = pb0 + min(wave * DEC_WB + g, npb - 1);
-    const int off = it.a_off < 0x7ffffff0 ? it.a_off + mx6_byte_offset(blk, 0) : 0x7ffffff0;
+    const int bl = min(wave * DEC_WB + g, npb - 1);
+    const int off = it.a_off < 0x7ffffff0 ? it.a_off + mx6_byte_offset(bl, 0) : 0x7ffffff0;
+    const int aso = pb0 / 4 * MX6_GROUP_BYTES;  // pb0 is a multiple of 4 blocks
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const auto t4 = __builtin_amdgcn_raw_buffer_load_b128(arsrc, off + 64 * q, 0, 0);
+      const auto t4 = __builtin_amdgcn_raw_buffer_load_b128(arsrc, off + 64 * q, aso, 0);
       av[q] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
     }
     // bytes 64 .. 75: the last term's codes and the scale bytes (the padding
     // dword is not loaded: a register that a load in flight writes must not
     // be dead, or the compiler waits for the load before reusing it)
-    const auto t3 = __builtin_amdgcn_raw_buffer_load_b96(arsrc, off + 256, 0, 0);
+    const auto t3 = __builtin_amdgcn_raw_buffer_load_b96(arsrc, off + 256, aso, 0);
     av[4] = make_uint4(t3[0], t3[1], t3[2], 0u);
   };
 
   v4f acc[1][NCB];
   auto consume = [&](int ph, int buf, const uint4 (&av)[5]) {
-    const int npb = min(DEC_KPH, nblk - ph * DEC_KPH);
+    const int npb = (NPH > 0 && ph < NPH - 1) ? DEC_KPH : min(DEC_KPH, nblk - ph * DEC_KPH);
     const int bl = wave * DEC_WB + g;  // logical block within the phase
     Stage<1, NCB> st;
 #pragma unroll
@@ -357,6 +405,9 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
     st.bs[2] = (int)((s2 >> sh) & 0xffu);
     st.bs[3] = (int)((s3 >> sh) & 0xffu);
     mma_stage(acc, st, keep_mask<1, NCB>(bl < npb));
+    // pin the MFMAs to this phase: unused until the epilogue, they could
+    // otherwise be sunk past later code, holding every phase's operands
+    asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]));
   };
 
   // ---- epilogue of item `it`: wave w takes accumulator element w, i.e.
@@ -378,19 +429,19 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
       v[j] = t;
     }
     const int row = 4 * g + wave;  // tile row of this lane's values
-    const int e = it.e, col0 = it.col0, rows = it.rows, row_base = it.row_base;
+    const int col0 = it.col0, rows = it.rows, row_base = it.row_base;
     if (!GATEUP) {
 #pragma unroll
       for (int j = 0; j < NCB; ++j) {
         if (!((it.ok_mask >> j) & 1)) continue;
         const int col = col0 + 16 * j + r;
-        if (row < rows) p.y[(size_t)(row_base + row) * N + col] = v[j] + p.bias[(size_t)e * N + col];
+        if (row < rows) p.y[(size_t)(row_base + row) * N + col] = v[j] + it.bias[j];
       }
       return;
     }
-    const int c0 = min(col0 + r, I - 1), c1 = min(col0 + 16 + r, I - 1);  // columns past I are never stored
-    const float h0 = clamped_swiglu(v[0] + p.bias[(size_t)e * N + c0], v[2] + p.bias[(size_t)e * N + I + c0], p.clamp);
-    const float h1 = clamped_swiglu(v[1] + p.bias[(size_t)e * N + c1], v[3] + p.bias[(size_t)e * N + I + c1], p.clamp);
+    // (columns past I are never stored)
+    const float h0 = clamped_swiglu(v[0] + it.bias[0], v[2] + it.bias[1], p.clamp);
+    const float h1 = clamped_swiglu(v[1] + it.bias[2], v[3] + it.bias[3], p.clamp);
     const uint32_t scw = split_h_row(h0, h1, r, s_codes[row]);
     if (r == 0) s_sc[row] = scw;
     lds_wave_sync();
@@ -434,9 +485,13 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
   for (int j = 0; j < NCB; ++j) acc[0][j] = (v4f){0.f, 0.f, 0.f, 0.f};
   uint4 av0[5], av1[5];
   issue(cur, 0, 0, av0);
-  auto step = [&](int ph, int buf, const uint4 (&avc)[5], uint4 (&avn)[5]) {
-    const bool more_ph = ph + 1 < nph;
-    issue(more_ph ? cur : nul, more_ph ? ph + 1 : 0, buf ^ 1, avn);
+  // step of phase ph: copies of phase ph + 1 of `cur`, or (last phase) of
+  // phase 0 of `nit`
+  auto step = [&](int ph, int buf, bool last, const DecItem& nit, const uint4 (&avc)[5], uint4 (&avn)[5]) {
+    if (last)
+      issue(nit, 0, buf ^ 1, avn);
+    else
+      issue(cur, ph + 1, buf ^ 1, avn);
     wait_vmcnt<Cfg::VM>();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
@@ -444,19 +499,22 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
+  // With the phase count known at compile time (NPH > 0) the loop is
+  // unrolled, so the A registers of consecutive phases are fixed and no copy
+  // of a load in flight forces an early wait.
   if constexpr (NPH > 0) {
     StaticFor<0, NPH>::run([&](auto pc) {
       constexpr int ph = decltype(pc)::value;
       if constexpr (ph % 2 == 0)
-        step(ph, 0, av0, av1);
+        step(ph, 0, ph == NPH - 1, nul, av0, av1);
       else
-        step(ph, 1, av1, av0);
+        step(ph, 1, ph == NPH - 1, nul, av1, av0);
     });
   } else {
     for (int ph = 0;;) {
-      step(ph, 0, av0, av1);
+      step(ph, 0, ph + 1 >= nph, nul, av0, av1);
       if (++ph >= nph) break;
-      step(ph, 1, av1, av0);
+      step(ph, 1, ph + 1 >= nph, nul, av1, av0);
       if (++ph >= nph) break;
     }
   }
@@ -842,18 +900,17 @@ static void launch_decode_u(const GemmParams& p, unsigned grid, int spans, hipSt
 }
 
 template <bool GATEUP>
-static void launch_decode(const GemmParams& p, unsigned grid, int spans, hipStream_t s) {
+static void launch_decode(const GemmParams& p, unsigned items, int spans, hipStream_t s) {
   if ((p.K / 32) % 2 == 0)
-    launch_decode_u<GATEUP, true>(p, grid, spans, s);
+    launch_decode_u<GATEUP, true>(p, items, spans, s);
   else
-    launch_decode_u<GATEUP, false>(p, grid, spans, s);
+    launch_decode_u<GATEUP, false>(p, items, spans, s);
 }
 
 // Launch configurations.
-//   small-M (tiles of 16 rows, decode): persistent workgroups (three per
-//     CU) walk the (tile, 64-row span) items, four waves stream each span's
-//     weights through LDS;
-//   large-M (prefill): one workgroup per (128-row tile, 256-column span)
+//   small-M (tiles of 16 rows, decode): one workgroup per (tile, 64-row
+//     span) item, four waves stream the span's weights through LDS;
+//   large-M (prefill): one workgroup per (64-row tile, 256-column span)
 //     work item, 1-D grid dealt to the XCDs in contiguous ranges.
 int launch_gemm_gateup(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s) {
   if (small_m) {

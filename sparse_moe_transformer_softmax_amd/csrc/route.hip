@@ -178,11 +178,13 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[u][i]),
                                                                __builtin_bit_cast(v8bf, b[u][j]), acc[i][j], 0, 0, 0);
     };
-    // full batches, then the remainder two blocks at a time (a short K
-    // range, as at decode, issues no more loads than it needs: each load
-    // instruction costs address-unit time even when it reads nothing)
+    // whole batches (the last one partly past the range) while more than two
+    // blocks remain, then two at a time: a short K range, as at decode,
+    // issues no more loads than it needs (each load instruction costs
+    // address-unit time even when it reads nothing), a long one needs no
+    // more round trips than full batches
     int sb = s0;
-    for (; sb + BATCH <= s1; sb += BATCH) batch(std::integral_constant<int, BATCH>{}, sb);
+    for (; sb + 2 < s1; sb += BATCH) batch(std::integral_constant<int, BATCH>{}, sb);
     for (; sb < s1; sb += 2) batch(std::integral_constant<int, 2>{}, sb);
 #pragma unroll
     for (int j = 0; j < NCBW; ++j) {
