@@ -1,9 +1,10 @@
 """Workload shapes of the gpt-oss-shaped MoE MLP layer.
 
 Sizes follow the gpt-oss architecture summaries: 32 experts for the 20b model
-and 128 for the 120b model, top-4 routing, hidden size and expert width 2880
-(dtcms.com "GPT-OSS 与 Qwen3" comparison, p5 model-architecture list), 36
-blocks for the 120b stack.  Each workload carries its seed.
+and 128 for the 120b model, top-4 routing ("OpenAI 最新开源模型 gpt-oss 架构与
+训练解析", 模型架构: MoE item), hidden size and expert width 2880 (same page,
+gpt-oss 与 Qwen3 模型对比), 36 blocks for the 120b stack.  Each workload
+carries its seed.
 """
 from __future__ import annotations
 
