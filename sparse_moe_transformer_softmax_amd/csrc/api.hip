@@ -184,7 +184,11 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
               uint16_t* norm_out = nullptr, float eps = 0.f) {
   const int P = a.T * a.k;
   const bool small_m = (long long)P <= 16LL * a.E;
-  const int mt = small_m ? MT_SMALL : MT_LARGE;
+  // 128-row tiles when experts average at least 128 rows and both
+  // projections copy their scale bytes in pairs (K/32 even)
+  const bool wide = !small_m && (long long)P >= 128LL * a.E && (a.d / 32) % 2 == 0 && (a.I / 32) % 2 == 0;
+  const int mode = small_m ? GEMM_DECODE : wide ? GEMM_WIDE : GEMM_PREFILL;
+  const int mt = small_m ? MT_SMALL : wide ? MT_WIDE : MT_LARGE;
   const int max_tiles = max_tiles_for(P, a.E, mt);
   int* hdr = (int*)ws;
 
@@ -228,7 +232,7 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   gp.y = nullptr;
   {
     Timed tm(1, s);
-    if (launch_gemm_gateup(gp, max_tiles, small_m, s)) return MOE_ERR_HIP;
+    if (launch_gemm_gateup(gp, max_tiles, mode, s)) return MOE_ERR_HIP;
   }
 
   gp.a = gp.hq;
@@ -238,7 +242,7 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   gp.y = (float*)(ws + L.y);
   {
     Timed tm(2, s);
-    if (launch_gemm_down(gp, max_tiles, small_m, s)) return MOE_ERR_HIP;
+    if (launch_gemm_down(gp, max_tiles, mode, s)) return MOE_ERR_HIP;
   }
 
   CombineParams cp;

@@ -163,6 +163,13 @@ __device__ __forceinline__ uint32_t split_h_row(float h0, float h1, int r, uint8
 // partials in a fixed order.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// 16-byte copy to LDS, in a plain (non-template) function: the compiler's
+// host pass cannot check this size against its own target, which it would
+// have to do for a call with template-dependent arguments
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t rsrc, lds_void_t* dst, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, (int)voffset, 0, 0, 0);
+}
+
 constexpr int DEC_KPH = 16;                // K blocks per phase
 constexpr int DEC_NW = 4;                  // waves per workgroup
 constexpr int DEC_Q = DEC_KPH / 4;         // copy instructions per wave per phase (codes; same for scales)
@@ -874,6 +881,275 @@ __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams 
 }
 
 // The prefill kernel addresses operands with 32-bit byte offsets.
+// Wide prefill kernel: tiles of PW_MT = 128 rows x PW_NT = 512 weight rows
+// (gate/up: 256 gate + the matching 256 up columns), eight waves, one
+// workgroup per CU.  Wave (wm, wn) owns rows 32wm .. 32wm+31 (two 16-row
+// blocks) and 16 column blocks (gate/up: 8 gate + the matching 8 up blocks),
+// so each A fragment feeds 48 MFMAs and each B fragment 6.  With the
+// three-term A operand (80 bytes per 32 elements) the operands of a 64 x 256
+// tile need about as many bytes per MFMA as a CU's L1 can deliver; this
+// tile moves half as many.
+//
+// Both operands reach LDS with buffer_load ... lds (no register staging):
+// per 4-block K chunk the A tile is 128 rows x 320 bytes (one piece-
+// interleaved group per row) and the weight tile 512 rows x 64 bytes of
+// codes plus their scale bytes (2-byte copies, one per LDS dword).  Each
+// copy instruction fills 1 KB (256 B for scales) of consecutive LDS, and
+// the lane -> source mapping places the pieces XOR-swizzled (A: piece s of
+// row m at slot s ^ ((m >> 1) & 3); B: piece g of row n at g ^ ((n >> 2) &
+// 3)), so the fragment reads are free of bank conflicts.  Two chunk buffers:
+// the copies of chunk c+1 are issued right after the barrier that opens
+// chunk c and waited for (vmcnt) before the next barrier.  The LDS reads are
+// asm blocks that wait for their own results, so the compiler never waits
+// for the copies in flight.  Offsets include the chunk (no scalar offset):
+// weight blocks past K are clamped to the row's last block, A rows past the
+// tile read past the A resource (zeros, no traffic).
+constexpr int PW_MT = 128;
+constexpr int PW_NT = 512;
+constexpr int PW_NW = 8;
+constexpr int PW_NCB = 16;
+constexpr int PW_A_BYTES = PW_MT * MX6_GROUP_BYTES;   // 40960
+constexpr int PW_B_BYTES = PW_NT * 64;                // 32768
+constexpr int PW_S_BYTES = PW_NT * 2 * 4;             // 4096
+constexpr int PW_BUF = PW_A_BYTES + PW_B_BYTES + PW_S_BYTES;
+constexpr int PW_A_COPIES = PW_A_BYTES / 1024 / PW_NW;  // 5 per wave
+constexpr int PW_B_COPIES = PW_B_BYTES / 1024 / PW_NW;  // 4 per wave
+constexpr int PW_S_COPIES = PW_NT * 2 / 64 / PW_NW;     // 2 per wave
+constexpr int PW_EPI_BYTES = 16 * (16 * PW_NCB + 4) * 4;
+static_assert(PW_A_COPIES == 5 && PW_B_COPIES == 4 && PW_S_COPIES == 2, "copy split");
+static_assert(PW_EPI_BYTES >= 16 * (8 * PW_NCB + 4) * 4 + 16 * (PW_NCB / 4) * MX6_BLOCK_BYTES, "gate/up staging fits");
+static_assert(PW_NW * PW_EPI_BYTES <= 2 * PW_BUF, "epilogue staging fits the operand buffers");
+
+template <bool GATEUP>
+__global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmParams p, int spans) {
+  constexpr int MB = 2, NCB = PW_NCB;
+  __shared__ __align__(16) uint8_t smem[2 * PW_BUF];
+  __shared__ float s_bias[PW_NT];
+
+  // ---- work item: dealt to the XCDs in contiguous ranges ----
+  const int total = *p.n_tiles * spans;
+  const int per = (total + PF_XCD - 1) / PF_XCD;
+  const int lin = blockIdx.x;
+  const int item = (lin % PF_XCD) * per + lin / PF_XCD;
+  if (lin / PF_XCD >= per || item >= total) return;
+  const int tile = item / spans, span = item - tile * spans;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int2 te = p.tiles[tile];
+  const int e = te.x, m0 = te.y;
+  const int rows = min(PW_MT, p.counts[e] - m0);
+  const int row_base = p.offsets[e] + m0;
+  const int K = p.K, N = p.N, I = p.I, nblk = K >> 5;
+  const int g = lane >> 4, r = lane & 15;
+
+  // tile columns: gate/up -- gate columns span*256 .. +255 (tile rows
+  // 0..255) and the same up columns (tile rows 256..511); down --
+  // span*512 .. +511
+  const int tcol0 = GATEUP ? span * (PW_NT / 2) : span * PW_NT;
+  // tile row of the wave's column block j
+  auto tile_row = [&](int j) -> int {
+    if (GATEUP) return (j < NCB / 2 ? 0 : PW_NT / 2) + wn * (8 * NCB) + 16 * (j % (NCB / 2));
+    return wn * (16 * NCB) + 16 * j;
+  };
+  // weight row (within the expert) of tile row n; rows past the output
+  // take a row of the span's first block (never stored)
+  auto weight_row = [&](int n) -> int {
+    if (GATEUP) {
+      const int c = tcol0 + (n % (PW_NT / 2));
+      return (n < PW_NT / 2 ? 0 : I) + (c < I ? c : tcol0 + (n & 15));
+    }
+    const int c = tcol0 + n;
+    return c < N ? c : tcol0 + (n & 15);
+  };
+  for (int n = tid; n < PW_NT; n += PW_NW * 64) {
+    if (GATEUP) {
+      const int c = min(tcol0 + (n % (PW_NT / 2)), I - 1);
+      s_bias[n] = p.bias[(size_t)e * N + (n < PW_NT / 2 ? 0 : I) + c];
+    } else {
+      s_bias[n] = p.bias[(size_t)e * N + min(tcol0 + n, N - 1)];
+    }
+  }
+
+  // ---- copy offsets (the chunk is added per chunk) ----
+  const uint32_t a_rowbytes = (uint32_t)mx6_row_bytes(nblk);
+  const uint32_t a_rows_total = GATEUP ? (uint32_t)p.T : (uint32_t)(p.T * p.k);
+  const __amdgpu_buffer_rsrc_t arsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.a, 0, (int)(a_rows_total * a_rowbytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.b_codes, 0, (int)((uint32_t)p.E * (uint32_t)N * (uint32_t)(K >> 1)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.b_scales, 0, (int)((uint32_t)p.E * (uint32_t)N * (uint32_t)nblk), 0x00020000);
+  constexpr uint32_t A_OOB = 0x7ffffff0u;  // at or past the A resource's end (it is below 2^31 bytes)
+  // A copy k of this wave fills LDS slots u = (5 wave + k) * 64 + lane:
+  // tile row u / 20, slot u % 20 holding piece (u % 20) ^ ((row >> 1) & 3)
+  uint32_t a_src[PW_A_COPIES];
+#pragma unroll
+  for (int k = 0; k < PW_A_COPIES; ++k) {
+    const int u = (PW_A_COPIES * wave + k) * 64 + lane;
+    const int m = u / 20, slot = u - 20 * m;
+    const int piece = slot ^ ((m >> 1) & 3);
+    uint32_t off = A_OOB;
+    if (m < rows) {
+      const uint32_t arow = GATEUP ? (uint32_t)(p.expert_rows[(size_t)e * p.T + m0 + m] / p.k)
+                                   : (uint32_t)(row_base + m);
+      off = arow * a_rowbytes + (uint32_t)piece * 16u;
+    }
+    a_src[k] = off;
+  }
+  // B copy k fills slots u = (4 wave + k) * 64 + lane: tile row u / 4,
+  // slot u % 4 holding block (u % 4) ^ ((n >> 2) & 3) of the chunk
+  uint32_t b_row[PW_B_COPIES];
+  int b_blk[PW_B_COPIES];
+#pragma unroll
+  for (int k = 0; k < PW_B_COPIES; ++k) {
+    const int u = (PW_B_COPIES * wave + k) * 64 + lane;
+    const int n = u >> 2, slot = u & 3;
+    b_row[k] = ((uint32_t)e * (uint32_t)N + (uint32_t)weight_row(n)) * (uint32_t)(K >> 1);
+    b_blk[k] = slot ^ ((n >> 2) & 3);
+  }
+  // scale copy k fills dwords u = (2 wave + k) * 64 + lane: tile row u / 2,
+  // block pair u % 2 of the chunk (two bytes, low half of the dword)
+  uint32_t s_row[PW_S_COPIES];
+  int s_pair[PW_S_COPIES];
+#pragma unroll
+  for (int k = 0; k < PW_S_COPIES; ++k) {
+    const int u = (PW_S_COPIES * wave + k) * 64 + lane;
+    s_row[k] = ((uint32_t)e * (uint32_t)N + (uint32_t)weight_row(u >> 1)) * (uint32_t)nblk;
+    s_pair[k] = u & 1;
+  }
+  auto issue = [&](int c, int buf) {
+    uint8_t* base = smem + buf * PW_BUF;
+#pragma unroll
+    for (int k = 0; k < PW_A_COPIES; ++k)
+      lds_copy16(arsrc, (lds_void_t*)(base + (PW_A_COPIES * wave + k) * 1024),
+                 a_src[k] == A_OOB ? A_OOB : a_src[k] + (uint32_t)c * MX6_GROUP_BYTES);
+#pragma unroll
+    for (int k = 0; k < PW_B_COPIES; ++k)
+      lds_copy16(crsrc, (lds_void_t*)(base + PW_A_BYTES + (PW_B_COPIES * wave + k) * 1024),
+                 b_row[k] + (uint32_t)min(4 * c + b_blk[k], nblk - 1) * 16u);
+#pragma unroll
+    for (int k = 0; k < PW_S_COPIES; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          srsrc, (lds_void_t*)(base + PW_A_BYTES + PW_B_BYTES + (PW_S_COPIES * wave + k) * 256), 2,
+          s_row[k] + (uint32_t)min(4 * c + 2 * s_pair[k], nblk - 2), 0, 0, 0);
+  };
+
+  v4f acc[MB][NCB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) acc[mb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  // LDS byte addresses of this lane's fragments inside a chunk buffer
+  uint32_t a_lds[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = 32 * wm + 16 * mb + r;
+    a_lds[mb] = (uint32_t)(m * MX6_GROUP_BYTES);  // piece s at slot s ^ ((m >> 1) & 3)
+  }
+  const int a_sw = ((32 * wm + r) >> 1) & 3;  // the same for both row blocks (16 rows apart)
+  uint32_t b_lds[NCB], s_lds[NCB];
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) {
+    const int n = tile_row(j) + r;
+    b_lds[j] = (uint32_t)(PW_A_BYTES + n * 64 + ((g ^ ((n >> 2) & 3)) * 16));
+    s_lds[j] = (uint32_t)(PW_A_BYTES + PW_B_BYTES + (2 * n + (g >> 1)) * 4);
+  }
+  const int s_shift = 8 * (g & 1);
+
+  const int nchunk = (nblk + 3) >> 2;
+  issue(0, 0);
+  for (int c = 0; c < nchunk; ++c) {
+    const int buf = c & 1;
+    const uint32_t bbase = (uint32_t)(uintptr_t)(smem + buf * PW_BUF);
+    wait_vmcnt<0>();  // this wave's copies of chunk c
+    __builtin_amdgcn_s_barrier();  // everyone's copies of chunk c; everyone done with chunk c - 1
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 1 < nchunk) issue(c + 1, buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t keep = (4 * c + g) < nblk ? 0xffffffffu : 0u;
+    // A fragments: pieces 0..4 of block g of the lane's row in each row block
+    v8i a[MB][3];
+    int as[MB][3];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      v4u w0, w1, w2, w3, w4;
+      const uint32_t ab = bbase + a_lds[mb];
+      const uint32_t o0 = ((0 * 4 + g) ^ a_sw) * 16, o1 = ((1 * 4 + g) ^ a_sw) * 16, o2 = ((2 * 4 + g) ^ a_sw) * 16,
+                     o3 = ((3 * 4 + g) ^ a_sw) * 16, o4 = ((4 * 4 + g) ^ a_sw) * 16;
+      asm volatile(
+          "ds_read_b128 %0, %5\n\t"
+          "ds_read_b128 %1, %6\n\t"
+          "ds_read_b128 %2, %7\n\t"
+          "ds_read_b128 %3, %8\n\t"
+          "ds_read_b128 %4, %9\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3), "=&v"(w4)
+          : "v"(ab + o0), "v"(ab + o1), "v"(ab + o2), "v"(ab + o3), "v"(ab + o4));
+      const uint32_t w[20] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w, w2.x, w2.y,
+                              w2.z, w2.w, w3.x, w3.y, w3.z, w3.w, w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        a[mb][t] = (v8i){(int)(w[6 * t] & keep), (int)(w[6 * t + 1] & keep), (int)(w[6 * t + 2] & keep),
+                         (int)(w[6 * t + 3] & keep), (int)(w[6 * t + 4] & keep), (int)(w[6 * t + 5] & keep), 0, 0};
+        as[mb][t] = (int)((((w[18] & keep) >> (8 * t)) & 0xffu) | (127u & ~keep));
+      }
+    }
+    // B fragments in groups of four column blocks (one asm block each),
+    // then their 24 MFMAs; the two row blocks alternate, so consecutive
+    // MFMAs never depend on each other
+#pragma unroll
+    for (int jg = 0; jg < NCB / 4; ++jg) {
+      v4u b0, b1, b2, b3;
+      uint32_t t0, t1, t2, t3;
+      asm volatile(
+          "ds_read_b128 %0, %8\n\t"
+          "ds_read_b128 %1, %9\n\t"
+          "ds_read_b128 %2, %10\n\t"
+          "ds_read_b128 %3, %11\n\t"
+          "ds_read_b32 %4, %12\n\t"
+          "ds_read_b32 %5, %13\n\t"
+          "ds_read_b32 %6, %14\n\t"
+          "ds_read_b32 %7, %15\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+          : "v"(bbase + b_lds[4 * jg]), "v"(bbase + b_lds[4 * jg + 1]), "v"(bbase + b_lds[4 * jg + 2]),
+            "v"(bbase + b_lds[4 * jg + 3]), "v"(bbase + s_lds[4 * jg]), "v"(bbase + s_lds[4 * jg + 1]),
+            "v"(bbase + s_lds[4 * jg + 2]), "v"(bbase + s_lds[4 * jg + 3]));
+      const v4u bb[4] = {b0, b1, b2, b3};
+      const uint32_t ss[4] = {t0, t1, t2, t3};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 4 * jg + jj;
+        const v8i b = {(int)(bb[jj].x & keep), (int)(bb[jj].y & keep), (int)(bb[jj].z & keep),
+                       (int)(bb[jj].w & keep), 0, 0, 0, 0};
+        const int bsc = (int)(((ss[jj] >> s_shift) & 0xffu & keep) | (127u & ~keep));
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[mb][t], b, acc[mb][j], 2, 4, 0,
+                                                                          as[mb][t], 0, bsc);
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with the operand buffers
+
+  float bias[NCB];
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) bias[j] = s_bias[tile_row(j) + r];
+  const int rows_w = rows - 32 * wm;
+  const int row_base_w = row_base + 32 * wm;
+  const int wcol0 = GATEUP ? tcol0 + wn * (8 * NCB) : tcol0 + wn * (16 * NCB);
+  uint8_t* scratch = smem + wave * PW_EPI_BYTES;
+  if (rows_w <= 0) return;
+  if (GATEUP)
+    pf_epilogue_gateup<NCB>(p, acc, bias, rows_w, row_base_w, wcol0, lane, scratch);
+  else
+    pf_epilogue_down<NCB>(p, acc, bias, rows_w, row_base_w, wcol0, lane, scratch);
+}
+
 static bool prefill_offsets_fit(const GemmParams& p) {
   const unsigned long long lim = 1ull << 32;
   const unsigned long long a_rows = p.hq ? (unsigned long long)p.T : (unsigned long long)p.T * p.k;
@@ -911,31 +1187,41 @@ static void launch_decode(const GemmParams& p, unsigned items, int spans, hipStr
 //   small-M (tiles of 16 rows, decode): one workgroup per (tile, 64-row
 //     span) item, four waves stream the span's weights through LDS;
 //   large-M (prefill): one workgroup per (64-row tile, 256-column span)
-//     work item, 1-D grid dealt to the XCDs in contiguous ranges.
-int launch_gemm_gateup(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s) {
-  if (small_m) {
+//     work item, 1-D grid dealt to the XCDs in contiguous ranges;
+//   wide (prefill with enough rows per expert and even K/32 for both
+//     projections): one workgroup per (128-row tile, 512-column span).
+int launch_gemm_gateup(const GemmParams& p, int max_tiles, int mode, hipStream_t s) {
+  if (mode == GEMM_DECODE) {
     const int spans = (p.I + 31) / 32;
     launch_decode<true>(p, (unsigned)((long long)max_tiles * spans), spans, s);
   } else {
     if (!prefill_offsets_fit(p)) return -1;
-    const int spans = (p.I + PF_NT / 2 - 1) / (PF_NT / 2);
+    const bool wide = mode == GEMM_WIDE;
+    const int spans = wide ? (p.I + PW_NT / 2 - 1) / (PW_NT / 2) : (p.I + PF_NT / 2 - 1) / (PF_NT / 2);
     const long long items = (long long)max_tiles * spans;
-    hipLaunchKernelGGL((expert_gemm_prefill<true>), dim3((unsigned)((items + PF_XCD - 1) / PF_XCD * PF_XCD)),
-                       dim3(PF_NW * 64), 0, s, p, spans);
+    const dim3 g((unsigned)((items + PF_XCD - 1) / PF_XCD * PF_XCD));
+    if (wide)
+      hipLaunchKernelGGL((expert_gemm_prefill_wide<true>), g, dim3(PW_NW * 64), 0, s, p, spans);
+    else
+      hipLaunchKernelGGL((expert_gemm_prefill<true>), g, dim3(PF_NW * 64), 0, s, p, spans);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_gemm_down(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s) {
-  if (small_m) {
+int launch_gemm_down(const GemmParams& p, int max_tiles, int mode, hipStream_t s) {
+  if (mode == GEMM_DECODE) {
     const int spans = (p.N + 63) / 64;
     launch_decode<false>(p, (unsigned)((long long)max_tiles * spans), spans, s);
   } else {
     if (!prefill_offsets_fit(p)) return -1;
-    const int spans = (p.N + PF_NT - 1) / PF_NT;
+    const bool wide = mode == GEMM_WIDE;
+    const int spans = wide ? (p.N + PW_NT - 1) / PW_NT : (p.N + PF_NT - 1) / PF_NT;
     const long long items = (long long)max_tiles * spans;
-    hipLaunchKernelGGL((expert_gemm_prefill<false>), dim3((unsigned)((items + PF_XCD - 1) / PF_XCD * PF_XCD)),
-                       dim3(PF_NW * 64), 0, s, p, spans);
+    const dim3 g((unsigned)((items + PF_XCD - 1) / PF_XCD * PF_XCD));
+    if (wide)
+      hipLaunchKernelGGL((expert_gemm_prefill_wide<false>), g, dim3(PW_NW * 64), 0, s, p, spans);
+    else
+      hipLaunchKernelGGL((expert_gemm_prefill<false>), g, dim3(PF_NW * 64), 0, s, p, spans);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

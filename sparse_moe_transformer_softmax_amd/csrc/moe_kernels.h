@@ -62,8 +62,11 @@ struct CombineParams {
 };
 
 int launch_route(const RouteParams& p, hipStream_t s);
-int launch_gemm_gateup(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s);
-int launch_gemm_down(const GemmParams& p, int max_tiles, bool small_m, hipStream_t s);
+// GEMM configurations: decode (16-row tiles), prefill (64-row tiles),
+// wide prefill (128-row tiles)
+enum GemmMode { GEMM_DECODE = 0, GEMM_PREFILL = 1, GEMM_WIDE = 2 };
+int launch_gemm_gateup(const GemmParams& p, int max_tiles, int mode, hipStream_t s);
+int launch_gemm_down(const GemmParams& p, int max_tiles, int mode, hipStream_t s);
 int launch_combine(const CombineParams& p, hipStream_t s);
 int launch_rmsnorm(const uint16_t* x, uint16_t* out, int T, int d, float eps, hipStream_t s);
 int launch_zero_ints(int* p, int n, hipStream_t s);
@@ -76,5 +79,6 @@ constexpr int ROUTE_MAX_SPLIT_BLOCKS = 16;
 // rows per GEMM tile of the two configurations
 constexpr int MT_SMALL = 16;
 constexpr int MT_LARGE = 64;
+constexpr int MT_WIDE = 128;
 
 }  // namespace moe
