@@ -44,10 +44,15 @@ struct StaticFor {
   }
 };
 
+// clamp(g) * sigmoid(clamp(g)) * (clamp(u) + 1) with the hardware exp2 and
+// reciprocal (a few ulp; the result is then rounded to 2^-13 of its block
+// maximum by the MX6x3 split).  Without a clamp, large |g| gives the limits
+// 0 and g (exp2 overflows to inf, its reciprocal to 0); a NaN propagates.
 __device__ __forceinline__ float clamped_swiglu(float g, float u, float c) {
   const float gc = (g != g) ? g : fminf(fmaxf(g, -c), c);
   const float uc = (u != u) ? u : fminf(fmaxf(u, -c), c);
-  return gc / (1.0f + expf(-gc)) * (uc + 1.0f);
+  const float e = __builtin_amdgcn_exp2f(-gc * 1.44269504088896341f);
+  return gc * __builtin_amdgcn_rcpf(1.0f + e) * (uc + 1.0f);
 }
 
 template <int MB, int NCB>
@@ -561,14 +566,13 @@ constexpr int PF_XCD = 8;                   // XCDs of the device
 constexpr int PF_BPRE = 2;                  // B fragments read ahead of their MFMAs
 
 // Prefill epilogues.  After the K loop the operand buffers are free; each
-// wave stages its results in its own part of them, 16 rows at a time, so
-// that the global stores are whole 16-byte pieces of consecutive bytes.
+// wave stages its results in its own part of them, 16 rows at a time.
 //
 // Gate/up: h = clamped SwiGLU of (gate + b13, up + b13) is written to LDS as
-// fp32 [16][16*HALF + 4]; then four lanes per (row, 32-column block) split
-// the block into its three E2M3 terms (block maximum reduced across the
-// quad with DPP), assemble the 80-byte MX6x3 blocks in LDS, and the wave
-// copies the rows' blocks out.
+// fp32 [16][16*HALF + 4], each 32-column block stored as its 16 even then
+// its 16 odd columns; then one lane per (row, 32-column block) reads the
+// block, splits it into its three E2M3 terms with the hardware conversions
+// and stores the 80-byte MX6x3 block as its five 16-byte pieces.
 template <int NCB>
 __device__ __forceinline__ void pf_epilogue_gateup(const GemmParams& p, const v4f (&acc)[2][NCB],
                                                    const float (&bias)[NCB], int rows_w, int row_base_w, int col0,
@@ -578,10 +582,14 @@ __device__ __forceinline__ void pf_epilogue_gateup(const GemmParams& p, const v4
   constexpr int NB = HALF / 2;       // MX blocks of h per row
   static_assert(HALF % 2 == 0, "gate span is whole 32-column blocks");
   float* sh_h = (float*)scratch;
-  uint8_t* sh_blk = scratch + 16 * HS * 4;
   const int g = lane >> 4, r = lane & 15, I = p.I;
   const int nvalid = min(NB, (I - col0) >> 5);
-  const int row = lane >> 2, q4 = lane & 3;
+  const size_t rowbytes = (size_t)mx6_row_bytes(I >> 5);
+  // the block this lane splits: row lane / NB, block lane % NB
+  const int srow = lane / NB, sblk = lane - srow * NB;
+  // column 16j + r of the wave's span lies in block j / 2 at position
+  // 16 (j & 1) + r, stored at 16 * (r & 1) + 8 (j & 1) + r / 2
+  const int cpos = 16 * (r & 1) + (r >> 1);
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     if (16 * mb >= rows_w) break;
@@ -589,35 +597,34 @@ __device__ __forceinline__ void pf_epilogue_gateup(const GemmParams& p, const v4
     for (int j = 0; j < HALF; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        sh_h[(4 * g + q) * HS + 16 * j + r] =
+        sh_h[(4 * g + q) * HS + 32 * (j >> 1) + 8 * (j & 1) + cpos] =
             clamped_swiglu(acc[mb][j][q] + bias[j], acc[mb][HALF + j][q] + bias[HALF + j], p.clamp);
     lds_wave_sync();
+    if (srow < 16) {
+      const float* src = sh_h + srow * HS + 32 * sblk;
+      v16f ve, vo;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float* src = sh_h + row * HS + 32 * b + 8 * q4;
-      const v4f lo = *(const v4f*)src, hi = *(const v4f*)(src + 4);
-      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      uint64_t bits[3];
-      int sc[3];
-      mx6x3_split_quad<1, 2>(v, bits, sc);
-      uint8_t* dst = sh_blk + (row * NB + b) * MX6_BLOCK_BYTES;
+      for (int i = 0; i < 4; ++i) {
+        const v4f e4 = *(const v4f*)(src + 4 * i), o4 = *(const v4f*)(src + 16 + 4 * i);
 #pragma unroll
-      for (int t = 0; t < 3; ++t) {
-        uint16_t* d16 = (uint16_t*)(dst + 24 * t + 6 * q4);
-        d16[0] = (uint16_t)bits[t];
-        d16[1] = (uint16_t)(bits[t] >> 16);
-        d16[2] = (uint16_t)(bits[t] >> 32);
+        for (int u = 0; u < 4; ++u) {
+          ve[4 * i + u] = e4[u];
+          vo[4 * i + u] = o4[u];
+        }
       }
-      if (q4 == 0) *(uint2*)(dst + 72) = make_uint2((uint32_t)sc[0] | ((uint32_t)sc[1] << 8) | ((uint32_t)sc[2] << 16), 0u);
-    }
-    lds_wave_sync();
-    const int ppr = nvalid * (MX6_BLOCK_BYTES / 16);  // 16-byte pieces per row
-    const size_t rowbytes = (size_t)mx6_row_bytes(I >> 5);
-    for (int pi = lane; pi < 16 * ppr; pi += 64) {
-      const int rw = pi / ppr, pc = pi - rw * ppr, bl = pc / 5, q = pc - 5 * bl;
-      if (16 * mb + rw < rows_w)
-        *(v4u*)(p.hq + (size_t)(row_base_w + 16 * mb + rw) * rowbytes + mx6_byte_offset((col0 >> 5) + bl, 16 * q)) =
-            *(const v4u*)(sh_blk + (rw * NB + bl) * MX6_BLOCK_BYTES + 16 * q);
+      uint32_t codes[18], scw;
+      mx6x3_split_lane(ve, vo, codes, scw);
+      if (16 * mb + srow < rows_w && sblk < nvalid) {
+        // bytes 16q .. 16q+15 of the block go to piece q of its group
+        uint8_t* dst = p.hq + (size_t)(row_base_w + 16 * mb + srow) * rowbytes;
+        const int blk = (col0 >> 5) + sblk;
+#pragma unroll
+        for (int q = 0; q < 5; ++q) {
+          const v4u piece = q < 4 ? (v4u){codes[4 * q], codes[4 * q + 1], codes[4 * q + 2], codes[4 * q + 3]}
+                                  : (v4u){codes[16], codes[17], scw, 0u};
+          *(v4u*)(dst + mx6_byte_offset(blk, 16 * q)) = piece;
+        }
+      }
     }
     lds_wave_sync();
   }
@@ -655,11 +662,11 @@ struct PfShared {
   uint8_t bs[2][PF_NT * 4];
 };
 // per-wave epilogue scratch: max of the down staging (16 x (128 + 4)
-// floats) and the gate/up staging (16 x (64 + 4) floats + 16 x 2 MX6x3
-// blocks); the weight buffers share the same bytes (the epilogue starts
-// after the loop's last barrier)
+// floats) and the gate/up staging (16 x (64 + 4) floats); the weight
+// buffers share the same bytes (the epilogue starts after the loop's last
+// barrier)
 constexpr int PF_EPI_BYTES = 16 * (16 * PF_NCB + 4) * 4;
-static_assert(PF_EPI_BYTES >= 16 * (8 * PF_NCB + 4) * 4 + 16 * (PF_NCB / 4) * MX6_BLOCK_BYTES, "gate/up staging fits");
+static_assert(PF_EPI_BYTES >= 16 * (8 * PF_NCB + 4) * 4, "gate/up staging fits");
 constexpr int PF_SMEM = (int)sizeof(PfShared) > PF_NW * PF_EPI_BYTES ? (int)sizeof(PfShared) : PF_NW * PF_EPI_BYTES;
 
 template <bool GATEUP>
@@ -917,7 +924,7 @@ constexpr int PW_B_COPIES = PW_B_BYTES / 1024 / PW_NW;  // 4 per wave
 constexpr int PW_S_COPIES = PW_NT * 2 / 64 / PW_NW;     // 2 per wave
 constexpr int PW_EPI_BYTES = 16 * (16 * PW_NCB + 4) * 4;
 static_assert(PW_A_COPIES == 5 && PW_B_COPIES == 4 && PW_S_COPIES == 2, "copy split");
-static_assert(PW_EPI_BYTES >= 16 * (8 * PW_NCB + 4) * 4 + 16 * (PW_NCB / 4) * MX6_BLOCK_BYTES, "gate/up staging fits");
+static_assert(PW_EPI_BYTES >= 16 * (8 * PW_NCB + 4) * 4, "gate/up staging fits");
 static_assert(PW_NW * PW_EPI_BYTES <= 2 * PW_BUF, "epilogue staging fits the operand buffers");
 
 template <bool GATEUP>

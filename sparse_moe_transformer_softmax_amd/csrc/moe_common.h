@@ -28,6 +28,9 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v32f __attribute__((ext_vector_type(32)));
+typedef unsigned int v6u __attribute__((ext_vector_type(6)));
 
 constexpr int MX6_BLOCK_BYTES = 80;
 constexpr int MX6_TERMS = 3;
@@ -178,6 +181,55 @@ __device__ __forceinline__ void mx6x3_split_quad(float (&v)[8], uint64_t (&bits)
       const uint32_t c = e2m3_round((v[i] * inv_hi) * inv_lo, q);
       v[i] -= (q * s_hi) * s_lo;  // exact residual
       bits[t] |= (uint64_t)c << (6 * i);
+    }
+  }
+}
+
+// One-lane form of mx6x3_split on the gfx950 scaled conversions: the lane
+// holds a whole 32-element block, even elements in ve and odd elements in vo
+// (the conversion packs source pair (ve[i], vo[i]) as elements 2i, 2i+1).
+// v_cvt_scalef32_2xpk16_fp6_f32 divides by the power-of-two scale and rounds
+// to nearest even, which for the non-saturating scale is exactly e2m3_round;
+// v_cvt_scalef32_pk32_f32_fp6 gives the rounded values back, so the residual
+// is exact.  Both are written as asm with early-clobber outputs: the
+// compiler's builtin lets the result registers overlap the sources, which
+// these instructions do not support.  On return codes[6t .. 6t+5] hold term
+// t's 32 codes packed little-endian (the MX6x3 byte layout), scw the three
+// scale bytes.  A block with a NaN gets scale 0xFF on every term.
+__device__ __forceinline__ void mx6x3_split_lane(v16f& ve, v16f& vo, uint32_t (&codes)[18], uint32_t& scw) {
+  scw = 0;
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    float amax = 0.0f;
+    bool nan = false;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      amax = fmaxf(amax, fmaxf(fabsf(ve[i]), fabsf(vo[i])));
+      nan |= (ve[i] != ve[i]) | (vo[i] != vo[i]);
+    }
+    if (nan) amax = __builtin_inff();
+    int se = mx6_scale_exp(amax);
+    // a subnormal maximum takes 2^-126 (one step coarser, still no
+    // saturation), so the scale operand is a normal float
+    se = se == 0 ? 1 : se;
+    scw |= (uint32_t)se << (8 * t);
+    if (se == 255) {
+#pragma unroll
+      for (int w = 0; w < 6; ++w) codes[6 * t + w] = 0;
+      continue;
+    }
+    const float scale = __uint_as_float((uint32_t)se << 23);
+    v6u c;
+    asm volatile("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(c) : "v"(ve), "v"(vo), "v"(scale));
+#pragma unroll
+    for (int w = 0; w < 6; ++w) codes[6 * t + w] = c[w];
+    if (t == 2) break;
+    v32f q;
+    asm volatile("v_cvt_scalef32_pk32_f32_fp6 %0, %1, %2" : "=&v"(q) : "v"(c), "v"(scale));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ve[i] -= q[2 * i];
+      vo[i] -= q[2 * i + 1];
     }
   }
 }
