@@ -1126,6 +1126,10 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
             "v"(bbase + s_lds[4 * jg + 2]), "v"(bbase + s_lds[4 * jg + 3]));
       const v4u bb[4] = {b0, b1, b2, b3};
       const uint32_t ss[4] = {t0, t1, t2, t3};
+      // raised priority while this wave issues its MFMAs, so that the
+      // other wave of the SIMD (reading LDS meanwhile) does not interleave
+      // and both keep the matrix pipe fed
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int j = 4 * jg + jj;
@@ -1139,6 +1143,7 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
             acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[mb][t], b, acc[mb][j], 2, 4, 0,
                                                                           as[mb][t], 0, bsc);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
   }
   __syncthreads();  // every wave is done with the operand buffers
