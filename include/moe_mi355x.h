@@ -19,8 +19,8 @@
  * Conventions shared by every entry point:
  *  - All array arguments are DEVICE pointers on the current HIP device,
  *    row-major and contiguous.  bf16 arrays are passed as raw 16-bit
- *    patterns.  x, router_w, out and the code arrays must be 16-byte
- *    aligned; fp32 arrays 4-byte aligned.
+ *    patterns.  x, router_w, out and the code and scale arrays must be
+ *    16-byte aligned; fp32 arrays 4-byte aligned.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is
  *    enqueued asynchronously; the library never synchronises the stream,
  *    so device faults surface at the caller's next synchronisation.

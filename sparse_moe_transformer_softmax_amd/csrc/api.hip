@@ -99,6 +99,7 @@ int check_layer(const LayerArgs& a, const void* out) {
   if (!a.x || !a.router_w || !a.router_b || !a.w13c || !a.w13s || !a.b13 || !a.w2c || !a.w2s || !a.b2)
     return MOE_ERR_NULL_PTR;
   if (!aligned(a.x, 16) || !aligned(a.router_w, 16) || !aligned(a.w13c, 16) || !aligned(a.w2c, 16) ||
+      !aligned(a.w13s, 16) || !aligned(a.w2s, 16) ||
       !aligned(a.router_b, 4) || !aligned(a.b13, 4) || !aligned(a.b2, 4))
     return MOE_ERR_MISALIGNED;
   if (out) {
