@@ -184,8 +184,7 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
               const uint16_t* resid_in = nullptr, uint16_t* resid_out = nullptr,
               uint16_t* norm_out = nullptr, float eps = 0.f) {
   const int P = a.T * a.k;
-  // (the decode GEMM holds a row's K in one pass of its steps)
-  const bool small_m = (long long)P <= 16LL * a.E && a.d <= 4096 && a.I <= 4096;
+  const bool small_m = (long long)P <= 16LL * a.E;
   // 128-row tiles when experts average at least 64 rows (measured faster
   // than 64-row tiles there even with half-filled tiles) and both
   // projections copy their scale bytes in pairs (K/32 even)

@@ -150,10 +150,13 @@ __device__ __forceinline__ uint32_t split_h_row(float h0, float h1, int r, uint8
 // weight stream.  Work items are (tile, 64-row weight span) pairs (gate/up:
 // 32 gate + the matching 32 up rows; down: 64 output rows), numbered
 // tile-major, one per workgroup; four workgroups share a CU, so one's
-// start and epilogue overlap the others' streams.  (A persistent variant
-// that walks several items and overlaps each epilogue with the next item's
-// first copies measured slower: it needs more registers per lane.)  An
-// item walks K in phases of DEC_KPH blocks.  Wave w
+// start and epilogue overlap the others' streams.  (Measured slower: a
+// persistent variant that walks several items and overlaps each epilogue
+// with the next item's first copies -- it needs more registers per lane --
+// and a variant that loads the codes straight into the MFMA operand
+// registers, each wave walking its own K steps with two in flight, about
+// 1.5 us per 20b gate/up launch.)  An item walks K in phases of DEC_KPH
+// blocks.  Wave w
 // copies the phase's code and scale segments of column block w (16
 // consecutive weight rows) from HBM straight to LDS with buffer_load ... lds
 // -- no register staging, and every instruction reads 1 KB of
@@ -291,71 +294,6 @@ __device__ __forceinline__ void dec_null_item(const GemmParams& p, DecItem& it) 
   it.bias[0] = it.bias[1] = it.bias[2] = it.bias[3] = 0.f;
 }
 
-// Epilogue of a decode item: wave w takes accumulator element w, i.e. tile
-// rows 4g + w, and sums the four waves' partials in a fixed order (s_acc:
-// 4 x 4 x 4 x 64 floats of LDS), adds the bias and writes y (down) or the
-// MX6x3 split of the clamped SwiGLU (gate/up; s_codes and s_sc are LDS
-// staging for the split).
-template <bool GATEUP>
-__device__ __forceinline__ void dec_epilogue(const GemmParams& p, const DecItem& it, const v4f (&acc)[1][4],
-                                             float* s_acc, uint8_t (*s_codes)[3][32], uint32_t* s_sc, int wave,
-                                             int lane) {
-  constexpr int NCB = 4, NW = DEC_NW;
-  const int g = lane >> 4, r = lane & 15;
-  const int N = p.N, I = p.I;
-#pragma unroll
-  for (int j = 0; j < NCB; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) s_acc[((wave * NCB + j) * 4 + q) * 64 + lane] = acc[0][j][q];
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the partials are in LDS
-  __builtin_amdgcn_s_barrier();
-  float v[NCB];
-#pragma unroll
-  for (int j = 0; j < NCB; ++j) {
-    float t = s_acc[((0 * NCB + j) * 4 + wave) * 64 + lane];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) t += s_acc[((w * NCB + j) * 4 + wave) * 64 + lane];
-    v[j] = t;
-  }
-  const int row = 4 * g + wave;  // tile row of this lane's values
-  const int col0 = it.col0, rows = it.rows, row_base = it.row_base;
-  if (!GATEUP) {
-#pragma unroll
-    for (int j = 0; j < NCB; ++j) {
-      if (!((it.ok_mask >> j) & 1)) continue;
-      const int col = col0 + 16 * j + r;
-      if (row < rows) p.y[(size_t)(row_base + row) * N + col] = v[j] + it.bias[j];
-    }
-    return;
-  }
-  // (columns past I are never stored)
-  const float h0 = clamped_swiglu(v[0] + it.bias[0], v[2] + it.bias[1], p.clamp);
-  const float h1 = clamped_swiglu(v[1] + it.bias[2], v[3] + it.bias[3], p.clamp);
-  const uint32_t scw = split_h_row(h0, h1, r, s_codes[row]);
-  if (r == 0) s_sc[row] = scw;
-  lds_wave_sync();
-  const int blk = col0 >> 5;
-  if (lane < 12) {
-    const int rw = 4 * (lane / 3) + wave, t = lane % 3;
-    if (rw < rows) {
-      uint32_t pk[6];
-      pack6x32(s_codes[rw][t], pk);
-      uint8_t* hrow = p.hq + (size_t)(row_base + rw) * mx6_row_bytes(I >> 5);
-      // 8-byte stores at multiples of 8 never straddle a 16-byte piece
-      *(uint2*)(hrow + mx6_byte_offset(blk, 24 * t)) = make_uint2(pk[0], pk[1]);
-      *(uint2*)(hrow + mx6_byte_offset(blk, 24 * t + 8)) = make_uint2(pk[2], pk[3]);
-      *(uint2*)(hrow + mx6_byte_offset(blk, 24 * t + 16)) = make_uint2(pk[4], pk[5]);
-    }
-  } else if (lane < 16) {
-    const int rw = 4 * (lane - 12) + wave;
-    if (rw < rows) {
-      uint8_t* hrow = p.hq + (size_t)(row_base + rw) * mx6_row_bytes(I >> 5);
-      *(uint2*)(hrow + mx6_byte_offset(blk, 72)) = make_uint2(s_sc[rw], 0u);
-    }
-  }
-  lds_wave_sync();
-}
-
 template <bool GATEUP, int NPH, bool U16>
 __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_gemm_decode(GemmParams p, int spans) {
   using Cfg = DecCfg<U16>;
@@ -487,6 +425,63 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
     asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]));
   };
 
+  // ---- epilogue of item `it`: wave w takes accumulator element w, i.e.
+  // tile rows 4g + w, and sums the four waves' partials in a fixed order.
+  // s_acc is the phase buffer consumed last (free until the next issue).
+  auto epilogue = [&](const DecItem& it, float* s_acc) {
+#pragma unroll
+    for (int j = 0; j < NCB; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s_acc[((wave * NCB + j) * 4 + q) * 64 + lane] = acc[0][j][q];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the partials are in LDS
+    __builtin_amdgcn_s_barrier();
+    float v[NCB];
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) {
+      float t = s_acc[((0 * NCB + j) * 4 + wave) * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) t += s_acc[((w * NCB + j) * 4 + wave) * 64 + lane];
+      v[j] = t;
+    }
+    const int row = 4 * g + wave;  // tile row of this lane's values
+    const int col0 = it.col0, rows = it.rows, row_base = it.row_base;
+    if (!GATEUP) {
+#pragma unroll
+      for (int j = 0; j < NCB; ++j) {
+        if (!((it.ok_mask >> j) & 1)) continue;
+        const int col = col0 + 16 * j + r;
+        if (row < rows) p.y[(size_t)(row_base + row) * N + col] = v[j] + it.bias[j];
+      }
+      return;
+    }
+    // (columns past I are never stored)
+    const float h0 = clamped_swiglu(v[0] + it.bias[0], v[2] + it.bias[1], p.clamp);
+    const float h1 = clamped_swiglu(v[1] + it.bias[2], v[3] + it.bias[3], p.clamp);
+    const uint32_t scw = split_h_row(h0, h1, r, s_codes[row]);
+    if (r == 0) s_sc[row] = scw;
+    lds_wave_sync();
+    const int blk = col0 >> 5;
+    if (lane < 12) {
+      const int rw = 4 * (lane / 3) + wave, t = lane % 3;
+      if (rw < rows) {
+        uint32_t pk[6];
+        pack6x32(s_codes[rw][t], pk);
+        uint8_t* hrow = p.hq + (size_t)(row_base + rw) * mx6_row_bytes(I >> 5);
+        // 8-byte stores at multiples of 8 never straddle a 16-byte piece
+        *(uint2*)(hrow + mx6_byte_offset(blk, 24 * t)) = make_uint2(pk[0], pk[1]);
+        *(uint2*)(hrow + mx6_byte_offset(blk, 24 * t + 8)) = make_uint2(pk[2], pk[3]);
+        *(uint2*)(hrow + mx6_byte_offset(blk, 24 * t + 16)) = make_uint2(pk[4], pk[5]);
+      }
+    } else if (lane < 16) {
+      const int rw = 4 * (lane - 12) + wave;
+      if (rw < rows) {
+        uint8_t* hrow = p.hq + (size_t)(row_base + rw) * mx6_row_bytes(I >> 5);
+        *(uint2*)(hrow + mx6_byte_offset(blk, 72)) = make_uint2(s_sc[rw], 0u);
+      }
+    }
+    lds_wave_sync();
+  };
+
   // The phase loop.  Each step: issue the copies of the next phase (past the
   // last phase, of the null item, so that every step has the same shape),
   // wait for this wave's copies of the current phase (vmcnt counts in issue
@@ -539,208 +534,7 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
     }
   }
   wait_vmcnt<0>();  // the null item's copies
-  dec_epilogue<GATEUP>(p, cur, acc, (float*)s_code[(nph - 1) & 1], s_codes, s_sc, wave, lane);
-}
-
-// Register-streamed decode kernel.  Same work items and epilogue as the
-// kernel above, but the weight codes go from HBM straight into the MFMA
-// operand registers: lane (r, g) loads the 16 code bytes of K block 4c + g
-// of weight row r of each of the item's four column blocks (the 16 lanes of
-// a block group read 16 rows, 64 consecutive bytes per row and
-// instruction).  Wave w takes the 128-wide K steps c = w, w + 4, ..., so
-// each wave consumes the codes it loaded itself, DR_PD steps of loads in
-// flight (codes and the step's A block), ring-indexed at compile time (the
-// loop over a wave's NST steps is unrolled, so the compiler counts the
-// loads of later steps that may stay in flight at each use).  The item's
-// scale bytes (64 rows x K/32, contiguous per column block) are copied to
-// LDS once with 16-byte buffer_load ... lds (two per wave; per-lane 2-byte
-// loads of the scales cost as many cache-line lookups as the codes), and
-// published with the one barrier before the K loop.  Steps past K are
-// issued as loads beyond their resources (zeros, no memory traffic), so
-// every wave's pipeline has the same shape.  K is at most DR_MAX_K (one
-// pass over the steps; larger K takes the prefill kernel).
-constexpr int DR_MAX_NST = 8;                        // steps per wave
-constexpr int DR_MAX_K = 128 * DEC_NW * DR_MAX_NST;  // 4096
-constexpr int DR_SCL_BYTES = 2 * DEC_NW * 1024;      // scale copies: two 1 KB instructions per wave
-static_assert(64 * (DR_MAX_K / 32) <= DR_SCL_BYTES, "an item's scale bytes fit the copy");
-template <int PD>
-struct DrCfg {
-  static constexpr int WG_PER_CU = PD <= 2 ? 4 : PD == 3 ? 3 : 2;
-};
-
-struct DrStep {
-  v4u bc[4];        // codes of K block 4c + g of row r of each column block
-  v4u a[4];         // pieces 0..3 of the lane's MX6x3 A block
-  uint32_t a4[3];   // piece 4: last term's codes and the three scale bytes
-};
-
-template <bool GATEUP, int NST, int PD>
-__global__ __launch_bounds__(DEC_NW * 64, DrCfg<PD>::WG_PER_CU) void expert_gemm_decode_reg(GemmParams p, int spans) {
-  constexpr int NCB = 4, NW = DEC_NW;
-  constexpr int PRE = PD < NST ? PD : NST;  // steps issued before the loop
-  constexpr uint32_t OOB = 0x80000000u;     // past every resource used here
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int K = p.K, N = p.N, I = p.I, nblk = K >> 5;
-  const int nsteps = (nblk + 3) >> 2;
-  const int g = lane >> 4, r = lane & 15;
-
-  __shared__ __align__(16) uint8_t s_scl[DR_SCL_BYTES];
-  __shared__ float s_acc[NW * NCB * 4 * 64];
-  __shared__ uint8_t s_codes[16][3][32];
-  __shared__ uint32_t s_sc[16];
-
-  // ---- the item: the tile count and the tile's entry are read together
-  // (the grid covers the largest tile count, so the entry lies inside the
-  // tile list even past the count); tile list, counts, offsets and row
-  // lists are read as constant memory ----
-  const int item = blockIdx.x;
-  const int tile = item / spans, span = item - tile * spans;
-  cint_t* te = (cint_t*)p.tiles + 2 * (size_t)tile;
-  const int n_tiles = *(cint_t*)p.n_tiles;
-  const int e = te[0], m0 = te[1];
-  // (the test takes both values, so both loads are in flight together)
-  if (item >= n_tiles * spans || (e | m0) < 0) return;
-  DecItem it;
-  it.e = e;
-  int ok = 0;
-  if (GATEUP) {
-    it.col0 = span * 32;
-    ok = (it.col0 < I ? 0x5 : 0) | (it.col0 + 16 < I ? 0xA : 0);
-  } else {
-    it.col0 = span * 64;
-#pragma unroll
-    for (int j = 0; j < NCB; ++j) ok |= (it.col0 + 16 * j < N) ? (1 << j) : 0;
-  }
-  it.ok_mask = ok;
-  // first weight row (within the expert) of column block j; a block past
-  // the output streams block 0's rows again (never stored)
-  uint32_t row_j[NCB];
-#pragma unroll
-  for (int j = 0; j < NCB; ++j) {
-    const int jj = ((ok >> j) & 1) ? j : 0;
-    row_j[j] = (uint32_t)(GATEUP ? (jj < 2 ? 0 : I) + it.col0 + 16 * (jj & 1) : it.col0 + 16 * jj);
-  }
-  const uint32_t rowb = (uint32_t)(K >> 1);
-  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.b_codes + (size_t)e * N * rowb), 0, (int)((uint32_t)N * rowb), 0x00020000);
-  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.b_scales + (size_t)e * N * nblk), 0, (int)((uint32_t)N * (uint32_t)nblk), 0x00020000);
-  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc((void*)p.a, 0, 0x7ffffff0, 0x00020000);
-
-  // ---- loads of step s into d: the weight codes, then the A block ----
-  auto issue_b = [&](int s, DrStep& d) {
-    const int c = NW * s + wave;  // uniform
-    const uint32_t cv = c < nsteps ? (uint32_t)r * rowb + 16u * (uint32_t)min(4 * c + g, nblk - 1) : OOB;
-#pragma unroll
-    for (int j = 0; j < NCB; ++j)
-      d.bc[j] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(crs, cv, row_j[j] * rowb, 0));
-  };
-  uint32_t a_row_off = 0;
-  bool a_live = false;
-  auto issue_a = [&](int s, DrStep& d) {
-    const int c = NW * s + wave;
-    const bool valid = c < nsteps;
-    // A block 4c + g of the lane's row (blocks past K re-read the row's
-    // last block; their products are masked off)
-    const uint32_t ag = (uint32_t)min(g, nblk - 1 - 4 * c);
-    const uint32_t av = (valid && a_live) ? a_row_off + 16u * ag : OOB;
-    const uint32_t aso = (uint32_t)(valid ? c : 0) * MX6_GROUP_BYTES;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      d.a[q] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(ars, av + 64u * q, aso, 0));
-    const auto t3 = __builtin_amdgcn_raw_buffer_load_b96(ars, av + 256u, aso, 0);
-    d.a4[0] = t3[0];
-    d.a4[1] = t3[1];
-    d.a4[2] = t3[2];
-  };
-
-  // the first steps' codes go out as soon as the expert is known
-  DrStep ring[PD];
-  StaticFor<0, PRE>::run([&](auto sc) { issue_b(decltype(sc)::value, ring[decltype(sc)::value]); });
-
-  // the item's scale bytes: byte (16 j + rr) * nblk + b of the copy is
-  // block b of row rr of column block j (contiguous in memory per block)
-  {
-    const uint32_t seg = 16u * (uint32_t)nblk;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int slot = 2 * wave + k;
-      const uint32_t b = 1024u * (uint32_t)slot + 16u * (uint32_t)lane;
-      const uint32_t j = b / seg, o = b - j * seg;
-      const uint32_t rj = j == 0 ? row_j[0] : j == 1 ? row_j[1] : j == 2 ? row_j[2] : row_j[3];
-      lds_copy16(srs, (lds_void_t*)(s_scl + 1024 * slot), b < 4u * seg ? rj * (uint32_t)nblk + o : OOB);
-    }
-  }
-
-  // ---- rows of the tile: count, offset, row list; bias ----
-  it.rows = min(16, ((cint_t*)p.counts)[e] - m0);
-  it.row_base = ((cint_t*)p.offsets)[e] + m0;
-  int arow = it.row_base + r;
-  if (GATEUP) {
-    // entries past the expert's T read on into the next expert's list or
-    // the workspace region after the lists; they are never used
-    cint_t* erow = (cint_t*)p.expert_rows + (size_t)e * p.T + m0;
-    int v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = erow[i];
-    int x = v[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) x = r == i ? v[i] : x;
-    arow = x / p.k;
-  }
-  a_live = r < it.rows;
-  a_row_off = a_live ? (uint32_t)arow * (uint32_t)mx6_row_bytes(nblk) : 0u;
-  StaticFor<0, PRE>::run([&](auto sc) { issue_a(decltype(sc)::value, ring[decltype(sc)::value]); });
-  {
-    const float* bias = p.bias + (size_t)e * N;
-    if (GATEUP) {
-      const int c0 = min(it.col0 + r, I - 1), c1 = min(it.col0 + 16 + r, I - 1);
-      it.bias[0] = bias[c0];
-      it.bias[1] = bias[I + c0];
-      it.bias[2] = bias[c1];
-      it.bias[3] = bias[I + c1];
-    } else {
-#pragma unroll
-      for (int j = 0; j < NCB; ++j) it.bias[j] = bias[min(it.col0 + 16 * j + r, N - 1)];
-    }
-  }
-  // every load issued so far has landed (the scale copies among them; the
-  // first steps are needed next anyway); the barrier publishes the scales
-  wait_vmcnt<0>();
-  __builtin_amdgcn_s_barrier();
-
-  v4f acc[1][NCB];
-#pragma unroll
-  for (int j = 0; j < NCB; ++j) acc[0][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-  const uint8_t* s_row = s_scl + r * nblk + g;  // + (16 j) * nblk + 4 c
-  auto consume = [&](int s, const DrStep& d) {
-    const int c = NW * s + wave;
-    Stage<1, NCB> st;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) st.a[0][q] = make_uint4(d.a[q].x, d.a[q].y, d.a[q].z, d.a[q].w);
-    st.a[0][4] = make_uint4(d.a4[0], d.a4[1], d.a4[2], 0u);
-#pragma unroll
-    for (int j = 0; j < NCB; ++j) {
-      st.bc[j] = make_uint4(d.bc[j].x, d.bc[j].y, d.bc[j].z, d.bc[j].w);
-      st.bs[j] = s_row[16 * j * nblk + 4 * c];
-    }
-    mma_stage(acc, st, keep_mask<1, NCB>(c < nsteps && 4 * c + g < nblk));
-    // pin the MFMAs to this step (otherwise they may sink to the epilogue,
-    // holding every step's operands)
-    asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]));
-  };
-
-  StaticFor<0, NST>::run([&](auto sc) {
-    constexpr int s = decltype(sc)::value;
-    __builtin_amdgcn_sched_barrier(0);
-    consume(s, ring[s % PD]);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (s + PD < NST) {
-      issue_b(s + PD, ring[s % PD]);
-      issue_a(s + PD, ring[s % PD]);
-    }
-  });
-  dec_epilogue<GATEUP>(p, it, acc, s_acc, s_codes, s_sc, wave, lane);
+  epilogue(cur, (float*)s_code[(nph - 1) & 1]);
 }
 
 // Prefill kernel: tiles of PF_MT = 64 rows x 256 output columns (gate/up:
@@ -1396,38 +1190,12 @@ static void launch_decode_u(const GemmParams& p, unsigned grid, int spans, hipSt
   }
 }
 
-// Register-streamed decode kernel instance: NST steps per wave (K of up to
-// 4 NST steps), DR_PD steps in flight.
-#ifndef DR_PD
-#define DR_PD 2
-#endif
-template <bool GATEUP>
-static void launch_decode_reg(const GemmParams& p, unsigned grid, int spans, hipStream_t s) {
-  const int nsteps = (p.K / 32 + 3) / 4;
-  const int nst = (nsteps + DEC_NW - 1) / DEC_NW;
-  const dim3 g(grid), b(DEC_NW * 64);
-  switch (nst) {
-    case 1: hipLaunchKernelGGL((expert_gemm_decode_reg<GATEUP, 1, DR_PD>), g, b, 0, s, p, spans); break;
-    case 2: hipLaunchKernelGGL((expert_gemm_decode_reg<GATEUP, 2, DR_PD>), g, b, 0, s, p, spans); break;
-    case 3: hipLaunchKernelGGL((expert_gemm_decode_reg<GATEUP, 3, DR_PD>), g, b, 0, s, p, spans); break;
-    case 4: hipLaunchKernelGGL((expert_gemm_decode_reg<GATEUP, 4, DR_PD>), g, b, 0, s, p, spans); break;
-    case 5: hipLaunchKernelGGL((expert_gemm_decode_reg<GATEUP, 5, DR_PD>), g, b, 0, s, p, spans); break;
-    case 6: hipLaunchKernelGGL((expert_gemm_decode_reg<GATEUP, 6, DR_PD>), g, b, 0, s, p, spans); break;
-    case 7: hipLaunchKernelGGL((expert_gemm_decode_reg<GATEUP, 7, DR_PD>), g, b, 0, s, p, spans); break;
-    default: hipLaunchKernelGGL((expert_gemm_decode_reg<GATEUP, 8, DR_PD>), g, b, 0, s, p, spans); break;
-  }
-}
-
 template <bool GATEUP>
 static void launch_decode(const GemmParams& p, unsigned items, int spans, hipStream_t s) {
-#ifdef DECODE_LDS
   if ((p.K / 32) % 2 == 0)
     launch_decode_u<GATEUP, true>(p, items, spans, s);
   else
     launch_decode_u<GATEUP, false>(p, items, spans, s);
-#else
-  launch_decode_reg<GATEUP>(p, items, spans, s);
-#endif
 }
 
 // Launch configurations.
@@ -1439,7 +1207,6 @@ static void launch_decode(const GemmParams& p, unsigned items, int spans, hipStr
 //     projections): one workgroup per (128-row tile, 512-column span).
 int launch_gemm_gateup(const GemmParams& p, int max_tiles, int mode, hipStream_t s) {
   if (mode == GEMM_DECODE) {
-    if (p.K > DR_MAX_K) return -1;
     const int spans = (p.I + 31) / 32;
     launch_decode<true>(p, (unsigned)((long long)max_tiles * spans), spans, s);
   } else {
@@ -1458,7 +1225,6 @@ int launch_gemm_gateup(const GemmParams& p, int max_tiles, int mode, hipStream_t
 
 int launch_gemm_down(const GemmParams& p, int max_tiles, int mode, hipStream_t s) {
   if (mode == GEMM_DECODE) {
-    if (p.K > DR_MAX_K) return -1;
     const int spans = (p.N + 63) / 64;
     launch_decode<false>(p, (unsigned)((long long)max_tiles * spans), spans, s);
   } else {
