@@ -993,7 +993,10 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
   constexpr uint32_t A_OOB = 0x7ffffff0u;  // at or past the A resource's end (it is below 2^31 bytes)
   // A copy k of this wave fills LDS slots u = (5 wave + k) * 64 + lane:
   // tile row u / 20, slot u % 20 holding piece (u % 20) ^ ((row >> 1) & 3)
+  // (pieces of blocks past K are copied from past the resource: zeros, so
+  // that those K positions contribute nothing whatever the weights hold)
   uint32_t a_src[PW_A_COPIES];
+  int a_blk[PW_A_COPIES];  // block of the piece within its group of four
 #pragma unroll
   for (int k = 0; k < PW_A_COPIES; ++k) {
     const int u = (PW_A_COPIES * wave + k) * 64 + lane;
@@ -1006,6 +1009,7 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
       off = arow * a_rowbytes + (uint32_t)piece * 16u;
     }
     a_src[k] = off;
+    a_blk[k] = piece & 3;
   }
   // B copy k fills slots u = (4 wave + k) * 64 + lane: tile row u / 4,
   // slot u % 4 holding block (u % 4) ^ ((n >> 2) & 3) of the chunk
@@ -1033,7 +1037,7 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
 #pragma unroll
     for (int k = 0; k < PW_A_COPIES; ++k)
       lds_copy16(arsrc, (lds_void_t*)(base + (PW_A_COPIES * wave + k) * 1024),
-                 a_src[k] == A_OOB ? A_OOB : a_src[k] + (uint32_t)c * MX6_GROUP_BYTES);
+                 (a_src[k] == A_OOB || 4 * c + a_blk[k] >= nblk) ? A_OOB : a_src[k] + (uint32_t)c * MX6_GROUP_BYTES);
 #pragma unroll
     for (int k = 0; k < PW_B_COPIES; ++k)
       lds_copy16(crsrc, (lds_void_t*)(base + PW_A_BYTES + (PW_B_COPIES * wave + k) * 1024),
@@ -1051,22 +1055,21 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
 #pragma unroll
     for (int j = 0; j < NCB; ++j) acc[mb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  // LDS byte addresses of this lane's fragments inside a chunk buffer
-  uint32_t a_lds[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int m = 32 * wm + 16 * mb + r;
-    a_lds[mb] = (uint32_t)(m * MX6_GROUP_BYTES);  // piece s at slot s ^ ((m >> 1) & 3)
-  }
-  const int a_sw = ((32 * wm + r) >> 1) & 3;  // the same for both row blocks (16 rows apart)
-  uint32_t b_lds[NCB], s_lds[NCB];
-#pragma unroll
-  for (int j = 0; j < NCB; ++j) {
-    const int n = tile_row(j) + r;
-    b_lds[j] = (uint32_t)(PW_A_BYTES + n * 64 + ((g ^ ((n >> 2) & 3)) * 16));
-    s_lds[j] = (uint32_t)(PW_A_BYTES + PW_B_BYTES + (2 * n + (g >> 1)) * 4);
-  }
-  const int s_shift = 8 * (g & 1);
+  // LDS byte offsets of this lane's fragments inside a chunk buffer: a lane
+  // part here, the row block / piece / column block part as the
+  // instructions' offset fields.  A: row m = 32 wm + 16 mb + r, piece
+  // 4q + g at slot (4q + g) ^ ((m >> 1) & 3) (the same for both row
+  // blocks); B: row n = tile_row(j) + r, whose swizzle (n >> 2) & 3 is
+  // (r >> 2) & 3; scales: byte g & 1 of dword 2n + g / 2.
+  constexpr int WNR = GATEUP ? 8 * NCB : 16 * NCB;  // tile rows per column half
+  const uint32_t a_lane = (uint32_t)((32 * wm + r) * MX6_GROUP_BYTES + 16 * (g ^ ((r >> 1) & 3)));
+  const uint32_t b_lane = (uint32_t)(PW_A_BYTES + (wn * WNR + r) * 64 + 16 * (g ^ ((r >> 2) & 3)));
+  const uint32_t s_lane = (uint32_t)(PW_A_BYTES + PW_B_BYTES + 8 * (wn * WNR + r) + 4 * (g >> 1) + (g & 1));
+  // tile row of column block j without the column half's part
+  auto jrow = [](auto jc) constexpr {
+    constexpr int j = decltype(jc)::value;
+    return GATEUP ? (j < NCB / 2 ? 0 : PW_NT / 2) + 16 * (j % (NCB / 2)) : 16 * j;
+  };
 
   const int nchunk = (nblk + 3) >> 2;
   issue(0, 0);
@@ -1078,57 +1081,59 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
     __builtin_amdgcn_sched_barrier(0);
     if (c + 1 < nchunk) issue(c + 1, buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
-    const uint32_t keep = (4 * c + g) < nblk ? 0xffffffffu : 0u;
-    // A fragments: pieces 0..4 of block g of the lane's row in each row block
+    // A fragments: pieces 0..4 of block g of the lane's row in each row
+    // block (zeros past K)
     v8i a[MB][3];
     int as[MB][3];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    const uint32_t ab = bbase + a_lane;
+    StaticFor<0, MB>::run([&](auto mc) {
+      constexpr int mb = decltype(mc)::value;
       v4u w0, w1, w2, w3, w4;
-      const uint32_t ab = bbase + a_lds[mb];
-      const uint32_t o0 = ((0 * 4 + g) ^ a_sw) * 16, o1 = ((1 * 4 + g) ^ a_sw) * 16, o2 = ((2 * 4 + g) ^ a_sw) * 16,
-                     o3 = ((3 * 4 + g) ^ a_sw) * 16, o4 = ((4 * 4 + g) ^ a_sw) * 16;
       asm volatile(
-          "ds_read_b128 %0, %5\n\t"
-          "ds_read_b128 %1, %6\n\t"
-          "ds_read_b128 %2, %7\n\t"
-          "ds_read_b128 %3, %8\n\t"
-          "ds_read_b128 %4, %9\n\t"
+          "ds_read_b128 %0, %5 offset:%6\n\t"
+          "ds_read_b128 %1, %5 offset:%7\n\t"
+          "ds_read_b128 %2, %5 offset:%8\n\t"
+          "ds_read_b128 %3, %5 offset:%9\n\t"
+          "ds_read_b128 %4, %5 offset:%10\n\t"
           "s_waitcnt lgkmcnt(0)"
           : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3), "=&v"(w4)
-          : "v"(ab + o0), "v"(ab + o1), "v"(ab + o2), "v"(ab + o3), "v"(ab + o4));
+          : "v"(ab), "i"(16 * MX6_GROUP_BYTES * mb), "i"(16 * MX6_GROUP_BYTES * mb + 64),
+            "i"(16 * MX6_GROUP_BYTES * mb + 128), "i"(16 * MX6_GROUP_BYTES * mb + 192),
+            "i"(16 * MX6_GROUP_BYTES * mb + 256));
       const uint32_t w[20] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w, w2.x, w2.y,
                               w2.z, w2.w, w3.x, w3.y, w3.z, w3.w, w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
-        a[mb][t] = (v8i){(int)(w[6 * t] & keep), (int)(w[6 * t + 1] & keep), (int)(w[6 * t + 2] & keep),
-                         (int)(w[6 * t + 3] & keep), (int)(w[6 * t + 4] & keep), (int)(w[6 * t + 5] & keep), 0, 0};
-        as[mb][t] = (int)((((w[18] & keep) >> (8 * t)) & 0xffu) | (127u & ~keep));
+        a[mb][t] = (v8i){(int)w[6 * t], (int)w[6 * t + 1], (int)w[6 * t + 2],
+                         (int)w[6 * t + 3], (int)w[6 * t + 4], (int)w[6 * t + 5], 0, 0};
+        as[mb][t] = (int)((w[18] >> (8 * t)) & 0xffu);
       }
-    }
+    });
     // B fragments in groups of four column blocks (one asm block each),
     // then their 24 MFMAs; the two row blocks alternate, so consecutive
     // MFMAs never depend on each other
-#pragma unroll
-    for (int jg = 0; jg < NCB / 4; ++jg) {
+    const uint32_t bb = bbase + b_lane, sb = bbase + s_lane;
+    StaticFor<0, NCB / 4>::run([&](auto gc) {
+      constexpr int jg = decltype(gc)::value;
+      constexpr int j0 = jrow(std::integral_constant<int, 4 * jg>{}), j1 = jrow(std::integral_constant<int, 4 * jg + 1>{}),
+                    j2 = jrow(std::integral_constant<int, 4 * jg + 2>{}), j3 = jrow(std::integral_constant<int, 4 * jg + 3>{});
       v4u b0, b1, b2, b3;
       uint32_t t0, t1, t2, t3;
       asm volatile(
-          "ds_read_b128 %0, %8\n\t"
-          "ds_read_b128 %1, %9\n\t"
-          "ds_read_b128 %2, %10\n\t"
-          "ds_read_b128 %3, %11\n\t"
-          "ds_read_b32 %4, %12\n\t"
-          "ds_read_b32 %5, %13\n\t"
-          "ds_read_b32 %6, %14\n\t"
-          "ds_read_b32 %7, %15\n\t"
+          "ds_read_b128 %0, %8 offset:%10\n\t"
+          "ds_read_b128 %1, %8 offset:%11\n\t"
+          "ds_read_b128 %2, %8 offset:%12\n\t"
+          "ds_read_b128 %3, %8 offset:%13\n\t"
+          "ds_read_u8 %4, %9 offset:%14\n\t"
+          "ds_read_u8 %5, %9 offset:%15\n\t"
+          "ds_read_u8 %6, %9 offset:%16\n\t"
+          "ds_read_u8 %7, %9 offset:%17\n\t"
           "s_waitcnt lgkmcnt(0)"
           : "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
-          : "v"(bbase + b_lds[4 * jg]), "v"(bbase + b_lds[4 * jg + 1]), "v"(bbase + b_lds[4 * jg + 2]),
-            "v"(bbase + b_lds[4 * jg + 3]), "v"(bbase + s_lds[4 * jg]), "v"(bbase + s_lds[4 * jg + 1]),
-            "v"(bbase + s_lds[4 * jg + 2]), "v"(bbase + s_lds[4 * jg + 3]));
-      const v4u bb[4] = {b0, b1, b2, b3};
-      const uint32_t ss[4] = {t0, t1, t2, t3};
+          : "v"(bb), "v"(sb), "i"(64 * j0), "i"(64 * j1), "i"(64 * j2), "i"(64 * j3), "i"(8 * j0), "i"(8 * j1),
+            "i"(8 * j2), "i"(8 * j3));
+      const v4u bq[4] = {b0, b1, b2, b3};
+      const uint32_t sq[4] = {t0, t1, t2, t3};
       // raised priority while this wave issues its MFMAs, so that the
       // other wave of the SIMD (reading LDS meanwhile) does not interleave
       // and both keep the matrix pipe fed
@@ -1136,18 +1141,16 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int j = 4 * jg + jj;
-        const v8i b = {(int)(bb[jj].x & keep), (int)(bb[jj].y & keep), (int)(bb[jj].z & keep),
-                       (int)(bb[jj].w & keep), 0, 0, 0, 0};
-        const int bsc = (int)(((ss[jj] >> s_shift) & 0xffu & keep) | (127u & ~keep));
+        const v8i b = {(int)bq[jj].x, (int)bq[jj].y, (int)bq[jj].z, (int)bq[jj].w, 0, 0, 0, 0};
 #pragma unroll
         for (int t = 0; t < 3; ++t)
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
             acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[mb][t], b, acc[mb][j], 2, 4, 0,
-                                                                          as[mb][t], 0, bsc);
+                                                                          as[mb][t], 0, (int)sq[jj]);
       }
       __builtin_amdgcn_s_setprio(0);
-    }
+    });
   }
   __syncthreads();  // every wave is done with the operand buffers
 
