@@ -1081,77 +1081,154 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
     __builtin_amdgcn_sched_barrier(0);
     if (c + 1 < nchunk) issue(c + 1, buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
-    // A fragments: pieces 0..4 of block g of the lane's row in each row
-    // block (zeros past K)
-    v8i a[MB][3];
-    int as[MB][3];
-    const uint32_t ab = bbase + a_lane;
-    StaticFor<0, MB>::run([&](auto mc) {
-      constexpr int mb = decltype(mc)::value;
-      v4u w0, w1, w2, w3, w4;
-      asm volatile(
-          "ds_read_b128 %0, %5 offset:%6\n\t"
-          "ds_read_b128 %1, %5 offset:%7\n\t"
-          "ds_read_b128 %2, %5 offset:%8\n\t"
-          "ds_read_b128 %3, %5 offset:%9\n\t"
-          "ds_read_b128 %4, %5 offset:%10\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3), "=&v"(w4)
-          : "v"(ab), "i"(16 * MX6_GROUP_BYTES * mb), "i"(16 * MX6_GROUP_BYTES * mb + 64),
-            "i"(16 * MX6_GROUP_BYTES * mb + 128), "i"(16 * MX6_GROUP_BYTES * mb + 192),
-            "i"(16 * MX6_GROUP_BYTES * mb + 256));
-      const uint32_t w[20] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w, w2.x, w2.y,
-                              w2.z, w2.w, w3.x, w3.y, w3.z, w3.w, w4.x, w4.y, w4.z, w4.w};
+    // A fragments (pieces 0..4 of block g of the lane's row in each row
+    // block, zeros past K) and the first group's B fragments, then the
+    // three FP6 terms of A as 6-register operands
+    const uint32_t ab = bbase + a_lane, bb = bbase + b_lane, sb = bbase + s_lane;
+    v4u w[MB][5];
+    v4u bq[2][4];
+    uint32_t sq[2][4];
+    asm volatile(
+        "ds_read_b128 %0, %18 offset:%21\n\t"
+        "ds_read_b128 %1, %18 offset:%22\n\t"
+        "ds_read_b128 %2, %18 offset:%23\n\t"
+        "ds_read_b128 %3, %18 offset:%24\n\t"
+        "ds_read_b128 %4, %18 offset:%25\n\t"
+        "ds_read_b128 %5, %18 offset:%26\n\t"
+        "ds_read_b128 %6, %18 offset:%27\n\t"
+        "ds_read_b128 %7, %18 offset:%28\n\t"
+        "ds_read_b128 %8, %18 offset:%29\n\t"
+        "ds_read_b128 %9, %18 offset:%30\n\t"
+        "ds_read_b128 %10, %19 offset:%31\n\t"
+        "ds_read_b128 %11, %19 offset:%32\n\t"
+        "ds_read_b128 %12, %19 offset:%33\n\t"
+        "ds_read_b128 %13, %19 offset:%34\n\t"
+        "ds_read_u8 %14, %20 offset:%35\n\t"
+        "ds_read_u8 %15, %20 offset:%36\n\t"
+        "ds_read_u8 %16, %20 offset:%37\n\t"
+        "ds_read_u8 %17, %20 offset:%38\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0][0]), "=&v"(w[0][1]), "=&v"(w[0][2]), "=&v"(w[0][3]), "=&v"(w[0][4]), "=&v"(w[1][0]),
+          "=&v"(w[1][1]), "=&v"(w[1][2]), "=&v"(w[1][3]), "=&v"(w[1][4]), "=&v"(bq[0][0]), "=&v"(bq[0][1]),
+          "=&v"(bq[0][2]), "=&v"(bq[0][3]), "=&v"(sq[0][0]), "=&v"(sq[0][1]), "=&v"(sq[0][2]), "=&v"(sq[0][3])
+        : "v"(ab), "v"(bb), "v"(sb), "i"(0), "i"(64), "i"(128), "i"(192), "i"(256),
+          "i"(16 * MX6_GROUP_BYTES), "i"(16 * MX6_GROUP_BYTES + 64), "i"(16 * MX6_GROUP_BYTES + 128),
+          "i"(16 * MX6_GROUP_BYTES + 192), "i"(16 * MX6_GROUP_BYTES + 256),
+          "i"(64 * jrow(std::integral_constant<int, 0>{})), "i"(64 * jrow(std::integral_constant<int, 1>{})),
+          "i"(64 * jrow(std::integral_constant<int, 2>{})), "i"(64 * jrow(std::integral_constant<int, 3>{})),
+          "i"(8 * jrow(std::integral_constant<int, 0>{})), "i"(8 * jrow(std::integral_constant<int, 1>{})),
+          "i"(8 * jrow(std::integral_constant<int, 2>{})), "i"(8 * jrow(std::integral_constant<int, 3>{})));
+    v6u a6[MB][3];
+    uint32_t as[MB][3];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const uint32_t* x = (const uint32_t*)&w[mb][0];
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
-        a[mb][t] = (v8i){(int)w[6 * t], (int)w[6 * t + 1], (int)w[6 * t + 2],
-                         (int)w[6 * t + 3], (int)w[6 * t + 4], (int)w[6 * t + 5], 0, 0};
-        as[mb][t] = (int)((w[18] >> (8 * t)) & 0xffu);
+        a6[mb][t] = (v6u){x[6 * t], x[6 * t + 1], x[6 * t + 2], x[6 * t + 3], x[6 * t + 4], x[6 * t + 5]};
+        as[mb][t] = (x[18] >> (8 * t)) & 0xffu;
       }
-    });
-    // B fragments in groups of four column blocks (one asm block each),
-    // then their 24 MFMAs; the two row blocks alternate, so consecutive
-    // MFMAs never depend on each other
-    const uint32_t bb = bbase + b_lane, sb = bbase + s_lane;
+    }
+    // column-block groups of four: each asm block reads the next group's B
+    // fragments while it issues this group's 24 MFMAs (term-major, so an
+    // accumulator's three updates are eight MFMAs apart), then waits for
+    // the reads.  s_nop: wait states for operands written just before by
+    // VALU instructions.  Raised priority while the MFMAs issue, so that the
+    // other wave of the SIMD (reading LDS meanwhile) does not interleave.
     StaticFor<0, NCB / 4>::run([&](auto gc) {
       constexpr int jg = decltype(gc)::value;
-      constexpr int j0 = jrow(std::integral_constant<int, 4 * jg>{}), j1 = jrow(std::integral_constant<int, 4 * jg + 1>{}),
-                    j2 = jrow(std::integral_constant<int, 4 * jg + 2>{}), j3 = jrow(std::integral_constant<int, 4 * jg + 3>{});
-      v4u b0, b1, b2, b3;
-      uint32_t t0, t1, t2, t3;
-      asm volatile(
-          "ds_read_b128 %0, %8 offset:%10\n\t"
-          "ds_read_b128 %1, %8 offset:%11\n\t"
-          "ds_read_b128 %2, %8 offset:%12\n\t"
-          "ds_read_b128 %3, %8 offset:%13\n\t"
-          "ds_read_u8 %4, %9 offset:%14\n\t"
-          "ds_read_u8 %5, %9 offset:%15\n\t"
-          "ds_read_u8 %6, %9 offset:%16\n\t"
-          "ds_read_u8 %7, %9 offset:%17\n\t"
+      constexpr int cur = jg & 1, nxt = cur ^ 1;
+      if constexpr (jg + 1 < NCB / 4) {
+        constexpr int k0 = 4 * (jg + 1);
+        asm volatile(
+          "s_nop 4\n\t"
+          "ds_read_b128 %8, %36 offset:%38\n\t"
+          "ds_read_b128 %9, %36 offset:%39\n\t"
+          "ds_read_b128 %10, %36 offset:%40\n\t"
+          "ds_read_b128 %11, %36 offset:%41\n\t"
+          "ds_read_u8 %12, %37 offset:%42\n\t"
+          "ds_read_u8 %13, %37 offset:%43\n\t"
+          "ds_read_u8 %14, %37 offset:%44\n\t"
+          "ds_read_u8 %15, %37 offset:%45\n\t"
+          "s_setprio 1\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %16, %28, %0, %22, %32 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %19, %28, %1, %25, %32 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %16, %29, %2, %22, %33 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %19, %29, %3, %25, %33 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %4, %16, %30, %4, %22, %34 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %5, %19, %30, %5, %25, %34 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %16, %31, %6, %22, %35 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %19, %31, %7, %25, %35 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %17, %28, %0, %23, %32 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %20, %28, %1, %26, %32 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %17, %29, %2, %23, %33 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %20, %29, %3, %26, %33 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %4, %17, %30, %4, %23, %34 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %5, %20, %30, %5, %26, %34 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %17, %31, %6, %23, %35 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %20, %31, %7, %26, %35 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %18, %28, %0, %24, %32 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %21, %28, %1, %27, %32 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %18, %29, %2, %24, %33 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %21, %29, %3, %27, %33 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %4, %18, %30, %4, %24, %34 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %5, %21, %30, %5, %27, %34 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %18, %31, %6, %24, %35 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %21, %31, %7, %27, %35 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "s_setprio 0\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
-          : "v"(bb), "v"(sb), "i"(64 * j0), "i"(64 * j1), "i"(64 * j2), "i"(64 * j3), "i"(8 * j0), "i"(8 * j1),
-            "i"(8 * j2), "i"(8 * j3));
-      const v4u bq[4] = {b0, b1, b2, b3};
-      const uint32_t sq[4] = {t0, t1, t2, t3};
-      // raised priority while this wave issues its MFMAs, so that the
-      // other wave of the SIMD (reading LDS meanwhile) does not interleave
-      // and both keep the matrix pipe fed
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j = 4 * jg + jj;
-        const v8i b = {(int)bq[jj].x, (int)bq[jj].y, (int)bq[jj].z, (int)bq[jj].w, 0, 0, 0, 0};
-#pragma unroll
-        for (int t = 0; t < 3; ++t)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[mb][t], b, acc[mb][j], 2, 4, 0,
-                                                                          as[mb][t], 0, (int)sq[jj]);
+          : "+v"(acc[0][4 * jg]), "+v"(acc[1][4 * jg]), "+v"(acc[0][4 * jg + 1]), "+v"(acc[1][4 * jg + 1]),
+            "+v"(acc[0][4 * jg + 2]), "+v"(acc[1][4 * jg + 2]), "+v"(acc[0][4 * jg + 3]), "+v"(acc[1][4 * jg + 3]),
+            "=&v"(bq[nxt][0]), "=&v"(bq[nxt][1]), "=&v"(bq[nxt][2]), "=&v"(bq[nxt][3]),
+            "=&v"(sq[nxt][0]), "=&v"(sq[nxt][1]), "=&v"(sq[nxt][2]), "=&v"(sq[nxt][3])
+          : "v"(a6[0][0]), "v"(a6[0][1]), "v"(a6[0][2]), "v"(a6[1][0]), "v"(a6[1][1]), "v"(a6[1][2]),
+            "v"(as[0][0]), "v"(as[0][1]), "v"(as[0][2]), "v"(as[1][0]), "v"(as[1][1]), "v"(as[1][2]),
+            "v"(bq[cur][0]), "v"(bq[cur][1]), "v"(bq[cur][2]), "v"(bq[cur][3]),
+            "v"(sq[cur][0]), "v"(sq[cur][1]), "v"(sq[cur][2]), "v"(sq[cur][3]), "v"(bb), "v"(sb),
+            "i"(64 * jrow(std::integral_constant<int, k0>{})), "i"(64 * jrow(std::integral_constant<int, k0 + 1>{})),
+            "i"(64 * jrow(std::integral_constant<int, k0 + 2>{})), "i"(64 * jrow(std::integral_constant<int, k0 + 3>{})),
+            "i"(8 * jrow(std::integral_constant<int, k0>{})), "i"(8 * jrow(std::integral_constant<int, k0 + 1>{})),
+            "i"(8 * jrow(std::integral_constant<int, k0 + 2>{})), "i"(8 * jrow(std::integral_constant<int, k0 + 3>{})));
+      } else {
+        asm volatile(
+          "s_nop 4\n\t"
+          "s_setprio 1\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %8, %20, %0, %14, %24 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %11, %20, %1, %17, %24 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %8, %21, %2, %14, %25 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %11, %21, %3, %17, %25 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %4, %8, %22, %4, %14, %26 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %5, %11, %22, %5, %17, %26 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %8, %23, %6, %14, %27 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %11, %23, %7, %17, %27 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %9, %20, %0, %15, %24 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %12, %20, %1, %18, %24 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %9, %21, %2, %15, %25 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %12, %21, %3, %18, %25 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %4, %9, %22, %4, %15, %26 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %5, %12, %22, %5, %18, %26 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %9, %23, %6, %15, %27 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %12, %23, %7, %18, %27 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %10, %20, %0, %16, %24 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %13, %20, %1, %19, %24 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %10, %21, %2, %16, %25 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %13, %21, %3, %19, %25 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %4, %10, %22, %4, %16, %26 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %5, %13, %22, %5, %19, %26 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %10, %23, %6, %16, %27 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %13, %23, %7, %19, %27 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "s_setprio 0"
+          : "+v"(acc[0][4 * jg]), "+v"(acc[1][4 * jg]), "+v"(acc[0][4 * jg + 1]), "+v"(acc[1][4 * jg + 1]),
+            "+v"(acc[0][4 * jg + 2]), "+v"(acc[1][4 * jg + 2]), "+v"(acc[0][4 * jg + 3]), "+v"(acc[1][4 * jg + 3])
+          : "v"(a6[0][0]), "v"(a6[0][1]), "v"(a6[0][2]), "v"(a6[1][0]), "v"(a6[1][1]), "v"(a6[1][2]),
+            "v"(as[0][0]), "v"(as[0][1]), "v"(as[0][2]), "v"(as[1][0]), "v"(as[1][1]), "v"(as[1][2]),
+            "v"(bq[cur][0]), "v"(bq[cur][1]), "v"(bq[cur][2]), "v"(bq[cur][3]),
+            "v"(sq[cur][0]), "v"(sq[cur][1]), "v"(sq[cur][2]), "v"(sq[cur][3]));
       }
-      __builtin_amdgcn_s_setprio(0);
     });
   }
+  // wait states before anything reads the accumulators the MFMAs wrote
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   __syncthreads();  // every wave is done with the operand buffers
 
   float bias[NCB];
