@@ -139,14 +139,59 @@ def clamped_swiglu(g: np.ndarray, u: np.ndarray, clamp: float) -> np.ndarray:
     return gc * sigmoid(gc) * (uc + 1.0)
 
 
+def e2m3_round(v: np.ndarray) -> np.ndarray:
+    """Nearest FP6 E2M3 value (ties to the even code) of |v| <= 7.5: sign,
+    two exponent bits (bias 1), three mantissa bits; the subnormals are
+    m/8, the normals 2^(e-1) * (1 + m/8) for e = 1..3, so the spacing is 1/8
+    below 2, 1/4 in [2, 4) and 1/2 in [4, 7.5].  Within a binade an even
+    multiple of the spacing is an even mantissa, and round() breaks ties to
+    even, so this is round-to-nearest-even on the codes."""
+    a = np.abs(v)
+    q = np.where(a < 2.0, 0.125, np.where(a < 4.0, 0.25, 0.5))
+    return np.sign(v) * np.round(a / q) * q
+
+
+def mx6_scale_exponent(amax: np.ndarray) -> np.ndarray:
+    """Smallest integer k with 7.5 * 2^k >= amax (a block's shared E8M0
+    exponent; 7.5 is the largest E2M3 value, so no element saturates).
+    amax = 0 gives k = -127 (the block quantises to zeros)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    safe = np.where(amax > 0, amax, 1.0)
+    k = np.ceil(np.log2(safe / 7.5))
+    # settle the float rounding of log2 exactly: powers of two are exact
+    k = np.where(7.5 * np.exp2(k - 1) >= safe, k - 1, k)
+    k = np.where(7.5 * np.exp2(k) < safe, k + 1, k)
+    return np.where(amax > 0, np.clip(k, -127, 127), -127.0)
+
+
+def mxfp6_quantize(v: np.ndarray) -> np.ndarray:
+    """Microscaling FP6 (E2M3 elements, one power-of-two scale per 32
+    consecutive values of a row -- the same block format as the MXFP4
+    weights of [A] 权重量化, with 6-bit elements): each block is divided by
+    2^k (mx6_scale_exponent of its largest magnitude), rounded to E2M3,
+    and multiplied back.  The activation-quantised fast mode feeds x and h
+    through this before the expert GEMMs."""
+    v = np.asarray(v, dtype=np.float64)
+    shape = v.shape
+    b = v.reshape(shape[:-1] + (shape[-1] // 32, 32))
+    k = mx6_scale_exponent(np.abs(b).max(axis=-1))[..., None]
+    s = np.exp2(k)
+    return (e2m3_round(b / s) * s).reshape(shape)
+
+
 def expert_ffn(xs: np.ndarray, w13: np.ndarray, b13: np.ndarray,
-               w2: np.ndarray, b2: np.ndarray, clamp: float) -> np.ndarray:
+               w2: np.ndarray, b2: np.ndarray, clamp: float, act_quant=None) -> np.ndarray:
     """One expert on rows xs [n, d] with dequantised weights: the three
     linear maps of the GLU ([C]): a = xs W13^T + b13, gate = a[:, :I],
-    up = a[:, I:], z = h W2^T + b2."""
+    up = a[:, I:], z = h W2^T + b2.  act_quant (fast mode only) is applied
+    to the rows entering each expert GEMM (xs and h)."""
     I = w13.shape[0] // 2
+    if act_quant is not None:
+        xs = act_quant(xs)
     a = xs @ w13.T + b13[None, :]
     h = clamped_swiglu(a[:, :I], a[:, I:], clamp)
+    if act_quant is not None:
+        h = act_quant(h)
     return h @ w2.T + b2[None, :]
 
 
@@ -181,12 +226,18 @@ def route(x_bits: np.ndarray, router_w_bits: np.ndarray, router_b: np.ndarray, k
 
 
 def moe_layer(x_bits: np.ndarray, router_w_bits: np.ndarray, router_b: np.ndarray,
-              experts: dict, k: int, clamp: float, cache: DequantCache | None = None):
+              experts: dict, k: int, clamp: float, cache: DequantCache | None = None,
+              act: str = "exact"):
     """Sparse MoE layer: y[t] = sum_j w[t,j] * FFN_{S_t[j]}(x[t]).
 
     Each expert runs only on the tokens routed to it ([B] 2.4.1).  Returns a
     dict with y (float64 [T, d]), logits, ids, w and per-expert counts.
+    act = "mxfp6": the activation-quantised fast mode (x and h rounded to
+    MXFP6 before the expert GEMMs, mxfp6_quantize); the router always sees x.
     """
+    if act not in ("exact", "mxfp6"):
+        raise ValueError(act)
+    aq = mxfp6_quantize if act == "mxfp6" else None
     x = bf16_bits_to_f64(x_bits)
     logits, ids, w = route(x_bits, router_w_bits, router_b, k)
     T = x.shape[0]
@@ -200,7 +251,7 @@ def moe_layer(x_bits: np.ndarray, router_w_bits: np.ndarray, router_b: np.ndarra
         if tok.size == 0:
             continue
         w13, b13, w2, b2 = cache(e)
-        z = expert_ffn(x[tok], w13, b13, w2, b2, clamp)
+        z = expert_ffn(x[tok], w13, b13, w2, b2, clamp, aq)
         y[tok] += w[tok, slot][:, None] * z
     return dict(y=y, logits=logits, ids=ids, w=w, counts=counts)
 
