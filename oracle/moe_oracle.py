@@ -251,7 +251,8 @@ def moe_layer(x_bits: np.ndarray, router_w_bits: np.ndarray, router_b: np.ndarra
         if tok.size == 0:
             continue
         w13, b13, w2, b2 = cache(e)
-        z = expert_ffn(x[tok], w13, b13, w2, b2, clamp, aq)
+        z = (expert_ffn(x[tok], w13, b13, w2, b2, clamp) if aq is None
+             else expert_ffn(x[tok], w13, b13, w2, b2, clamp, aq))
         y[tok] += w[tok, slot][:, None] * z
     return dict(y=y, logits=logits, ids=ids, w=w, counts=counts)
 
