@@ -78,7 +78,7 @@ def read_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(wl, inp, budget_s: float):
+def cpu_baseline(wl, inp, budget_s: float, act: str = "exact"):
     """The fp64 oracle on a bounded sample of the workload's tokens, on this
     host: the sample doubles until one run takes a quarter of the budget."""
     from oracle import moe_oracle as O
@@ -90,7 +90,7 @@ def cpu_baseline(wl, inp, budget_s: float):
     n, spent = 1, 0.0
     while True:
         t0 = time.perf_counter()
-        O.moe_layer(inp["x"][:n], inp["router_w"], inp["router_b"], inp, wl.k, wl.clamp)
+        O.moe_layer(inp["x"][:n], inp["router_w"], inp["router_b"], inp, wl.k, wl.clamp, act=act)
         spent = time.perf_counter() - t0
         if spent > budget_s / 4 or n >= wl.T:
             break
@@ -99,7 +99,7 @@ def cpu_baseline(wl, inp, budget_s: float):
     reps, total = 1, spent
     while total < budget_s / 2:
         t0 = time.perf_counter()
-        O.moe_layer(inp["x"][:n], inp["router_w"], inp["router_b"], inp, wl.k, wl.clamp)
+        O.moe_layer(inp["x"][:n], inp["router_w"], inp["router_b"], inp, wl.k, wl.clamp, act=act)
         total += time.perf_counter() - t0
         reps += 1
     tok_s = reps * n / (total * wl.layers)
@@ -119,10 +119,16 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="weight sets to rotate over (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--act", default="exact", choices=["exact", "mxfp6"],
+                    help="expert-GEMM activations: exact (bf16 precision, three FP6 terms) or mxfp6 "
+                         "(the activation-quantised fast mode, moe_layer_forward_mx6)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 256 MiB bitwise_not kernel (reads and writes 256 MiB: "
                          "the reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.act != "exact" and WORKLOADS[args.workload].layers > 1:
+        print("the fast mode has a single-layer entry point only", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the MoE layer here is built and measured on a single MI355X, "
               f"and no multi-GPU path exists (asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -175,9 +181,11 @@ def main():
     x_bytes = wl.T * wl.d * 2
 
     if nlay == 1:
+        fwd = moe.moe_layer_forward if args.act == "exact" else moe.moe_layer_forward_mx6
+
         def step(i):
             g = sets[i % nsets]
-            return moe.moe_layer_forward(*[g[k] for k in KEYS], k=wl.k, clamp=wl.clamp, out=outs[i % nsets])
+            return fwd(*[g[k] for k in KEYS], k=wl.k, clamp=wl.clamp, out=outs[i % nsets])
         outs = [torch.empty((wl.T, wl.d), dtype=torch.bfloat16, device="cuda:0") for _ in range(nsets)]
         layers_per_step = 1
     else:
@@ -249,20 +257,20 @@ def main():
     gu_unit_bytes = mxfp4_bytes(2 * wl.I, wl.d) + 4 * 2 * wl.I
     if decode_like:
         achieved = (nsel_mean * gu_unit_bytes + x_bytes) / (gu_us * 1e-6)
-        traffic = read_traffic("gateup_gemm", wl.name)
+        traffic = read_traffic("gateup_gemm", wl.name) if args.act == "exact" else None
         roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK, "traffic": traffic, "kernel": "gateup_gemm",
                 "kernel_us": gu_us}
     else:
         achieved = (2.0 * P * wl.d * 2 * wl.I) / (gu_us * 1e-6)
-        traffic = read_traffic("gateup_gemm", wl.name)
+        traffic = read_traffic("gateup_gemm", wl.name) if args.act == "exact" else None
         roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": MFMA_FP6_FP4_PEAK / 1e12,
                 "unit": "TFLOP/s", "frac": achieved / MFMA_FP6_FP4_PEAK, "traffic": traffic,
                 "kernel": "gateup_gemm", "kernel_us": gu_us}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, host0, args.cpu_budget)
+        cpu = cpu_baseline(wl, host0, args.cpu_budget, args.act)
         log(f"cpu baseline: {cpu}")
 
     rec = {
@@ -288,6 +296,8 @@ def main():
             "mxfp4_mfma_frac": step_flops / (ms_step * 1e-3) / MFMA_FP6_FP4_PEAK,
             "kernel_us": {k: (v[0] / v[1] * 1e3 if v[1] else None) for k, v in kt.items()},
             "parallelism": "single-gpu",
+            "activations": "exact (bf16 precision as three FP6 terms)" if args.act == "exact"
+                           else "mxfp6 (activation-quantised fast mode)",
         },
         "roofline": roof,
         "cpu_baseline": cpu,

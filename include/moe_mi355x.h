@@ -98,6 +98,29 @@ int moe_layer_forward_dbg(const void* x, const void* router_w, const float* rout
                           int T, int d, int I, int E, int k, float clamp, void* out, float* out_f32,
                           int32_t* topk_id, float* topk_w, int32_t* counts, void* stream);
 
+/* Activation-quantised fast mode of moe_layer_forward (same arguments,
+ * layouts, ownership and errors).  The rows entering each expert GEMM (x
+ * for gate/up, h for down) are rounded to MXFP6 -- E2M3 elements with one
+ * power-of-two scale per 32 consecutive values, the smallest scale 2^k with
+ * 7.5 * 2^k >= the block's largest magnitude, round-to-nearest-even -- the
+ * block format of the pages' MXFP4 weights ("OpenAI 最新开源模型 gpt-oss
+ * 架构与训练解析", 权重量化 item) with 6-bit elements.  One block-scaled
+ * MFMA per 128-wide K step instead of three.  The router sees x unrounded,
+ * so expert ids and weights equal moe_layer_forward's.  The result is that
+ * of the layer on the rounded activations, not of the exact layer: it
+ * differs from moe_layer_forward by a few per cent of rms. */
+int moe_layer_forward_mx6(const void* x, const void* router_w, const float* router_b,
+                          const uint8_t* w13_codes, const uint8_t* w13_scales, const float* b13,
+                          const uint8_t* w2_codes, const uint8_t* w2_scales, const float* b2,
+                          int T, int d, int I, int E, int k, float clamp, void* out, void* stream);
+
+/* moe_layer_forward_dbg for the fast mode (outputs as there). */
+int moe_layer_forward_mx6_dbg(const void* x, const void* router_w, const float* router_b,
+                              const uint8_t* w13_codes, const uint8_t* w13_scales, const float* b13,
+                              const uint8_t* w2_codes, const uint8_t* w2_scales, const float* b2,
+                              int T, int d, int I, int E, int k, float clamp, void* out, float* out_f32,
+                              int32_t* topk_id, float* topk_w, int32_t* counts, void* stream);
+
 /* Router, top-k and selected softmax only ("【LLM】GPT-OSS架构变化详解",
  * 2.4.1; "OpenAI 最新开源模型 gpt-oss 架构与训练解析", MoE item).  Outputs as
  * in moe_layer_forward_dbg. */

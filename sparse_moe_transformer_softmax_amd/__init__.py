@@ -14,7 +14,7 @@ __all__ = [
     "MoeError", "lib", "moe_layer_forward", "moe_layer_forward_dbg", "moe_route",
     "moe_workspace_bytes", "moe_workspace_init", "moe_layer_forward_ws", "moe_rmsnorm",
     "moe_stack_forward", "moe_release", "moe_status_string", "moe_version", "LIB_PATH",
-    "moe_timing_enable", "moe_timing_read", "KERNELS",
+    "moe_timing_enable", "moe_timing_read", "KERNELS", "moe_layer_forward_mx6", "moe_layer_forward_mx6_dbg",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
@@ -26,6 +26,8 @@ _F = ctypes.c_float
 _SIGS = {
     "moe_layer_forward": (_I, [_P] * 9 + [_I] * 5 + [_F, _P, _P]),
     "moe_layer_forward_dbg": (_I, [_P] * 9 + [_I] * 5 + [_F] + [_P] * 6),
+    "moe_layer_forward_mx6": (_I, [_P] * 9 + [_I] * 5 + [_F, _P, _P]),
+    "moe_layer_forward_mx6_dbg": (_I, [_P] * 9 + [_I] * 5 + [_F] + [_P] * 6),
     "moe_route": (_I, [_P] * 3 + [_I] * 4 + [_P] * 4),
     "moe_workspace_bytes": (ctypes.c_size_t, [_I] * 5),
     "moe_workspace_init": (_I, [_P, ctypes.c_size_t, _P]),
@@ -149,19 +151,34 @@ def _layer_ptrs(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_
 
 
 def moe_layer_forward(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
-                      k: int = 4, clamp: float = 7.0, out=None, stream=None):
+                      k: int = 4, clamp: float = 7.0, out=None, stream=None, _fn="moe_layer_forward"):
     """out = MoE(x) in bf16 [T, d]; see include/moe_mi355x.h."""
     torch = _torch()
     ptrs, T, d, I, E = _layer_ptrs(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2)
     if out is None:
         out = torch.empty((T, d), dtype=torch.bfloat16, device=x.device)
     po = _check(out, "out", torch.bfloat16, (T, d))
-    _ok("moe_layer_forward", lib().moe_layer_forward(*ptrs, T, d, I, E, k, clamp, po, _stream(stream)))
+    _ok(_fn, getattr(lib(), _fn)(*ptrs, T, d, I, E, k, clamp, po, _stream(stream)))
     return out
 
 
+def moe_layer_forward_mx6(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
+                          k: int = 4, clamp: float = 7.0, out=None, stream=None):
+    """Activation-quantised fast mode (MXFP6 activations into the expert
+    GEMMs); see include/moe_mi355x.h."""
+    return moe_layer_forward(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
+                             k=k, clamp=clamp, out=out, stream=stream, _fn="moe_layer_forward_mx6")
+
+
+def moe_layer_forward_mx6_dbg(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
+                              k: int = 4, clamp: float = 7.0, stream=None):
+    """moe_layer_forward_dbg for the fast mode."""
+    return moe_layer_forward_dbg(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
+                                 k=k, clamp=clamp, stream=stream, _fn="moe_layer_forward_mx6_dbg")
+
+
 def moe_layer_forward_dbg(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
-                          k: int = 4, clamp: float = 7.0, stream=None):
+                          k: int = 4, clamp: float = 7.0, stream=None, _fn="moe_layer_forward_dbg"):
     """Returns (out bf16, out_f32, topk_id int32 [T,k], topk_w fp32 [T,k], counts int32 [E])."""
     torch = _torch()
     ptrs, T, d, I, E = _layer_ptrs(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2)
@@ -171,7 +188,7 @@ def moe_layer_forward_dbg(x, router_w, router_b, w13_codes, w13_scales, b13, w2_
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     counts = torch.empty((E,), dtype=torch.int32, device=dev)
-    _ok("moe_layer_forward_dbg", lib().moe_layer_forward_dbg(
+    _ok(_fn, getattr(lib(), _fn)(
         *ptrs, T, d, I, E, k, clamp, _check(out, "out", torch.bfloat16), _check(out_f32, "out_f32", torch.float32),
         _check(ids, "ids", torch.int32), _check(w, "w", torch.float32), _check(counts, "counts", torch.int32),
         _stream(stream)))

@@ -89,6 +89,7 @@ struct LayerArgs {
   const uint8_t* w13c; const uint8_t* w13s; const float* b13;
   const uint8_t* w2c; const uint8_t* w2s; const float* b2;
   int T, d, I, E, k; float clamp;
+  int terms = 3;  // FP6 terms of the expert GEMMs' activations: 3 (exact path) or 1 (fast mode)
 };
 
 int check_layer(const LayerArgs& a, const void* out) {
@@ -230,6 +231,7 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   gp.b_codes = a.w13c; gp.b_scales = a.w13s; gp.bias = a.b13;
   gp.N = 2 * a.I; gp.K = a.d; gp.I = a.I; gp.E = a.E;
   gp.clamp = a.clamp;
+  gp.terms = a.terms;
   gp.hq = ws + L.hq;
   gp.y = nullptr;
   {
@@ -317,19 +319,37 @@ int moe_layer_forward_ws(const void* x, const void* router_w, const float* route
   return run_layer(a, L, (uint8_t*)ws, out, nullptr, nullptr, nullptr, nullptr, false, (hipStream_t)stream);
 }
 
+static int forward_owned(const LayerArgs& a, void* out, void* stream) {
+  if (int st = check_layer(a, out)) return st;
+  if (a.T == 0) return MOE_OK;
+  if (!out) return MOE_ERR_NULL_PTR;
+  if (int st = check_device()) return st;
+  const Layout L = layout(a.T, a.d, a.I, a.E, a.k);
+  void* ws = nullptr;
+  if (int st = owned_workspace(L.total, (hipStream_t)stream, &ws)) return st;
+  return run_layer(a, L, (uint8_t*)ws, out, nullptr, nullptr, nullptr, nullptr, false, (hipStream_t)stream);
+}
+
+static int forward_dbg(const LayerArgs& a, void* out, float* out_f32, int32_t* topk_id, float* topk_w,
+                       int32_t* counts, void* stream) {
+  if (int st = check_layer(a, out)) return st;
+  if (a.T == 0) return MOE_OK;
+  if (!topk_id || !topk_w || !counts) return MOE_ERR_NULL_PTR;
+  if (!aligned(topk_id, 4) || !aligned(topk_w, 4) || !aligned(counts, 4) || (out_f32 && !aligned(out_f32, 16)))
+    return MOE_ERR_MISALIGNED;
+  if (int st = check_device()) return st;
+  const Layout L = layout(a.T, a.d, a.I, a.E, a.k);
+  void* ws = nullptr;
+  if (int st = owned_workspace(L.total, (hipStream_t)stream, &ws)) return st;
+  return run_layer(a, L, (uint8_t*)ws, out, out_f32, topk_id, topk_w, counts, false, (hipStream_t)stream);
+}
+
 int moe_layer_forward(const void* x, const void* router_w, const float* router_b, const uint8_t* w13_codes,
                       const uint8_t* w13_scales, const float* b13, const uint8_t* w2_codes,
                       const uint8_t* w2_scales, const float* b2, int T, int d, int I, int E, int k, float clamp,
                       void* out, void* stream) {
   LayerArgs a{x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, d, I, E, k, clamp};
-  if (int st = check_layer(a, out)) return st;
-  if (T == 0) return MOE_OK;
-  if (!out) return MOE_ERR_NULL_PTR;
-  if (int st = check_device()) return st;
-  const Layout L = layout(T, d, I, E, k);
-  void* ws = nullptr;
-  if (int st = owned_workspace(L.total, (hipStream_t)stream, &ws)) return st;
-  return run_layer(a, L, (uint8_t*)ws, out, nullptr, nullptr, nullptr, nullptr, false, (hipStream_t)stream);
+  return forward_owned(a, out, stream);
 }
 
 int moe_layer_forward_dbg(const void* x, const void* router_w, const float* router_b, const uint8_t* w13_codes,
@@ -338,16 +358,26 @@ int moe_layer_forward_dbg(const void* x, const void* router_w, const float* rout
                           float clamp, void* out, float* out_f32, int32_t* topk_id, float* topk_w,
                           int32_t* counts, void* stream) {
   LayerArgs a{x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, d, I, E, k, clamp};
-  if (int st = check_layer(a, out)) return st;
-  if (T == 0) return MOE_OK;
-  if (!topk_id || !topk_w || !counts) return MOE_ERR_NULL_PTR;
-  if (!aligned(topk_id, 4) || !aligned(topk_w, 4) || !aligned(counts, 4) || (out_f32 && !aligned(out_f32, 16)))
-    return MOE_ERR_MISALIGNED;
-  if (int st = check_device()) return st;
-  const Layout L = layout(T, d, I, E, k);
-  void* ws = nullptr;
-  if (int st = owned_workspace(L.total, (hipStream_t)stream, &ws)) return st;
-  return run_layer(a, L, (uint8_t*)ws, out, out_f32, topk_id, topk_w, counts, false, (hipStream_t)stream);
+  return forward_dbg(a, out, out_f32, topk_id, topk_w, counts, stream);
+}
+
+int moe_layer_forward_mx6(const void* x, const void* router_w, const float* router_b, const uint8_t* w13_codes,
+                          const uint8_t* w13_scales, const float* b13, const uint8_t* w2_codes,
+                          const uint8_t* w2_scales, const float* b2, int T, int d, int I, int E, int k,
+                          float clamp, void* out, void* stream) {
+  LayerArgs a{x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, d, I, E, k, clamp};
+  a.terms = 1;
+  return forward_owned(a, out, stream);
+}
+
+int moe_layer_forward_mx6_dbg(const void* x, const void* router_w, const float* router_b,
+                              const uint8_t* w13_codes, const uint8_t* w13_scales, const float* b13,
+                              const uint8_t* w2_codes, const uint8_t* w2_scales, const float* b2, int T, int d,
+                              int I, int E, int k, float clamp, void* out, float* out_f32, int32_t* topk_id,
+                              float* topk_w, int32_t* counts, void* stream) {
+  LayerArgs a{x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, d, I, E, k, clamp};
+  a.terms = 1;
+  return forward_dbg(a, out, out_f32, topk_id, topk_w, counts, stream);
 }
 
 int moe_route(const void* x, const void* router_w, const float* router_b, int T, int d, int E, int k,

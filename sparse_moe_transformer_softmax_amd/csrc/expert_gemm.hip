@@ -69,7 +69,9 @@ struct Stage {
 template <int MB, int NCB>
 __device__ __forceinline__ uint32_t keep_mask(bool in) { return in ? 0xffffffffu : 0u; }
 
-template <int MB, int NCB>
+// TERMS = 1 (the activation-quantised fast mode): only the first FP6 term
+// of A takes part.
+template <int MB, int NCB, int TERMS = 3>
 __device__ __forceinline__ void mma_stage(v4f (&acc)[MB][NCB], const Stage<MB, NCB>& st, uint32_t keep) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -91,12 +93,14 @@ __device__ __forceinline__ void mma_stage(v4f (&acc)[MB][NCB], const Stage<MB, N
 #pragma unroll
     for (int j = 0; j < NCB; ++j)
       acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, b[j], acc[mb][j], 2, 4, 0, s0, 0, bsc[j]);
+    if constexpr (TERMS == 3) {
 #pragma unroll
-    for (int j = 0; j < NCB; ++j)
-      acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, b[j], acc[mb][j], 2, 4, 0, s1, 0, bsc[j]);
+      for (int j = 0; j < NCB; ++j)
+        acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, b[j], acc[mb][j], 2, 4, 0, s1, 0, bsc[j]);
 #pragma unroll
-    for (int j = 0; j < NCB; ++j)
-      acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a2, b[j], acc[mb][j], 2, 4, 0, s2, 0, bsc[j]);
+      for (int j = 0; j < NCB; ++j)
+        acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a2, b[j], acc[mb][j], 2, 4, 0, s2, 0, bsc[j]);
+    }
   }
 }
 
@@ -294,9 +298,12 @@ __device__ __forceinline__ void dec_null_item(const GemmParams& p, DecItem& it) 
   it.bias[0] = it.bias[1] = it.bias[2] = it.bias[3] = 0.f;
 }
 
-template <bool GATEUP, int NPH, bool U16>
+template <bool GATEUP, int NPH, bool U16, int TERMS>
 __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_gemm_decode(GemmParams p, int spans) {
   using Cfg = DecCfg<U16>;
+  // vector-memory instructions per wave per phase (the fast mode loads two
+  // fewer A pieces)
+  constexpr int VM = Cfg::VM - (TERMS == 1 ? 2 : 0);
   constexpr int NCB = 4, NW = DEC_NW;
   // readfirstlane: the wave index is uniform, so the buffer resources and
   // LDS bases derived from it live in scalar registers
@@ -370,6 +377,10 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
     const int aso = pb0 / 4 * MX6_GROUP_BYTES;  // pb0 is a multiple of 4 blocks
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+      if (TERMS == 1 && q >= 2) {  // pieces 2 and 3 hold only the other terms' codes
+        av[q] = make_uint4(0u, 0u, 0u, 0u);
+        continue;
+      }
       const auto t4 = __builtin_amdgcn_raw_buffer_load_b128(arsrc, off + 64 * q, aso, 0);
       av[q] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
     }
@@ -419,7 +430,7 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
     st.bs[1] = (int)((s1 >> sh) & 0xffu);
     st.bs[2] = (int)((s2 >> sh) & 0xffu);
     st.bs[3] = (int)((s3 >> sh) & 0xffu);
-    mma_stage(acc, st, keep_mask<1, NCB>(bl < npb));
+    mma_stage<1, NCB, TERMS>(acc, st, keep_mask<1, NCB>(bl < npb));
     // pin the MFMAs to this phase: unused until the epilogue, they could
     // otherwise be sunk past later code, holding every phase's operands
     asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]));
@@ -507,7 +518,7 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
       issue(nit, 0, buf ^ 1, avn);
     else
       issue(cur, ph + 1, buf ^ 1, avn);
-    wait_vmcnt<Cfg::VM>();
+    wait_vmcnt<VM>();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     consume(ph, buf, avc);
@@ -672,7 +683,7 @@ constexpr int PF_EPI_BYTES = 16 * (16 * PF_NCB + 4) * 4;
 static_assert(PF_EPI_BYTES >= 16 * (8 * PF_NCB + 4) * 4, "gate/up staging fits");
 constexpr int PF_SMEM = (int)sizeof(PfShared) > PF_NW * PF_EPI_BYTES ? (int)sizeof(PfShared) : PF_NW * PF_EPI_BYTES;
 
-template <bool GATEUP>
+template <bool GATEUP, int TERMS>
 __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams p, int spans) {
   constexpr int MB = 2, NCB = PF_NCB;
   constexpr int B_PIECES = PF_NT * 4 / (PF_NW * 64);  // 16-B weight pieces per thread per chunk
@@ -761,13 +772,20 @@ __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams 
     s_off[q] = brow * (uint32_t)nblk + (uint32_t)bpiece;
   });
 
+  // (the fast mode loads pieces 0, 1 and 4 only: the first term's codes
+  // and the scale bytes)
   auto load_a = [&](int c, v4u (&av)[MB][5]) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int q = 0; q < 5; ++q)
+      for (int q = 0; q < 5; ++q) {
+        if (TERMS == 1 && (q == 2 || q == 3)) {
+          av[mb][q] = (v4u){0u, 0u, 0u, 0u};
+          continue;
+        }
         av[mb][q] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(arsrc, a_off[mb] + 64 * q,
                                                                                   c * MX6_GROUP_BYTES, 0));
+      }
   };
   v4u rb[B_PIECES];
   uint32_t rs[B_PIECES];
@@ -866,7 +884,7 @@ __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams 
       // the two row blocks alternate, so consecutive MFMAs never depend on
       // each other
 #pragma unroll
-      for (int t = 0; t < 3; ++t)
+      for (int t = 0; t < TERMS; ++t)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
           acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[mb][t], b, acc[mb][j], 2, 4, 0, as[mb][t],
@@ -930,8 +948,12 @@ static_assert(PW_A_COPIES == 5 && PW_B_COPIES == 4 && PW_S_COPIES == 2, "copy sp
 static_assert(PW_EPI_BYTES >= 16 * (8 * PW_NCB + 4) * 4, "gate/up staging fits");
 static_assert(PW_NW * PW_EPI_BYTES <= 2 * PW_BUF, "epilogue staging fits the operand buffers");
 
-template <bool GATEUP>
+template <bool GATEUP, int TERMS>
 __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmParams p, int spans) {
+  // (the body is compiled for the device only: the host pass, which only
+  // needs the kernel's signature for its launch stub, cannot type the
+  // 6-register operands of the asm blocks)
+#if defined(__HIP_DEVICE_COMPILE__)
   constexpr int MB = 2, NCB = PW_NCB;
   __shared__ __align__(16) uint8_t smem[2 * PW_BUF];
   __shared__ float s_bias[PW_NT];
@@ -1008,7 +1030,9 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
                                    : (uint32_t)(row_base + m);
       off = arow * a_rowbytes + (uint32_t)piece * 16u;
     }
-    a_src[k] = off;
+    // (the fast mode copies pieces 0, 1 and 4 only: the first term's codes
+    // and the scale bytes)
+    a_src[k] = (TERMS == 1 && (piece >> 2) >= 2 && (piece >> 2) <= 3) ? A_OOB : off;
     a_blk[k] = piece & 3;
   }
   // B copy k fills slots u = (4 wave + k) * 64 + lane: tile row u / 4,
@@ -1082,13 +1106,15 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
     if (c + 1 < nchunk) issue(c + 1, buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
     // A fragments (pieces 0..4 of block g of the lane's row in each row
-    // block, zeros past K) and the first group's B fragments, then the
-    // three FP6 terms of A as 6-register operands
+    // block, zeros past K; the fast mode reads pieces 0, 1 and 4 only) and
+    // the first group's B fragments, then the FP6 terms of A as 6-register
+    // operands
     const uint32_t ab = bbase + a_lane, bb = bbase + b_lane, sb = bbase + s_lane;
     v4u w[MB][5];
     v4u bq[2][4];
     uint32_t sq[2][4];
-    asm volatile(
+    if constexpr (TERMS == 3) {
+      asm volatile(
         "ds_read_b128 %0, %18 offset:%21\n\t"
         "ds_read_b128 %1, %18 offset:%22\n\t"
         "ds_read_b128 %2, %18 offset:%23\n\t"
@@ -1108,40 +1134,72 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
         "ds_read_u8 %16, %20 offset:%37\n\t"
         "ds_read_u8 %17, %20 offset:%38\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(w[0][0]), "=&v"(w[0][1]), "=&v"(w[0][2]), "=&v"(w[0][3]), "=&v"(w[0][4]), "=&v"(w[1][0]),
-          "=&v"(w[1][1]), "=&v"(w[1][2]), "=&v"(w[1][3]), "=&v"(w[1][4]), "=&v"(bq[0][0]), "=&v"(bq[0][1]),
-          "=&v"(bq[0][2]), "=&v"(bq[0][3]), "=&v"(sq[0][0]), "=&v"(sq[0][1]), "=&v"(sq[0][2]), "=&v"(sq[0][3])
-        : "v"(ab), "v"(bb), "v"(sb), "i"(0), "i"(64), "i"(128), "i"(192), "i"(256),
-          "i"(16 * MX6_GROUP_BYTES), "i"(16 * MX6_GROUP_BYTES + 64), "i"(16 * MX6_GROUP_BYTES + 128),
-          "i"(16 * MX6_GROUP_BYTES + 192), "i"(16 * MX6_GROUP_BYTES + 256),
-          "i"(64 * jrow(std::integral_constant<int, 0>{})), "i"(64 * jrow(std::integral_constant<int, 1>{})),
-          "i"(64 * jrow(std::integral_constant<int, 2>{})), "i"(64 * jrow(std::integral_constant<int, 3>{})),
-          "i"(8 * jrow(std::integral_constant<int, 0>{})), "i"(8 * jrow(std::integral_constant<int, 1>{})),
+        : "=&v"(w[0][0]), "=&v"(w[0][1]), "=&v"(w[0][2]), "=&v"(w[0][3]),
+          "=&v"(w[0][4]), "=&v"(w[1][0]), "=&v"(w[1][1]), "=&v"(w[1][2]),
+          "=&v"(w[1][3]), "=&v"(w[1][4]), "=&v"(bq[0][0]), "=&v"(bq[0][1]),
+          "=&v"(bq[0][2]), "=&v"(bq[0][3]), "=&v"(sq[0][0]), "=&v"(sq[0][1]),
+          "=&v"(sq[0][2]), "=&v"(sq[0][3])
+        : "v"(ab), "v"(bb), "v"(sb),
+          "i"(16 * MX6_GROUP_BYTES * 0 + 0), "i"(16 * MX6_GROUP_BYTES * 0 + 64), "i"(16 * MX6_GROUP_BYTES * 0 + 128),
+          "i"(16 * MX6_GROUP_BYTES * 0 + 192), "i"(16 * MX6_GROUP_BYTES * 0 + 256), "i"(16 * MX6_GROUP_BYTES * 1 + 0),
+          "i"(16 * MX6_GROUP_BYTES * 1 + 64), "i"(16 * MX6_GROUP_BYTES * 1 + 128), "i"(16 * MX6_GROUP_BYTES * 1 + 192),
+          "i"(16 * MX6_GROUP_BYTES * 1 + 256), "i"(64 * jrow(std::integral_constant<int, 0>{})), "i"(64 * jrow(std::integral_constant<int, 1>{})),
+          "i"(64 * jrow(std::integral_constant<int, 2>{})), "i"(64 * jrow(std::integral_constant<int, 3>{})), "i"(8 * jrow(std::integral_constant<int, 0>{})),
+          "i"(8 * jrow(std::integral_constant<int, 1>{})), "i"(8 * jrow(std::integral_constant<int, 2>{})), "i"(8 * jrow(std::integral_constant<int, 3>{})));
+    } else {
+      asm volatile(
+        "ds_read_b128 %0, %14 offset:%17\n\t"
+        "ds_read_b128 %1, %14 offset:%18\n\t"
+        "ds_read_b128 %2, %14 offset:%19\n\t"
+        "ds_read_b128 %3, %14 offset:%20\n\t"
+        "ds_read_b128 %4, %14 offset:%21\n\t"
+        "ds_read_b128 %5, %14 offset:%22\n\t"
+        "ds_read_b128 %6, %15 offset:%23\n\t"
+        "ds_read_b128 %7, %15 offset:%24\n\t"
+        "ds_read_b128 %8, %15 offset:%25\n\t"
+        "ds_read_b128 %9, %15 offset:%26\n\t"
+        "ds_read_u8 %10, %16 offset:%27\n\t"
+        "ds_read_u8 %11, %16 offset:%28\n\t"
+        "ds_read_u8 %12, %16 offset:%29\n\t"
+        "ds_read_u8 %13, %16 offset:%30\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0][0]), "=&v"(w[0][1]), "=&v"(w[0][4]), "=&v"(w[1][0]),
+          "=&v"(w[1][1]), "=&v"(w[1][4]), "=&v"(bq[0][0]), "=&v"(bq[0][1]),
+          "=&v"(bq[0][2]), "=&v"(bq[0][3]), "=&v"(sq[0][0]), "=&v"(sq[0][1]),
+          "=&v"(sq[0][2]), "=&v"(sq[0][3])
+        : "v"(ab), "v"(bb), "v"(sb),
+          "i"(16 * MX6_GROUP_BYTES * 0 + 0), "i"(16 * MX6_GROUP_BYTES * 0 + 64), "i"(16 * MX6_GROUP_BYTES * 0 + 256),
+          "i"(16 * MX6_GROUP_BYTES * 1 + 0), "i"(16 * MX6_GROUP_BYTES * 1 + 64), "i"(16 * MX6_GROUP_BYTES * 1 + 256),
+          "i"(64 * jrow(std::integral_constant<int, 0>{})), "i"(64 * jrow(std::integral_constant<int, 1>{})), "i"(64 * jrow(std::integral_constant<int, 2>{})),
+          "i"(64 * jrow(std::integral_constant<int, 3>{})), "i"(8 * jrow(std::integral_constant<int, 0>{})), "i"(8 * jrow(std::integral_constant<int, 1>{})),
           "i"(8 * jrow(std::integral_constant<int, 2>{})), "i"(8 * jrow(std::integral_constant<int, 3>{})));
-    v6u a6[MB][3];
-    uint32_t as[MB][3];
+      w[0][2] = w[0][3] = w[1][2] = w[1][3] = (v4u){0u, 0u, 0u, 0u};
+    }
+    v6u a6[MB][TERMS];
+    uint32_t as[MB][TERMS];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const uint32_t* x = (const uint32_t*)&w[mb][0];
 #pragma unroll
-      for (int t = 0; t < 3; ++t) {
+      for (int t = 0; t < TERMS; ++t) {
         a6[mb][t] = (v6u){x[6 * t], x[6 * t + 1], x[6 * t + 2], x[6 * t + 3], x[6 * t + 4], x[6 * t + 5]};
         as[mb][t] = (x[18] >> (8 * t)) & 0xffu;
       }
     }
     // column-block groups of four: each asm block reads the next group's B
-    // fragments while it issues this group's 24 MFMAs (term-major, so an
-    // accumulator's three updates are eight MFMAs apart), then waits for
-    // the reads.  s_nop: wait states for operands written just before by
-    // VALU instructions.  Raised priority while the MFMAs issue, so that the
-    // other wave of the SIMD (reading LDS meanwhile) does not interleave.
+    // fragments while it issues this group's 8 * TERMS MFMAs (term-major, so
+    // an accumulator's updates are eight MFMAs apart), then waits for the
+    // reads.  s_nop: wait states for operands written just before by VALU
+    // instructions.  Raised priority while the MFMAs issue, so that the other
+    // wave of the SIMD (reading LDS meanwhile) does not interleave.
     StaticFor<0, NCB / 4>::run([&](auto gc) {
       constexpr int jg = decltype(gc)::value;
       constexpr int cur = jg & 1, nxt = cur ^ 1;
-      if constexpr (jg + 1 < NCB / 4) {
-        constexpr int k0 = 4 * (jg + 1);
-        asm volatile(
-          "s_nop 4\n\t"
+      if constexpr (TERMS == 3) {
+        if constexpr (jg + 1 < NCB / 4) {
+          constexpr int k0 = 4 * (jg + 1);
+          asm volatile(
+            "s_nop 4\n\t"
           "ds_read_b128 %8, %36 offset:%38\n\t"
           "ds_read_b128 %9, %36 offset:%39\n\t"
           "ds_read_b128 %10, %36 offset:%40\n\t"
@@ -1177,21 +1235,21 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
           "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %21, %31, %7, %27, %35 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
           "s_setprio 0\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "+v"(acc[0][4 * jg]), "+v"(acc[1][4 * jg]), "+v"(acc[0][4 * jg + 1]), "+v"(acc[1][4 * jg + 1]),
+            : "+v"(acc[0][4 * jg]), "+v"(acc[1][4 * jg]), "+v"(acc[0][4 * jg + 1]), "+v"(acc[1][4 * jg + 1]),
             "+v"(acc[0][4 * jg + 2]), "+v"(acc[1][4 * jg + 2]), "+v"(acc[0][4 * jg + 3]), "+v"(acc[1][4 * jg + 3]),
-            "=&v"(bq[nxt][0]), "=&v"(bq[nxt][1]), "=&v"(bq[nxt][2]), "=&v"(bq[nxt][3]),
-            "=&v"(sq[nxt][0]), "=&v"(sq[nxt][1]), "=&v"(sq[nxt][2]), "=&v"(sq[nxt][3])
-          : "v"(a6[0][0]), "v"(a6[0][1]), "v"(a6[0][2]), "v"(a6[1][0]), "v"(a6[1][1]), "v"(a6[1][2]),
-            "v"(as[0][0]), "v"(as[0][1]), "v"(as[0][2]), "v"(as[1][0]), "v"(as[1][1]), "v"(as[1][2]),
-            "v"(bq[cur][0]), "v"(bq[cur][1]), "v"(bq[cur][2]), "v"(bq[cur][3]),
-            "v"(sq[cur][0]), "v"(sq[cur][1]), "v"(sq[cur][2]), "v"(sq[cur][3]), "v"(bb), "v"(sb),
-            "i"(64 * jrow(std::integral_constant<int, k0>{})), "i"(64 * jrow(std::integral_constant<int, k0 + 1>{})),
-            "i"(64 * jrow(std::integral_constant<int, k0 + 2>{})), "i"(64 * jrow(std::integral_constant<int, k0 + 3>{})),
-            "i"(8 * jrow(std::integral_constant<int, k0>{})), "i"(8 * jrow(std::integral_constant<int, k0 + 1>{})),
-            "i"(8 * jrow(std::integral_constant<int, k0 + 2>{})), "i"(8 * jrow(std::integral_constant<int, k0 + 3>{})));
-      } else {
-        asm volatile(
-          "s_nop 4\n\t"
+              "=&v"(bq[nxt][0]), "=&v"(bq[nxt][1]), "=&v"(bq[nxt][2]), "=&v"(bq[nxt][3]),
+              "=&v"(sq[nxt][0]), "=&v"(sq[nxt][1]), "=&v"(sq[nxt][2]), "=&v"(sq[nxt][3])
+            : "v"(a6[0][0]), "v"(a6[0][1]), "v"(a6[0][2]), "v"(a6[1][0]), "v"(a6[1][1]), "v"(a6[1][2]),
+              "v"(as[0][0]), "v"(as[0][1]), "v"(as[0][2]), "v"(as[1][0]), "v"(as[1][1]), "v"(as[1][2]),
+              "v"(bq[cur][0]), "v"(bq[cur][1]), "v"(bq[cur][2]), "v"(bq[cur][3]),
+              "v"(sq[cur][0]), "v"(sq[cur][1]), "v"(sq[cur][2]), "v"(sq[cur][3]), "v"(bb), "v"(sb),
+              "i"(64 * jrow(std::integral_constant<int, k0>{})), "i"(64 * jrow(std::integral_constant<int, k0 + 1>{})),
+              "i"(64 * jrow(std::integral_constant<int, k0 + 2>{})), "i"(64 * jrow(std::integral_constant<int, k0 + 3>{})),
+              "i"(8 * jrow(std::integral_constant<int, k0>{})), "i"(8 * jrow(std::integral_constant<int, k0 + 1>{})),
+              "i"(8 * jrow(std::integral_constant<int, k0 + 2>{})), "i"(8 * jrow(std::integral_constant<int, k0 + 3>{})));
+        } else {
+          asm volatile(
+            "s_nop 4\n\t"
           "s_setprio 1\n\t"
           "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %8, %20, %0, %14, %24 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
           "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %11, %20, %1, %17, %24 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
@@ -1218,12 +1276,69 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
           "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %10, %23, %6, %16, %27 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
           "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %13, %23, %7, %19, %27 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
           "s_setprio 0"
-          : "+v"(acc[0][4 * jg]), "+v"(acc[1][4 * jg]), "+v"(acc[0][4 * jg + 1]), "+v"(acc[1][4 * jg + 1]),
+            : "+v"(acc[0][4 * jg]), "+v"(acc[1][4 * jg]), "+v"(acc[0][4 * jg + 1]), "+v"(acc[1][4 * jg + 1]),
             "+v"(acc[0][4 * jg + 2]), "+v"(acc[1][4 * jg + 2]), "+v"(acc[0][4 * jg + 3]), "+v"(acc[1][4 * jg + 3])
-          : "v"(a6[0][0]), "v"(a6[0][1]), "v"(a6[0][2]), "v"(a6[1][0]), "v"(a6[1][1]), "v"(a6[1][2]),
-            "v"(as[0][0]), "v"(as[0][1]), "v"(as[0][2]), "v"(as[1][0]), "v"(as[1][1]), "v"(as[1][2]),
-            "v"(bq[cur][0]), "v"(bq[cur][1]), "v"(bq[cur][2]), "v"(bq[cur][3]),
-            "v"(sq[cur][0]), "v"(sq[cur][1]), "v"(sq[cur][2]), "v"(sq[cur][3]));
+            : "v"(a6[0][0]), "v"(a6[0][1]), "v"(a6[0][2]), "v"(a6[1][0]), "v"(a6[1][1]), "v"(a6[1][2]),
+              "v"(as[0][0]), "v"(as[0][1]), "v"(as[0][2]), "v"(as[1][0]), "v"(as[1][1]), "v"(as[1][2]),
+              "v"(bq[cur][0]), "v"(bq[cur][1]), "v"(bq[cur][2]), "v"(bq[cur][3]),
+              "v"(sq[cur][0]), "v"(sq[cur][1]), "v"(sq[cur][2]), "v"(sq[cur][3]));
+        }
+      } else {
+        if constexpr (jg + 1 < NCB / 4) {
+          constexpr int k0 = 4 * (jg + 1);
+          asm volatile(
+            "s_nop 4\n\t"
+          "ds_read_b128 %8, %28 offset:%30\n\t"
+          "ds_read_b128 %9, %28 offset:%31\n\t"
+          "ds_read_b128 %10, %28 offset:%32\n\t"
+          "ds_read_b128 %11, %28 offset:%33\n\t"
+          "ds_read_u8 %12, %29 offset:%34\n\t"
+          "ds_read_u8 %13, %29 offset:%35\n\t"
+          "ds_read_u8 %14, %29 offset:%36\n\t"
+          "ds_read_u8 %15, %29 offset:%37\n\t"
+          "s_setprio 1\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %16, %20, %0, %18, %24 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %17, %20, %1, %19, %24 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %16, %21, %2, %18, %25 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %17, %21, %3, %19, %25 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %4, %16, %22, %4, %18, %26 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %5, %17, %22, %5, %19, %26 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %16, %23, %6, %18, %27 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %17, %23, %7, %19, %27 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "s_setprio 0\n\t"
+          "s_waitcnt lgkmcnt(0)"
+            : "+v"(acc[0][4 * jg]), "+v"(acc[1][4 * jg]), "+v"(acc[0][4 * jg + 1]), "+v"(acc[1][4 * jg + 1]),
+            "+v"(acc[0][4 * jg + 2]), "+v"(acc[1][4 * jg + 2]), "+v"(acc[0][4 * jg + 3]), "+v"(acc[1][4 * jg + 3]),
+              "=&v"(bq[nxt][0]), "=&v"(bq[nxt][1]), "=&v"(bq[nxt][2]), "=&v"(bq[nxt][3]),
+              "=&v"(sq[nxt][0]), "=&v"(sq[nxt][1]), "=&v"(sq[nxt][2]), "=&v"(sq[nxt][3])
+            : "v"(a6[0][0]), "v"(a6[1][0]),
+              "v"(as[0][0]), "v"(as[1][0]),
+              "v"(bq[cur][0]), "v"(bq[cur][1]), "v"(bq[cur][2]), "v"(bq[cur][3]),
+              "v"(sq[cur][0]), "v"(sq[cur][1]), "v"(sq[cur][2]), "v"(sq[cur][3]), "v"(bb), "v"(sb),
+              "i"(64 * jrow(std::integral_constant<int, k0>{})), "i"(64 * jrow(std::integral_constant<int, k0 + 1>{})),
+              "i"(64 * jrow(std::integral_constant<int, k0 + 2>{})), "i"(64 * jrow(std::integral_constant<int, k0 + 3>{})),
+              "i"(8 * jrow(std::integral_constant<int, k0>{})), "i"(8 * jrow(std::integral_constant<int, k0 + 1>{})),
+              "i"(8 * jrow(std::integral_constant<int, k0 + 2>{})), "i"(8 * jrow(std::integral_constant<int, k0 + 3>{})));
+        } else {
+          asm volatile(
+            "s_nop 4\n\t"
+          "s_setprio 1\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %8, %12, %0, %10, %16 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %9, %12, %1, %11, %16 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %8, %13, %2, %10, %17 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %9, %13, %3, %11, %17 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %4, %8, %14, %4, %10, %18 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %5, %9, %14, %5, %11, %18 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %8, %15, %6, %10, %19 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %9, %15, %7, %11, %19 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "s_setprio 0"
+            : "+v"(acc[0][4 * jg]), "+v"(acc[1][4 * jg]), "+v"(acc[0][4 * jg + 1]), "+v"(acc[1][4 * jg + 1]),
+            "+v"(acc[0][4 * jg + 2]), "+v"(acc[1][4 * jg + 2]), "+v"(acc[0][4 * jg + 3]), "+v"(acc[1][4 * jg + 3])
+            : "v"(a6[0][0]), "v"(a6[1][0]),
+              "v"(as[0][0]), "v"(as[1][0]),
+              "v"(bq[cur][0]), "v"(bq[cur][1]), "v"(bq[cur][2]), "v"(bq[cur][3]),
+              "v"(sq[cur][0]), "v"(sq[cur][1]), "v"(sq[cur][2]), "v"(sq[cur][3]));
+        }
       }
     });
   }
@@ -1243,6 +1358,7 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
     pf_epilogue_gateup<NCB>(p, acc, bias, rows_w, row_base_w, wcol0, lane, scratch);
   else
     pf_epilogue_down<NCB>(p, acc, bias, rows_w, row_base_w, wcol0, lane, scratch);
+#endif
 }
 
 static bool prefill_offsets_fit(const GemmParams& p) {
@@ -1253,29 +1369,50 @@ static bool prefill_offsets_fit(const GemmParams& p) {
 }
 
 // Decode kernel instance for the phase count of K (unrolled up to 8 phases).
-template <bool GATEUP, bool U16>
+template <bool GATEUP, bool U16, int TERMS>
 static void launch_decode_u(const GemmParams& p, unsigned grid, int spans, hipStream_t s) {
   const int nph = (p.K / 32 + DEC_KPH - 1) / DEC_KPH;
   const dim3 g(grid), b(DEC_NW * 64);
   switch (nph) {
-    case 1: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 1, U16>), g, b, 0, s, p, spans); break;
-    case 2: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 2, U16>), g, b, 0, s, p, spans); break;
-    case 3: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 3, U16>), g, b, 0, s, p, spans); break;
-    case 4: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 4, U16>), g, b, 0, s, p, spans); break;
-    case 5: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 5, U16>), g, b, 0, s, p, spans); break;
-    case 6: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 6, U16>), g, b, 0, s, p, spans); break;
-    case 7: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 7, U16>), g, b, 0, s, p, spans); break;
-    case 8: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 8, U16>), g, b, 0, s, p, spans); break;
-    default: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 0, U16>), g, b, 0, s, p, spans); break;
+    case 1: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 1, U16, TERMS>), g, b, 0, s, p, spans); break;
+    case 2: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 2, U16, TERMS>), g, b, 0, s, p, spans); break;
+    case 3: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 3, U16, TERMS>), g, b, 0, s, p, spans); break;
+    case 4: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 4, U16, TERMS>), g, b, 0, s, p, spans); break;
+    case 5: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 5, U16, TERMS>), g, b, 0, s, p, spans); break;
+    case 6: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 6, U16, TERMS>), g, b, 0, s, p, spans); break;
+    case 7: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 7, U16, TERMS>), g, b, 0, s, p, spans); break;
+    case 8: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 8, U16, TERMS>), g, b, 0, s, p, spans); break;
+    default: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 0, U16, TERMS>), g, b, 0, s, p, spans); break;
   }
 }
 
-template <bool GATEUP>
+template <bool GATEUP, int TERMS>
 static void launch_decode(const GemmParams& p, unsigned items, int spans, hipStream_t s) {
   if ((p.K / 32) % 2 == 0)
-    launch_decode_u<GATEUP, true>(p, items, spans, s);
+    launch_decode_u<GATEUP, true, TERMS>(p, items, spans, s);
   else
-    launch_decode_u<GATEUP, false>(p, items, spans, s);
+    launch_decode_u<GATEUP, false, TERMS>(p, items, spans, s);
+}
+
+template <bool GATEUP, int TERMS>
+static int launch_gemm(const GemmParams& p, int max_tiles, int mode, hipStream_t s) {
+  const int n_out = GATEUP ? p.I : p.N;  // output columns
+  if (mode == GEMM_DECODE) {
+    const int spans = GATEUP ? (n_out + 31) / 32 : (n_out + 63) / 64;
+    launch_decode<GATEUP, TERMS>(p, (unsigned)((long long)max_tiles * spans), spans, s);
+  } else {
+    if (!prefill_offsets_fit(p)) return -1;
+    const bool wide = mode == GEMM_WIDE;
+    const int span_cols = wide ? (GATEUP ? PW_NT / 2 : PW_NT) : (GATEUP ? PF_NT / 2 : PF_NT);
+    const int spans = (n_out + span_cols - 1) / span_cols;
+    const long long items = (long long)max_tiles * spans;
+    const dim3 g((unsigned)((items + PF_XCD - 1) / PF_XCD * PF_XCD));
+    if (wide)
+      hipLaunchKernelGGL((expert_gemm_prefill_wide<GATEUP, TERMS>), g, dim3(PW_NW * 64), 0, s, p, spans);
+    else
+      hipLaunchKernelGGL((expert_gemm_prefill<GATEUP, TERMS>), g, dim3(PF_NW * 64), 0, s, p, spans);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 // Launch configurations.
@@ -1285,40 +1422,17 @@ static void launch_decode(const GemmParams& p, unsigned items, int spans, hipStr
 //     work item, 1-D grid dealt to the XCDs in contiguous ranges;
 //   wide (prefill with enough rows per expert and even K/32 for both
 //     projections): one workgroup per (128-row tile, 512-column span).
+// p.terms: 3 (the exact path) or 1 (the activation-quantised fast mode).
 int launch_gemm_gateup(const GemmParams& p, int max_tiles, int mode, hipStream_t s) {
-  if (mode == GEMM_DECODE) {
-    const int spans = (p.I + 31) / 32;
-    launch_decode<true>(p, (unsigned)((long long)max_tiles * spans), spans, s);
-  } else {
-    if (!prefill_offsets_fit(p)) return -1;
-    const bool wide = mode == GEMM_WIDE;
-    const int spans = wide ? (p.I + PW_NT / 2 - 1) / (PW_NT / 2) : (p.I + PF_NT / 2 - 1) / (PF_NT / 2);
-    const long long items = (long long)max_tiles * spans;
-    const dim3 g((unsigned)((items + PF_XCD - 1) / PF_XCD * PF_XCD));
-    if (wide)
-      hipLaunchKernelGGL((expert_gemm_prefill_wide<true>), g, dim3(PW_NW * 64), 0, s, p, spans);
-    else
-      hipLaunchKernelGGL((expert_gemm_prefill<true>), g, dim3(PF_NW * 64), 0, s, p, spans);
-  }
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  if (p.terms == 1) return launch_gemm<true, 1>(p, max_tiles, mode, s);
+  if (p.terms == 3) return launch_gemm<true, 3>(p, max_tiles, mode, s);
+  return -1;
 }
 
 int launch_gemm_down(const GemmParams& p, int max_tiles, int mode, hipStream_t s) {
-  if (mode == GEMM_DECODE) {
-    const int spans = (p.N + 63) / 64;
-    launch_decode<false>(p, (unsigned)((long long)max_tiles * spans), spans, s);
-  } else {
-    if (!prefill_offsets_fit(p)) return -1;
-    const bool wide = mode == GEMM_WIDE;
-    const int spans = wide ? (p.N + PW_NT - 1) / PW_NT : (p.N + PF_NT - 1) / PF_NT;
-    const long long items = (long long)max_tiles * spans;
-    const dim3 g((unsigned)((items + PF_XCD - 1) / PF_XCD * PF_XCD));
-    if (wide)
-      hipLaunchKernelGGL((expert_gemm_prefill_wide<false>), g, dim3(PW_NW * 64), 0, s, p, spans);
-    else
-      hipLaunchKernelGGL((expert_gemm_prefill<false>), g, dim3(PF_NW * 64), 0, s, p, spans);
-  }
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  if (p.terms == 1) return launch_gemm<false, 1>(p, max_tiles, mode, s);
+  if (p.terms == 3) return launch_gemm<false, 3>(p, max_tiles, mode, s);
+  return -1;
 }
 
 }  // namespace moe

@@ -43,6 +43,7 @@ struct GemmParams {
   float clamp;
   uint8_t* hq;               // gate/up output: MX6x3 rows [P, I/32, 80]
   float* y;                  // down output: fp32 [P, N]
+  int terms;                 // FP6 terms of A taking part: 3 (exact path) or 1 (fast mode)
 };
 
 struct CombineParams {
