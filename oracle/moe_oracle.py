@@ -139,6 +139,18 @@ def clamped_swiglu(g: np.ndarray, u: np.ndarray, clamp: float) -> np.ndarray:
     return gc * sigmoid(gc) * (uc + 1.0)
 
 
+ALT_SWISH_SLOPE = 1.702
+
+
+def clamped_swiglu_alt(g: np.ndarray, u: np.ndarray, clamp: float) -> np.ndarray:
+    """The alternative activation reading (the variant layout's): Swish with
+    slope 1.702, v * sigmoid(1.702 v), on the gate clamped from above only,
+    times the symmetrically clamped up branch plus one."""
+    gc = np.minimum(g, clamp)
+    uc = np.clip(u, -clamp, clamp)
+    return gc * sigmoid(ALT_SWISH_SLOPE * gc) * (uc + 1.0)
+
+
 def e2m3_round(v: np.ndarray) -> np.ndarray:
     """Nearest FP6 E2M3 value (ties to the even code) of |v| <= 7.5: sign,
     two exponent bits (bias 1), three mantissa bits; the subnormals are
@@ -180,16 +192,21 @@ def mxfp6_quantize(v: np.ndarray) -> np.ndarray:
 
 
 def expert_ffn(xs: np.ndarray, w13: np.ndarray, b13: np.ndarray,
-               w2: np.ndarray, b2: np.ndarray, clamp: float, act_quant=None) -> np.ndarray:
+               w2: np.ndarray, b2: np.ndarray, clamp: float, act_quant=None, alt: bool = False) -> np.ndarray:
     """One expert on rows xs [n, d] with dequantised weights: the three
     linear maps of the GLU ([C]): a = xs W13^T + b13, gate = a[:, :I],
     up = a[:, I:], z = h W2^T + b2.  act_quant (fast mode only) is applied
-    to the rows entering each expert GEMM (xs and h)."""
+    to the rows entering each expert GEMM (xs and h).  alt: the variant
+    layout and activation -- gate and up rows interleaved (gate of column i
+    in row 2i, up in row 2i + 1, b13 likewise) and clamped_swiglu_alt."""
     I = w13.shape[0] // 2
     if act_quant is not None:
         xs = act_quant(xs)
     a = xs @ w13.T + b13[None, :]
-    h = clamped_swiglu(a[:, :I], a[:, I:], clamp)
+    if alt:
+        h = clamped_swiglu_alt(a[:, 0::2], a[:, 1::2], clamp)
+    else:
+        h = clamped_swiglu(a[:, :I], a[:, I:], clamp)
     if act_quant is not None:
         h = act_quant(h)
     return h @ w2.T + b2[None, :]
@@ -227,13 +244,14 @@ def route(x_bits: np.ndarray, router_w_bits: np.ndarray, router_b: np.ndarray, k
 
 def moe_layer(x_bits: np.ndarray, router_w_bits: np.ndarray, router_b: np.ndarray,
               experts: dict, k: int, clamp: float, cache: DequantCache | None = None,
-              act: str = "exact"):
+              act: str = "exact", alt: bool = False):
     """Sparse MoE layer: y[t] = sum_j w[t,j] * FFN_{S_t[j]}(x[t]).
 
     Each expert runs only on the tokens routed to it ([B] 2.4.1).  Returns a
     dict with y (float64 [T, d]), logits, ids, w and per-expert counts.
     act = "mxfp6": the activation-quantised fast mode (x and h rounded to
     MXFP6 before the expert GEMMs, mxfp6_quantize); the router always sees x.
+    alt: the variant weight layout and activation of expert_ffn.
     """
     if act not in ("exact", "mxfp6"):
         raise ValueError(act)
@@ -251,8 +269,8 @@ def moe_layer(x_bits: np.ndarray, router_w_bits: np.ndarray, router_b: np.ndarra
         if tok.size == 0:
             continue
         w13, b13, w2, b2 = cache(e)
-        z = (expert_ffn(x[tok], w13, b13, w2, b2, clamp) if aq is None
-             else expert_ffn(x[tok], w13, b13, w2, b2, clamp, aq))
+        z = (expert_ffn(x[tok], w13, b13, w2, b2, clamp) if aq is None and not alt
+             else expert_ffn(x[tok], w13, b13, w2, b2, clamp, aq, alt))
         y[tok] += w[tok, slot][:, None] * z
     return dict(y=y, logits=logits, ids=ids, w=w, counts=counts)
 
