@@ -121,6 +121,30 @@ int moe_layer_forward_mx6_dbg(const void* x, const void* router_w, const float* 
                               int T, int d, int I, int E, int k, float clamp, void* out, float* out_f32,
                               int32_t* topk_id, float* topk_w, int32_t* counts, void* stream);
 
+/* Flags of moe_layer_forward_ex. */
+enum moe_layer_flags {
+  /* the activation-quantised fast mode of moe_layer_forward_mx6 */
+  MOE_LAYER_MXFP6 = 1,
+  /* the variant activation reading: h = g' * sigmoid(1.702 g') * (u' + 1)
+   * with g' = min(g, clamp) (the gate clamped from above only) and
+   * u' = clamp(u, -clamp, clamp); and the variant weight layout of
+   * w13_codes / w13_scales / b13: gate and up rows interleaved, row 2i the
+   * gate of output column i and row 2i+1 its up (b13 likewise).  The pages
+   * give Swish with unit slope and a clamp without its placement
+   * ("OpenAI 最新开源模型 gpt-oss 架构与训练解析", MoE item and Swish/SwiGLU
+   * 替换 GELU); this flag selects the other reading of both. */
+  MOE_LAYER_ALT_ACT = 2
+};
+
+/* moe_layer_forward with flags (any OR of moe_layer_flags; unknown bits give
+ * MOE_ERR_BAD_SHAPE).  topk_id, topk_w and counts are all null or all set
+ * (as in moe_layer_forward_dbg); out_f32 may be set only with them. */
+int moe_layer_forward_ex(const void* x, const void* router_w, const float* router_b,
+                         const uint8_t* w13_codes, const uint8_t* w13_scales, const float* b13,
+                         const uint8_t* w2_codes, const uint8_t* w2_scales, const float* b2,
+                         int T, int d, int I, int E, int k, float clamp, int flags, void* out,
+                         float* out_f32, int32_t* topk_id, float* topk_w, int32_t* counts, void* stream);
+
 /* Router, top-k and selected softmax only ("【LLM】GPT-OSS架构变化详解",
  * 2.4.1; "OpenAI 最新开源模型 gpt-oss 架构与训练解析", MoE item).  Outputs as
  * in moe_layer_forward_dbg. */

@@ -15,7 +15,11 @@ __all__ = [
     "moe_workspace_bytes", "moe_workspace_init", "moe_layer_forward_ws", "moe_rmsnorm",
     "moe_stack_forward", "moe_release", "moe_status_string", "moe_version", "LIB_PATH",
     "moe_timing_enable", "moe_timing_read", "KERNELS", "moe_layer_forward_mx6", "moe_layer_forward_mx6_dbg",
+    "moe_layer_forward_ex", "MOE_LAYER_MXFP6", "MOE_LAYER_ALT_ACT",
 ]
+
+MOE_LAYER_MXFP6 = 1
+MOE_LAYER_ALT_ACT = 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 _lib = None
@@ -28,6 +32,7 @@ _SIGS = {
     "moe_layer_forward_dbg": (_I, [_P] * 9 + [_I] * 5 + [_F] + [_P] * 6),
     "moe_layer_forward_mx6": (_I, [_P] * 9 + [_I] * 5 + [_F, _P, _P]),
     "moe_layer_forward_mx6_dbg": (_I, [_P] * 9 + [_I] * 5 + [_F] + [_P] * 6),
+    "moe_layer_forward_ex": (_I, [_P] * 9 + [_I] * 5 + [_F, _I] + [_P] * 6),
     "moe_route": (_I, [_P] * 3 + [_I] * 4 + [_P] * 4),
     "moe_workspace_bytes": (ctypes.c_size_t, [_I] * 5),
     "moe_workspace_init": (_I, [_P, ctypes.c_size_t, _P]),
@@ -193,6 +198,31 @@ def moe_layer_forward_dbg(x, router_w, router_b, w13_codes, w13_scales, b13, w2_
         _check(ids, "ids", torch.int32), _check(w, "w", torch.float32), _check(counts, "counts", torch.int32),
         _stream(stream)))
     return out, out_f32, ids, w, counts
+
+
+def moe_layer_forward_ex(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
+                         k: int = 4, clamp: float = 7.0, flags: int = 0, debug: bool = False, out=None,
+                         stream=None):
+    """moe_layer_forward with flags (MOE_LAYER_MXFP6, MOE_LAYER_ALT_ACT).
+    debug=False: returns out; debug=True: (out, out_f32, topk_id, topk_w, counts)."""
+    torch = _torch()
+    ptrs, T, d, I, E = _layer_ptrs(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2)
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    po = _check(out, "out", torch.bfloat16, (T, d))
+    if debug:
+        out_f32 = torch.empty((T, d), dtype=torch.float32, device=dev)
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        counts = torch.empty((E,), dtype=torch.int32, device=dev)
+        extra = [_check(out_f32, "out_f32", torch.float32), _check(ids, "ids", torch.int32),
+                 _check(w, "w", torch.float32), _check(counts, "counts", torch.int32)]
+    else:
+        extra = [None, None, None, None]
+    _ok("moe_layer_forward_ex", lib().moe_layer_forward_ex(*ptrs, T, d, I, E, k, clamp, flags, po, *extra,
+                                                           _stream(stream)))
+    return (out, out_f32, ids, w, counts) if debug else out
 
 
 def moe_route(x, router_w, router_b, k: int = 4, stream=None):

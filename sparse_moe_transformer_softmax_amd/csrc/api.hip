@@ -90,6 +90,7 @@ struct LayerArgs {
   const uint8_t* w2c; const uint8_t* w2s; const float* b2;
   int T, d, I, E, k; float clamp;
   int terms = 3;  // FP6 terms of the expert GEMMs' activations: 3 (exact path) or 1 (fast mode)
+  int alt = 0;    // 1: the variant gate/up layout and activation
 };
 
 int check_layer(const LayerArgs& a, const void* out) {
@@ -232,6 +233,7 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   gp.N = 2 * a.I; gp.K = a.d; gp.I = a.I; gp.E = a.E;
   gp.clamp = a.clamp;
   gp.terms = a.terms;
+  gp.alt = a.alt;
   gp.hq = ws + L.hq;
   gp.y = nullptr;
   {
@@ -244,6 +246,7 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   gp.N = a.d; gp.K = a.I;
   gp.hq = nullptr;
   gp.y = (float*)(ws + L.y);
+  gp.alt = 0;  // (the down projection has no gate/up rows)
   {
     Timed tm(2, s);
     if (launch_gemm_down(gp, max_tiles, mode, s)) return MOE_ERR_HIP;
@@ -358,6 +361,22 @@ int moe_layer_forward_dbg(const void* x, const void* router_w, const float* rout
                           float clamp, void* out, float* out_f32, int32_t* topk_id, float* topk_w,
                           int32_t* counts, void* stream) {
   LayerArgs a{x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, d, I, E, k, clamp};
+  return forward_dbg(a, out, out_f32, topk_id, topk_w, counts, stream);
+}
+
+int moe_layer_forward_ex(const void* x, const void* router_w, const float* router_b, const uint8_t* w13_codes,
+                         const uint8_t* w13_scales, const float* b13, const uint8_t* w2_codes,
+                         const uint8_t* w2_scales, const float* b2, int T, int d, int I, int E, int k, float clamp,
+                         int flags, void* out, float* out_f32, int32_t* topk_id, float* topk_w, int32_t* counts,
+                         void* stream) {
+  if (flags & ~(MOE_LAYER_MXFP6 | MOE_LAYER_ALT_ACT)) return MOE_ERR_BAD_SHAPE;
+  LayerArgs a{x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, d, I, E, k, clamp};
+  a.terms = (flags & MOE_LAYER_MXFP6) ? 1 : 3;
+  a.alt = (flags & MOE_LAYER_ALT_ACT) ? 1 : 0;
+  const bool any = topk_id || topk_w || counts, all = topk_id && topk_w && counts;
+  if (any && !all) return MOE_ERR_NULL_PTR;
+  if (!all && !out_f32) return forward_owned(a, out, stream);
+  if (!all) return MOE_ERR_NULL_PTR;  // (the fp32 output comes with the routing outputs)
   return forward_dbg(a, out, out_f32, topk_id, topk_w, counts, stream);
 }
 

@@ -55,6 +55,24 @@ __device__ __forceinline__ float clamped_swiglu(float g, float u, float c) {
   return gc * __builtin_amdgcn_rcpf(1.0f + e) * (uc + 1.0f);
 }
 
+// The variant activation reading: Swish with slope 1.702 on the gate
+// clamped from above only, times the symmetrically clamped up plus one.
+__device__ __forceinline__ float clamped_swiglu_alt(float g, float u, float c) {
+  const float gc = (g != g) ? g : fminf(g, c);
+  const float uc = (u != u) ? u : fminf(fmaxf(u, -c), c);
+  const float e = __builtin_amdgcn_exp2f(-gc * (1.702f * 1.44269504088896341f));
+  return gc * __builtin_amdgcn_rcpf(1.0f + e) * (uc + 1.0f);
+}
+
+__device__ __forceinline__ float swiglu_act(float g, float u, float c, int alt) {
+  return alt ? clamped_swiglu_alt(g, u, c) : clamped_swiglu(g, u, c);
+}
+
+// Row of the fused gate/up weight (and index of its bias) that holds output
+// column c of the gate (up = 0) or up (up = 1) projection: gate rows then up
+// rows, or (the variant layout) interleaved, gate of column c in row 2c.
+__device__ __forceinline__ int gu_row(int c, int up, int I, int alt) { return alt ? 2 * c + up : up * I + c; }
+
 template <int MB, int NCB>
 struct Stage {
   uint4 a[MB][5];  // MX6x3 block of each 16-row block (3 x 24 B codes, 3 scale bytes)
@@ -216,6 +234,7 @@ struct DecItem {
   __amdgpu_buffer_rsrc_t crsrc;     // this wave's 16 weight rows: codes
   __amdgpu_buffer_rsrc_t srsrc;     //   and scales
   int a_off;                        // this lane's A row offset, or past the A resource
+  int rs;                           // weight rows between consecutive columns of a block (1, or 2 interleaved)
   float bias[4];                    // this lane's epilogue bias values (gate/up: gate and up of
                                     // columns col0 + r and col0 + 16 + r; down: column col0 + 16j + r)
 };
@@ -248,7 +267,8 @@ __device__ __forceinline__ void dec_load_item(const GemmParams& p, int item, int
   // first weight row of this wave's column block (a missing block copies
   // block 0); its 16 rows are consecutive weight rows
   const int cbv = ((ok >> wave) & 1) ? wave : 0;
-  const int n = GATEUP ? (cbv < 2 ? 0 : I) + it.col0 + 16 * (cbv & 1) : it.col0 + 16 * cbv;
+  const int n = GATEUP ? gu_row(it.col0 + 16 * (cbv & 1), cbv >= 2, I, p.alt) : it.col0 + 16 * cbv;
+  it.rs = (GATEUP && p.alt) ? 2 : 1;
   const size_t my_row = (size_t)e * N + n;
   // resources end at the end of the arrays, so that copies past the last
   // row return zeros instead of reading past the allocation
@@ -277,10 +297,10 @@ __device__ __forceinline__ void dec_load_item(const GemmParams& p, int item, int
   const float* bias = p.bias + (size_t)e * N;
   if (GATEUP) {
     const int c0 = min(it.col0 + r, I - 1), c1 = min(it.col0 + 16 + r, I - 1);
-    it.bias[0] = bias[c0];
-    it.bias[1] = bias[I + c0];
-    it.bias[2] = bias[c1];
-    it.bias[3] = bias[I + c1];
+    it.bias[0] = bias[gu_row(c0, 0, I, p.alt)];
+    it.bias[1] = bias[gu_row(c0, 1, I, p.alt)];
+    it.bias[2] = bias[gu_row(c1, 0, I, p.alt)];
+    it.bias[3] = bias[gu_row(c1, 1, I, p.alt)];
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) it.bias[j] = bias[min(it.col0 + 16 * j + r, N - 1)];
@@ -295,6 +315,7 @@ __device__ __forceinline__ void dec_null_item(const GemmParams& p, DecItem& it) 
   it.crsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.b_codes, 0, 0, 0x00020000);
   it.srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.b_scales, 0, 0, 0x00020000);
   it.a_off = 0x7ffffff0;
+  it.rs = 1;
   it.bias[0] = it.bias[1] = it.bias[2] = it.bias[3] = 0.f;
 }
 
@@ -350,10 +371,10 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
       const int b = min(slot ^ rr, npb - 1);       // logical block stored at `slot`
       const int row_off = (wave * 16 + 4 * q) * DEC_KPH;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(it.crsrc, (lds_void_t*)(s_code[buf] + row_off * 16), 16,
-                                               rr * (K >> 1) + b * 16, pb0 * 16, 0, 0);
+                                               rr * it.rs * (K >> 1) + b * 16, pb0 * 16, 0, 0);
       if constexpr (!U16)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(it.srsrc, (lds_void_t*)(s_scl[buf] + row_off), 1,
-                                                 rr * nblk + min(slot, npb - 1), pb0, 0, 0);
+                                                 rr * it.rs * nblk + min(slot, npb - 1), pb0, 0, 0);
     }
     if constexpr (U16) {
       // instruction q moves rows 8q .. 8q+7; lane L holds the block pair
@@ -366,7 +387,7 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
         const int uc = 2 * u < npb ? u : 0;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(it.srsrc,
                                                  (lds_void_t*)(s_scl[buf] + (wave * 16 + 8 * q) * Cfg::SROW), 2,
-                                                 rr * nblk + 2 * uc, pb0, 0, 0);
+                                                 rr * it.rs * nblk + 2 * uc, pb0, 0, 0);
       }
     }
     // block pb0 + 4w + g of the phase (blocks past K read the last block;
@@ -466,8 +487,8 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
       return;
     }
     // (columns past I are never stored)
-    const float h0 = clamped_swiglu(v[0] + it.bias[0], v[2] + it.bias[1], p.clamp);
-    const float h1 = clamped_swiglu(v[1] + it.bias[2], v[3] + it.bias[3], p.clamp);
+    const float h0 = swiglu_act(v[0] + it.bias[0], v[2] + it.bias[1], p.clamp, p.alt);
+    const float h1 = swiglu_act(v[1] + it.bias[2], v[3] + it.bias[3], p.clamp, p.alt);
     const uint32_t scw = split_h_row(h0, h1, r, s_codes[row]);
     if (r == 0) s_sc[row] = scw;
     lds_wave_sync();
@@ -612,7 +633,7 @@ __device__ __forceinline__ void pf_epilogue_gateup(const GemmParams& p, const v4
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         sh_h[(4 * g + q) * HS + 32 * (j >> 1) + 8 * (j & 1) + cpos] =
-            clamped_swiglu(acc[mb][j][q] + bias[j], acc[mb][HALF + j][q] + bias[HALF + j], p.clamp);
+            swiglu_act(acc[mb][j][q] + bias[j], acc[mb][HALF + j][q] + bias[HALF + j], p.clamp, p.alt);
     lds_wave_sync();
     if (srow < 16) {
       const float* src = sh_h + srow * HS + 32 * sblk;
@@ -724,7 +745,7 @@ __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams 
   for (int n = tid; n < PF_NT; n += PF_NW * 64) {
     if (GATEUP) {
       const int c = min(tcol0 + (n % (PF_NT / 2)), I - 1);
-      s_bias[n] = p.bias[(size_t)e * N + (n < PF_NT / 2 ? 0 : I) + c];
+      s_bias[n] = p.bias[(size_t)e * N + gu_row(c, n >= PF_NT / 2, I, p.alt)];
     } else {
       s_bias[n] = p.bias[(size_t)e * N + min(tcol0 + n, N - 1)];
     }
@@ -762,7 +783,7 @@ __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams 
     int row;
     if (GATEUP) {
       const int c = tcol0 + (n % (PF_NT / 2));
-      row = (n < PF_NT / 2 ? 0 : I) + (c < I ? c : tcol0 + (n & 15));
+      row = gu_row(c < I ? c : tcol0 + (n & 15), n >= PF_NT / 2, I, p.alt);
     } else {
       const int c = tcol0 + n;
       row = c < N ? c : tcol0 + (n & 15);
@@ -989,7 +1010,7 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
   auto weight_row = [&](int n) -> int {
     if (GATEUP) {
       const int c = tcol0 + (n % (PW_NT / 2));
-      return (n < PW_NT / 2 ? 0 : I) + (c < I ? c : tcol0 + (n & 15));
+      return gu_row(c < I ? c : tcol0 + (n & 15), n >= PW_NT / 2, I, p.alt);
     }
     const int c = tcol0 + n;
     return c < N ? c : tcol0 + (n & 15);
@@ -997,7 +1018,7 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
   for (int n = tid; n < PW_NT; n += PW_NW * 64) {
     if (GATEUP) {
       const int c = min(tcol0 + (n % (PW_NT / 2)), I - 1);
-      s_bias[n] = p.bias[(size_t)e * N + (n < PW_NT / 2 ? 0 : I) + c];
+      s_bias[n] = p.bias[(size_t)e * N + gu_row(c, n >= PW_NT / 2, I, p.alt)];
     } else {
       s_bias[n] = p.bias[(size_t)e * N + min(tcol0 + n, N - 1)];
     }

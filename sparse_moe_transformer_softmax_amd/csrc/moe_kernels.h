@@ -44,6 +44,8 @@ struct GemmParams {
   uint8_t* hq;               // gate/up output: MX6x3 rows [P, I/32, 80]
   float* y;                  // down output: fp32 [P, N]
   int terms;                 // FP6 terms of A taking part: 3 (exact path) or 1 (fast mode)
+  int alt;                   // gate/up only: 1 = the variant layout and activation (interleaved rows,
+                             // Swish slope 1.702, gate clamped from above only)
 };
 
 struct CombineParams {
