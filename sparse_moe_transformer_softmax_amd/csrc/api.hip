@@ -27,7 +27,7 @@ constexpr int kHeaderInts = kTbDone0 + CURSOR_STRIDE * ROUTE_MAX_SPLIT_BLOCKS;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t topk_id, topk_w, rel_pos, counts, offsets, n_tiles, tiles, expert_rows, part, xq, hq, y, total;
+  size_t topk_id, topk_w, rel_pos, counts, offsets, n_tiles, tiles, expert_rows, part, xq, hq, y, fold, pair_row, total;
   int max_tiles;
 };
 
@@ -50,6 +50,8 @@ Layout layout(int T, int d, int I, int E, int k) {
   L.xq = o; o = up(o + (size_t)T * mx6_row_bytes(d / 32));
   L.hq = o; o = up(o + P * mx6_row_bytes(I / 32));
   L.y = o; o = up(o + P * d * 4);
+  L.fold = o; o = up(o + (size_t)T * ((d + 63) / 64) * 4);
+  L.pair_row = o; o = up(o + P * 4);
   L.total = o;
   return L;
 }
@@ -215,6 +217,11 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   rp.offsets = (int*)(ws + L.offsets);
   rp.n_tiles = (int*)(ws + L.n_tiles);
   rp.tiles = (int2*)(ws + L.tiles);
+  // decode-sized single layers fold the combine into the down GEMM (the
+  // stack's combine also adds the residual and stays a kernel of its own)
+  const bool fold = small_m && !route_only && resid_out == nullptr && out != nullptr;
+  rp.fold_cnt = fold ? (int*)(ws + L.fold) : nullptr;
+  rp.n_fold = a.T * ((a.d + 63) / 64);
   {
     Timed tm(0, s);
     if (launch_route(rp, s)) return MOE_ERR_HIP;
@@ -236,6 +243,11 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   gp.alt = a.alt;
   gp.hq = ws + L.hq;
   gp.y = nullptr;
+  gp.fold_cnt = nullptr;
+  gp.pair_row = fold ? (int*)(ws + L.pair_row) : nullptr;
+  gp.topk_w = rp.topk_w;
+  gp.out = (uint16_t*)out;
+  gp.out_f32 = out_f32;
   {
     Timed tm(1, s);
     if (launch_gemm_gateup(gp, max_tiles, mode, s)) return MOE_ERR_HIP;
@@ -247,10 +259,13 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   gp.hq = nullptr;
   gp.y = (float*)(ws + L.y);
   gp.alt = 0;  // (the down projection has no gate/up rows)
+  gp.fold_cnt = rp.fold_cnt;
   {
     Timed tm(2, s);
     if (launch_gemm_down(gp, max_tiles, mode, s)) return MOE_ERR_HIP;
   }
+
+  if (fold) return MOE_OK;
 
   CombineParams cp;
   cp.y = gp.y;

@@ -229,7 +229,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Everything the decode kernel needs to know about one work item.
 struct DecItem {
-  int e, rows, row_base, col0;
+  int e, m0, rows, row_base, col0;
+  int pair;                         // lane r's row: its (token, slot) pair (row r < rows)
   int ok_mask;                      // bit j: column block j lies inside the output
   __amdgpu_buffer_rsrc_t crsrc;     // this wave's 16 weight rows: codes
   __amdgpu_buffer_rsrc_t srsrc;     //   and scales
@@ -252,6 +253,7 @@ __device__ __forceinline__ void dec_load_item(const GemmParams& p, int item, int
   cint_t* te = (cint_t*)p.tiles + 2 * (size_t)tile;
   const int e = te[0], m0 = te[1];
   it.e = e;
+  it.m0 = m0;
   it.rows = min(16, ((cint_t*)p.counts)[e] - m0);
   it.row_base = ((cint_t*)p.offsets)[e] + m0;
   int ok = 0;
@@ -288,7 +290,11 @@ __device__ __forceinline__ void dec_load_item(const GemmParams& p, int item, int
     int x = v[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) x = r == i ? v[i] : x;
+    it.pair = x;
     arow = x / p.k;
+  } else {
+    // (entries past the expert's rows are read but never used, as above)
+    it.pair = p.expert_rows[(size_t)e * p.T + m0 + r];
   }
   it.a_off = r < it.rows ? arow * mx6_row_bytes(nblk) : 0x7ffffff0;
   // the epilogue's bias, loaded now so that its latency hides under the
@@ -311,7 +317,7 @@ __device__ __forceinline__ void dec_load_item(const GemmParams& p, int item, int
 // without touching memory (issued after the last real phase so that every
 // step has the same shape).
 __device__ __forceinline__ void dec_null_item(const GemmParams& p, DecItem& it) {
-  it.e = 0; it.rows = 0; it.row_base = 0; it.col0 = 0; it.ok_mask = 0;
+  it.e = 0; it.m0 = 0; it.pair = 0; it.rows = 0; it.row_base = 0; it.col0 = 0; it.ok_mask = 0;
   it.crsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.b_codes, 0, 0, 0x00020000);
   it.srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.b_scales, 0, 0, 0x00020000);
   it.a_off = 0x7ffffff0;
@@ -478,11 +484,87 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
     const int row = 4 * g + wave;  // tile row of this lane's values
     const int col0 = it.col0, rows = it.rows, row_base = it.row_base;
     if (!GATEUP) {
+      const bool fold = p.fold_cnt != nullptr;
 #pragma unroll
       for (int j = 0; j < NCB; ++j) {
         if (!((it.ok_mask >> j) & 1)) continue;
         const int col = col0 + 16 * j + r;
-        if (row < rows) p.y[(size_t)(row_base + row) * N + col] = v[j] + it.bias[j];
+        if (row < rows) {
+          const size_t o = (size_t)(row_base + row) * N + col;
+          // (with the fold, stores that reach the device-coherent level:
+          // the token's last arrival, maybe on another XCD, reads them)
+          if (fold)
+            __hip_atomic_store(p.y + o, v[j] + it.bias[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else
+            p.y[o] = v[j] + it.bias[j];
+        }
+      }
+      if (!fold) return;
+      // The combine, folded in: once every wave's rows have landed, one lane
+      // per tile row counts its token in for this 64-column span; the
+      // arrival that completes a token's k rows sums them for the span, in
+      // slot order, exactly as the separate combine does (an fma per slot,
+      // one rounding to bf16).  The router launch cleared the counters.
+      // First the slots of the tile rows' tokens, one (row, slot) per thread
+      // of the first two waves: where each sits in y (the gate/up launch
+      // recorded it) and its weight, issued before the wait for the stores
+      // so that the two round trips overlap.
+      const int k = p.k, tok_r = it.pair / k;
+      int fpos = 0;
+      float fw = 0.f;
+      if (tid < 128) {
+        const int i = tid >> 3, j = tid & 7, ti = __shfl(tok_r, i);
+        if (i < rows && j < k) {
+          fpos = p.pair_row[ti * k + j];
+          fw = p.topk_w[ti * k + j];
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's rows are stored
+      // (staged in the split's buffers, unused by the down projection)
+      int* s_tok = (int*)s_sc;
+      int* s_pos = (int*)&s_codes[0][0][0];
+      float* s_w = (float*)s_pos + 128;
+      if (tid < 128) {
+        s_pos[tid] = fpos;
+        s_w[tid] = fw;
+      }
+      __syncthreads();
+      const int spans = (N + 63) >> 6, span = col0 >> 6;
+      if (wave == 0 && lane < 16) {
+        int t = -1;
+        if (lane < rows && atomicAdd(p.fold_cnt + (size_t)tok_r * spans + span, 1) == k - 1) t = tok_r;
+        s_tok[lane] = t;
+      }
+      __syncthreads();
+      // each wave sums tile rows wave, wave + 4, ... for the span's 64
+      // columns, one per lane; every y load of the wave is issued before
+      // the first sum
+      static_assert(NW * 4 == 16, "four tile rows per wave");
+      const int col = col0 + lane, colc = min(col, N - 1);
+      int tq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = wave + NW * q;
+        tq[q] = i < rows ? s_tok[i] : -1;
+      }
+      float yv[4][8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (tq[q] >= 0 && j < k)
+            yv[q][j] = __hip_atomic_load(p.y + (size_t)s_pos[(wave + NW * q) * 8 + j] * N + colc, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (tq[q] < 0 || col >= N) continue;
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j < k) acc = fmaf(s_w[(wave + NW * q) * 8 + j], yv[q][j], acc);
+        const size_t o = (size_t)tq[q] * N + col;
+        if (p.out_f32) p.out_f32[o] = acc;
+        p.out[o] = f32_to_bf16(acc);
       }
       return;
     }
@@ -528,6 +610,9 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
   DecItem cur, nul;
   dec_load_item<GATEUP>(p, item, spans, wave, r, cur);
   dec_null_item(p, nul);
+  // for the down projection's folded combine: where each pair's row sits
+  if (GATEUP && p.pair_row != nullptr && cur.col0 == 0 && wave == 0 && lane < cur.rows)
+    p.pair_row[cur.pair] = cur.row_base + lane;
 #pragma unroll
   for (int j = 0; j < NCB; ++j) acc[0][j] = (v4f){0.f, 0.f, 0.f, 0.f};
   uint4 av0[5], av1[5];

@@ -26,6 +26,8 @@ struct RouteParams {
   float* part;               // [ROUTE_MAX_SPLIT_BLOCKS * 16][E] partial logits
   int* tb_done;              // [ROUTE_MAX_SPLIT_BLOCKS * CURSOR_STRIDE] zero between calls
   uint8_t* xq;               // MX6x3 rows of x [T, d/32, 80], or null (no split)
+  int* fold_cnt;             // [n_fold] arrival counters of the combine folded into the down
+  int n_fold;                //   GEMM, zeroed by the trailing workgroups (null: no fold)
 };
 
 struct GemmParams {
@@ -46,6 +48,13 @@ struct GemmParams {
   int terms;                 // FP6 terms of A taking part: 3 (exact path) or 1 (fast mode)
   int alt;                   // gate/up only: 1 = the variant layout and activation (interleaved rows,
                              // Swish slope 1.702, gate clamped from above only)
+  // down, decode only: the combine folded into the epilogue (fold_cnt null: no fold)
+  int* fold_cnt;             // [T, ceil(N/64)] arrivals per (token, 64-column span), zero at launch
+  int* pair_row;             // [T, k] row of y holding each (token, slot) pair: written by the
+                             //   gate/up decode launch, read by the fold (null: no fold)
+  const float* topk_w;       // [T, k]
+  uint16_t* out;             // bf16 [T, N]
+  float* out_f32;            // fp32 [T, N] or null
 };
 
 struct CombineParams {

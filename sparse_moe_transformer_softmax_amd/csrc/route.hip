@@ -92,6 +92,10 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
   const int nrw = p.n_tb * p.ks;
   if ((int)blockIdx.x >= nrw) {
     const int u = ((int)blockIdx.x - nrw) * (RT_THREADS / 4) + (tid >> 2);
+    // (and clear the arrival counters of the down GEMM's folded combine)
+    if (p.fold_cnt)
+      for (int i = ((int)blockIdx.x - nrw) * RT_THREADS + tid; i < p.n_fold; i += ((int)gridDim.x - nrw) * RT_THREADS)
+        p.fold_cnt[i] = 0;
     split_block(p.x, p.xq, u, nblk, d, tid & 3, u < T * nblk);
     return;
   }

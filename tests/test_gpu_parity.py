@@ -299,3 +299,16 @@ def test_stack_against_oracle(torch):
     say(f"stack: excess/rms={ex:.3e} (beyond the rounding allowance); final-rounding-only excess/rms="
         f"{bf16_excess(g64, ref):.3e}")
     assert ex <= TOL
+
+
+def test_folded_combine_across_call_sizes(torch):
+    """Decode-sized calls sum each token's slots in the down GEMM, with
+    arrival counters that the router launch clears: calls of changing
+    sizes in a row (a token count larger than an earlier one, T = 1, a
+    count that leaves the last 64-column span ragged) each meet the bar."""
+    wl = Workload("fold", T=48, d=160, I=96, E=12, k=4, seed=0x5EED3000)
+    inp = make_inputs(wl)
+    for T in (48, 7, 48, 1, 30):
+        sub = dict(inp)
+        sub["x"] = inp["x"][:T]
+        run_and_check(torch, sub, wl.k, 7.0, label=f"fold T={T}")
