@@ -246,16 +246,14 @@ struct DecItem {
 // tile too, then picked per lane by a select ladder).
 typedef __attribute__((address_space(4))) const int cint_t;
 
+// The head of an item: what its weight copies need (the tile's expert e and
+// first row m0, already loaded, and the item's column span), so that the
+// first copies go out before the row list is read.
 template <bool GATEUP>
-__device__ __forceinline__ void dec_load_item(const GemmParams& p, int item, int spans, int wave, int r, DecItem& it) {
+__device__ __forceinline__ void dec_item_head(const GemmParams& p, int e, int m0, int span, int wave, DecItem& it) {
   const int K = p.K, N = p.N, I = p.I, nblk = K >> 5;
-  const int tile = item / spans, span = item - tile * spans;
-  cint_t* te = (cint_t*)p.tiles + 2 * (size_t)tile;
-  const int e = te[0], m0 = te[1];
   it.e = e;
   it.m0 = m0;
-  it.rows = min(16, ((cint_t*)p.counts)[e] - m0);
-  it.row_base = ((cint_t*)p.offsets)[e] + m0;
   int ok = 0;
   if (GATEUP) {
     it.col0 = span * 32;
@@ -279,6 +277,16 @@ __device__ __forceinline__ void dec_load_item(const GemmParams& p, int item, int
                                                (int)(rows_left * (size_t)(K >> 1)), 0x00020000);
   it.srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_scales + my_row * (size_t)nblk), 0,
                                                (int)(rows_left * (size_t)nblk), 0x00020000);
+}
+
+// The tail of an item: its rows (count, place in the grouped order, the
+// row list) and A offsets, and the epilogue's bias.
+template <bool GATEUP>
+__device__ __forceinline__ void dec_item_tail(const GemmParams& p, int r, DecItem& it) {
+  const int N = p.N, I = p.I, nblk = p.K >> 5;
+  const int e = it.e, m0 = it.m0;
+  it.rows = min(16, ((cint_t*)p.counts)[e] - m0);
+  it.row_base = ((cint_t*)p.offsets)[e] + m0;
   int arow = it.row_base + r;
   if (GATEUP) {
     // entries past the expert's T read on into the next expert's list or
@@ -335,9 +343,13 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
   // readfirstlane: the wave index is uniform, so the buffer resources and
   // LDS bases derived from it live in scalar registers
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int total = *p.n_tiles * spans;
-  int item = blockIdx.x;
-  if (item >= total) return;
+  // the item's tile entry is read together with the tile count (the list
+  // has room for every tile of the grid): one round trip for both
+  const int item = blockIdx.x, tile = item / spans, span = item - tile * spans;
+  const int n_tiles = *(cint_t*)p.n_tiles;
+  const int te_e = ((cint_t*)p.tiles)[2 * tile], te_m0 = ((cint_t*)p.tiles)[2 * tile + 1];
+  asm volatile("" ::"s"(n_tiles), "s"(te_e), "s"(te_m0));
+  if (item >= n_tiles * spans) return;
   const int K = p.K, N = p.N, I = p.I, nblk = K >> 5;
   const int g = lane >> 4, r = lane & 15;
   const int nph = (nblk + DEC_KPH - 1) / DEC_KPH;
@@ -364,12 +376,12 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
   // resource's end; every other access lies inside its row.
   // (with the phase count known, every phase but the last is full: its
   // offsets are then the same in every phase)
-  auto issue = [&](const DecItem& it, int ph, int buf, uint4 (&av)[5]) {
+  auto issue_b = [&](const DecItem& it, int ph, int buf) {
     // the lane offsets are recomputed at every issue (a few instructions)
     // rather than held in registers across the item loop
     int lane = lane_id;
     asm volatile("" : "+v"(lane));
-    const int sub = lane / DEC_KPH, slot = lane % DEC_KPH, g = lane >> 4;
+    const int sub = lane / DEC_KPH, slot = lane % DEC_KPH;
     const int pb0 = ph * DEC_KPH, npb = (NPH > 0 && ph < NPH - 1) ? DEC_KPH : min(DEC_KPH, nblk - pb0);
 #pragma unroll
     for (int q = 0; q < DEC_Q; ++q) {
@@ -396,6 +408,10 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
                                                  rr * it.rs * nblk + 2 * uc, pb0, 0, 0);
       }
     }
+  };
+  auto issue_a = [&](const DecItem& it, int ph, uint4 (&av)[5]) {
+    const int g = lane_id >> 4;
+    const int pb0 = ph * DEC_KPH, npb = (NPH > 0 && ph < NPH - 1) ? DEC_KPH : min(DEC_KPH, nblk - pb0);
     // block pb0 + 4w + g of the phase (blocks past K read the last block;
     // their products are masked off); piece q of the lanes g = 0..3 is one
     // 64-byte line of the piece-interleaved row
@@ -416,6 +432,10 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
     // be dead, or the compiler waits for the load before reusing it)
     const auto t3 = __builtin_amdgcn_raw_buffer_load_b96(arsrc, off + 256, aso, 0);
     av[4] = make_uint4(t3[0], t3[1], t3[2], 0u);
+  };
+  auto issue = [&](const DecItem& it, int ph, int buf, uint4 (&av)[5]) {
+    issue_b(it, ph, buf);
+    issue_a(it, ph, av);
   };
 
   v4f acc[1][NCB];
@@ -607,8 +627,12 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
   // A registers of consecutive phases are fixed and no copy of a load in
   // flight forces an early wait; the scheduling barrier keeps the consume's
   // register moves behind the wait.
+  // The first phase's weight copies go out as soon as the expert is known;
+  // the row list, the A offsets and the bias follow.
   DecItem cur, nul;
-  dec_load_item<GATEUP>(p, item, spans, wave, r, cur);
+  dec_item_head<GATEUP>(p, te_e, te_m0, span, wave, cur);
+  issue_b(cur, 0, 0);
+  dec_item_tail<GATEUP>(p, r, cur);
   dec_null_item(p, nul);
   // for the down projection's folded combine: where each pair's row sits
   if (GATEUP && p.pair_row != nullptr && cur.col0 == 0 && wave == 0 && lane < cur.rows)
@@ -616,7 +640,7 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
 #pragma unroll
   for (int j = 0; j < NCB; ++j) acc[0][j] = (v4f){0.f, 0.f, 0.f, 0.f};
   uint4 av0[5], av1[5];
-  issue(cur, 0, 0, av0);
+  issue_a(cur, 0, av0);
   // step of phase ph: copies of phase ph + 1 of `cur`, or (last phase) of
   // phase 0 of `nit`
   auto step = [&](int ph, int buf, bool last, const DecItem& nit, const uint4 (&avc)[5], uint4 (&avn)[5]) {
