@@ -1235,6 +1235,10 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
     __builtin_amdgcn_sched_barrier(0);
     if (c + 1 < nchunk) issue(c + 1, buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
+    // a wave whose 32 rows all lie past the tile's rows (the last tile of
+    // an expert) only copies and keeps the barriers: its SIMD's other wave
+    // then has the MFMA pipe and the LDS port to itself
+    if (32 * wm >= rows) continue;
     // A fragments (pieces 0..4 of block g of the lane's row in each row
     // block, zeros past K; the fast mode reads pieces 0, 1 and 4 only) and
     // the first group's B fragments, then the FP6 terms of A as 6-register
