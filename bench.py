@@ -253,7 +253,7 @@ def main():
     step_flops = 2.0 * P * 3 * wl.d * wl.I * layers_per_step
     gu_ms, gu_n = kt_live["gateup_gemm"]
     gu_us = gu_ms / max(gu_n, 1) * 1e3
-    decode_like = (P <= 16 * wl.E)
+    decode_like = (P <= 32 * wl.E)  # the decode kernels' regime
     gu_unit_bytes = mxfp4_bytes(2 * wl.I, wl.d) + 4 * 2 * wl.I
     if decode_like:
         achieved = (nsel_mean * gu_unit_bytes + x_bytes) / (gu_us * 1e-6)

@@ -40,6 +40,9 @@ WORKLOADS = {
     "tiny": Workload("tiny", T=16, d=128, I=128, E=8, k=4, seed=0x5EED0000),
     "20b_decode": Workload("20b_decode", T=32, d=2880, I=2880, E=32, k=4, seed=0x5EED0001),
     "20b_prefill": Workload("20b_prefill", T=4096, d=2880, I=2880, E=32, k=4, seed=0x5EED0002),
+    # a mid-sized batch (32 rows per expert on average: the largest batch
+    # the decode kernels take)
+    "20b_batch256": Workload("20b_batch256", T=256, d=2880, I=2880, E=32, k=4, seed=0x5EED0006),
     "120b_prefill_zipf": Workload("120b_prefill_zipf", T=8192, d=2880, I=2880, E=128, k=4,
                                   seed=0x5EED0003, routing="zipf"),
     "120b_stack36": Workload("120b_stack36", T=2048, d=2880, I=2880, E=128, k=4,

@@ -88,6 +88,13 @@ def test_decode_20b(torch):
     run_and_check(torch, inputs_for("20b_decode"), wl.k, wl.clamp, label="20b-decode")
 
 
+def test_batch256_20b_sampled(torch):
+    wl = WORKLOADS["20b_batch256"]
+    rng = np.random.default_rng(3)
+    sample = np.sort(rng.choice(wl.T, 40, replace=False))
+    run_and_check(torch, inputs_for("20b_batch256"), wl.k, wl.clamp, sample=sample, label="20b-batch256")
+
+
 def test_prefill_20b_sampled(torch):
     wl = WORKLOADS["20b_prefill"]
     rng = np.random.default_rng(7)
