@@ -198,7 +198,10 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   // projections copy their scale bytes in pairs (K/32 even)
   const bool wide = !small_m && (long long)P >= 64LL * a.E && (a.d / 32) % 2 == 0 && (a.I / 32) % 2 == 0;
   const int mode = small_m ? GEMM_DECODE : wide ? GEMM_WIDE : GEMM_PREFILL;
-  const int mt = small_m ? MT_SMALL : wide ? MT_WIDE : MT_LARGE;
+  // decode sizes above 16 rows per expert: 32-row tiles (two row blocks),
+  // which read an expert's weights once
+  const bool mb2 = small_m && (long long)P > 16LL * a.E;
+  const int mt = small_m ? (mb2 ? MT_SMALL2 : MT_SMALL) : wide ? MT_WIDE : MT_LARGE;
   const int max_tiles = max_tiles_for(P, a.E, mt);
   int* hdr = (int*)ws;
 
@@ -223,7 +226,7 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   rp.tiles = (int2*)(ws + L.tiles);
   // decode-sized single layers fold the combine into the down GEMM (the
   // stack's combine also adds the residual and stays a kernel of its own)
-  const bool fold = small_m && !route_only && resid_out == nullptr && out != nullptr;
+  const bool fold = small_m && !mb2 && !route_only && resid_out == nullptr && out != nullptr;
   rp.fold_cnt = fold ? (int*)(ws + L.fold) : nullptr;
   rp.n_fold = a.T * ((a.d + 63) / 64);
   {
@@ -248,6 +251,7 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   gp.hq = ws + L.hq;
   gp.y = nullptr;
   gp.fold_cnt = nullptr;
+  gp.mb = mb2 ? 2 : 1;
   gp.pair_row = fold ? (int*)(ws + L.pair_row) : nullptr;
   gp.topk_w = rp.topk_w;
   gp.out = (uint16_t*)out;

@@ -234,7 +234,7 @@ struct DecItem {
   int ok_mask;                      // bit j: column block j lies inside the output
   __amdgpu_buffer_rsrc_t crsrc;     // this wave's 16 weight rows: codes
   __amdgpu_buffer_rsrc_t srsrc;     //   and scales
-  int a_off;                        // this lane's A row offset, or past the A resource
+  int a_off[2];                     // this lane's A row offsets (rows r, r + 16), or past the A resource
   int rs;                           // weight rows between consecutive columns of a block (1, or 2 interleaved)
   float bias[4];                    // this lane's epilogue bias values (gate/up: gate and up of
                                     // columns col0 + r and col0 + 16 + r; down: column col0 + 16j + r)
@@ -281,30 +281,35 @@ __device__ __forceinline__ void dec_item_head(const GemmParams& p, int e, int m0
 
 // The tail of an item: its rows (count, place in the grouped order, the
 // row list) and A offsets, and the epilogue's bias.
-template <bool GATEUP>
+template <bool GATEUP, int MB>
 __device__ __forceinline__ void dec_item_tail(const GemmParams& p, int r, DecItem& it) {
   const int N = p.N, I = p.I, nblk = p.K >> 5;
   const int e = it.e, m0 = it.m0;
-  it.rows = min(16, ((cint_t*)p.counts)[e] - m0);
+  it.rows = min(16 * MB, ((cint_t*)p.counts)[e] - m0);
   it.row_base = ((cint_t*)p.offsets)[e] + m0;
-  int arow = it.row_base + r;
+  int arow[2] = {it.row_base + r, it.row_base + 16 + r};
   if (GATEUP) {
     // entries past the expert's T read on into the next expert's list or
     // the workspace region after the lists; they are never used
     cint_t* erow = (cint_t*)p.expert_rows + (size_t)e * p.T + m0;
-    int v[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = erow[i];
-    int x = v[0];
+    for (int mb = 0; mb < MB; ++mb) {
+      int v[16];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) x = r == i ? v[i] : x;
-    it.pair = x;
-    arow = x / p.k;
+      for (int i = 0; i < 16; ++i) v[i] = erow[16 * mb + i];
+      int x = v[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) x = r == i ? v[i] : x;
+      if (mb == 0) it.pair = x;
+      arow[mb] = x / p.k;
+    }
   } else {
     // (entries past the expert's rows are read but never used, as above)
     it.pair = p.expert_rows[(size_t)e * p.T + m0 + r];
   }
-  it.a_off = r < it.rows ? arow * mx6_row_bytes(nblk) : 0x7ffffff0;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+    it.a_off[mb] = (mb < MB && 16 * mb + r < it.rows) ? arow[mb] * mx6_row_bytes(nblk) : 0x7ffffff0;
   // the epilogue's bias, loaded now so that its latency hides under the
   // weight stream (columns past the output read the last column, never
   // stored)
@@ -328,17 +333,20 @@ __device__ __forceinline__ void dec_null_item(const GemmParams& p, DecItem& it) 
   it.e = 0; it.m0 = 0; it.pair = 0; it.rows = 0; it.row_base = 0; it.col0 = 0; it.ok_mask = 0;
   it.crsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.b_codes, 0, 0, 0x00020000);
   it.srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.b_scales, 0, 0, 0x00020000);
-  it.a_off = 0x7ffffff0;
+  it.a_off[0] = it.a_off[1] = 0x7ffffff0;
   it.rs = 1;
   it.bias[0] = it.bias[1] = it.bias[2] = it.bias[3] = 0.f;
 }
 
-template <bool GATEUP, int NPH, bool U16, int TERMS>
-__global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_gemm_decode(GemmParams p, int spans) {
+// MB = 2: 32-row tiles (two A row blocks per lane), for batches of up to
+// 32 rows per expert, so that an expert's weights are read once.
+template <bool GATEUP, int NPH, bool U16, int TERMS, int MB>
+__global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) void expert_gemm_decode(GemmParams p,
+                                                                                                     int spans) {
   using Cfg = DecCfg<U16>;
   // vector-memory instructions per wave per phase (the fast mode loads two
-  // fewer A pieces)
-  constexpr int VM = Cfg::VM - (TERMS == 1 ? 2 : 0);
+  // fewer A pieces per row block)
+  constexpr int VM = Cfg::VM - 5 + MB * (TERMS == 1 ? 3 : 5);
   constexpr int NCB = 4, NW = DEC_NW;
   // readfirstlane: the wave index is uniform, so the buffer resources and
   // LDS bases derived from it live in scalar registers
@@ -409,42 +417,48 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
       }
     }
   };
-  auto issue_a = [&](const DecItem& it, int ph, uint4 (&av)[5]) {
+  auto issue_a = [&](const DecItem& it, int ph, uint4 (&av)[MB][5]) {
     const int g = lane_id >> 4;
     const int pb0 = ph * DEC_KPH, npb = (NPH > 0 && ph < NPH - 1) ? DEC_KPH : min(DEC_KPH, nblk - pb0);
     // block pb0 + 4w + g of the phase (blocks past K read the last block;
     // their products are masked off); piece q of the lanes g = 0..3 is one
     // 64-byte line of the piece-interleaved row
     const int bl = min(wave * DEC_WB + g, npb - 1);
-    const int off = it.a_off < 0x7ffffff0 ? it.a_off + mx6_byte_offset(bl, 0) : 0x7ffffff0;
     const int aso = pb0 / 4 * MX6_GROUP_BYTES;  // pb0 is a multiple of 4 blocks
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (TERMS == 1 && q >= 2) {  // pieces 2 and 3 hold only the other terms' codes
-        av[q] = make_uint4(0u, 0u, 0u, 0u);
-        continue;
+    for (int mb = 0; mb < MB; ++mb) {
+      const int off = it.a_off[mb] < 0x7ffffff0 ? it.a_off[mb] + mx6_byte_offset(bl, 0) : 0x7ffffff0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (TERMS == 1 && q >= 2) {  // pieces 2 and 3 hold only the other terms' codes
+          av[mb][q] = make_uint4(0u, 0u, 0u, 0u);
+          continue;
+        }
+        const auto t4 = __builtin_amdgcn_raw_buffer_load_b128(arsrc, off + 64 * q, aso, 0);
+        av[mb][q] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
       }
-      const auto t4 = __builtin_amdgcn_raw_buffer_load_b128(arsrc, off + 64 * q, aso, 0);
-      av[q] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
+      // bytes 64 .. 75: the last term's codes and the scale bytes (the
+      // padding dword is not loaded: a register that a load in flight
+      // writes must not be dead, or the compiler waits for the load before
+      // reusing it)
+      const auto t3 = __builtin_amdgcn_raw_buffer_load_b96(arsrc, off + 256, aso, 0);
+      av[mb][4] = make_uint4(t3[0], t3[1], t3[2], 0u);
     }
-    // bytes 64 .. 75: the last term's codes and the scale bytes (the padding
-    // dword is not loaded: a register that a load in flight writes must not
-    // be dead, or the compiler waits for the load before reusing it)
-    const auto t3 = __builtin_amdgcn_raw_buffer_load_b96(arsrc, off + 256, aso, 0);
-    av[4] = make_uint4(t3[0], t3[1], t3[2], 0u);
   };
-  auto issue = [&](const DecItem& it, int ph, int buf, uint4 (&av)[5]) {
+  auto issue = [&](const DecItem& it, int ph, int buf, uint4 (&av)[MB][5]) {
     issue_b(it, ph, buf);
     issue_a(it, ph, av);
   };
 
-  v4f acc[1][NCB];
-  auto consume = [&](int ph, int buf, const uint4 (&av)[5]) {
+  v4f acc[MB][NCB];
+  auto consume = [&](int ph, int buf, const uint4 (&av)[MB][5]) {
     const int npb = (NPH > 0 && ph < NPH - 1) ? DEC_KPH : min(DEC_KPH, nblk - ph * DEC_KPH);
     const int bl = wave * DEC_WB + g;  // logical block within the phase
-    Stage<1, NCB> st;
+    Stage<MB, NCB> st;
 #pragma unroll
-    for (int q = 0; q < 5; ++q) st.a[0][q] = av[q];
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int q = 0; q < 5; ++q) st.a[mb][q] = av[mb][q];
     // The LDS reads are written as one asm block that waits for its own
     // results: the compiler cannot tell the two phase buffers apart, and
     // would otherwise wait for every copy in flight (the next phase's too)
@@ -477,20 +491,24 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
     st.bs[1] = (int)((s1 >> sh) & 0xffu);
     st.bs[2] = (int)((s2 >> sh) & 0xffu);
     st.bs[3] = (int)((s3 >> sh) & 0xffu);
-    mma_stage<1, NCB, TERMS>(acc, st, keep_mask<1, NCB>(bl < npb));
+    mma_stage<MB, NCB, TERMS>(acc, st, keep_mask<MB, NCB>(bl < npb));
     // pin the MFMAs to this phase: unused until the epilogue, they could
     // otherwise be sunk past later code, holding every phase's operands
-    asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      asm volatile("" : "+v"(acc[mb][0]), "+v"(acc[mb][1]), "+v"(acc[mb][2]), "+v"(acc[mb][3]));
   };
 
   // ---- epilogue of item `it`: wave w takes accumulator element w, i.e.
   // tile rows 4g + w, and sums the four waves' partials in a fixed order.
   // s_acc is the phase buffer consumed last (free until the next issue).
-  auto epilogue = [&](const DecItem& it, float* s_acc) {
+  // With two row blocks it runs once per block (tile rows 16 mb + 4g + w).
+  auto epilogue = [&](const DecItem& it, float* s_acc, auto mbc) {
+    constexpr int mb = decltype(mbc)::value;
 #pragma unroll
     for (int j = 0; j < NCB; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) s_acc[((wave * NCB + j) * 4 + q) * 64 + lane] = acc[0][j][q];
+      for (int q = 0; q < 4; ++q) s_acc[((wave * NCB + j) * 4 + q) * 64 + lane] = acc[mb][j][q];
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the partials are in LDS
     __builtin_amdgcn_s_barrier();
     float v[NCB];
@@ -501,10 +519,10 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
       for (int w = 1; w < NW; ++w) t += s_acc[((w * NCB + j) * 4 + wave) * 64 + lane];
       v[j] = t;
     }
-    const int row = 4 * g + wave;  // tile row of this lane's values
+    const int lrow = 4 * g + wave, row = 16 * mb + lrow;  // tile row of this lane's values
     const int col0 = it.col0, rows = it.rows, row_base = it.row_base;
     if (!GATEUP) {
-      const bool fold = p.fold_cnt != nullptr;
+      const bool fold = MB == 1 && p.fold_cnt != nullptr;
 #pragma unroll
       for (int j = 0; j < NCB; ++j) {
         if (!((it.ok_mask >> j) & 1)) continue;
@@ -591,16 +609,16 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
     // (columns past I are never stored)
     const float h0 = swiglu_act(v[0] + it.bias[0], v[2] + it.bias[1], p.clamp, p.alt);
     const float h1 = swiglu_act(v[1] + it.bias[2], v[3] + it.bias[3], p.clamp, p.alt);
-    const uint32_t scw = split_h_row(h0, h1, r, s_codes[row]);
-    if (r == 0) s_sc[row] = scw;
+    const uint32_t scw = split_h_row(h0, h1, r, s_codes[lrow]);
+    if (r == 0) s_sc[lrow] = scw;
     lds_wave_sync();
     const int blk = col0 >> 5;
     if (lane < 12) {
       const int rw = 4 * (lane / 3) + wave, t = lane % 3;
-      if (rw < rows) {
+      if (16 * mb + rw < rows) {
         uint32_t pk[6];
         pack6x32(s_codes[rw][t], pk);
-        uint8_t* hrow = p.hq + (size_t)(row_base + rw) * mx6_row_bytes(I >> 5);
+        uint8_t* hrow = p.hq + (size_t)(row_base + 16 * mb + rw) * mx6_row_bytes(I >> 5);
         // 8-byte stores at multiples of 8 never straddle a 16-byte piece
         *(uint2*)(hrow + mx6_byte_offset(blk, 24 * t)) = make_uint2(pk[0], pk[1]);
         *(uint2*)(hrow + mx6_byte_offset(blk, 24 * t + 8)) = make_uint2(pk[2], pk[3]);
@@ -608,8 +626,8 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
       }
     } else if (lane < 16) {
       const int rw = 4 * (lane - 12) + wave;
-      if (rw < rows) {
-        uint8_t* hrow = p.hq + (size_t)(row_base + rw) * mx6_row_bytes(I >> 5);
+      if (16 * mb + rw < rows) {
+        uint8_t* hrow = p.hq + (size_t)(row_base + 16 * mb + rw) * mx6_row_bytes(I >> 5);
         *(uint2*)(hrow + mx6_byte_offset(blk, 72)) = make_uint2(s_sc[rw], 0u);
       }
     }
@@ -632,18 +650,21 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
   DecItem cur, nul;
   dec_item_head<GATEUP>(p, te_e, te_m0, span, wave, cur);
   issue_b(cur, 0, 0);
-  dec_item_tail<GATEUP>(p, r, cur);
+  dec_item_tail<GATEUP, MB>(p, r, cur);
   dec_null_item(p, nul);
   // for the down projection's folded combine: where each pair's row sits
-  if (GATEUP && p.pair_row != nullptr && cur.col0 == 0 && wave == 0 && lane < cur.rows)
+  // (single row block only)
+  if (GATEUP && MB == 1 && p.pair_row != nullptr && cur.col0 == 0 && wave == 0 && lane < cur.rows)
     p.pair_row[cur.pair] = cur.row_base + lane;
 #pragma unroll
-  for (int j = 0; j < NCB; ++j) acc[0][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-  uint4 av0[5], av1[5];
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) acc[mb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  uint4 av0[MB][5], av1[MB][5];
   issue_a(cur, 0, av0);
   // step of phase ph: copies of phase ph + 1 of `cur`, or (last phase) of
   // phase 0 of `nit`
-  auto step = [&](int ph, int buf, bool last, const DecItem& nit, const uint4 (&avc)[5], uint4 (&avn)[5]) {
+  auto step = [&](int ph, int buf, bool last, const DecItem& nit, const uint4 (&avc)[MB][5], uint4 (&avn)[MB][5]) {
     if (last)
       issue(nit, 0, buf ^ 1, avn);
     else
@@ -675,7 +696,11 @@ __global__ __launch_bounds__(DEC_NW * 64, DecCfg<U16>::WG_PER_CU) void expert_ge
     }
   }
   wait_vmcnt<0>();  // the null item's copies
-  epilogue(cur, (float*)s_code[(nph - 1) & 1]);
+  epilogue(cur, (float*)s_code[(nph - 1) & 1], std::integral_constant<int, 0>{});
+  if constexpr (MB == 2) {
+    __syncthreads();  // every wave has read its sums of the first row block
+    epilogue(cur, (float*)s_code[(nph - 1) & 1], std::integral_constant<int, 1>{});
+  }
 }
 
 // Prefill kernel: tiles of PF_MT = 64 rows x 256 output columns (gate/up:
@@ -1503,29 +1528,37 @@ static bool prefill_offsets_fit(const GemmParams& p) {
 }
 
 // Decode kernel instance for the phase count of K (unrolled up to 8 phases).
-template <bool GATEUP, bool U16, int TERMS>
+template <bool GATEUP, bool U16, int TERMS, int MB>
 static void launch_decode_u(const GemmParams& p, unsigned grid, int spans, hipStream_t s) {
   const int nph = (p.K / 32 + DEC_KPH - 1) / DEC_KPH;
   const dim3 g(grid), b(DEC_NW * 64);
   switch (nph) {
-    case 1: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 1, U16, TERMS>), g, b, 0, s, p, spans); break;
-    case 2: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 2, U16, TERMS>), g, b, 0, s, p, spans); break;
-    case 3: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 3, U16, TERMS>), g, b, 0, s, p, spans); break;
-    case 4: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 4, U16, TERMS>), g, b, 0, s, p, spans); break;
-    case 5: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 5, U16, TERMS>), g, b, 0, s, p, spans); break;
-    case 6: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 6, U16, TERMS>), g, b, 0, s, p, spans); break;
-    case 7: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 7, U16, TERMS>), g, b, 0, s, p, spans); break;
-    case 8: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 8, U16, TERMS>), g, b, 0, s, p, spans); break;
-    default: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 0, U16, TERMS>), g, b, 0, s, p, spans); break;
+    case 1: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 1, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
+    case 2: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 2, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
+    case 3: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 3, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
+    case 4: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 4, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
+    case 5: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 5, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
+    case 6: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 6, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
+    case 7: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 7, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
+    case 8: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 8, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
+    default: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 0, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
   }
+}
+
+template <bool GATEUP, int TERMS, int MB>
+static void launch_decode_mb(const GemmParams& p, unsigned items, int spans, hipStream_t s) {
+  if ((p.K / 32) % 2 == 0)
+    launch_decode_u<GATEUP, true, TERMS, MB>(p, items, spans, s);
+  else
+    launch_decode_u<GATEUP, false, TERMS, MB>(p, items, spans, s);
 }
 
 template <bool GATEUP, int TERMS>
 static void launch_decode(const GemmParams& p, unsigned items, int spans, hipStream_t s) {
-  if ((p.K / 32) % 2 == 0)
-    launch_decode_u<GATEUP, true, TERMS>(p, items, spans, s);
+  if (p.mb == 2)
+    launch_decode_mb<GATEUP, TERMS, 2>(p, items, spans, s);
   else
-    launch_decode_u<GATEUP, false, TERMS>(p, items, spans, s);
+    launch_decode_mb<GATEUP, TERMS, 1>(p, items, spans, s);
 }
 
 template <bool GATEUP, int TERMS>

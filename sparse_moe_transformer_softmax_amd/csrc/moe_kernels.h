@@ -46,6 +46,7 @@ struct GemmParams {
   uint8_t* hq;               // gate/up output: MX6x3 rows [P, I/32, 80]
   float* y;                  // down output: fp32 [P, N]
   int terms;                 // FP6 terms of A taking part: 3 (exact path) or 1 (fast mode)
+  int mb;                    // decode only: 16-row A blocks per tile (1, or 2 for 32-row tiles)
   int alt;                   // gate/up only: 1 = the variant layout and activation (interleaved rows,
                              // Swish slope 1.702, gate clamped from above only)
   // down, decode only: the combine folded into the epilogue (fold_cnt null: no fold)
@@ -90,6 +91,7 @@ constexpr int ROUTE_MAX_SPLIT_BLOCKS = 16;
 
 // rows per GEMM tile of the two configurations
 constexpr int MT_SMALL = 16;
+constexpr int MT_SMALL2 = 32;  // decode tiles of two row blocks
 constexpr int MT_LARGE = 64;
 constexpr int MT_WIDE = 128;
 
