@@ -188,7 +188,7 @@ int moe_stack_forward(const void* x0, int n_layers, const void* const* router_w,
 /* Per-kernel timing for profiling.  Bit i of mask selects kernel kind i of
  * {0 route (including the MX6x3 split of x, done by the same launch),
  * 1 gate/up GEMM, 2 down GEMM, 3 combine, 4 reserved (never launched)};
- * single-layer calls at decode sizes (T * k <= 32 * E) fold the combine
+ * single-layer calls at decode sizes (T * k <= 16 * E) fold the combine
  * into the down GEMM, and then launch no kind 3 kernel;
  * while a kind is selected, every layer call records a HIP event pair
  * around each launch of that kernel on the call's stream (mask 0 turns
