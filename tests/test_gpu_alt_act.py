@@ -84,8 +84,10 @@ def test_alt_prefill_20b_sampled(torch):
 
 
 @pytest.mark.parametrize("T,d,I,E,k", [
-    (37, 160, 96, 24, 2),    # decode tiles, K/32 odd
-    (300, 128, 128, 16, 1),  # 64-row prefill tiles
+    (37, 160, 96, 24, 2),    # 16-row decode tiles, K/32 odd
+    (300, 128, 128, 16, 1),  # 32-row decode tiles
+    (150, 160, 96, 24, 4),   # 32-row decode tiles, K/32 odd
+    (400, 256, 192, 32, 4),  # 64-row prefill tiles
     (1500, 256, 192, 8, 3),  # 128-row prefill tiles
 ])
 def test_alt_ragged(torch, T, d, I, E, k):

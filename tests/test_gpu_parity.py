@@ -129,6 +129,7 @@ RAGGED = [
     (1, 64, 32, 8, 8),
     (200, 96, 64, 5, 5),
     (300, 128, 128, 16, 1),
+    (150, 160, 96, 24, 4),
     (70, 256, 160, 40, 4),
     (1500, 256, 192, 8, 3),
     (129, 2880, 2880, 32, 4),
