@@ -193,10 +193,11 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   // (20b shapes: 160 tokens 189 vs 245 us, 256 tokens 241 vs 284 us; from
   // 36 rows per expert on they lose)
   const bool small_m = (long long)P <= 32LL * a.E;
-  // 128-row tiles when experts average at least 64 rows (measured faster
-  // than 64-row tiles there even with half-filled tiles) and both
-  // projections copy their scale bytes in pairs (K/32 even)
-  const bool wide = !small_m && (long long)P >= 64LL * a.E && (a.d / 32) % 2 == 0 && (a.I / 32) % 2 == 0;
+  // 128-row tiles above the decode sizes whenever both projections copy
+  // their scale bytes in pairs (K/32 even): measured faster than 64-row
+  // tiles from 33 rows per expert on, partly filled tiles included (20b
+  // shapes: 264 tokens 233 vs 256 us, 384 tokens 242 vs 296 us)
+  const bool wide = !small_m && (a.d / 32) % 2 == 0 && (a.I / 32) % 2 == 0;
   const int mode = small_m ? GEMM_DECODE : wide ? GEMM_WIDE : GEMM_PREFILL;
   // decode sizes above 16 rows per expert: 32-row tiles (two row blocks),
   // which read an expert's weights once

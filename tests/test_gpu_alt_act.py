@@ -87,7 +87,8 @@ def test_alt_prefill_20b_sampled(torch):
     (37, 160, 96, 24, 2),    # 16-row decode tiles, K/32 odd
     (300, 128, 128, 16, 1),  # 32-row decode tiles
     (150, 160, 96, 24, 4),   # 32-row decode tiles, K/32 odd
-    (400, 256, 192, 32, 4),  # 64-row prefill tiles
+    (400, 256, 192, 32, 4),  # 128-row tiles, partly filled
+    (264, 128, 96, 32, 4),   # 64-row prefill tiles (I/32 odd)
     (1500, 256, 192, 8, 3),  # 128-row prefill tiles
 ])
 def test_alt_ragged(torch, T, d, I, E, k):

@@ -81,7 +81,8 @@ def test_fast_prefill_20b_sampled(torch):
     (300, 128, 128, 16, 1),  # 32-row decode tiles
     (150, 160, 96, 24, 4),   # 32-row decode tiles, K/32 odd
     (200, 96, 64, 5, 5),     # 64-row prefill tiles, K/32 odd
-    (400, 256, 192, 32, 4),  # 64-row prefill tiles
+    (400, 256, 192, 32, 4),  # 128-row tiles, partly filled
+    (264, 128, 96, 32, 4),   # 64-row prefill tiles (I/32 odd)
     (1500, 256, 192, 8, 3),  # 128-row prefill tiles
 ])
 def test_fast_ragged(torch, T, d, I, E, k):

@@ -133,8 +133,9 @@ RAGGED = [
     (70, 256, 160, 40, 4),
     (1500, 256, 192, 8, 3),
     (129, 2880, 2880, 32, 4),
-    # around the switch from 16-row decode tiles to 64-row tiles (32 rows
-    # per expert on average): 2 decode tiles per expert, then 64-row tiles
+    # around the switch from decode tiles to prefill tiles (32 rows per
+    # expert on average): decode tiles, then 64-row tiles (I/32 odd), then
+    # partly filled 128-row tiles
     (256, 128, 96, 32, 4),
     (264, 128, 96, 32, 4),
     (400, 256, 192, 32, 4),
