@@ -292,27 +292,59 @@ def test_stack_against_oracle(torch):
     got = moe.moe_stack_forward(_bf16_gpu(torch, x0), [{kk: g[kk] for kk in _STACK_KEYS} for g in gl],
                                 k=STACK.k, clamp=STACK.clamp, eps=1e-5)
     torch.cuda.synchronize()
-    x = O.bf16_bits_to_f64(x0)
-    min_gap = np.full(STACK.T, np.inf)
+    ex = _stack_excess_vs_oracle(x0, layers, got, STACK)
+    assert ex <= TOL
+
+
+def _stack_excess_vs_oracle(x0, layers, got, wl, sel=None):
+    """Largest error beyond the rounding allowance, over rms(ref), of the
+    stack output rows `sel` (all rows if None) against the oracle's pre-norm
+    residual stack run on those rows only (every token's path through the
+    stack is independent of the others)."""
+    sel = np.arange(wl.T) if sel is None else np.asarray(sel)
+    x = O.bf16_bits_to_f64(x0[sel])
+    min_gap = np.full(len(sel), np.inf)
     allow = np.zeros_like(x)
     for li, L in enumerate(layers):
         if li > 0:
             allow += 2.0 * bf16_half_ulp(x)
         n_bits = O._f64_bf16_to_bits(O.round_to_bf16(O.rmsnorm(x, 1e-5)))
-        logits, _, _ = O.route(n_bits, L["router_w"], L["router_b"], STACK.k)
-        min_gap = np.minimum(min_gap, O.topk_gap(logits, STACK.k))
-        y = O.moe_layer(n_bits, L["router_w"], L["router_b"], L, STACK.k, STACK.clamp)["y"]
+        logits, _, _ = O.route(n_bits, L["router_w"], L["router_b"], wl.k)
+        min_gap = np.minimum(min_gap, O.topk_gap(logits, wl.k))
+        y = O.moe_layer(n_bits, L["router_w"], L["router_b"], L, wl.k, wl.clamp)["y"]
         x = O.round_to_bf16(x + y)
     keep = min_gap > 1e-3
-    say(f"stack: {int((~keep).sum())} of {STACK.T} tokens left out (gap <= 1e-3 at a later layer)")
-    assert keep.sum() >= STACK.T * 3 // 4
-    g64 = bf16_tensor_to_f64(got)[keep]
+    say(f"stack: {int((~keep).sum())} of {len(sel)} tokens left out (gap <= 1e-3 at a later layer)")
+    assert keep.sum() >= len(sel) * 3 // 4
+    g64 = bf16_tensor_to_f64(got)[sel][keep]
     ref = x[keep]
     rms = float(np.sqrt(np.mean(ref ** 2)))
     ex = float(np.max(np.abs(g64 - ref) - bf16_half_ulp(ref) - allow[keep]) / rms)
     say(f"stack: excess/rms={ex:.3e} (beyond the rounding allowance); final-rounding-only excess/rms="
         f"{bf16_excess(g64, ref):.3e}")
-    assert ex <= TOL
+    return ex
+
+
+def test_stack_full_size_two_layers(torch):
+    """The 36-layer stack's shapes (T 2048, E 128, d = I = 2880) over its
+    first two seeded layers: the stack entry point equals its steps bit for
+    bit, and 12 sampled tokens meet the oracle bar."""
+    wl = WORKLOADS["120b_stack36"]
+    layers = [make_inputs(wl, layer=l) for l in range(2)]
+    x0 = layers[0]["x"]
+    say(f"stack full size T={wl.T} d={wl.d} E={wl.E} L=2")
+    gl = [to_gpu(L) for L in layers]
+    x = _bf16_gpu(torch, x0)
+    got = moe.moe_stack_forward(x, [{kk: g[kk] for kk in _STACK_KEYS} for g in gl], k=wl.k, clamp=wl.clamp,
+                                eps=1e-5)
+    for g in gl:
+        n = moe.moe_rmsnorm(x, 1e-5)
+        _, out_f32, _, _, _ = moe.moe_layer_forward_dbg(n, *[g[kk] for kk in _STACK_KEYS], k=wl.k, clamp=wl.clamp)
+        x = (x.float() + out_f32).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(got, x)
+    sel = np.sort(np.random.default_rng(11).choice(wl.T, 12, replace=False))
+    assert _stack_excess_vs_oracle(x0, layers, got, wl, sel) <= TOL
 
 
 def test_folded_combine_across_call_sizes(torch):
