@@ -173,6 +173,26 @@ int moe_layer_forward_ws(const void* x, const void* router_w, const float* route
  * x, out bf16 [T, d]; d a multiple of 32; eps >= 0.  out may equal x. */
 int moe_rmsnorm(const void* x, void* out, int T, int d, float eps, void* stream);
 
+/* The residual add and RMSNorm between two layers of the stack, fused
+ * ("OpenAI 最新开源模型 gpt-oss 架构与训练解析", RMSNorm 替换 LayerNorm: a
+ * pre-norm block adds its output to the residual stream, and the next
+ * block normalises that stream by its root mean square, unit gain):
+ *   x_out = bf16(x + y)                                  (the add in fp32)
+ *   n_out = bf16(x_out / sqrt(mean(x_out^2) + eps))      (per row)
+ *   x      bf16 [T, d]   residual stream
+ *   y_bf16 bf16 [T, d]   layer output, or NULL
+ *   y_f32  fp32 [T, d]   layer output, or NULL (exactly one of the two is set;
+ *                        the fp32 form is what moe_layer_forward_dbg returns
+ *                        as out_f32, and what the stack adds internally)
+ *   x_out  bf16 [T, d]   written; may be x itself, otherwise must not overlap
+ *                        x, y or n_out
+ *   n_out  bf16 [T, d]   written, or NULL (residual add only); must not
+ *                        overlap x, y or x_out
+ * d a multiple of 32 and eps >= 0.  Sums of squares are taken over the
+ * rounded x_out values, in fp32. */
+int moe_rmsnorm_residual(const void* x, const void* y_bf16, const float* y_f32, void* x_out, void* n_out, int T,
+                         int d, float eps, void* stream);
+
 /* Pre-norm residual stack of n_layers MoE layers on one GPU:
  *   n = bf16(RMSNorm(x)); x = bf16(x + MoE_l(n))   for l = 0 .. n_layers-1
  * Each per-layer argument is a HOST array of n_layers device pointers with

@@ -22,6 +22,9 @@ architecture summaries, "模型架构 / MoE" and "权重量化" entries):
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 # stream ids, one per tensor kind
@@ -51,9 +54,34 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     return out
 
 
-def _random_bytes(g: np.random.Generator, n: int) -> np.ndarray:
+# Bulk byte draws are split into chunks of CHUNK_WORDS 64-bit words; chunk c
+# of a stream comes from its own Philox counter block (the chunk index is
+# the third counter word), so the chunks can be drawn in parallel threads
+# (numpy's bit generators release the interpreter lock while they fill).
+CHUNK_WORDS = 1 << 21
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _random_bytes(seed: int, stream: int, n: int) -> np.ndarray:
+    """n uniformly random bytes of (seed, stream), chunk by chunk."""
     words = (n + 7) // 8
-    return g.bit_generator.random_raw(words).view(np.uint8)[:n].copy()
+    buf = np.empty(words, dtype=np.uint64)
+    nchunk = (words + CHUNK_WORDS - 1) // CHUNK_WORDS
+
+    def fill(c: int) -> None:
+        lo = c * CHUNK_WORDS
+        hi = min(words, lo + CHUNK_WORDS)
+        buf[lo:hi] = _gen(seed, stream, c).bit_generator.random_raw(hi - lo)
+
+    if nchunk == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(min(_threads(), nchunk)) as ex:
+            list(ex.map(fill, range(nchunk)))
+    return buf.view(np.uint8)[:n]
 
 
 def gen_x(seed: int, T: int, d: int, redraw: dict[int, int] | None = None) -> np.ndarray:
@@ -84,8 +112,8 @@ def zipf_router_bias(seed: int, E: int, beta: float) -> np.ndarray:
 def gen_mxfp4(seed: int, stream_codes: int, stream_scales: int, E: int, rows: int, K: int):
     """MXFP4 matrix stack: codes uint8 [E, rows, K/2], scales uint8 [E, rows, K/32]."""
     assert K % 32 == 0
-    codes = _random_bytes(_gen(seed, stream_codes), E * rows * (K // 2)).reshape(E, rows, K // 2)
-    sb = _random_bytes(_gen(seed, stream_scales), E * rows * (K // 32)).reshape(E, rows, K // 32)
+    codes = _random_bytes(seed, stream_codes, E * rows * (K // 2)).reshape(E, rows, K // 2)
+    sb = _random_bytes(seed, stream_scales, E * rows * (K // 32)).reshape(E, rows, K // 32)
     scales = (sb & np.uint8(3)) + np.uint8(SCALE_LO)
     return codes, scales
 

@@ -212,8 +212,19 @@ def expert_ffn(xs: np.ndarray, w13: np.ndarray, b13: np.ndarray,
     return h @ w2.T + b2[None, :]
 
 
+def dequant_expert(experts: dict, e: int) -> tuple:
+    """Expert e's weights in float64: (W13, b13, W2, b2)."""
+    return (
+        mxfp4_dequant(experts["w13_codes"][e], experts["w13_scales"][e]),
+        np.asarray(experts["b13"][e], dtype=np.float64),
+        mxfp4_dequant(experts["w2_codes"][e], experts["w2_scales"][e]),
+        np.asarray(experts["b2"][e], dtype=np.float64),
+    )
+
+
 class DequantCache:
-    """Dequantises expert e's weights on first use (float64)."""
+    """Dequantises expert e's weights on first use (float64) and keeps them
+    (about 200 MB per expert at d = I = 2880)."""
 
     def __init__(self, experts: dict):
         self.ex = experts
@@ -221,13 +232,7 @@ class DequantCache:
 
     def __call__(self, e: int):
         if e not in self._c:
-            ex = self.ex
-            self._c[e] = (
-                mxfp4_dequant(ex["w13_codes"][e], ex["w13_scales"][e]),
-                np.asarray(ex["b13"][e], dtype=np.float64),
-                mxfp4_dequant(ex["w2_codes"][e], ex["w2_scales"][e]),
-                np.asarray(ex["b2"][e], dtype=np.float64),
-            )
+            self._c[e] = dequant_expert(self.ex, e)
         return self._c[e]
 
 
@@ -261,14 +266,16 @@ def moe_layer(x_bits: np.ndarray, router_w_bits: np.ndarray, router_b: np.ndarra
     T = x.shape[0]
     E = router_w_bits.shape[0]
     d = x.shape[1]
-    cache = cache or DequantCache(experts)
+    # without a cache each expert is dequantised for its own tokens and
+    # dropped afterwards, so memory stays at one expert
+    get = cache if cache is not None else (lambda e: dequant_expert(experts, e))
     y = np.zeros((T, d), dtype=np.float64)
     counts = np.bincount(ids.reshape(-1), minlength=E)
     for e in range(E):
         tok, slot = np.nonzero(ids == e)
         if tok.size == 0:
             continue
-        w13, b13, w2, b2 = cache(e)
+        w13, b13, w2, b2 = get(e)
         z = (expert_ffn(x[tok], w13, b13, w2, b2, clamp) if aq is None and not alt
              else expert_ffn(x[tok], w13, b13, w2, b2, clamp, aq, alt))
         y[tok] += w[tok, slot][:, None] * z
@@ -340,7 +347,9 @@ def _f64_bf16_to_bits(v: np.ndarray) -> np.ndarray:
 
 def topk_gap(logits: np.ndarray, k: int) -> np.ndarray:
     """Gap between the k-th and (k+1)-th largest logit of each row (inf when
-    k equals the number of experts)."""
+    k equals the number of experts).  The top-k set of a row is decided by
+    that gap: a perturbation of every logit by less than half of it leaves
+    the set unchanged."""
     s = -np.sort(-logits, axis=1)
     if s.shape[1] <= k:
         return np.full(s.shape[0], np.inf)

@@ -10,8 +10,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from sparse_moe_transformer_softmax_amd import synth
-from sparse_moe_transformer_softmax_amd.workloads import ZIPF_BETA, Workload
+from moe_inputs import synth
+from moe_inputs.workloads import ZIPF_BETA, Workload
 
 from .moe_oracle import route, topk_gap
 

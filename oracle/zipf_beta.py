@@ -11,8 +11,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from sparse_moe_transformer_softmax_amd import synth
-from sparse_moe_transformer_softmax_amd.workloads import WORKLOADS
+from moe_inputs import synth
+from moe_inputs.workloads import WORKLOADS
 
 from .moe_oracle import route
 

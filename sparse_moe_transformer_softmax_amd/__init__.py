@@ -15,7 +15,7 @@ __all__ = [
     "moe_workspace_bytes", "moe_workspace_init", "moe_layer_forward_ws", "moe_rmsnorm",
     "moe_stack_forward", "moe_release", "moe_status_string", "moe_version", "LIB_PATH",
     "moe_timing_enable", "moe_timing_read", "KERNELS", "moe_layer_forward_mx6", "moe_layer_forward_mx6_dbg",
-    "moe_layer_forward_ex", "MOE_LAYER_MXFP6", "MOE_LAYER_ALT_ACT",
+    "moe_layer_forward_ex", "MOE_LAYER_MXFP6", "MOE_LAYER_ALT_ACT", "moe_rmsnorm_residual",
 ]
 
 MOE_LAYER_MXFP6 = 1
@@ -38,6 +38,7 @@ _SIGS = {
     "moe_workspace_init": (_I, [_P, ctypes.c_size_t, _P]),
     "moe_layer_forward_ws": (_I, [_P] * 9 + [_I] * 5 + [_F, _P, _P, ctypes.c_size_t, _P]),
     "moe_rmsnorm": (_I, [_P, _P, _I, _I, _F, _P]),
+    "moe_rmsnorm_residual": (_I, [_P] * 5 + [_I, _I, _F, _P]),
     "moe_stack_forward": (_I, [_P, _I] + [_P] * 8 + [_I] * 5 + [_F, _F, _P, _P]),
     "moe_release": (None, []),
     "moe_timing_enable": (_I, [_I]),
@@ -272,6 +273,26 @@ def moe_rmsnorm(x, eps: float = 1e-5, out=None, stream=None):
     _ok("moe_rmsnorm", lib().moe_rmsnorm(_check(x, "x", torch.bfloat16, (T, d)),
                                          _check(out, "out", torch.bfloat16, (T, d)), T, d, eps, _stream(stream)))
     return out
+
+
+def moe_rmsnorm_residual(x, y, eps: float = 1e-5, x_out=None, n_out=None, normalize: bool = True, stream=None):
+    """x_out = bf16(x + y), n_out = bf16(RMSNorm(x_out)); y bf16 or fp32 [T, d].
+    Returns (x_out, n_out) (n_out None when normalize is False)."""
+    torch = _torch()
+    T, d = x.shape
+    px = _check(x, "x", torch.bfloat16, (T, d))
+    if y.dtype == torch.float32:
+        yb, yf = None, _check(y, "y", torch.float32, (T, d))
+    else:
+        yb, yf = _check(y, "y", torch.bfloat16, (T, d)), None
+    if x_out is None:
+        x_out = torch.empty_like(x)
+    if n_out is None and normalize:
+        n_out = torch.empty_like(x)
+    pxo = _check(x_out, "x_out", torch.bfloat16, (T, d))
+    pno = _check(n_out, "n_out", torch.bfloat16, (T, d)) if normalize else None
+    _ok("moe_rmsnorm_residual", lib().moe_rmsnorm_residual(px, yb, yf, pxo, pno, T, d, eps, _stream(stream)))
+    return x_out, (n_out if normalize else None)
 
 
 def moe_stack_forward(x0, layers, k: int = 4, clamp: float = 7.0, eps: float = 1e-5, out=None, stream=None):

@@ -450,6 +450,25 @@ int moe_rmsnorm(const void* x, void* out, int T, int d, float eps, void* stream)
   return launch_rmsnorm((const uint16_t*)x, (uint16_t*)out, T, d, eps, (hipStream_t)stream) ? MOE_ERR_HIP : MOE_OK;
 }
 
+int moe_rmsnorm_residual(const void* x, const void* y_bf16, const float* y_f32, void* x_out, void* n_out, int T,
+                         int d, float eps, void* stream) {
+  if (T < 0 || d <= 0 || (d % 32) || !(eps >= 0.0f)) return MOE_ERR_BAD_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !x_out || (!y_bf16 == !y_f32)) return MOE_ERR_NULL_PTR;
+  const void* y = y_f32 ? (const void*)y_f32 : y_bf16;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(x_out, 16) || (n_out && !aligned(n_out, 16)))
+    return MOE_ERR_MISALIGNED;
+  const size_t nb = (size_t)T * d * 2, ny = (size_t)T * d * (y_f32 ? 4 : 2);
+  if ((x_out != x && overlap(x_out, nb, x, nb)) || overlap(x_out, nb, y, ny)) return MOE_ERR_ALIAS;
+  if (n_out && (overlap(n_out, nb, x, nb) || overlap(n_out, nb, y, ny) || overlap(n_out, nb, x_out, nb)))
+    return MOE_ERR_ALIAS;
+  if (int st = check_device()) return st;
+  return launch_residual_rmsnorm((const uint16_t*)x, y, y_f32 != nullptr, (uint16_t*)x_out, (uint16_t*)n_out, T, d,
+                                 eps, (hipStream_t)stream)
+             ? MOE_ERR_HIP
+             : MOE_OK;
+}
+
 int moe_stack_forward(const void* x0, int n_layers, const void* const* router_w, const float* const* router_b,
                       const uint8_t* const* w13_codes, const uint8_t* const* w13_scales, const float* const* b13,
                       const uint8_t* const* w2_codes, const uint8_t* const* w2_scales, const float* const* b2,

@@ -29,6 +29,28 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Residual step of the pre-norm stack for one float4 column group c of a
+// row: xo[c] = bf16(xi[c] + add) with the add in fp32; returns the sum of
+// squares of the rounded values (the RMSNorm statistic).
+__device__ __forceinline__ float residual_add4(const uint16_t* xi, uint16_t* xo, int c, float4 add) {
+  const float4 x = unpack_bf16x4(((const uint2*)xi)[c]);
+  const uint2 xb = pack_bf16x4(make_float4(x.x + add.x, x.y + add.y, x.z + add.z, x.w + add.w));
+  ((uint2*)xo)[c] = xb;
+  const float4 xn = unpack_bf16x4(xb);
+  return xn.x * xn.x + xn.y * xn.y + xn.z * xn.z + xn.w * xn.w;
+}
+
+// Second pass of the RMSNorm of one row held by one wave: no = bf16(xr *
+// 1/sqrt(ss/d + eps)), ss the wave's summed squares (reduced here).
+__device__ __forceinline__ void rmsnorm_row(const uint16_t* xr, uint16_t* no, float ss, int d, float eps, int lane) {
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  for (int c = lane; c < (d >> 2); c += 64) {
+    const float4 x = unpack_bf16x4(((const uint2*)xr)[c]);
+    ((uint2*)no)[c] = pack_bf16x4(make_float4(x.x * inv, x.y * inv, x.z * inv, x.w * inv));
+  }
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -55,21 +77,28 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     }
     if (p.out_f32) ((float4*)(p.out_f32 + (size_t)t * d))[c] = acc;
     if (p.out) ((uint2*)(p.out + (size_t)t * d))[c] = pack_bf16x4(acc);
-    if (stack) {
-      const float4 x = unpack_bf16x4(((const uint2*)(p.resid_in + (size_t)t * d))[c]);
-      const uint2 xb = pack_bf16x4(make_float4(x.x + acc.x, x.y + acc.y, x.z + acc.z, x.w + acc.w));
-      ((uint2*)(p.resid_out + (size_t)t * d))[c] = xb;
-      const float4 xn = unpack_bf16x4(xb);
-      ss += xn.x * xn.x + xn.y * xn.y + xn.z * xn.z + xn.w * xn.w;
-    }
+    if (stack) ss += residual_add4(p.resid_in + (size_t)t * d, p.resid_out + (size_t)t * d, c, acc);
   }
   if (!stack || p.norm_out == nullptr) return;
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)d + p.eps);
-  for (int c = lane; c < d4; c += 64) {
-    const float4 x = unpack_bf16x4(((const uint2*)(p.resid_out + (size_t)t * d))[c]);
-    ((uint2*)(p.norm_out + (size_t)t * d))[c] = pack_bf16x4(make_float4(x.x * inv, x.y * inv, x.z * inv, x.w * inv));
+  rmsnorm_row(p.resid_out + (size_t)t * d, p.norm_out + (size_t)t * d, ss, d, p.eps, lane);
+}
+
+// The residual add and RMSNorm on their own (one wave per row): x_out =
+// bf16(x + y), n_out = bf16(RMSNorm(x_out)); y is bf16 or fp32.
+template <bool YF32>
+__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const uint16_t* x, const void* y, uint16_t* x_out,
+                                                               uint16_t* n_out, int T, int d, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const size_t ro = (size_t)t * d;
+  float ss = 0.f;
+  for (int c = lane; c < (d >> 2); c += 64) {
+    const float4 a = YF32 ? ((const float4*)((const float*)y + ro))[c]
+                          : unpack_bf16x4(((const uint2*)((const uint16_t*)y + ro))[c]);
+    ss += residual_add4(x + ro, x_out + ro, c, a);
   }
+  if (n_out != nullptr) rmsnorm_row(x_out + ro, n_out + ro, ss, d, eps, lane);
 }
 
 // Plain combine: one thread per float4 column group of one token, so that a
@@ -129,6 +158,16 @@ int launch_combine(const CombineParams& p, hipStream_t s) {
 
 int launch_rmsnorm(const uint16_t* x, uint16_t* out, int T, int d, float eps, hipStream_t s) {
   hipLaunchKernelGGL(rmsnorm_kernel, dim3((T + 3) / 4), dim3(256), 0, s, x, out, T, d, eps);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_residual_rmsnorm(const uint16_t* x, const void* y, bool y_f32, uint16_t* x_out, uint16_t* n_out, int T,
+                            int d, float eps, hipStream_t s) {
+  const dim3 g((T + 3) / 4), b(256);
+  if (y_f32)
+    hipLaunchKernelGGL(residual_rmsnorm_kernel<true>, g, b, 0, s, x, y, x_out, n_out, T, d, eps);
+  else
+    hipLaunchKernelGGL(residual_rmsnorm_kernel<false>, g, b, 0, s, x, y, x_out, n_out, T, d, eps);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -14,8 +14,8 @@
 // E8M0 scale each, per 32-element block); every 16x16x128 step issues one
 // MFMA per term into the same fp32 accumulator.
 //
-// Operand layout of the 16x16x128 scaled MFMA (checked by the one-hot
-// probe tests): lane l carries row (A) or column (B) l % 16 and the 32
+// Operand layout of the 16x16x128 scaled MFMA (checked bit for bit by the
+// one-hot layout probe tests, in every tile configuration): lane l carries row (A) or column (B) l % 16 and the 32
 // consecutive K values of block l / 16 of the 128-wide step; the result
 // C[4*(l/16) + q][l % 16] sits in accumulator element q of lane l.
 //
@@ -218,14 +218,6 @@ struct DecCfg {
   static constexpr int WG_PER_CU = U16 ? 4 : 3;             // resident workgroups per CU
 };
 static_assert(DEC_WB == 4, "one 4-block chunk per wave per phase");
-
-// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt[3:0] bits 3:0, vmcnt[5:4] bits
-// 15:14; expcnt and lgkmcnt left at their maxima, i.e. not waited on)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // Everything the decode kernel needs to know about one work item.
 struct DecItem {
@@ -509,7 +501,7 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
     for (int j = 0; j < NCB; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) s_acc[((wave * NCB + j) * 4 + q) * 64 + lane] = acc[mb][j][q];
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the partials are in LDS
+    wait_lgkmcnt<0>();  // the partials are in LDS
     __builtin_amdgcn_s_barrier();
     float v[NCB];
 #pragma unroll
@@ -529,12 +521,7 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
         const int col = col0 + 16 * j + r;
         if (row < rows) {
           const size_t o = (size_t)(row_base + row) * N + col;
-          // (with the fold, stores that reach the device-coherent level:
-          // the token's last arrival, maybe on another XCD, reads them)
-          if (fold)
-            __hip_atomic_store(p.y + o, v[j] + it.bias[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          else
-            p.y[o] = v[j] + it.bias[j];
+          p.y[o] = v[j] + it.bias[j];
         }
       }
       if (!fold) return;
@@ -545,8 +532,8 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
       // one rounding to bf16).  The router launch cleared the counters.
       // First the slots of the tile rows' tokens, one (row, slot) per thread
       // of the first two waves: where each sits in y (the gate/up launch
-      // recorded it) and its weight, issued before the wait for the stores
-      // so that the two round trips overlap.
+      // recorded it) and its weight, issued before the arrival (whose
+      // release waits for the stores) so that the two round trips overlap.
       const int k = p.k, tok_r = it.pair / k;
       int fpos = 0;
       float fw = 0.f;
@@ -557,7 +544,6 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
           fw = p.topk_w[ti * k + j];
         }
       }
-      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's rows are stored
       // (staged in the split's buffers, unused by the down projection)
       int* s_tok = (int*)s_sc;
       int* s_pos = (int*)&s_codes[0][0][0];
@@ -570,7 +556,10 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
       const int spans = (N + 63) >> 6, span = col0 >> 6;
       if (wave == 0 && lane < 16) {
         int t = -1;
-        if (lane < rows && atomicAdd(p.fold_cnt + (size_t)tok_r * spans + span, 1) == k - 1) t = tok_r;
+        // (acquire-release: the rows stored above are visible to the token's
+        // last arrival, maybe on another XCD, and that one sees the rows of
+        // every earlier arrival)
+        if (lane < rows && arrive_acq_rel(p.fold_cnt + (size_t)tok_r * spans + span) == k - 1) t = tok_r;
         s_tok[lane] = t;
       }
       __syncthreads();
@@ -591,8 +580,7 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           if (tq[q] >= 0 && j < k)
-            yv[q][j] = __hip_atomic_load(p.y + (size_t)s_pos[(wave + NW * q) * 8 + j] * N + colc, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
+            yv[q][j] = p.y[(size_t)s_pos[(wave + NW * q) * 8 + j] * N + colc];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (tq[q] < 0 || col >= N) continue;

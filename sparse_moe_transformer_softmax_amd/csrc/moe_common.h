@@ -44,6 +44,31 @@ __host__ __device__ __forceinline__ int mx6_byte_offset(int b, int i) {
   return (b >> 2) * MX6_GROUP_BYTES + (((i >> 4) << 2) + (b & 3)) * 16 + (i & 15);
 }
 
+// s_waitcnt with only the vector-memory counter (vmcnt, 6 bits: bits 3:0
+// and 15:14 of the gfx9 encoding) or only the LDS/scalar counter (lgkmcnt,
+// bits 11:8) waited on; the other fields are left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt is 4 bits");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (N << 8));
+}
+
+// Counts a workgroup in on a device-wide arrival counter and returns the
+// count before it.  Acquire-release at agent scope: the stores the
+// workgroup made before (the caller passes a workgroup barrier between
+// them and this call) are visible to every workgroup whose own arrival
+// comes later, and the caller sees the stores of every earlier arrival --
+// across XCDs too (the compiler brackets the atomic with the L2 write-back
+// and invalidate that this needs on gfx950).
+__device__ __forceinline__ int arrive_acq_rel(int* counter) {
+  return __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }

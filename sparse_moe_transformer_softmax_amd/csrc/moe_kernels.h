@@ -82,6 +82,8 @@ int launch_gemm_gateup(const GemmParams& p, int max_tiles, int mode, hipStream_t
 int launch_gemm_down(const GemmParams& p, int max_tiles, int mode, hipStream_t s);
 int launch_combine(const CombineParams& p, hipStream_t s);
 int launch_rmsnorm(const uint16_t* x, uint16_t* out, int T, int d, float eps, hipStream_t s);
+int launch_residual_rmsnorm(const uint16_t* x, const void* y, bool y_f32, uint16_t* x_out, uint16_t* n_out, int T,
+                            int d, float eps, hipStream_t s);
 int launch_zero_ints(int* p, int n, hipStream_t s);
 
 // ints between consecutive expert cursors (one 128-byte cache line)

@@ -212,20 +212,19 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
     }
   } else {
     // ---- K-split exchange: every workgroup of the token block writes its
-    // partial logits with stores that reach the device-coherent level, waits
-    // for them, and counts itself in; the last one sums the partials in
-    // slice order (loads from the same level), adds the bias and carries on
-    // alone ----
+    // partial logits and counts itself in on the block's arrival counter
+    // (acquire-release, so the partials of every slice are visible to the
+    // last arrival); the last one sums the partials in slice order, adds
+    // the bias and carries on alone ----
     float* part = p.part + (size_t)tb * p.ks * MT * E;
     for (int u = tid; u < MT * E; u += RT_THREADS) {
       const int tl = u / E, e = u - tl * E;
       float v = 0.f;
       for (int q = 0; q < KS; ++q) v += s_part[(q * MT + tl) * ES + e];
-      __hip_atomic_store(part + (size_t)kslice * MT * E + u, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      part[(size_t)kslice * MT * E + u] = v;
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the partials have reached memory
     __syncthreads();
-    if (tid == 0) s_flag = (atomicAdd(p.tb_done + tb * CURSOR_STRIDE, 1) == p.ks - 1);
+    if (tid == 0) s_flag = (arrive_acq_rel(p.tb_done + tb * CURSOR_STRIDE) == p.ks - 1);
     __syncthreads();
     if (!s_flag) return;
     for (int u = tid; u < MT * E; u += RT_THREADS) {
@@ -234,9 +233,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
       const float bias = p.router_b[u - (u / E) * E];
       float pv[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        pv[q] = q < p.ks ? __hip_atomic_load(part + (size_t)q * MT * E + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                         : 0.f;
+      for (int q = 0; q < 8; ++q) pv[q] = q < p.ks ? part[(size_t)q * MT * E + u] : 0.f;
       float v = 0.f;
 #pragma unroll
       for (int q = 0; q < 8; ++q)

@@ -43,7 +43,9 @@ def rel_max_err(out: np.ndarray, ref: np.ndarray) -> float:
 
 
 TOL = 1e-2  # max |err| <= 1e-2 * rms(ref)
-W_TOL = 1e-5  # gate weights, relative
+# gate weights, relative: the fp32 router's logits carry errors of a few
+# 1e-7 at d = 2880 (measured gate-weight error up to 7e-7)
+W_TOL = 1e-6
 
 
 def bf16_tensor_to_f64(t) -> np.ndarray:
@@ -66,8 +68,6 @@ def check_routing(ids_gpu: np.ndarray, w_gpu: np.ndarray, counts_gpu: np.ndarray
     wr = np.take_along_axis(w_ref, order_r, 1)
     werr = float(np.max(np.abs(wg - wr) / np.abs(wr)))
     print(f"[gpu-case]   gate weight max rel err {werr:.2e}", flush=True)
-    # fp32 router: logits carry ~1e-6 absolute error at d = 2880, the
-    # selected softmax about twice that in relative terms
     assert werr <= W_TOL
     assert np.array_equal(counts_gpu, np.bincount(ids_ref.reshape(-1), minlength=E))
     # slots in descending logit order

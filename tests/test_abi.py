@@ -65,3 +65,21 @@ def test_zero_tokens_is_a_no_op():
     assert _call(T=0) == 0
     assert _call(T=0, ptr=0, out=0) == 0
     assert _call(T=0, d=100) == -2
+
+
+def _resid(x=0x10000, yb=None, yf=0x20000, xo=0x30000, no=0x40000, T=4, d=64, eps=1e-5):
+    P = ctypes.c_void_p
+    return moe.lib().moe_rmsnorm_residual(P(x), P(yb), P(yf), P(xo), P(no), T, d, eps, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=48), -2), (dict(T=-1), -2), (dict(eps=-1.0), -2), (dict(yb=0x50000), -1), (dict(yf=None), -1),
+    (dict(x=None), -1), (dict(xo=None), -1), (dict(xo=0x30004), -4), (dict(no=0x10040), -7),
+    (dict(xo=0x10040), -7), (dict(no=0x30000), -7), (dict(xo=0x20000), -7),
+])
+def test_rmsnorm_residual_argument_errors(kw, status):
+    assert _resid(**kw) == status
+
+
+def test_rmsnorm_residual_zero_rows_is_a_no_op():
+    assert _resid(T=0) == 0

@@ -11,7 +11,7 @@ import pytest
 
 from oracle import moe_oracle as O
 from oracle.workload_inputs import make_inputs
-from sparse_moe_transformer_softmax_amd.workloads import WORKLOADS, Workload
+from moe_inputs.workloads import WORKLOADS, Workload
 import sparse_moe_transformer_softmax_amd as moe
 from tests.parity_util import TOL, KEYS, bf16_excess, bf16_tensor_to_f64, check_routing, rel_max_err, to_gpu
 

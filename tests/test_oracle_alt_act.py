@@ -8,7 +8,7 @@ import torch
 
 from oracle import moe_oracle as O
 from oracle.workload_inputs import make_inputs
-from sparse_moe_transformer_softmax_amd.workloads import WORKLOADS
+from moe_inputs.workloads import WORKLOADS
 
 
 def test_alt_swish_is_scaled_silu():

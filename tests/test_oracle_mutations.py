@@ -52,6 +52,16 @@ def _b2_outside(xs, w13, b13, w2, b2, c):
     return ORIG["expert_ffn"](xs, w13, b13, w2, b2, c) - b2[None, :] + (b2[None, :] * 0.5)
 
 
+def _gap_inner_slots(logits, k):
+    srt = -np.sort(-logits, axis=1)
+    return srt[:, k - 2] - srt[:, k - 1]
+
+
+def _gap_wrong_end(logits, k):
+    srt = np.sort(logits, axis=1)
+    return srt[:, k] - srt[:, k - 1]
+
+
 def _router_no_bias(x, wr, b):
     return x @ wr.T
 
@@ -73,6 +83,8 @@ MUTATIONS = [
     ("expert_ffn", _w2_transposed),
     ("expert_ffn", _b2_outside),
     ("router_logits", _router_no_bias),
+    ("topk_gap", _gap_inner_slots),
+    ("topk_gap", _gap_wrong_end),
     ("rmsnorm", _rmsnorm_no_eps_mean),
 ]
 

@@ -9,7 +9,7 @@ import pytest
 
 from oracle import moe_oracle as O
 from oracle.workload_inputs import make_inputs
-from sparse_moe_transformer_softmax_amd.workloads import WORKLOADS
+from moe_inputs.workloads import WORKLOADS
 
 
 def e2m3_grid():

@@ -13,7 +13,7 @@ import scipy.special
 import torch
 
 from oracle import moe_oracle as O
-from sparse_moe_transformer_softmax_amd import synth
+from moe_inputs import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -178,6 +178,38 @@ def test_topk_ties_go_to_lower_index():
     assert ids[2].tolist() == [1, 2, 4, 6]
 
 
+def test_topk_gap_against_subset_brute_force():
+    """The gap of a row is the distance from the weakest selected logit to
+    the strongest unselected one, the selected set taken by brute force over
+    all C(8,4) = 70 subsets; moving those two logits towards each other by
+    half the gap plus a little changes the set, any perturbation below half
+    the gap keeps it (catches the gap between slots k-2 and k-1, a sign
+    error, or a gap measured from the wrong end of the order)."""
+    x, wr, br = _tiny_router(T=120)
+    logits, _, _ = O.route(x, wr, br, 4)
+    gap = O.topk_gap(logits, 4)
+    rng = np.random.default_rng(4)
+    for t in range(logits.shape[0]):
+        l = logits[t]
+        best = max(itertools.combinations(range(8), 4), key=lambda s: sum(l[list(s)]))
+        rest = [e for e in range(8) if e not in best]
+        want = min(l[list(best)]) - max(l[rest])
+        assert gap[t] == want
+        assert gap[t] > 0
+        lo = min(best, key=lambda e: l[e])
+        hi = max(rest, key=lambda e: l[e])
+        moved = l.copy()
+        moved[lo] -= 0.5 * gap[t] * 1.01
+        moved[hi] += 0.5 * gap[t] * 1.01
+        assert hi in O.topk_experts(moved[None, :], 4)[0]
+        noise = rng.uniform(-0.49, 0.49, 8) * gap[t]
+        assert set(O.topk_experts((l + noise)[None, :], 4)[0]) == set(best)
+    # k = E: no unselected expert; a tie at the boundary: gap 0
+    assert np.all(np.isinf(O.topk_gap(logits, 8)))
+    tie = np.array([[3.0, 1.0, 2.0, 2.0, 0.5]])
+    assert O.topk_gap(tie, 2)[0] == 0.0 and O.topk_gap(tie, 1)[0] == 1.0 and O.topk_gap(tie, 3)[0] == 1.0
+
+
 def test_router_one_hot_input():
     """x = e_j makes each logit W_r[e, j] + b[e] (catches a transposed
     router weight or a dropped bias)."""
@@ -298,7 +330,7 @@ def test_dense_masked_equals_sparse_tiny(stress):
     layer on the tiny workload (T16 d128 I128 E8 k4), and on a clamp-stress
     variant whose scale exponents are 0..2 (pre-activations hit the clamp)."""
     from oracle.workload_inputs import make_inputs
-    from sparse_moe_transformer_softmax_amd.workloads import WORKLOADS
+    from moe_inputs.workloads import WORKLOADS
     wl = WORKLOADS["tiny"]
     inp = make_inputs(wl)
     if stress:

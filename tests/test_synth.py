@@ -3,8 +3,8 @@ distributions of the workloads."""
 import numpy as np
 
 from oracle import moe_oracle as O
-from sparse_moe_transformer_softmax_amd import synth
-from sparse_moe_transformer_softmax_amd.workloads import WORKLOADS
+from moe_inputs import synth
+from moe_inputs.workloads import WORKLOADS
 
 
 def test_deterministic_and_seed_sensitive():
