@@ -43,9 +43,14 @@ def rel_max_err(out: np.ndarray, ref: np.ndarray) -> float:
 
 
 TOL = 1e-2  # max |err| <= 1e-2 * rms(ref)
-# gate weights, relative: the fp32 router's logits carry errors of a few
-# 1e-7 at d = 2880 (measured gate-weight error up to 7e-7)
-W_TOL = 1e-6
+# gate weights, relative.  The pages fix no precision for the router; the
+# kernel sums each logit's d = 2880 exact bf16 products in fp32, about d/32
+# + 24 roundings of partial sums of order 1-3, i.e. a logit error of order
+# sqrt(114) * 2^-24 * 2 ~ 2e-6 in the far tail, and a selected-softmax weight
+# moves by at most twice the largest logit error in relative terms.  The
+# largest error measured over every case (E 8 .. 256, d up to 4160) is
+# 1.1e-6.
+W_TOL = 4e-6
 
 
 def bf16_tensor_to_f64(t) -> np.ndarray:

@@ -5,7 +5,7 @@ at its full depth on one GPU, checked two ways:
 
 * every one of the 36 seeded layers against the fp64 oracle on its own
   gap-conditioned input: expert ids and per-expert counts bit-exact and gate
-  weights to 1e-6 on all 2048 tokens, and the layer output on two sampled
+  weights to 4e-6 on all 2048 tokens, and the layer output on two sampled
   tokens within the bf16 bound;
 * the stack entry point against its own steps -- RMSNorm, the layer, the
   fused residual add + RMSNorm -- called layer by layer through the C ABI,
