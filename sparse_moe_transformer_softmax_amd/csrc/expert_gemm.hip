@@ -28,6 +28,13 @@
 #include "moe_common.h"
 #include "moe_kernels.h"
 
+// The folded combine's cross-workgroup ordering relies on gfx950's cache
+// behaviour for agent-scope atomic stores and loads (see the down
+// projection's epilogue).
+#if defined(__HIP_DEVICE_COMPILE__) && !defined(__gfx950__)
+#error "expert_gemm.hip is written for gfx950 only"
+#endif
+
 namespace moe {
 
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1: array indices
@@ -521,7 +528,11 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
         const int col = col0 + 16 * j + r;
         if (row < rows) {
           const size_t o = (size_t)(row_base + row) * N + col;
-          p.y[o] = v[j] + it.bias[j];
+          // (with the fold, a device-coherent store: see below)
+          if (fold)
+            __hip_atomic_store(p.y + o, v[j] + it.bias[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else
+            p.y[o] = v[j] + it.bias[j];
         }
       }
       if (!fold) return;
@@ -530,10 +541,23 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
       // arrival that completes a token's k rows sums them for the span, in
       // slot order, exactly as the separate combine does (an fma per slot,
       // one rounding to bf16).  The router launch cleared the counters.
+      //
+      // Ordering across workgroups (the last arrival may run on another
+      // XCD, whose L2 is not coherent with this one's): the rows are stored
+      // with agent-scope atomic stores, which gfx950 writes through to the
+      // device-coherent level, and every wave waits for its stores to
+      // complete (vmcnt 0) before the workgroup barrier that precedes the
+      // arrival, so the arrival is performed after the rows are visible at
+      // that level; the last arrival reads them with agent-scope atomic
+      // loads, which read from that level, issued after it has seen the
+      // count.  An acquire-release arrival would order the same accesses in
+      // the language's memory model, but on gfx950 it writes back the XCD's
+      // whole L2 once per workgroup: 103 instead of 36.5 us for the 20b
+      // decode down projection.
       // First the slots of the tile rows' tokens, one (row, slot) per thread
       // of the first two waves: where each sits in y (the gate/up launch
-      // recorded it) and its weight, issued before the arrival (whose
-      // release waits for the stores) so that the two round trips overlap.
+      // recorded it) and its weight, issued before the wait for the stores
+      // so that the two round trips overlap.
       const int k = p.k, tok_r = it.pair / k;
       int fpos = 0;
       float fw = 0.f;
@@ -544,6 +568,7 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
           fw = p.topk_w[ti * k + j];
         }
       }
+      wait_vmcnt<0>();  // this wave's rows are stored
       // (staged in the split's buffers, unused by the down projection)
       int* s_tok = (int*)s_sc;
       int* s_pos = (int*)&s_codes[0][0][0];
@@ -556,10 +581,10 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
       const int spans = (N + 63) >> 6, span = col0 >> 6;
       if (wave == 0 && lane < 16) {
         int t = -1;
-        // (acquire-release: the rows stored above are visible to the token's
-        // last arrival, maybe on another XCD, and that one sees the rows of
-        // every earlier arrival)
-        if (lane < rows && arrive_acq_rel(p.fold_cnt + (size_t)tok_r * spans + span) == k - 1) t = tok_r;
+        if (lane < rows &&
+            __hip_atomic_fetch_add(p.fold_cnt + (size_t)tok_r * spans + span, 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT) == k - 1)
+          t = tok_r;
         s_tok[lane] = t;
       }
       __syncthreads();
@@ -580,7 +605,8 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           if (tq[q] >= 0 && j < k)
-            yv[q][j] = p.y[(size_t)s_pos[(wave + NW * q) * 8 + j] * N + colc];
+            yv[q][j] = __hip_atomic_load(p.y + (size_t)s_pos[(wave + NW * q) * 8 + j] * N + colc, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (tq[q] < 0 || col >= N) continue;
