@@ -155,6 +155,24 @@ int moe_route(const void* x, const void* router_w, const float* router_b, int T,
  * (0 if the sizes are invalid). */
 size_t moe_workspace_bytes(int T, int d, int I, int E, int k);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the layer
+ * of moe_layer_forward (same arguments, layouts, results and errors) with
+ * its scratch in a static device array of MOE_NOALLOC_SCRATCH_BYTES that
+ * every GPU the library runs on holds until the process ends.  The call
+ * allocates nothing (no hipMalloc or hipFree, no library allocation); it
+ * launches one small kernel that clears the array's counters, then the
+ * layer.  Sizes whose workspace (moe_workspace_bytes) exceeds the array
+ * return MOE_ERR_WORKSPACE -- about 800 tokens at d = I = 2880, k = 4.
+ * All calls on one GPU share its array: calls that overlap in time on one
+ * GPU (different streams, or different host threads) race and must not be
+ * issued; calls on one stream are ordered and safe. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_layer_forward_noalloc(const void* x, const void* router_w, const float* router_b,
+                              const uint8_t* w13_codes, const uint8_t* w13_scales, const float* b13,
+                              const uint8_t* w2_codes, const uint8_t* w2_scales, const float* b2, int T, int d, int I,
+                              int E, int k, float clamp, void* out, void* stream);
+
 /* Prepares a caller-owned workspace (256-byte aligned, at least
  * moe_workspace_bytes) for first use by clearing its counter block with a
  * kernel on `stream`.  Every completed call leaves the block cleared again. */

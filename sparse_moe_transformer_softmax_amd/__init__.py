@@ -16,10 +16,12 @@ __all__ = [
     "moe_stack_forward", "moe_release", "moe_status_string", "moe_version", "LIB_PATH",
     "moe_timing_enable", "moe_timing_read", "KERNELS", "moe_layer_forward_mx6", "moe_layer_forward_mx6_dbg",
     "moe_layer_forward_ex", "MOE_LAYER_MXFP6", "MOE_LAYER_ALT_ACT", "moe_rmsnorm_residual",
+    "moe_layer_forward_noalloc", "MOE_NOALLOC_SCRATCH_BYTES",
 ]
 
 MOE_LAYER_MXFP6 = 1
 MOE_LAYER_ALT_ACT = 2
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 _lib = None
@@ -31,6 +33,7 @@ _SIGS = {
     "moe_layer_forward": (_I, [_P] * 9 + [_I] * 5 + [_F, _P, _P]),
     "moe_layer_forward_dbg": (_I, [_P] * 9 + [_I] * 5 + [_F] + [_P] * 6),
     "moe_layer_forward_mx6": (_I, [_P] * 9 + [_I] * 5 + [_F, _P, _P]),
+    "moe_layer_forward_noalloc": (_I, [_P] * 9 + [_I] * 5 + [_F, _P, _P]),
     "moe_layer_forward_mx6_dbg": (_I, [_P] * 9 + [_I] * 5 + [_F] + [_P] * 6),
     "moe_layer_forward_ex": (_I, [_P] * 9 + [_I] * 5 + [_F, _I] + [_P] * 6),
     "moe_route": (_I, [_P] * 3 + [_I] * 4 + [_P] * 4),
@@ -181,6 +184,15 @@ def moe_layer_forward_mx6_dbg(x, router_w, router_b, w13_codes, w13_scales, b13,
     """moe_layer_forward_dbg for the fast mode."""
     return moe_layer_forward_dbg(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
                                  k=k, clamp=clamp, stream=stream, _fn="moe_layer_forward_mx6_dbg")
+
+
+def moe_layer_forward_noalloc(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
+                              k: int = 4, clamp: float = 7.0, out=None, stream=None):
+    """moe_layer_forward with its scratch in the library's static device
+    array (no allocation inside the call; pass `out` to allocate nothing
+    here either); see include/moe_mi355x.h."""
+    return moe_layer_forward(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
+                             k=k, clamp=clamp, out=out, stream=stream, _fn="moe_layer_forward_noalloc")
 
 
 def moe_layer_forward_dbg(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,

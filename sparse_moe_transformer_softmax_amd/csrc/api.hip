@@ -296,6 +296,33 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free entry point: its scratch is this file-scope device array,
+// one copy per GPU the library runs on, held until the process ends.  In
+// host code `scratch` only names the symbol; its device address on each GPU
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[64] = {};
+
+int scratch_for_current_device(uint8_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return MOE_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = (uint8_t*)ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -377,6 +404,27 @@ int moe_layer_forward(const void* x, const void* router_w, const float* router_b
                       void* out, void* stream) {
   LayerArgs a{x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, d, I, E, k, clamp};
   return forward_owned(a, out, stream);
+}
+
+int moe_layer_forward_noalloc(const void* x, const void* router_w, const float* router_b,
+                              const uint8_t* w13_codes, const uint8_t* w13_scales, const float* b13,
+                              const uint8_t* w2_codes, const uint8_t* w2_scales, const float* b2, int T, int d, int I,
+                              int E, int k, float clamp, void* out, void* stream) {
+  LayerArgs a{x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, d, I, E, k, clamp};
+  if (int st = check_layer(a, out)) return st;
+  if (T == 0) return MOE_OK;
+  if (!out) return MOE_ERR_NULL_PTR;
+  const Layout L = layout(T, d, I, E, k);
+  if (L.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  if (int st = check_device()) return st;
+  uint8_t* ws = nullptr;
+  if (int st = scratch_for_current_device(&ws)) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // the counters the kernels expect at zero, cleared by a kernel (not a
+  // memset) so that the call can be captured into a graph; the rest of the
+  // scratch is written before it is read within the call
+  if (launch_zero_ints((int*)ws, kHeaderInts, s)) return MOE_ERR_HIP;
+  return run_layer(a, L, ws, out, nullptr, nullptr, nullptr, nullptr, false, s);
 }
 
 int moe_layer_forward_dbg(const void* x, const void* router_w, const float* router_b, const uint8_t* w13_codes,
