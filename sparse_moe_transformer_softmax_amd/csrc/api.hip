@@ -22,7 +22,7 @@ constexpr size_t kAlign = 256;
 // each so that atomics on different counters do not serialize
 constexpr int kCursor0 = 64;
 constexpr int kTbDone0 = kCursor0 + CURSOR_STRIDE * 256;
-constexpr int kHeaderInts = kTbDone0 + CURSOR_STRIDE * ROUTE_MAX_SPLIT_BLOCKS;
+constexpr int kHeaderInts = kTbDone0 + CURSOR_STRIDE * ROUTE_MAX_TB;
 
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -46,7 +46,7 @@ Layout layout(int T, int d, int I, int E, int k) {
   L.n_tiles = o; o = up(o + 4);
   L.tiles = o; o = up(o + (size_t)L.max_tiles * 8);
   L.expert_rows = o; o = up(o + (size_t)E * T * 4);
-  L.part = o; o = up(o + (size_t)ROUTE_MAX_SPLIT_BLOCKS * 16 * E * 4);
+  L.part = o; o = up(o + route_partial_bytes(T, E));
   L.xq = o; o = up(o + (size_t)T * mx6_row_bytes(d / 32));
   L.hq = o; o = up(o + P * mx6_row_bytes(I / 32));
   L.y = o; o = up(o + P * d * 4);

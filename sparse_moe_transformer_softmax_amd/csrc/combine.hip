@@ -7,8 +7,13 @@
 // weighting of the chosen experts).  RMSNorm divides by the root mean square
 // with no bias or shift (same page, RMSNorm 替换 LayerNorm).
 //
-// One wave per token; every lane handles float4 column groups, so each
-// expert row is read with fully coalesced 16-byte loads.
+// The plain combine has one thread per float4 column group of a token.  The
+// row kernels of the stack (the combine with the residual add and RMSNorm,
+// the residual add + RMSNorm on its own, and RMSNorm) give each row one
+// 256-thread workgroup: thread i handles float4 column groups i, i + 256,
+// ...; the row's sum of squares is reduced the same way in all three
+// (within each wave, then the four waves' sums in wave order), so the stack
+// entry point equals its steps bit for bit.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -29,32 +34,54 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Residual step of the pre-norm stack for one float4 column group c of a
-// row: xo[c] = bf16(xi[c] + add) with the add in fp32; returns the sum of
-// squares of the rounded values (the RMSNorm statistic).
-__device__ __forceinline__ float residual_add4(const uint16_t* xi, uint16_t* xo, int c, float4 add) {
-  const float4 x = unpack_bf16x4(((const uint2*)xi)[c]);
-  const uint2 xb = pack_bf16x4(make_float4(x.x + add.x, x.y + add.y, x.z + add.z, x.w + add.w));
-  ((uint2*)xo)[c] = xb;
-  const float4 xn = unpack_bf16x4(xb);
-  return xn.x * xn.x + xn.y * xn.y + xn.z * xn.z + xn.w * xn.w;
+constexpr int ROW_THREADS = 256;
+constexpr int ROW_KEEP = 4;  // float4 groups per thread kept in registers (rows up to 4096 wide)
+
+// Sum over the row's 256 threads of each thread's partial sum of squares:
+// within each wave (butterfly), then the four waves' sums in wave order.
+__device__ __forceinline__ float row_sum(float v, float* s_red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  return ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3];
 }
 
-// Second pass of the RMSNorm of one row held by one wave: no = bf16(xr *
-// 1/sqrt(ss/d + eps)), ss the wave's summed squares (reduced here).
-__device__ __forceinline__ void rmsnorm_row(const uint16_t* xr, uint16_t* no, float ss, int d, float eps, int lane) {
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int c = lane; c < (d >> 2); c += 64) {
-    const float4 x = unpack_bf16x4(((const uint2*)xr)[c]);
+__device__ __forceinline__ float rms_scale(float ss, int d, float eps) { return 1.0f / sqrtf(ss / (float)d + eps); }
+
+__device__ __forceinline__ float sumsq4(float4 v) { return v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w; }
+
+// The RMSNorm pass of one row: no[c] = bf16(x[c] * inv) for this thread's
+// groups; the first ROW_KEEP come from registers (xk), later ones are re-read
+// from xr, which this same thread wrote or read earlier.
+__device__ __forceinline__ void norm_row(const uint16_t* xr, uint16_t* no, const float4 (&xk)[ROW_KEEP], float inv,
+                                         int d4) {
+  int i = 0;
+  for (int c = threadIdx.x; c < d4; c += ROW_THREADS, ++i) {
+    float4 x;
+    if (i < ROW_KEEP) {
+#pragma unroll
+      for (int q = 0; q < ROW_KEEP; ++q)
+        if (q == i) x = xk[q];
+    } else {
+      x = unpack_bf16x4(((const uint2*)xr)[c]);
+    }
     ((uint2*)no)[c] = pack_bf16x4(make_float4(x.x * inv, x.y * inv, x.z * inv, x.w * inv));
   }
 }
 
-__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= p.T) return;
+__device__ __forceinline__ void keep(float4 (&xk)[ROW_KEEP], int i, float4 v) {
+#pragma unroll
+  for (int q = 0; q < ROW_KEEP; ++q)
+    if (q == i) xk[q] = v;
+}
+
+// Stack variant of the combine, one row per workgroup: the combine sum,
+// x_out = bf16(x + sum) (the add in fp32) and, unless it is the last layer,
+// n_out = bf16(RMSNorm(x_out)).
+__global__ __launch_bounds__(ROW_THREADS) void combine_kernel(CombineParams p) {
+  __shared__ float s_red[ROW_THREADS / 64];
+  const int t = blockIdx.x;
   const int k = p.k, d = p.d, d4 = d >> 2;
   const float4* rows[8];
   float w[8];
@@ -64,9 +91,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     rows[j] = (const float4*)(p.y + (size_t)(p.offsets[e] + p.rel_pos[pair]) * d);
     w[j] = p.topk_w[pair];
   }
-  const bool stack = p.resid_out != nullptr;
+  const uint2* xi = (const uint2*)(p.resid_in + (size_t)t * d);
+  uint2* xo = (uint2*)(p.resid_out + (size_t)t * d);
   float ss = 0.f;
-  for (int c = lane; c < d4; c += 64) {
+  float4 xk[ROW_KEEP];
+  int i = 0;
+  for (int c = threadIdx.x; c < d4; c += ROW_THREADS, ++i) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
       const float4 v = rows[j][c];
@@ -77,28 +107,45 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     }
     if (p.out_f32) ((float4*)(p.out_f32 + (size_t)t * d))[c] = acc;
     if (p.out) ((uint2*)(p.out + (size_t)t * d))[c] = pack_bf16x4(acc);
-    if (stack) ss += residual_add4(p.resid_in + (size_t)t * d, p.resid_out + (size_t)t * d, c, acc);
+    const float4 x = unpack_bf16x4(xi[c]);
+    const uint2 xb = pack_bf16x4(make_float4(x.x + acc.x, x.y + acc.y, x.z + acc.z, x.w + acc.w));
+    xo[c] = xb;
+    const float4 xn = unpack_bf16x4(xb);
+    keep(xk, i, xn);
+    ss += sumsq4(xn);
   }
-  if (!stack || p.norm_out == nullptr) return;
-  rmsnorm_row(p.resid_out + (size_t)t * d, p.norm_out + (size_t)t * d, ss, d, p.eps, lane);
+  if (p.norm_out == nullptr) return;
+  const float inv = rms_scale(row_sum(ss, s_red), d, p.eps);
+  norm_row(p.resid_out + (size_t)t * d, p.norm_out + (size_t)t * d, xk, inv, d4);
 }
 
-// The residual add and RMSNorm on their own (one wave per row): x_out =
-// bf16(x + y), n_out = bf16(RMSNorm(x_out)); y is bf16 or fp32.
+// The residual add and RMSNorm on their own, one row per workgroup:
+// x_out = bf16(x + y), n_out = bf16(RMSNorm(x_out)); y is bf16 or fp32.
 template <bool YF32>
-__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const uint16_t* x, const void* y, uint16_t* x_out,
-                                                               uint16_t* n_out, int T, int d, float eps) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+__global__ __launch_bounds__(ROW_THREADS) void residual_rmsnorm_kernel(const uint16_t* x, const void* y,
+                                                                       uint16_t* x_out, uint16_t* n_out, int T, int d,
+                                                                       float eps) {
+  __shared__ float s_red[ROW_THREADS / 64];
+  const int t = blockIdx.x, d4 = d >> 2;
   const size_t ro = (size_t)t * d;
+  const uint2* xi = (const uint2*)(x + ro);
+  uint2* xo = (uint2*)(x_out + ro);
   float ss = 0.f;
-  for (int c = lane; c < (d >> 2); c += 64) {
+  float4 xk[ROW_KEEP];
+  int i = 0;
+  for (int c = threadIdx.x; c < d4; c += ROW_THREADS, ++i) {
     const float4 a = YF32 ? ((const float4*)((const float*)y + ro))[c]
                           : unpack_bf16x4(((const uint2*)((const uint16_t*)y + ro))[c]);
-    ss += residual_add4(x + ro, x_out + ro, c, a);
+    const float4 xv = unpack_bf16x4(xi[c]);
+    const uint2 xb = pack_bf16x4(make_float4(xv.x + a.x, xv.y + a.y, xv.z + a.z, xv.w + a.w));
+    xo[c] = xb;
+    const float4 xn = unpack_bf16x4(xb);
+    keep(xk, i, xn);
+    ss += sumsq4(xn);
   }
-  if (n_out != nullptr) rmsnorm_row(x_out + ro, n_out + ro, ss, d, eps, lane);
+  if (n_out == nullptr) return;
+  const float inv = rms_scale(row_sum(ss, s_red), d, eps);
+  norm_row(x_out + ro, n_out + ro, xk, inv, d4);
 }
 
 // Plain combine: one thread per float4 column group of one token, so that a
@@ -122,24 +169,23 @@ __global__ __launch_bounds__(256) void combine_cols_kernel(CombineParams p) {
   if (p.out) ((uint2*)(p.out + (size_t)t * d))[c] = pack_bf16x4(acc);
 }
 
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* x, uint16_t* out, int T, int d, float eps) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const int d4 = d >> 2;
+// RMSNorm of one row per workgroup (out may equal x: every thread reads its
+// groups before the barrier inside row_sum and rewrites only its own).
+__global__ __launch_bounds__(ROW_THREADS) void rmsnorm_kernel(const uint16_t* x, uint16_t* out, int T, int d,
+                                                             float eps) {
+  __shared__ float s_red[ROW_THREADS / 64];
+  const int t = blockIdx.x, d4 = d >> 2;
   const uint2* xr = (const uint2*)(x + (size_t)t * d);
   float ss = 0.f;
-  for (int c = lane; c < d4; c += 64) {
+  float4 xk[ROW_KEEP];
+  int i = 0;
+  for (int c = threadIdx.x; c < d4; c += ROW_THREADS, ++i) {
     const float4 v = unpack_bf16x4(xr[c]);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    keep(xk, i, v);
+    ss += sumsq4(v);
   }
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  uint2* orow = (uint2*)(out + (size_t)t * d);
-  for (int c = lane; c < d4; c += 64) {
-    const float4 v = unpack_bf16x4(xr[c]);
-    orow[c] = pack_bf16x4(make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv));
-  }
+  const float inv = rms_scale(row_sum(ss, s_red), d, eps);
+  norm_row(x + (size_t)t * d, out + (size_t)t * d, xk, inv, d4);
 }
 
 __global__ void zero_ints_kernel(int* p, int n) {
@@ -151,19 +197,19 @@ int launch_combine(const CombineParams& p, hipStream_t s) {
   if (p.resid_out == nullptr) {
     hipLaunchKernelGGL(combine_cols_kernel, dim3((p.d / 4 + 255) / 256, p.T), dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL(combine_kernel, dim3((p.T + 3) / 4), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(combine_kernel, dim3(p.T), dim3(ROW_THREADS), 0, s, p);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_rmsnorm(const uint16_t* x, uint16_t* out, int T, int d, float eps, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3((T + 3) / 4), dim3(256), 0, s, x, out, T, d, eps);
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(ROW_THREADS), 0, s, x, out, T, d, eps);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_residual_rmsnorm(const uint16_t* x, const void* y, bool y_f32, uint16_t* x_out, uint16_t* n_out, int T,
                             int d, float eps, hipStream_t s) {
-  const dim3 g((T + 3) / 4), b(256);
+  const dim3 g(T), b(ROW_THREADS);
   if (y_f32)
     hipLaunchKernelGGL(residual_rmsnorm_kernel<true>, g, b, 0, s, x, y, x_out, n_out, T, d, eps);
   else

@@ -58,17 +58,6 @@ __device__ __forceinline__ void wait_lgkmcnt() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (N << 8));
 }
 
-// Counts a workgroup in on a device-wide arrival counter and returns the
-// count before it.  Acquire-release at agent scope: the stores the
-// workgroup made before (the caller passes a workgroup barrier between
-// them and this call) are visible to every workgroup whose own arrival
-// comes later, and the caller sees the stores of every earlier arrival --
-// across XCDs too (the compiler brackets the atomic with the L2 write-back
-// and invalidate that this needs on gfx950).
-__device__ __forceinline__ int arrive_acq_rel(int* counter) {
-  return __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
@@ -133,84 +122,7 @@ __device__ __forceinline__ void pack6x32(const uint8_t* c, uint32_t out[6]) {
   }
 }
 
-// Splits one 32-element block (values in registers, v[32]) into three E2M3
-// terms with their own scales: pk[t] receives the 32 six-bit codes of term t
-// packed little-endian, sc[t] its E8M0 byte.  On return v holds the residual.
-__device__ __forceinline__ void mx6x3_split(float (&v)[32], uint32_t (&pk)[3][6], int (&sc)[3]) {
-#pragma unroll
-  for (int t = 0; t < 3; ++t) {
-#pragma unroll
-    for (int w = 0; w < 6; ++w) pk[t][w] = 0;
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-#pragma unroll
-    for (int i = 0; i < 32; ++i)
-      if (v[i] != v[i]) amax = __builtin_inff();
-    const int se = mx6_scale_exp(amax);
-    sc[t] = se;
-    if (se == 255) continue;
-    const int k = se - 127;
-    // scale by 2^-k in two steps so that neither factor leaves the normal range
-    const float inv_hi = exp2i(-(k >> 1)), inv_lo = exp2i(-(k - (k >> 1)));
-    const float s_hi = exp2i(k >> 1), s_lo = exp2i(k - (k >> 1));
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      float q;
-      const uint32_t c = e2m3_round((v[i] * inv_hi) * inv_lo, q);
-      v[i] -= (q * s_hi) * s_lo;  // exact residual
-      const int bit = 6 * i;
-      pk[t][bit >> 5] |= c << (bit & 31);
-      if ((bit & 31) > 26) pk[t][(bit >> 5) + 1] |= c >> (32 - (bit & 31));
-    }
-  }
-}
-
-// Four-lane form of mx6x3_split: the 32 elements of a block live in four
-// lanes whose ids differ by X1 and X2 (lane group q holds elements
-// 8q .. 8q+7).  The block
-// maximum of every term is reduced across the four lanes; each lane returns
-// the 48 bits of its 8 codes per term (bits[t] low 48 bits = elements
-// 8q..8q+7 of term t, 6 bits each, little-endian), to be stored at byte
-// 6q of that term's 24-byte code field.
-template <int X1 = 1, int X2 = 2>
-__device__ __forceinline__ void mx6x3_split_quad(float (&v)[8], uint64_t (&bits)[3], int (&sc)[3]) {
-#pragma unroll
-  for (int t = 0; t < 3; ++t) {
-    bits[t] = 0;
-    float amax = 0.0f;
-    bool nan = false;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      amax = fmaxf(amax, fabsf(v[i]));
-      nan |= (v[i] != v[i]);
-    }
-    if (nan) amax = __builtin_inff();
-    if constexpr (X1 == 1 && X2 == 2) {
-      // lanes of a quad: DPP quad_perm [1,0,3,2] and [2,3,0,1]
-      amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0xB1, 0xf, 0xf, false)));
-      amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x4E, 0xf, 0xf, false)));
-    } else {
-      amax = fmaxf(amax, __shfl_xor(amax, X1));
-      amax = fmaxf(amax, __shfl_xor(amax, X2));
-    }
-    const int se = mx6_scale_exp(amax);
-    sc[t] = se;
-    if (se == 255) continue;
-    const int k = se - 127;
-    const float inv_hi = exp2i(-(k >> 1)), inv_lo = exp2i(-(k - (k >> 1)));
-    const float s_hi = exp2i(k >> 1), s_lo = exp2i(k - (k >> 1));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float q;
-      const uint32_t c = e2m3_round((v[i] * inv_hi) * inv_lo, q);
-      v[i] -= (q * s_hi) * s_lo;  // exact residual
-      bits[t] |= (uint64_t)c << (6 * i);
-    }
-  }
-}
-
-// One-lane form of mx6x3_split on the gfx950 scaled conversions: the lane
+// MX6x3 split of one 32-element block on the gfx950 scaled conversions: the lane
 // holds a whole 32-element block, even elements in ve and odd elements in vo
 // (the conversion packs source pair (ve[i], vo[i]) as elements 2i, 2i+1).
 // v_cvt_scalef32_2xpk16_fp6_f32 divides by the power-of-two scale and rounds

@@ -23,8 +23,8 @@ struct RouteParams {
   int2* tiles;               // [max_tiles] (expert, first row)
   // K split over workgroups (set by launch_route)
   int n_tb, ks;              // token blocks, workgroups per token block
-  float* part;               // [ROUTE_MAX_SPLIT_BLOCKS * 16][E] partial logits
-  int* tb_done;              // [ROUTE_MAX_SPLIT_BLOCKS * CURSOR_STRIDE] zero between calls
+  float* part;               // [n_tb * ks * 16 * mbr][E] partial logits (route_partial_bytes)
+  int* tb_done;              // [ROUTE_MAX_TB * CURSOR_STRIDE] zero between calls
   uint8_t* xq;               // MX6x3 rows of x [T, d/32, 80], or null (no split)
   int* fold_cnt;             // [n_fold] arrival counters of the combine folded into the down
   int n_fold;                //   GEMM, zeroed by the trailing workgroups (null: no fold)
@@ -88,8 +88,23 @@ int launch_zero_ints(int* p, int n, hipStream_t s);
 
 // ints between consecutive expert cursors (one 128-byte cache line)
 constexpr int CURSOR_STRIDE = 32;
-// most workgroups in the K-split router mode (token blocks x K slices)
-constexpr int ROUTE_MAX_SPLIT_BLOCKS = 16;
+// most token blocks whose K range the router splits over workgroups (one
+// arrival counter each), and the workgroups it aims for
+constexpr int ROUTE_MAX_TB = 256;
+constexpr int ROUTE_TARGET_WG = 256;
+// bytes of partial logits the router's K split exchanges for T tokens over E
+// experts (0: no split)
+size_t route_partial_bytes(int T, int E);
+
+// K sub-slices of a router workgroup's 16 waves: 16 / (its expert groups),
+// fewer where the LDS partials (sub-slices x 16 * mbr tokens x (16 * ncb + 1)
+// floats) would not fit 16 * 1032 floats
+__host__ __device__ inline int route_wave_kslices(int ncb, int ncbw, int mbr) {
+  const int eg = (ncb + ncbw - 1) / ncbw;
+  int ks = 16 / eg;
+  while (ks > 1 && ks * 16 * mbr * (16 * ncb + 1) > 16 * 1032) --ks;
+  return ks;
+}
 
 // rows per GEMM tile of the two configurations
 constexpr int MT_SMALL = 16;

@@ -33,6 +33,12 @@
 #include "moe_common.h"
 #include "moe_kernels.h"
 
+// The K-split exchange relies on gfx950's cache behaviour for agent-scope
+// atomic stores and loads (see the exchange in route_kernel).
+#if defined(__HIP_DEVICE_COMPILE__) && !defined(__gfx950__)
+#error "route.hip is written for gfx950 only"
+#endif
+
 namespace moe {
 
 constexpr int RT_THREADS = 1024;  // 16 waves
@@ -44,35 +50,35 @@ __device__ __forceinline__ void lds_wave_sync_route() {
 }
 constexpr int RT_LS = 260;        // LDS row stride of the logits (16-byte aligned rows)
 
-// MX6x3 split of one 32-element block of x by four lanes (q4 = lane % 4
-// holds elements 8q4 .. 8q4+7): the activation operand of the gate/up GEMM,
-// written in the piece-interleaved row layout.
+// MX6x3 split of one 32-element block of x by one lane (block u of the
+// token rows, u < T * nblk): the activation operand of the gate/up GEMM,
+// written in the piece-interleaved row layout as five 16-byte pieces.  The
+// split uses the gfx950 scaled FP6 conversions (round to nearest even with
+// the non-saturating block scale), as the split of h does.
 __device__ __forceinline__ void split_block(const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, int u, int nblk,
-                                            int d, int q4, bool ok) {
-  const int uu = ok ? u : 0;  // out-of-range quads compute on block 0 and store nothing
-  const int t = uu / nblk, b = uu - t * nblk;
-  const uint4 w4 = *(const uint4*)(x + (size_t)t * d + 32 * b + 8 * q4);
-  const uint32_t ws[4] = {w4.x, w4.y, w4.z, w4.w};
-  float v[8];
+                                            int d) {
+  const int t = u / nblk, b = u - t * nblk;
+  const uint4* src = (const uint4*)(x + (size_t)t * d + 32 * b);
+  v16f ve, vo;  // even and odd elements of the block
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    v[2 * h] = __uint_as_float(ws[h] << 16);
-    v[2 * h + 1] = __uint_as_float(ws[h] & 0xffff0000u);
+  for (int i = 0; i < 4; ++i) {
+    const uint4 w = src[i];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      ve[4 * i + h] = __uint_as_float(ws[h] << 16);
+      vo[4 * i + h] = __uint_as_float(ws[h] & 0xffff0000u);
+    }
   }
-  uint64_t bits[3];
-  int sc[3];
-  mx6x3_split_quad<1, 2>(v, bits, sc);
-  if (!ok) return;
+  uint32_t codes[18], scw;
+  mx6x3_split_lane(ve, vo, codes, scw);
   uint8_t* row = xq + (size_t)t * mx6_row_bytes(nblk);
-  // 2-byte stores never straddle a 16-byte piece (even offsets)
 #pragma unroll
-  for (int tt = 0; tt < 3; ++tt)
-#pragma unroll
-    for (int h = 0; h < 3; ++h)
-      *(uint16_t*)(row + mx6_byte_offset(b, 24 * tt + 6 * q4 + 2 * h)) = (uint16_t)(bits[tt] >> (16 * h));
-  if (q4 == 0)
-    *(uint2*)(row + mx6_byte_offset(b, 72)) =
-        make_uint2((uint32_t)sc[0] | ((uint32_t)sc[1] << 8) | ((uint32_t)sc[2] << 16), 0u);
+  for (int q = 0; q < 5; ++q) {
+    const v4u piece = q < 4 ? (v4u){codes[4 * q], codes[4 * q + 1], codes[4 * q + 2], codes[4 * q + 3]}
+                            : (v4u){codes[16], codes[17], scw, 0u};
+    *(v4u*)(row + mx6_byte_offset(b, 16 * q)) = piece;
+  }
 }
 
 // NCBW: 16-expert column blocks per wave (1 for E <= 64, 2 for E <= 128,
@@ -88,15 +94,15 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
   const int T = p.T, d = p.d, E = p.E, k = p.k;
   const int nblk = d >> 5;
 
-  // ---- trailing workgroups: MX6x3 split of x (256 blocks each) ----------
+  // ---- trailing workgroups: MX6x3 split of x (1024 blocks each) ---------
   const int nrw = p.n_tb * p.ks;
   if ((int)blockIdx.x >= nrw) {
-    const int u = ((int)blockIdx.x - nrw) * (RT_THREADS / 4) + (tid >> 2);
+    const int u = ((int)blockIdx.x - nrw) * RT_THREADS + tid;
     // (and clear the arrival counters of the down GEMM's folded combine)
     if (p.fold_cnt)
       for (int i = ((int)blockIdx.x - nrw) * RT_THREADS + tid; i < p.n_fold; i += ((int)gridDim.x - nrw) * RT_THREADS)
         p.fold_cnt[i] = 0;
-    split_block(p.x, p.xq, u, nblk, d, tid & 3, u < T * nblk);
+    if (u < T * nblk) split_block(p.x, p.xq, u, nblk, d);
     return;
   }
 
@@ -107,7 +113,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
   // groups, a wave owning column blocks eg, eg + EG, ... of its sub-slice
   const int kb0 = kslice * nblk / p.ks, kb1 = (kslice + 1) * nblk / p.ks;
   const int EG = (ncb + NCBW - 1) / NCBW;
-  const int KS = 16 / EG;
+  const int KS = route_wave_kslices(ncb, NCBW, MBR);
   const int eg = wave % EG, ks = wave / EG;  // waves with ks >= KS idle in the GEMM
   const int ES = 16 * ncb + 1;               // row stride of the partials
 
@@ -212,19 +218,29 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
     }
   } else {
     // ---- K-split exchange: every workgroup of the token block writes its
-    // partial logits and counts itself in on the block's arrival counter
-    // (acquire-release, so the partials of every slice are visible to the
-    // last arrival); the last one sums the partials in slice order, adds
-    // the bias and carries on alone ----
+    // partial logits and counts itself in on the block's arrival counter;
+    // the last one sums the partials in slice order, adds the bias and
+    // carries on alone.  The workgroups may run on different XCDs, whose
+    // L2s are not coherent with each other: the partials go out as
+    // device-coherent stores (agent-scope atomic stores, written through to
+    // the device-coherent level on gfx950), every wave waits for its stores
+    // (vmcnt 0) before the barrier that precedes the arrival, and the last
+    // arrival reads them with device-coherent loads issued after it has
+    // seen the count.  (An acquire-release arrival orders the same accesses
+    // but writes back the XCD's whole L2 per workgroup, which with the x
+    // split's rows in flight costs tens of microseconds at prefill sizes.)
     float* part = p.part + (size_t)tb * p.ks * MT * E;
     for (int u = tid; u < MT * E; u += RT_THREADS) {
       const int tl = u / E, e = u - tl * E;
       float v = 0.f;
       for (int q = 0; q < KS; ++q) v += s_part[(q * MT + tl) * ES + e];
-      part[(size_t)kslice * MT * E + u] = v;
+      __hip_atomic_store(part + (size_t)kslice * MT * E + u, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    wait_vmcnt<0>();  // this wave's partials are stored
     __syncthreads();
-    if (tid == 0) s_flag = (arrive_acq_rel(p.tb_done + tb * CURSOR_STRIDE) == p.ks - 1);
+    if (tid == 0)
+      s_flag = (__hip_atomic_fetch_add(p.tb_done + tb * CURSOR_STRIDE, 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT) == p.ks - 1);
     __syncthreads();
     if (!s_flag) return;
     for (int u = tid; u < MT * E; u += RT_THREADS) {
@@ -233,7 +249,9 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
       const float bias = p.router_b[u - (u / E) * E];
       float pv[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) pv[q] = q < p.ks ? part[(size_t)q * MT * E + u] : 0.f;
+      for (int q = 0; q < 8; ++q)
+        pv[q] = q < p.ks ? __hip_atomic_load(part + (size_t)q * MT * E + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : 0.f;
       float v = 0.f;
 #pragma unroll
       for (int q = 0; q < 8; ++q)
@@ -416,28 +434,43 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteParams p) {
 
 // LDS partials of a configuration: KS * MT * ES floats must fit s_part
 static bool route_fits(int ncb, int ncbw, int mbr) {
-  const int eg = (ncb + ncbw - 1) / ncbw, ks = 16 / eg;
+  const int ks = route_wave_kslices(ncb, ncbw, mbr);
   return ks >= 1 && ks * 16 * mbr * (16 * ncb + 1) <= 16 * 1032;
 }
 
 // Launch shape of the router: token-block height (16 * mbr), column blocks
-// per wave, token blocks and the workgroups per token block.  Small batches
-// split K over several workgroups so that the router weight streams through
-// more CUs; a batch of up to 32 tokens over at most 64 experts is one token
-// block.
+// per wave, token blocks and the workgroups per token block.  Every
+// workgroup streams the router weight of its K slice, so the K range is
+// split over enough workgroups (at most 8 per token block) that about 256
+// of them share the weight; batches of 512 tokens or more take 32-token
+// blocks; a batch of up to 32 tokens over at most 64 experts is one token
+// block.  (Measured at the 20b prefill, 120b Zipf prefill and 120b stack
+// sizes against 16- and 64-token blocks and against 512 workgroups: the
+// router launch with the x split takes 33, 80 and 39 us; 64-token blocks
+// take 35, 101 and 54 us, 16-token blocks 33, 106 and 39 us.)
 struct RouteShape {
   int mbr, ncbw, n_tb, ks;
 };
 static bool route_shape(int T, int E, RouteShape& r) {
   const int ncb = (E + 15) / 16;
-  const bool big = T >= 2048 && ncb <= 8;
-  const bool one32 = T > 16 && T <= 32 && ncb <= 4 && route_fits(ncb, 1, 2);
-  r.mbr = (big || one32) ? 2 : 1;
-  r.ncbw = big ? (ncb <= 4 ? 1 : 2) : one32 ? 1 : (ncb <= 8 ? 2 : 4);
+  if (T >= 512) {
+    r.mbr = 2;
+    r.ncbw = ncb <= 4 ? 1 : 2;
+  } else {
+    const bool one32 = T > 16 && T <= 32 && ncb <= 4 && route_fits(ncb, 1, 2);
+    r.mbr = one32 ? 2 : 1;
+    r.ncbw = one32 ? 1 : (ncb <= 8 ? 2 : 4);
+  }
   r.n_tb = (T + 16 * r.mbr - 1) / (16 * r.mbr);
-  r.ks = r.n_tb >= ROUTE_MAX_SPLIT_BLOCKS ? 1 : ROUTE_MAX_SPLIT_BLOCKS / r.n_tb;
+  r.ks = r.n_tb > ROUTE_MAX_TB ? 1 : (ROUTE_TARGET_WG + r.n_tb - 1) / r.n_tb;
   if (r.ks > 8) r.ks = 8;
   return route_fits(ncb, r.ncbw, r.mbr);
+}
+
+size_t route_partial_bytes(int T, int E) {
+  RouteShape r;
+  if (T <= 0 || !route_shape(T, E, r) || r.ks == 1) return 0;
+  return (size_t)r.n_tb * r.ks * 16 * r.mbr * E * sizeof(float);
 }
 
 int launch_route(const RouteParams& p0, hipStream_t stream) {
@@ -447,11 +480,9 @@ int launch_route(const RouteParams& p0, hipStream_t stream) {
   p.n_tb = r.n_tb;
   p.ks = r.ks;
   // the partials of all K slices: n_tb * ks * 16 * mbr rows of E floats
-  if (p.ks > 1 && (p.part == nullptr || p.tb_done == nullptr || p.n_tb * p.ks > ROUTE_MAX_SPLIT_BLOCKS ||
-                   p.n_tb * p.ks * r.mbr > ROUTE_MAX_SPLIT_BLOCKS))
-    return -1;
-  const long long quads = p.xq ? (long long)p.T * (p.d / 32) : 0;
-  const long long grid = (long long)p.n_tb * p.ks + (quads + RT_THREADS / 4 - 1) / (RT_THREADS / 4);
+  if (p.ks > 1 && (p.part == nullptr || p.tb_done == nullptr || p.n_tb > ROUTE_MAX_TB)) return -1;
+  const long long blocks = p.xq ? (long long)p.T * (p.d / 32) : 0;
+  const long long grid = (long long)p.n_tb * p.ks + (blocks + RT_THREADS - 1) / RT_THREADS;
   const dim3 g((unsigned)grid), b(RT_THREADS);
   const int epl = (p.E + 63) / 64;
 #define MOE_ROUTE(NCBW, MBR)                                                                      \
