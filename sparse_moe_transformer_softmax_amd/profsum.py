@@ -3,6 +3,7 @@
     python -m sparse_moe_transformer_softmax_amd.profsum stats KERNEL_STATS_CSV [--cmd CMD]
     python -m sparse_moe_transformer_softmax_amd.profsum traffic --fetch CSV --write CSV \
         --kernel SUBSTR --copy-kernel SUBSTR --copy-bytes BYTES [--cmd CMD]
+    python -m sparse_moe_transformer_softmax_amd.profsum busy COUNTER_CSV --kernel SUBSTR [--cmd CMD]
 
 `stats` prints the per-kernel call count and mean/min/max duration from a
 `--kernel-trace --stats --output-format csv` run.  `traffic` reads two
@@ -11,6 +12,8 @@ dispatch), scales each counter by what it reads for a reference copy kernel
 that moves a known number of bytes each way, and prints the HBM bytes per
 launch of the kernel whose name contains SUBSTR, as `key: value` lines that
 bench.py reads back (with the hash of the kernel sources they belong to).
+`busy` prints the MFMA-busy share of a kernel from a `--pmc
+SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE` run.
 """
 from __future__ import annotations
 
@@ -96,6 +99,33 @@ def cmd_traffic(args) -> None:
     print(f"src_sha: {src_sha()}")
 
 
+def cmd_busy(args) -> None:
+    """MFMA-busy share of one kernel from SQ_VALU_MFMA_BUSY_CYCLES (summed over
+    every SIMD) and GRBM_GUI_ACTIVE (summed over the XCDs): busy /
+    (simds * active / xcds)."""
+    busy = per_dispatch(args.csv, "SQ_VALU_MFMA_BUSY_CYCLES", args.kernel)
+    active = per_dispatch(args.csv, "GRBM_GUI_ACTIVE", args.kernel)
+    sq = per_dispatch(args.csv, "SQ_BUSY_CYCLES", args.kernel)
+    if not (busy and active):
+        sys.exit(f"missing dispatches: busy {len(busy)} active {len(active)}")
+    simds, xcds = args.cus * 4, args.xcds
+    frac = statistics.mean(busy) / simds / (statistics.mean(active) / xcds)
+    print("# MFMA-busy share of a kernel from rocprofv3 counters")
+    if args.cmd:
+        for c in args.cmd:
+            print(f"# command: {c}")
+    print(f"kernel: {args.kernel}")
+    print(f"dispatches: {len(busy)}")
+    print(f"SQ_VALU_MFMA_BUSY_CYCLES_per_dispatch: {statistics.mean(busy):.0f}")
+    print(f"GRBM_GUI_ACTIVE_per_dispatch: {statistics.mean(active):.0f}")
+    if sq:
+        print(f"SQ_BUSY_CYCLES_per_dispatch: {statistics.mean(sq):.0f}")
+    print(f"simds: {simds}")
+    print(f"xcds: {xcds}")
+    print(f"mfma_busy_frac: {frac:.4f}")
+    print(f"src_sha: {src_sha()}")
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -109,9 +139,17 @@ def main(argv=None) -> None:
     t.add_argument("--copy-kernel", required=True)
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--cmd", action="append", default=[])
+    b = sub.add_parser("busy")
+    b.add_argument("csv")
+    b.add_argument("--kernel", required=True)
+    b.add_argument("--cus", type=int, default=256)
+    b.add_argument("--xcds", type=int, default=8)
+    b.add_argument("--cmd", action="append", default=[])
     args = ap.parse_args(argv)
     if args.cmd_name == "stats":
         cmd_stats(args)
+    elif args.cmd_name == "busy":
+        cmd_busy(args)
     else:
         cmd_traffic(args)
 
