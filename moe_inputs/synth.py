@@ -19,6 +19,12 @@ architecture summaries, "模型架构 / MoE" and "权重量化" entries):
   codes   uniform over all 16 E2M1 nibbles
   scales  E8M0 bytes uniform in {121, 122, 123, 124} (2^-6 .. 2^-3)
   b13, b2 ~ N(0, 0.01)
+
+Attention inputs (the attention steps next to the layer; "OpenAI 最新开源模型
+gpt-oss 架构与训练解析", 模型架构: Attention item):
+  q, k, v ~ N(0, 1), rounded to bf16, layouts [B, T, H, D]
+  sinks   uniform in [-2, 6] (one logit per query head; wide enough that the
+          sink ranges from negligible to dominant against a 128-key band)
 """
 from __future__ import annotations
 
@@ -29,6 +35,7 @@ import numpy as np
 
 # stream ids, one per tensor kind
 _S_X, _S_X_REDRAW, _S_WR, _S_BR, _S_W13C, _S_W13S, _S_B13, _S_W2C, _S_W2S, _S_B2, _S_PERM = range(11)
+_S_AQ, _S_AK, _S_AV, _S_ASINK = range(11, 15)
 
 SCALE_LO = 121  # E8M0 byte for 2^-6
 SCALE_HI = 124  # E8M0 byte for 2^-3
@@ -126,3 +133,12 @@ def gen_experts(seed: int, E: int, d: int, I: int):
     b13 = (_gen(seed, _S_B13).standard_normal((E, 2 * I)) * 0.1).astype(np.float32)
     b2 = (_gen(seed, _S_B2).standard_normal((E, d)) * 0.1).astype(np.float32)
     return dict(w13_codes=w13c, w13_scales=w13s, b13=b13, w2_codes=w2c, w2_scales=w2s, b2=b2)
+
+
+def gen_attention(seed: int, B: int, Tq: int, S: int, Hq: int, Hkv: int, D: int):
+    """q bf16 bits [B, Tq, Hq, D], k and v bf16 bits [B, S, Hkv, D], sinks fp32 [Hq]."""
+    q = f32_to_bf16_bits(_gen(seed, _S_AQ).standard_normal((B, Tq, Hq, D), dtype=np.float32))
+    k = f32_to_bf16_bits(_gen(seed, _S_AK).standard_normal((B, S, Hkv, D), dtype=np.float32))
+    v = f32_to_bf16_bits(_gen(seed, _S_AV).standard_normal((B, S, Hkv, D), dtype=np.float32))
+    sinks = _gen(seed, _S_ASINK).uniform(-2.0, 6.0, Hq).astype(np.float32)
+    return q, k, v, sinks
