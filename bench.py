@@ -8,7 +8,10 @@ printed: the headline is the 36-layer 120b stack (T 2048, E 128 -- the
 largest configuration, HBM-bound), and "legs" holds the same record for the
 20b decode batch (T 32, HBM-bound), the 20b prefill batch (T 4096,
 MFMA-bound) and the 120b prefill batch with Zipf-skewed expert loads
-(T 8192, E 128).  --workload NAME runs that one workload as the headline.
+(T 8192, E 128), plus the attention steps beside the layer (grouped-query
+attention with sinks over a 128-position band or dense, at prefill and
+decode sizes; --no-attention leaves them out).  --workload NAME runs that one
+workload as the headline.
 
 A step is one call of the whole layer -- router + top-k + softmax, expert
 row lists, gate/up GEMM with the clamped-SwiGLU epilogue, down GEMM, weighted
@@ -42,6 +45,9 @@ KEYS = ["x", "router_w", "router_b", "w13_codes", "w13_scales", "b13", "w2_codes
 LAYER_KEYS = KEYS[1:]
 # legs of the default run: (workload, roofline bound); the last is the headline
 LEGS = [("20b_decode", "hbm"), ("20b_prefill", "mfma"), ("120b_prefill_zipf", "mfma"), ("120b_stack36", "hbm")]
+# the attention steps beside the layer, reported under "legs" (not the headline)
+ATTN_LEGS = ["attn_prefill_band", "attn_prefill_dense", "attn_decode_dense", "attn_decode_band"]
+BF16_MFMA_PEAK = 2.5e15    # MI355X dense bf16 MFMA, FLOP/s
 TIME_EVERY = 10            # every TIME_EVERY-th timed step brackets the dominant kernel with events
 
 
@@ -319,13 +325,110 @@ def run_leg(wl, bound, args, torch, moe, want_cpu):
     return rec
 
 
+def attn_work(wl):
+    """Algorithmic work of one attention call: (FLOPs, HBM bytes).  FLOPs
+    count 2 per multiply-add of q.k and of p.v over the keys each query sees;
+    bytes read q and every key/value row some query sees once, and write out."""
+    import numpy as np
+    pos = wl.q_pos0 + np.arange(wl.Tq)
+    lo = np.maximum(0, pos - wl.window + 1) if wl.window > 0 else np.zeros_like(pos)
+    seen = int(np.sum(pos - lo + 1))
+    flops = 4.0 * wl.D * wl.Hq * seen * wl.B
+    keys = int(pos[-1] - lo[0] + 1)
+    nbytes = wl.B * (2 * wl.Tq * wl.Hq * wl.D * 2 + 2 * keys * wl.Hkv * wl.D * 2)
+    return flops, float(nbytes)
+
+
+def run_attn_leg(wl, args, torch, moe, want_cpu):
+    """Times one attention workload (one kernel per call); the roofline is
+    bf16 MFMA for dense prefill, HBM otherwise."""
+    import numpy as np
+    from moe_inputs import synth
+    flops, nbytes = attn_work(wl)
+    per_set = wl.B * (wl.Tq * wl.Hq + 2 * wl.S * wl.Hkv) * wl.D * 2
+    nsets = max(1, min(4, int(np.ceil(1.1e9 / per_set))))
+    log(f"attention workload {wl.name}: B={wl.B} Tq={wl.Tq} S={wl.S} q_pos0={wl.q_pos0} Hq={wl.Hq} "
+        f"Hkv={wl.Hkv} D={wl.D} window={wl.window} sets={nsets}")
+    sets, host0 = [], None
+    for i in range(nsets):
+        q, k, v, sinks = synth.gen_attention(wl.seed + 1000 * i, wl.B, wl.Tq, wl.S, wl.Hq, wl.Hkv, wl.D)
+        if i == 0 and want_cpu:
+            host0 = (q, k, v, sinks)
+        dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+        sets.append((dev(q), dev(k), dev(v), torch.from_numpy(sinks).to("cuda:0"), torch.empty(
+            (wl.B, wl.Tq, wl.Hq, wl.D), dtype=torch.bfloat16, device="cuda:0")))
+    torch.cuda.synchronize()
+
+    def step(i):
+        q, k, v, s, o = sets[i % nsets]
+        moe.moe_attn_forward(q, k, v, s, q_pos0=wl.q_pos0, window=wl.window, out=o)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) / args.steps * 1e3
+    log(f"timed {args.steps} calls: {us:.1f} us/call")
+    dense_prefill = wl.window == 0 and wl.Tq > 1
+    if dense_prefill:
+        roof = {"bound": "mfma", "achieved": flops / (us * 1e-6) / 1e12, "peak": BF16_MFMA_PEAK / 1e12,
+                "unit": "TFLOP/s", "frac": flops / (us * 1e-6) / BF16_MFMA_PEAK, "traffic": None,
+                "kernel": "attn_kernel", "kernel_us": us, "algorithmic_flops_per_launch": flops}
+    else:
+        roof = {"bound": "hbm", "achieved": nbytes / (us * 1e-6) / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": nbytes / (us * 1e-6) / HBM_PEAK, "traffic": None, "kernel": "attn_kernel",
+                "kernel_us": us, "algorithmic_bytes_per_launch": nbytes}
+    rec = {"value": wl.B * wl.Tq / (us * 1e-6), "unit": "tokens/s", "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": us * 1e-3,
+           "config": {"workload": wl.name, "B": wl.B, "Tq": wl.Tq, "S": wl.S, "q_pos0": wl.q_pos0, "Hq": wl.Hq,
+                      "Hkv": wl.Hkv, "D": wl.D, "window": wl.window, "sets": nsets,
+                      "flops_per_call": flops, "hbm_bytes_per_call": nbytes,
+                      "note": "one kernel per call; the time is HIP events around the timed calls"},
+           "roofline": roof, "cpu_baseline": None}
+    sets.clear()
+    torch.cuda.empty_cache()
+    if want_cpu and host0 is not None:
+        rec["cpu_baseline"] = attn_cpu_baseline(wl, host0, args.cpu_budget / 2)
+        log(f"cpu baseline: {rec['cpu_baseline']}")
+    return rec
+
+
+def attn_cpu_baseline(wl, host, budget_s):
+    """The fp64 attention oracle on query tokens taken from the end of the
+    batch (all heads of each), repeated until about budget_s is spent."""
+    from oracle import attention_oracle as A
+    from oracle.moe_oracle import bf16_bits_to_f64
+    q, k, v, sinks = host
+    b = wl.B - 1
+    qf = bf16_bits_to_f64(q[b:b + 1])
+    kf, vf = bf16_bits_to_f64(k[b:b + 1]), bf16_bits_to_f64(v[b:b + 1])
+    s64 = sinks.astype("float64")
+    model, ncpu = host_cpu()
+    done, total, i = 0, 0.0, wl.Tq - 1
+    while total < budget_s and done < wl.Tq:
+        rows = [(0, i, h) for h in range(wl.Hq)]
+        t0 = time.perf_counter()
+        A.attention_rows(qf, kf, vf, s64, wl.q_pos0, wl.window, rows)
+        total += time.perf_counter() - t0
+        done += 1
+        i = (i - 1) % wl.Tq
+    return {"value": done / total, "unit": "tokens/s", "cores": 1, "kind": "oracle", "cpu_model": model,
+            "nproc": ncpu, "sample": f"{done} query tokens (all {wl.Hq} heads) from the end of sequence {b}, "
+                                     f"fp64 numpy oracle row by row, {total:.1f} s"}
+
+
 def main():
-    from moe_inputs.workloads import WORKLOADS
+    from moe_inputs.workloads import ATTN_WORKLOADS, WORKLOADS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS),
+    ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS) + sorted(ATTN_WORKLOADS),
                     help="one workload as the headline (default: every leg of the metric)")
     ap.add_argument("--sets", type=int, default=0, help="weight sets to rotate over (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -333,6 +436,7 @@ def main():
     ap.add_argument("--act", default="exact", choices=["exact", "mxfp6"],
                     help="expert-GEMM activations: exact (three FP6 terms) or mxfp6 "
                          "(the activation-quantised fast mode, moe_layer_forward_mx6)")
+    ap.add_argument("--no-attention", action="store_true", help="leave out the attention legs of the default run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 256 MiB bitwise_not kernel (reads and writes 256 MiB: "
                          "the reference for HBM byte counters)")
@@ -344,8 +448,13 @@ def main():
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be at least 1 and --warmup at least 0", file=sys.stderr)
         sys.exit(2)
-    legs = LEGS if args.workload is None else [(args.workload, None)]
-    if args.act != "exact" and any(WORKLOADS[n].layers > 1 for n, _ in legs):
+    if args.workload in ATTN_WORKLOADS:
+        legs = [(args.workload, "attn")]
+    else:
+        legs = LEGS if args.workload is None else [(args.workload, None)]
+        if args.workload is None and not args.no_attention:
+            legs = [(n, "attn") for n in ATTN_LEGS] + legs
+    if args.act != "exact" and any(b != "attn" and WORKLOADS[n].layers > 1 for n, b in legs):
         print("the fast mode has a single-layer entry point only; pick a single-layer --workload", file=sys.stderr)
         sys.exit(2)
 
@@ -364,6 +473,9 @@ def main():
 
     recs = {}
     for name, bound in legs:
+        if bound == "attn":
+            recs[name] = run_attn_leg(ATTN_WORKLOADS[name], args, torch, moe, want_cpu=not args.no_cpu_baseline)
+            continue
         wl = WORKLOADS[name]
         if bound is None:
             bound = "hbm" if wl.T * wl.k <= 32 * wl.E or wl.layers > 1 else "mfma"
@@ -382,7 +494,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4",
+        "dtype": "bf16" if legs[-1][1] == "attn" else "mxfp4",
         "data": "synthetic",
         "config": head["config"],
         "roofline": head["roofline"],

@@ -223,6 +223,49 @@ int moe_stack_forward(const void* x0, int n_layers, const void* const* router_w,
                       const float* const* b2, int T, int d, int I, int E, int k, float clamp,
                       float eps, void* out, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The attention steps beside the layer ("OpenAI 最新开源模型 gpt-oss 架构与训练
+ * 解析", 模型架构: Attention item -- grouped-query attention with 64 query
+ * heads over 8 key/value heads, layers alternating between a band of the
+ * last 128 positions and dense attention, rotary position encoding, and a
+ * learned per-head bias logit in the softmax denominator; same page,
+ * "RoPE 替换了绝对位置编码" and "Attention Bias and Attention Sinks").
+ * The projections that produce q, k and v (and the output projection) are
+ * plain dense GEMMs and are not part of this library.
+ * ------------------------------------------------------------------------ */
+
+/* Rotary position encoding of n rows of H heads of width D:
+ *   out[t, h, 2i]   = x[t, h, 2i] cos(a) - x[t, h, 2i+1] sin(a)
+ *   out[t, h, 2i+1] = x[t, h, 2i] sin(a) + x[t, h, 2i+1] cos(a)
+ * with a = (pos0 + t) * theta^(-2i/D) (theta = 10000 in the workloads).  x,
+ * out bf16 [n, H, D], 16-byte aligned; out may equal x (in place), otherwise
+ * must not overlap it.  D even, 2 <= D <= 256; n, H >= 0 (0 is a no-op);
+ * pos0 >= 0, pos0 + n < 2^31; theta > 1.  The angle is formed in double
+ * precision; the rotation is fp32, rounded once to bf16. */
+int moe_attn_rope(const void* x, void* out, int n, int H, int D, int pos0, float theta, void* stream);
+
+/* Attention of B sequences, each with Tq queries at positions
+ * q_pos0 .. q_pos0 + Tq - 1 over S keys at positions 0 .. S - 1:
+ *   s_j    = q . k_j / sqrt(D)               for keys j the query sees:
+ *            j <= p (causal), and p - j < window when window > 0
+ *   out    = sum_j e^(s_j) v_j / (sum_j e^(s_j) + e^(sinks[h]))
+ * Query head h reads key/value head h / (Hq / Hkv).
+ *   q      bf16 [B, Tq, Hq, D]   (rotary encoding already applied)
+ *   k, v   bf16 [B, S, Hkv, D]   (k with rotary encoding applied)
+ *   sinks  fp32 [Hq]             sink logit of each query head (on the scale
+ *                                of s_j; -inf removes it)
+ *   out    bf16 [B, Tq, Hq, D]   written; must not overlap q, k, v or sinks
+ * D == 64; Hq a multiple of Hkv with Hq / Hkv in {1, 2, 4, 8, 16}; B and Hkv
+ * at most 65535 (larger values return MOE_ERR_UNSUPPORTED); B, Tq >= 0
+ * (0 is a no-op); S >= 1; 0 <= q_pos0 and q_pos0 + Tq <= S; window >= 0
+ * (0 = dense).  q, k, v and out 16-byte aligned, sinks 4-byte aligned.
+ * Unsupported widths or group sizes return MOE_ERR_UNSUPPORTED, other bad
+ * sizes MOE_ERR_BAD_SHAPE.  Scores and the softmax are fp32, the products
+ * run on bf16 MFMAs with fp32 accumulation, and the output is rounded once
+ * to bf16.  The result does not depend on timing. */
+int moe_attn_forward(const void* q, const void* k, const void* v, const float* sinks, void* out, int B, int Tq,
+                     int S, int q_pos0, int Hq, int Hkv, int D, int window, void* stream);
+
 /* Per-kernel timing for profiling.  Bit i of mask selects kernel kind i of
  * {0 route (including the MX6x3 split of x, done by the same launch),
  * 1 gate/up GEMM, 2 down GEMM, 3 combine, 4 reserved (never launched)};

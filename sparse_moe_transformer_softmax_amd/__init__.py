@@ -16,7 +16,7 @@ __all__ = [
     "moe_stack_forward", "moe_release", "moe_status_string", "moe_version", "LIB_PATH",
     "moe_timing_enable", "moe_timing_read", "KERNELS", "moe_layer_forward_mx6", "moe_layer_forward_mx6_dbg",
     "moe_layer_forward_ex", "MOE_LAYER_MXFP6", "MOE_LAYER_ALT_ACT", "moe_rmsnorm_residual",
-    "moe_layer_forward_noalloc", "MOE_NOALLOC_SCRATCH_BYTES",
+    "moe_layer_forward_noalloc", "MOE_NOALLOC_SCRATCH_BYTES", "moe_attn_rope", "moe_attn_forward",
 ]
 
 MOE_LAYER_MXFP6 = 1
@@ -42,6 +42,8 @@ _SIGS = {
     "moe_layer_forward_ws": (_I, [_P] * 9 + [_I] * 5 + [_F, _P, _P, ctypes.c_size_t, _P]),
     "moe_rmsnorm": (_I, [_P, _P, _I, _I, _F, _P]),
     "moe_rmsnorm_residual": (_I, [_P] * 5 + [_I, _I, _F, _P]),
+    "moe_attn_rope": (_I, [_P, _P] + [_I] * 4 + [_F, _P]),
+    "moe_attn_forward": (_I, [_P] * 5 + [_I] * 8 + [_P]),
     "moe_stack_forward": (_I, [_P, _I] + [_P] * 8 + [_I] * 5 + [_F, _F, _P, _P]),
     "moe_release": (None, []),
     "moe_timing_enable": (_I, [_I]),
@@ -305,6 +307,35 @@ def moe_rmsnorm_residual(x, y, eps: float = 1e-5, x_out=None, n_out=None, normal
     pno = _check(n_out, "n_out", torch.bfloat16, (T, d)) if normalize else None
     _ok("moe_rmsnorm_residual", lib().moe_rmsnorm_residual(px, yb, yf, pxo, pno, T, d, eps, _stream(stream)))
     return x_out, (n_out if normalize else None)
+
+
+def moe_attn_rope(x, pos0: int = 0, theta: float = 10000.0, out=None, stream=None):
+    """Rotary encoding of x bf16 [n, H, D] at positions pos0 .. pos0 + n - 1
+    (out may be x itself)."""
+    torch = _torch()
+    n, H, D = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _ok("moe_attn_rope", lib().moe_attn_rope(_check(x, "x", torch.bfloat16, (n, H, D)),
+                                             _check(out, "out", torch.bfloat16, (n, H, D)), n, H, D, pos0,
+                                             theta, _stream(stream)))
+    return out
+
+
+def moe_attn_forward(q, k, v, sinks, q_pos0: int = 0, window: int = 0, out=None, stream=None):
+    """Grouped-query attention with per-head sink logits: q bf16 [B, Tq, Hq, D],
+    k and v bf16 [B, S, Hkv, D], sinks fp32 [Hq]; window 0 is dense causal
+    attention, otherwise the band of the last `window` positions."""
+    torch = _torch()
+    B, Tq, Hq, D = q.shape
+    S, Hkv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    _ok("moe_attn_forward", lib().moe_attn_forward(
+        _check(q, "q", torch.bfloat16, (B, Tq, Hq, D)), _check(k, "k", torch.bfloat16, (B, S, Hkv, D)),
+        _check(v, "v", torch.bfloat16, (B, S, Hkv, D)), _check(sinks, "sinks", torch.float32, (Hq,)),
+        _check(out, "out", torch.bfloat16, (B, Tq, Hq, D)), B, Tq, S, q_pos0, Hq, Hkv, D, window, _stream(stream)))
+    return out
 
 
 def moe_stack_forward(x0, layers, k: int = 4, clamp: float = 7.0, eps: float = 1e-5, out=None, stream=None):

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
-SOURCES = ["api.hip", "route.hip", "expert_gemm.hip", "combine.hip"]
+SOURCES = ["api.hip", "route.hip", "expert_gemm.hip", "combine.hip", "attention.hip"]
 
 
 def hipcc() -> str:
@@ -23,18 +23,38 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+def _flags():
+    return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-unused-command-line-argument",
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wno-unused-command-line-argument",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
+    """Compiles every source to an object in parallel, then links the
+    shared library (and replaces the old one only when all of it worked)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import tempfile
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="moe_build_") as tmpd:
+        def compile_one(src):
+            obj = os.path.join(tmpd, src.replace(".hip", ".o"))
+            cmd = [cc] + _flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n" + r.stdout + r.stderr)
+            return obj
+        with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 1)) as ex:
+            objs = list(ex.map(compile_one, SOURCES))
+        tmp = LIB + ".tmp"
+        cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
     return LIB
 

@@ -517,6 +517,42 @@ int moe_rmsnorm_residual(const void* x, const void* y_bf16, const float* y_f32, 
              : MOE_OK;
 }
 
+int moe_attn_rope(const void* x, void* out, int n, int H, int D, int pos0, float theta, void* stream) {
+  if (n < 0 || H < 0 || D < 2 || D > 256 || (D & 1) || pos0 < 0 || (long long)pos0 + n >= (1ll << 31) ||
+      !(theta > 1.0f) || theta == INFINITY)
+    return MOE_ERR_BAD_SHAPE;
+  if (n == 0 || H == 0) return MOE_OK;
+  if (!x || !out) return MOE_ERR_NULL_PTR;
+  if (!aligned(x, 16) || !aligned(out, 16)) return MOE_ERR_MISALIGNED;
+  const size_t nb = (size_t)n * H * D * 2;
+  if (out != x && overlap(out, nb, x, nb)) return MOE_ERR_ALIAS;
+  if (int st = check_device()) return st;
+  return launch_rope((const uint16_t*)x, (uint16_t*)out, n, H, D, pos0, theta, (hipStream_t)stream) ? MOE_ERR_HIP
+                                                                                                      : MOE_OK;
+}
+
+int moe_attn_forward(const void* q, const void* k, const void* v, const float* sinks, void* out, int B, int Tq,
+                     int S, int q_pos0, int Hq, int Hkv, int D, int window, void* stream) {
+  if (B < 0 || Tq < 0 || S < 1 || q_pos0 < 0 || (long long)q_pos0 + Tq > S || Hq < 1 || Hkv < 1 || window < 0)
+    return MOE_ERR_BAD_SHAPE;
+  if (D != 64 || Hq % Hkv || B > 65535 || Hkv > 65535) return MOE_ERR_UNSUPPORTED;
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return MOE_ERR_UNSUPPORTED;
+  const size_t nq = (size_t)B * Tq * Hq * D * 2, nk = (size_t)B * S * Hkv * D * 2;
+  if (nq / 2 >= (1ull << 40) || nk / 2 >= (1ull << 40)) return MOE_ERR_UNSUPPORTED;
+  if (B == 0 || Tq == 0) return MOE_OK;
+  if (!q || !k || !v || !sinks || !out) return MOE_ERR_NULL_PTR;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(sinks, 4))
+    return MOE_ERR_MISALIGNED;
+  if (overlap(out, nq, q, nq) || overlap(out, nq, k, nk) || overlap(out, nq, v, nk) ||
+      overlap(out, nq, sinks, (size_t)Hq * 4))
+    return MOE_ERR_ALIAS;
+  if (int st = check_device()) return st;
+  AttnParams p{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sinks, (uint16_t*)out,
+               B, Tq, S, q_pos0, Hq, Hkv, window, (float)(1.4426950408889634 / sqrt((double)D))};
+  return launch_attention(p, (hipStream_t)stream) ? MOE_ERR_HIP : MOE_OK;
+}
+
 int moe_stack_forward(const void* x0, int n_layers, const void* const* router_w, const float* const* router_b,
                       const uint8_t* const* w13_codes, const uint8_t* const* w13_scales, const float* const* b13,
                       const uint8_t* const* w2_codes, const uint8_t* const* w2_scales, const float* const* b2,

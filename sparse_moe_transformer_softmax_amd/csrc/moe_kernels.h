@@ -112,4 +112,20 @@ constexpr int MT_SMALL2 = 32;  // decode tiles of two row blocks
 constexpr int MT_LARGE = 64;
 constexpr int MT_WIDE = 128;
 
+// Attention beside the layer: q bf16 [B, Tq, Hq, D], k and v bf16 [B, S, Hkv, D],
+// out bf16 [B, Tq, Hq, D], D = 64; query i at position q_pos0 + i.
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* sinks;        // [Hq] sink logits
+  uint16_t* out;
+  int B, Tq, S, q_pos0, Hq, Hkv;
+  int window;                // 0: dense causal; otherwise the band of the last `window` positions
+  float qk_scale;            // log2(e) / sqrt(D)
+};
+int launch_attention(const AttnParams& p, hipStream_t s);
+int attn_positions_per_wave(int G);
+int launch_rope(const uint16_t* x, uint16_t* out, int n, int H, int D, int pos0, float theta, hipStream_t s);
+
 }  // namespace moe

@@ -83,3 +83,44 @@ def test_rmsnorm_residual_argument_errors(kw, status):
 
 def test_rmsnorm_residual_zero_rows_is_a_no_op():
     assert _resid(T=0) == 0
+
+
+def _attn(q=0x100000, k=0x200000, v=0x300000, sinks=0x400000, out=0x500000, B=2, Tq=8, S=16, q_pos0=4, Hq=16,
+          Hkv=2, D=64, window=0):
+    P = ctypes.c_void_p
+    return moe.lib().moe_attn_forward(P(q), P(k), P(v), P(sinks), P(out), B, Tq, S, q_pos0, Hq, Hkv, D, window,
+                                      None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=128), -3), (dict(Hkv=3), -3), (dict(Hq=96, Hkv=3), -3), (dict(Hq=64, Hkv=2), -3),
+    (dict(S=0), -2), (dict(q_pos0=-1), -2), (dict(q_pos0=9), -2), (dict(Tq=-1), -2), (dict(window=-1), -2),
+    (dict(B=-1), -2), (dict(Hkv=0), -2), (dict(q=None), -1), (dict(sinks=None), -1), (dict(out=None), -1),
+    (dict(q=0x100008), -4), (dict(v=0x300008), -4), (dict(sinks=0x400002), -4), (dict(out=0x100000), -7),
+    (dict(out=0x200100), -7), (dict(out=0x400000), -7),
+])
+def test_attention_argument_errors(kw, status):
+    assert _attn(**kw) == status
+
+
+def test_attention_empty_batch_is_a_no_op():
+    assert _attn(B=0) == 0
+    assert _attn(Tq=0, q=None, out=None) == 0
+
+
+def _rope(x=0x100000, out=0x200000, n=8, H=4, D=64, pos0=0, theta=10000.0):
+    P = ctypes.c_void_p
+    return moe.lib().moe_attn_rope(P(x), P(out), n, H, D, pos0, theta, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=63), -2), (dict(D=0), -2), (dict(D=258), -2), (dict(n=-1), -2), (dict(pos0=-3), -2),
+    (dict(theta=1.0), -2), (dict(theta=float("nan")), -2), (dict(x=None), -1), (dict(out=None), -1),
+    (dict(x=0x100004), -4), (dict(out=0x100040), -7),
+])
+def test_rope_argument_errors(kw, status):
+    assert _rope(**kw) == status
+
+
+def test_rope_empty_is_a_no_op():
+    assert _rope(n=0, x=None, out=None) == 0
