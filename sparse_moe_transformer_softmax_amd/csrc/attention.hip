@@ -29,13 +29,15 @@
 // state, so rescaling needs no data movement.
 //
 // Two launch shapes:
-//   query split (KS = false): the four waves own 4 * NQ blocks of columns and
+//   query split (KS = false): four waves own 4 * NQ blocks of columns and
 //     share every key/value tile, which the workgroup stages in LDS (double
-//     buffered, one barrier per tile);
+//     buffered, one barrier per tile, three tiles' loads in flight);
 //   key split (KS = true, a workgroup's positions fit one wave, as in decode):
-//     the four waves own the same columns and take every fourth tile each,
-//     each staging its own tiles; their partial states are merged at the end
-//     in wave order, so the result does not depend on timing.
+//     eight waves own the same columns and take every eighth tile each,
+//     each staging its own tiles (two tiles' loads in flight); their partial
+//     states are merged at the end in wave order, so the result does not
+//     depend on timing.
+// Tiles that every column of a wave sees whole skip the masking.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -47,7 +49,6 @@ namespace moe {
 
 constexpr int AT_D = 64;              // head width
 constexpr int AT_BK = 32;             // keys per tile
-constexpr int AT_NW = 4;              // waves per workgroup
 constexpr int AT_NQ = 2;              // 16-column blocks per wave
 constexpr int AT_TILE_BYTES = AT_BK * AT_D * 2;  // 4 KB of keys or of values
 
@@ -104,8 +105,28 @@ __device__ __forceinline__ void tile_store(AttnTile& s, int first, int step, con
   }
 }
 
+typedef float at_f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 at_b2 __attribute__((ext_vector_type(2)));
+
+// two floats -> two bf16 (round to nearest even; v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((at_f2){a, b}, at_b2));
+}
+
+// Reductions over the four lanes r, r + 16, r + 32, r + 48 (one query column):
+// gfx950's permlane swaps hand each lane the values of the lane pair
+// {l, l ^ 16} (then {l, l ^ 32}) in their two results, in either order.
+__device__ __forceinline__ float col_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Running softmax state of the lane's NQ query columns and their O^T blocks
@@ -117,7 +138,9 @@ struct AttnState {
 
 // One tile for the lane's NQ column blocks.  pos[n] is the position of the
 // lane's column in block n (any value for columns past the batch: their keys
-// are all masked).
+// are all masked).  MASK = false for a tile every column of the wave sees
+// whole (the caller checks that), which skips the masking.
+template <bool MASK>
 __device__ __forceinline__ void attn_tile(const AttnTile& s, int t, const v8bf (&qf)[AT_NQ][2],
                                           const int (&pos)[AT_NQ], const bool (&live)[AT_NQ], int window,
                                           float scale, AttnState& st) {
@@ -141,6 +164,8 @@ __device__ __forceinline__ void attn_tile(const AttnTile& s, int t, const v8bf (
   }
 #pragma unroll
   for (int n = 0; n < AT_NQ; ++n) {
+    // a block whose columns are all past the batch (decode) is skipped whole
+    if (n > 0 && !__builtin_amdgcn_ballot_w64(live[n])) continue;
     v4f sc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -148,7 +173,9 @@ __device__ __forceinline__ void attn_tile(const AttnTile& s, int t, const v8bf (
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][ks], qf[n][ks], sc[kb], 0, 0, 0);
     }
-    // mask and scale; key of sc[kb][e] is 32 t + 16 kb + 4 g + e
+    // mask; key of sc[kb][e] is 32 t + 16 kb + 4 g + e.  The running max is
+    // kept in scaled (log2) units; the scale is positive, so the max of the
+    // raw scores is taken first and scaled once.
     float x[8];
     float mx = -INFINITY;
 #pragma unroll
@@ -156,49 +183,75 @@ __device__ __forceinline__ void attn_tile(const AttnTile& s, int t, const v8bf (
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = AT_BK * t + 16 * kb + 4 * g + e;
-        const bool ok = live[n] && key <= pos[n] && (window == 0 || pos[n] - key < window);
-        const float v = ok ? sc[kb][e] * scale : -INFINITY;
+        const bool ok = !MASK || (live[n] && key <= pos[n] && (window == 0 || pos[n] - key < window));
+        const float v = ok ? sc[kb][e] : -INFINITY;
         x[4 * kb + e] = v;
         mx = fmaxf(mx, v);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(st.m[n], mx);
-    const bool none = mnew == -INFINITY;  // no key and no finite sink yet
-    const float alpha = none ? 1.f : exp2f(st.m[n] - mnew);
-    float ps = 0.f;
+    mx = col_max(mx);
+    // The reference point of the exponentials moves only when the column's
+    // max passes it by more than 2^8: the weights then stay below 256 (well
+    // inside fp32, and the two-term bf16 split is relative), and most tiles
+    // leave the output unscaled.  (The hardware exp2: results below 2^-126
+    // flush to zero, negligible next to the running sum.)
+    const float mcand = fmaxf(st.m[n], mx * scale);
+    const float mnew = mcand > st.m[n] + 8.f ? mcand : st.m[n];
+    float alpha, ps = 0.f;
     uint32_t hi[4], lo[4];
+    if (MASK && mnew == -INFINITY) {  // no key and no finite sink yet
+      alpha = 1.f;
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const float p0 = none ? 0.f : exp2f(x[e] - mnew), p1 = none ? 0.f : exp2f(x[e + 1] - mnew);
-      ps += p0 + p1;
-      const uint32_t h = pack_bf16x2(p0, p1);
-      hi[e >> 1] = h;
-      lo[e >> 1] = pack_bf16x2(p0 - __uint_as_float(h << 16), p1 - __uint_as_float(h & 0xffff0000u));
+      for (int e = 0; e < 4; ++e) hi[e] = lo[e] = 0u;
+    } else {
+      alpha = __builtin_amdgcn_exp2f(st.m[n] - mnew);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(x[e], scale, -mnew));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(x[e + 1], scale, -mnew));
+        ps += p0 + p1;
+        const uint32_t h = pack_bf16x2(p0, p1);
+        hi[e >> 1] = h;
+        lo[e >> 1] = pack_bf16x2(p0 - __uint_as_float(h << 16), p1 - __uint_as_float(h & 0xffff0000u));
+      }
     }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
+    ps = col_sum(ps);
     st.l[n] = st.l[n] * alpha + ps;
     st.m[n] = mnew;
     const v8bf phi = __builtin_bit_cast(v8bf, make_uint4(hi[0], hi[1], hi[2], hi[3]));
     const v8bf plo = __builtin_bit_cast(v8bf, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+    // rescale the output only when some column's reference point moved
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < AT_D / 16; ++db) st.acc[n][db] *= alpha;
+    }
 #pragma unroll
     for (int db = 0; db < AT_D / 16; ++db) {
-      v4f a = st.acc[n][db] * alpha;
-      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], phi, a, 0, 0, 0);
+      const v4f a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], phi, st.acc[n][db], 0, 0, 0);
       st.acc[n][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], plo, a, 0, 0, 0);
     }
   }
 }
 
+// Waves per workgroup and tiles whose loads are in flight ahead of the one
+// being computed, per launch shape.
+template <bool KS>
+struct AttnShape {
+  static constexpr int NW = KS ? 8 : 4;
+  static constexpr int PF = KS ? 2 : 3;
+  static constexpr int NCH = KS ? 4 : 1;      // 16-byte chunks of keys (and of values) a thread loads per tile
+};
+
 template <int G, bool KS>
-__global__ __launch_bounds__(AT_NW * 64) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(AttnShape<KS>::NW * 64) void attn_kernel(AttnParams p) {
+  constexpr int NW = AttnShape<KS>::NW, PF = AttnShape<KS>::PF, NCH = AttnShape<KS>::NCH;
   constexpr int PPB = 16 / G;            // positions per column block
   constexpr int PPW = AT_NQ * PPB;       // positions per wave
-  constexpr int QB = KS ? PPW : AT_NW * PPW;  // positions per workgroup
-  constexpr int MRG = 2 * AT_NQ + AT_NQ * AT_D / 4;  // m, l and O^T of a lane's columns
-  __shared__ AttnTile s_tile[KS ? AT_NW : 2];
-  __shared__ float s_merge[KS ? AT_NW : 1][KS ? 64 : 1][KS ? MRG : 1];
+  constexpr int QB = KS ? PPW : NW * PPW;  // positions per workgroup
+  // query split: two tiles (double buffer); key split: one per wave, whose
+  // space then holds the wave's O^T for the merge (64 lanes x 32 floats)
+  __shared__ AttnTile s_tile[KS ? NW : 2];
+  __shared__ float s_ml[KS ? NW : 1][KS ? 64 : 1][2 * AT_NQ];
+  static_assert(!KS || 64 * AT_NQ * AT_D / 4 * 4 <= (int)sizeof(AttnTile), "O^T fits the wave's tile");
 
   const int b = blockIdx.z, hk = blockIdx.y;
   // causal work grows with the position: the last blocks go first
@@ -211,9 +264,10 @@ __global__ __launch_bounds__(AT_NW * 64) void attn_kernel(AttnParams p) {
   bool live[AT_NQ];
   v8bf qf[AT_NQ][2];
   const int h = hk * G + r % G;
+  const int wq0 = i0 + (KS ? 0 : wave * PPW);  // the wave's first query
 #pragma unroll
   for (int n = 0; n < AT_NQ; ++n) {
-    qi[n] = i0 + (KS ? 0 : wave * PPW) + n * PPB + r / G;
+    qi[n] = wq0 + n * PPB + r / G;
     live[n] = qi[n] < p.Tq;
     pos[n] = p.q_pos0 + qi[n];
 #pragma unroll
@@ -223,6 +277,18 @@ __global__ __launch_bounds__(AT_NW * 64) void attn_kernel(AttnParams p) {
       qf[n][ks] = __builtin_bit_cast(v8bf, w);
     }
   }
+  // tiles that every column of the wave sees whole need no mask
+  const bool wave_full = wq0 + PPW <= p.Tq;
+  const int wp0 = p.q_pos0 + wq0, wp1 = wp0 + PPW - 1;
+  auto unmasked = [&](int t) {
+    return wave_full && AT_BK * t + AT_BK - 1 <= wp0 && (p.window == 0 || wp1 - AT_BK * t < p.window);
+  };
+  auto tile = [&](const AttnTile& s, int t, AttnState& st) {
+    if (unmasked(t))
+      attn_tile<false>(s, t, qf, pos, live, p.window, p.qk_scale, st);
+    else
+      attn_tile<true>(s, t, qf, pos, live, p.window, p.qk_scale, st);
+  };
   // the sink starts the running state of one wave per column (all in the
   // query split, wave 0 in the key split)
   const float sink = p.sinks[h] * 1.4426950408889634f;
@@ -242,40 +308,56 @@ __global__ __launch_bounds__(AT_NW * 64) void attn_kernel(AttnParams p) {
   const int lo = p.window > 0 ? max(0, pmin - p.window + 1) : 0;
   const int t0 = lo / AT_BK, t1 = pmax / AT_BK;
 
+  // a ring of PF tiles in registers: the loads of tile t + PF are issued
+  // once tile t has left its registers
+  TileRegs<NCH> rg[PF];
   if constexpr (!KS) {
-    // query split: 256 threads stage each tile, one chunk of keys and one of
-    // values each; the next tile's loads are in flight during this tile
-    TileRegs<1> rg;
-    tile_load<1>(p, b, hk, t0, tid, AT_NW * 64, rg);
-    for (int t = t0; t <= t1; ++t) {
-      AttnTile& s = s_tile[(t - t0) & 1];
-      tile_store<1>(s, tid, AT_NW * 64, rg);
-      __syncthreads();  // tile t staged; every wave is done with tile t - 2's buffer
-      if (t < t1) tile_load<1>(p, b, hk, t + 1, tid, AT_NW * 64, rg);
-      attn_tile(s, t, qf, pos, live, p.window, p.qk_scale, st);
+    // query split: all threads stage each tile (one chunk of keys and one of
+    // values each) into one of two LDS buffers, one barrier per tile
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+      if (t0 + j <= t1) tile_load<NCH>(p, b, hk, t0 + j, tid, NW * 64, rg[j]);
+    for (int tb = t0; tb <= t1; tb += PF) {
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        const int t = tb + j;
+        if (t > t1) break;
+        AttnTile& s = s_tile[(t - t0) & 1];
+        tile_store<NCH>(s, tid, NW * 64, rg[j]);
+        __syncthreads();  // tile t staged; every wave is done with tile t - 2's buffer
+        if (t + PF <= t1) tile_load<NCH>(p, b, hk, t + PF, tid, NW * 64, rg[j]);
+        tile(s, t, st);
+      }
     }
   } else {
-    // key split: wave w takes tiles t0 + w, t0 + w + 4, ..., staging each in
-    // its own LDS tile (64 lanes, four chunks of keys and four of values each)
+    // key split: wave w takes tiles t0 + w, t0 + w + NW, ..., staging each in
+    // its own LDS tile (the 64 lanes load four chunks of keys and four of
+    // values each)
     AttnTile& s = s_tile[wave];
-    TileRegs<4> rg;
-    int t = t0 + wave;
-    if (t <= t1) tile_load<4>(p, b, hk, t, lane, 64, rg);
-    for (; t <= t1; t += AT_NW) {
-      tile_store<4>(s, lane, 64, rg);
-      if (t + AT_NW <= t1) tile_load<4>(p, b, hk, t + AT_NW, lane, 64, rg);
-      attn_tile(s, t, qf, pos, live, p.window, p.qk_scale, st);
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+      if (t0 + wave + j * NW <= t1) tile_load<NCH>(p, b, hk, t0 + wave + j * NW, lane, 64, rg[j]);
+    for (int tb = t0 + wave; tb <= t1; tb += PF * NW) {
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        const int t = tb + j * NW;
+        if (t > t1) break;
+        tile_store<NCH>(s, lane, 64, rg[j]);
+        if (t + PF * NW <= t1) tile_load<NCH>(p, b, hk, t + PF * NW, lane, 64, rg[j]);
+        tile(s, t, st);
+      }
     }
-    // merge the four waves' states in wave order
-    float* mine = &s_merge[wave][lane][0];
+    // merge the waves' states in wave order: m and l in s_ml, O^T in the
+    // wave's own tile space
+    float* acc_out = (float*)&s_tile[wave] + lane * (AT_NQ * AT_D / 4);
 #pragma unroll
     for (int n = 0; n < AT_NQ; ++n) {
-      mine[0 + n] = st.m[n];
-      mine[AT_NQ + n] = st.l[n];
+      s_ml[wave][lane][n] = st.m[n];
+      s_ml[wave][lane][AT_NQ + n] = st.l[n];
 #pragma unroll
       for (int db = 0; db < AT_D / 16; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mine[2 * AT_NQ + (n * (AT_D / 16) + db) * 4 + e] = st.acc[n][db][e];
+        for (int e = 0; e < 4; ++e) acc_out[(n * (AT_D / 16) + db) * 4 + e] = st.acc[n][db][e];
     }
     __syncthreads();
     if (wave != 0) return;
@@ -283,20 +365,21 @@ __global__ __launch_bounds__(AT_NW * 64) void attn_kernel(AttnParams p) {
     for (int n = 0; n < AT_NQ; ++n) {
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < AT_NW; ++w) M = fmaxf(M, s_merge[w][lane][n]);
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][lane][n]);
       float L = 0.f;
       v4f O[AT_D / 16];
 #pragma unroll
       for (int db = 0; db < AT_D / 16; ++db) O[db] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < AT_NW; ++w) {
-        const float mw = s_merge[w][lane][n];
+      for (int w = 0; w < NW; ++w) {
+        const float mw = s_ml[w][lane][n];
         const float f = (M == -INFINITY || mw == -INFINITY) ? 0.f : exp2f(mw - M);
-        L += s_merge[w][lane][AT_NQ + n] * f;
+        L += s_ml[w][lane][AT_NQ + n] * f;
+        const float* aw = (const float*)&s_tile[w] + lane * (AT_NQ * AT_D / 4);
 #pragma unroll
         for (int db = 0; db < AT_D / 16; ++db)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) O[db][e] += s_merge[w][lane][2 * AT_NQ + (n * (AT_D / 16) + db) * 4 + e] * f;
+          for (int e = 0; e < 4; ++e) O[db][e] += aw[(n * (AT_D / 16) + db) * 4 + e] * f;
       }
       st.l[n] = L;
 #pragma unroll
@@ -348,10 +431,11 @@ static void launch_attn_g(const AttnParams& p, bool ks, hipStream_t s) {
   constexpr int PPW = AT_NQ * (16 / G);
   if (ks) {
     const dim3 grid((p.Tq + PPW - 1) / PPW, p.Hkv, p.B);
-    hipLaunchKernelGGL((attn_kernel<G, true>), grid, dim3(AT_NW * 64), 0, s, p);
+    hipLaunchKernelGGL((attn_kernel<G, true>), grid, dim3(AttnShape<true>::NW * 64), 0, s, p);
   } else {
-    const dim3 grid((p.Tq + AT_NW * PPW - 1) / (AT_NW * PPW), p.Hkv, p.B);
-    hipLaunchKernelGGL((attn_kernel<G, false>), grid, dim3(AT_NW * 64), 0, s, p);
+    constexpr int QB = AttnShape<false>::NW * PPW;
+    const dim3 grid((p.Tq + QB - 1) / QB, p.Hkv, p.B);
+    hipLaunchKernelGGL((attn_kernel<G, false>), grid, dim3(AttnShape<false>::NW * 64), 0, s, p);
   }
 }
 
