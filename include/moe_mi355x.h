@@ -133,7 +133,13 @@ enum moe_layer_flags {
    * give Swish with unit slope and a clamp without its placement
    * ("OpenAI 最新开源模型 gpt-oss 架构与训练解析", MoE item and Swish/SwiGLU
    * 替换 GELU); this flag selects the other reading of both. */
-  MOE_LAYER_ALT_ACT = 2
+  MOE_LAYER_ALT_ACT = 2,
+  /* the expert weights (w13_codes, w13_scales, w2_codes, w2_scales) are in
+   * the packed layout written by moe_pack_weights; biases unchanged.  Only
+   * prefill sizes take it (T * k > 32 * E, d and I multiples of 64);
+   * other sizes return MOE_ERR_UNSUPPORTED.  Results are bitwise those of
+   * the row-major weights. */
+  MOE_LAYER_PACKED = 4
 };
 
 /* moe_layer_forward with flags (any OR of moe_layer_flags; unknown bits give
@@ -211,6 +217,27 @@ int moe_rmsnorm(const void* x, void* out, int T, int d, float eps, void* stream)
 int moe_rmsnorm_residual(const void* x, const void* y_bf16, const float* y_f32, void* x_out, void* n_out, int T,
                          int d, float eps, void* stream);
 
+/* Repacks one stack of MXFP4 matrices, as stored ("OpenAI 最新开源模型 gpt-oss
+ * 架构与训练解析", 权重量化 item): codes u8 [E, N, K/2] (two E2M1 codes per
+ * byte, row-major) and scales u8 [E, N, K/32] (E8M0), into the layout the
+ * prefill GEMM streams whole 128-byte lines of (MOE_LAYER_PACKED):
+ *   codes_out  u8 [E, N/2, K]: for each pair of weight rows (2p, 2p+1) and
+ *              each chunk c of four 32-element blocks (64 bytes of a row),
+ *              row 2p's chunk bytes then row 2p+1's (a last chunk of two
+ *              blocks keeps 32 + 32 bytes); E * N * K/2 bytes in all
+ *   scales_out u8 [E, ceil(K/128), N, 4]: for each chunk c, the four scale
+ *              bytes of blocks 4c .. 4c+3 of every row, rows consecutive
+ *              (blocks past K/32 hold 127); moe_packed_scale_bytes bytes
+ * Call it once per weight matrix (W13 with N = 2I, K = d; W2 with N = d,
+ * K = I).  N even and K a multiple of 64; codes and codes_out 16-byte
+ * aligned, scales_out 4-byte aligned; outputs must not overlap the inputs
+ * or each other.  Byte values are copied unchanged. */
+int moe_pack_weights(const uint8_t* codes, const uint8_t* scales, int E, int N, int K, uint8_t* codes_out,
+                     uint8_t* scales_out, void* stream);
+
+/* Bytes of moe_pack_weights' scales_out for these sizes (0 if invalid). */
+size_t moe_packed_scale_bytes(int E, int N, int K);
+
 /* Pre-norm residual stack of n_layers MoE layers on one GPU:
  *   n = bf16(RMSNorm(x)); x = bf16(x + MoE_l(n))   for l = 0 .. n_layers-1
  * Each per-layer argument is a HOST array of n_layers device pointers with
@@ -222,6 +249,15 @@ int moe_stack_forward(const void* x0, int n_layers, const void* const* router_w,
                       const uint8_t* const* w2_codes, const uint8_t* const* w2_scales,
                       const float* const* b2, int T, int d, int I, int E, int k, float clamp,
                       float eps, void* out, void* stream);
+
+/* moe_stack_forward with flags: MOE_LAYER_ALT_ACT and MOE_LAYER_PACKED (the
+ * per-layer expert weights in the packed layout); other bits give
+ * MOE_ERR_BAD_SHAPE. */
+int moe_stack_forward_ex(const void* x0, int n_layers, const void* const* router_w, const float* const* router_b,
+                         const uint8_t* const* w13_codes, const uint8_t* const* w13_scales, const float* const* b13,
+                         const uint8_t* const* w2_codes, const uint8_t* const* w2_scales, const float* const* b2,
+                         int T, int d, int I, int E, int k, float clamp, float eps, int flags, void* out,
+                         void* stream);
 
 /* ------------------------------------------------------------------------
  * The attention steps beside the layer ("OpenAI 最新开源模型 gpt-oss 架构与训练

@@ -17,10 +17,12 @@ __all__ = [
     "moe_timing_enable", "moe_timing_read", "KERNELS", "moe_layer_forward_mx6", "moe_layer_forward_mx6_dbg",
     "moe_layer_forward_ex", "MOE_LAYER_MXFP6", "MOE_LAYER_ALT_ACT", "moe_rmsnorm_residual",
     "moe_layer_forward_noalloc", "MOE_NOALLOC_SCRATCH_BYTES", "moe_attn_rope", "moe_attn_forward",
+    "moe_pack_weights", "moe_packed_scale_bytes", "MOE_LAYER_PACKED", "packed_shapes",
 ]
 
 MOE_LAYER_MXFP6 = 1
 MOE_LAYER_ALT_ACT = 2
+MOE_LAYER_PACKED = 4
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
@@ -44,6 +46,9 @@ _SIGS = {
     "moe_rmsnorm_residual": (_I, [_P] * 5 + [_I, _I, _F, _P]),
     "moe_attn_rope": (_I, [_P, _P] + [_I] * 4 + [_F, _P]),
     "moe_attn_forward": (_I, [_P] * 5 + [_I] * 8 + [_P]),
+    "moe_pack_weights": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
+    "moe_packed_scale_bytes": (ctypes.c_size_t, [_I, _I, _I]),
+    "moe_stack_forward_ex": (_I, [_P, _I] + [_P] * 8 + [_I] * 5 + [_F, _F, _I, _P, _P]),
     "moe_stack_forward": (_I, [_P, _I] + [_P] * 8 + [_I] * 5 + [_F, _F, _P, _P]),
     "moe_release": (None, []),
     "moe_timing_enable": (_I, [_I]),
@@ -142,20 +147,31 @@ def _ok(fn, st):
         raise MoeError(fn, st)
 
 
-def _layer_ptrs(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2):
+def packed_shapes(E: int, N: int, K: int):
+    """Shapes of moe_pack_weights' outputs: codes [E, N/2, K], scales
+    [E, ceil(K/128), N, 4]."""
+    return (E, N // 2, K), (E, (K // 32 + 3) // 4, N, 4)
+
+
+def _layer_ptrs(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, packed=False):
     torch = _torch()
     T, d = x.shape
     E = router_w.shape[0]
-    I = w2_codes.shape[2] * 2
+    I = b13.shape[1] // 2
+    if packed:
+        c13, s13 = packed_shapes(E, 2 * I, d)
+        c2, s2 = packed_shapes(E, d, I)
+    else:
+        c13, s13, c2, s2 = (E, 2 * I, d // 2), (E, 2 * I, d // 32), (E, d, I // 2), (E, d, I // 32)
     ptrs = [
         _check(x, "x", torch.bfloat16, (T, d)),
         _check(router_w, "router_w", torch.bfloat16, (E, d)),
         _check(router_b, "router_b", torch.float32, (E,)),
-        _check(w13_codes, "w13_codes", torch.uint8, (E, 2 * I, d // 2)),
-        _check(w13_scales, "w13_scales", torch.uint8, (E, 2 * I, d // 32)),
+        _check(w13_codes, "w13_codes", torch.uint8, c13),
+        _check(w13_scales, "w13_scales", torch.uint8, s13),
         _check(b13, "b13", torch.float32, (E, 2 * I)),
-        _check(w2_codes, "w2_codes", torch.uint8, (E, d, I // 2)),
-        _check(w2_scales, "w2_scales", torch.uint8, (E, d, I // 32)),
+        _check(w2_codes, "w2_codes", torch.uint8, c2),
+        _check(w2_scales, "w2_scales", torch.uint8, s2),
         _check(b2, "b2", torch.float32, (E, d)),
     ]
     return ptrs, T, d, I, E
@@ -218,10 +234,11 @@ def moe_layer_forward_dbg(x, router_w, router_b, w13_codes, w13_scales, b13, w2_
 def moe_layer_forward_ex(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
                          k: int = 4, clamp: float = 7.0, flags: int = 0, debug: bool = False, out=None,
                          stream=None):
-    """moe_layer_forward with flags (MOE_LAYER_MXFP6, MOE_LAYER_ALT_ACT).
+    """moe_layer_forward with flags (MOE_LAYER_MXFP6, MOE_LAYER_ALT_ACT, MOE_LAYER_PACKED).
     debug=False: returns out; debug=True: (out, out_f32, topk_id, topk_w, counts)."""
     torch = _torch()
-    ptrs, T, d, I, E = _layer_ptrs(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2)
+    ptrs, T, d, I, E = _layer_ptrs(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
+                                   packed=bool(flags & MOE_LAYER_PACKED))
     dev = x.device
     if out is None:
         out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
@@ -338,8 +355,10 @@ def moe_attn_forward(q, k, v, sinks, q_pos0: int = 0, window: int = 0, out=None,
     return out
 
 
-def moe_stack_forward(x0, layers, k: int = 4, clamp: float = 7.0, eps: float = 1e-5, out=None, stream=None):
-    """layers: list of dicts with router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2."""
+def moe_stack_forward(x0, layers, k: int = 4, clamp: float = 7.0, eps: float = 1e-5, out=None, stream=None,
+                      flags: int = 0):
+    """layers: list of dicts with router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2
+    (flags: MOE_LAYER_ALT_ACT, MOE_LAYER_PACKED; any set flag calls moe_stack_forward_ex)."""
     torch = _torch()
     T, d = x0.shape
     n = len(layers)
@@ -347,12 +366,37 @@ def moe_stack_forward(x0, layers, k: int = 4, clamp: float = 7.0, eps: float = 1
     arrays = {kk: (ctypes.c_void_p * n)() for kk in keys}
     I = E = None
     for l, L in enumerate(layers):
-        ptrs, _, _, I, E = _layer_ptrs(x0, *[L[kk] for kk in keys])
+        ptrs, _, _, I, E = _layer_ptrs(x0, *[L[kk] for kk in keys], packed=bool(flags & MOE_LAYER_PACKED))
         for kk, p in zip(keys, ptrs[1:]):
             arrays[kk][l] = p.value
     if out is None:
         out = torch.empty_like(x0)
-    _ok("moe_stack_forward", lib().moe_stack_forward(
-        _check(x0, "x0", torch.bfloat16, (T, d)), n, *[ctypes.cast(arrays[kk], ctypes.c_void_p) for kk in keys],
-        T, d, I, E, k, clamp, eps, _check(out, "out", torch.bfloat16, (T, d)), _stream(stream)))
+    args = [_check(x0, "x0", torch.bfloat16, (T, d)), n] + [ctypes.cast(arrays[kk], ctypes.c_void_p) for kk in keys]
+    if flags:
+        _ok("moe_stack_forward_ex", lib().moe_stack_forward_ex(
+            *args, T, d, I, E, k, clamp, eps, flags, _check(out, "out", torch.bfloat16, (T, d)), _stream(stream)))
+    else:
+        _ok("moe_stack_forward", lib().moe_stack_forward(
+            *args, T, d, I, E, k, clamp, eps, _check(out, "out", torch.bfloat16, (T, d)), _stream(stream)))
     return out
+
+
+def moe_pack_weights(codes, scales, stream=None):
+    """Packed copies of one MXFP4 weight stack (codes uint8 [E, N, K/2],
+    scales uint8 [E, N, K/32]) for MOE_LAYER_PACKED: returns (codes [E, N/2, K],
+    scales [E, ceil(K/128), N, 4])."""
+    torch = _torch()
+    E, N, half = codes.shape
+    K = 2 * half
+    cs, ss = packed_shapes(E, N, K)
+    co = torch.empty(cs, dtype=torch.uint8, device=codes.device)
+    so = torch.empty(ss, dtype=torch.uint8, device=codes.device)
+    _ok("moe_pack_weights", lib().moe_pack_weights(
+        _check(codes, "codes", torch.uint8, (E, N, K // 2)), _check(scales, "scales", torch.uint8, (E, N, K // 32)),
+        E, N, K, _check(co, "codes_out", torch.uint8, cs), _check(so, "scales_out", torch.uint8, ss),
+        _stream(stream)))
+    return co, so
+
+
+def moe_packed_scale_bytes(E: int, N: int, K: int) -> int:
+    return int(lib().moe_packed_scale_bytes(E, N, K))

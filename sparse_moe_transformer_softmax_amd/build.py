@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
-SOURCES = ["api.hip", "route.hip", "expert_gemm.hip", "combine.hip", "attention.hip"]
+SOURCES = ["api.hip", "route.hip", "expert_gemm.hip", "combine.hip", "attention.hip", "pack.hip"]
 
 
 def hipcc() -> str:

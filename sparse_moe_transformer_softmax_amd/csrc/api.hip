@@ -93,7 +93,10 @@ struct LayerArgs {
   int T, d, I, E, k; float clamp;
   int terms = 3;  // FP6 terms of the expert GEMMs' activations: 3 (exact path) or 1 (fast mode)
   int alt = 0;    // 1: the variant gate/up layout and activation
+  int packed = 0; // 1: expert weights in the packed layout of moe_pack_weights
 };
+
+size_t packed_scale_bytes(int E, int N, int K) { return (size_t)E * N * 4 * (size_t)(((K >> 5) + 3) >> 2); }
 
 int check_layer(const LayerArgs& a, const void* out) {
   int st = check_shape(a.T, a.d, a.I, a.E, a.k);
@@ -106,14 +109,20 @@ int check_layer(const LayerArgs& a, const void* out) {
       !aligned(a.w13s, 16) || !aligned(a.w2s, 16) ||
       !aligned(a.router_b, 4) || !aligned(a.b13, 4) || !aligned(a.b2, 4))
     return MOE_ERR_MISALIGNED;
+  // the packed layout is read by the 128-row prefill kernel only, which
+  // needs an even number of 32-element blocks in both projections and more
+  // than 32 rows per expert on average
+  if (a.packed && ((a.d % 64) || (a.I % 64) || (long long)a.T * a.k <= 32LL * a.E)) return MOE_ERR_UNSUPPORTED;
   if (out) {
     if (!aligned(out, 16)) return MOE_ERR_MISALIGNED;
     const size_t no = (size_t)a.T * a.d * 2;
     const size_t E = a.E, d = a.d, I = a.I;
+    const size_t s13 = a.packed ? packed_scale_bytes(a.E, 2 * a.I, a.d) : E * 2 * I * d / 32;
+    const size_t s2 = a.packed ? packed_scale_bytes(a.E, a.d, a.I) : E * d * I / 32;
     if (overlap(out, no, a.x, no) || overlap(out, no, a.router_w, E * d * 2) ||
         overlap(out, no, a.router_b, E * 4) || overlap(out, no, a.w13c, E * 2 * I * d / 2) ||
-        overlap(out, no, a.w13s, E * 2 * I * d / 32) || overlap(out, no, a.b13, E * 2 * I * 4) ||
-        overlap(out, no, a.w2c, E * d * I / 2) || overlap(out, no, a.w2s, E * d * I / 32) ||
+        overlap(out, no, a.w13s, s13) || overlap(out, no, a.b13, E * 2 * I * 4) ||
+        overlap(out, no, a.w2c, E * d * I / 2) || overlap(out, no, a.w2s, s2) ||
         overlap(out, no, a.b2, E * d * 4))
       return MOE_ERR_ALIAS;
   }
@@ -249,6 +258,7 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   gp.clamp = a.clamp;
   gp.terms = a.terms;
   gp.alt = a.alt;
+  gp.packed = a.packed;
   gp.hq = ws + L.hq;
   gp.y = nullptr;
   gp.fold_cnt = nullptr;
@@ -441,10 +451,11 @@ int moe_layer_forward_ex(const void* x, const void* router_w, const float* route
                          const uint8_t* w2_scales, const float* b2, int T, int d, int I, int E, int k, float clamp,
                          int flags, void* out, float* out_f32, int32_t* topk_id, float* topk_w, int32_t* counts,
                          void* stream) {
-  if (flags & ~(MOE_LAYER_MXFP6 | MOE_LAYER_ALT_ACT)) return MOE_ERR_BAD_SHAPE;
+  if (flags & ~(MOE_LAYER_MXFP6 | MOE_LAYER_ALT_ACT | MOE_LAYER_PACKED)) return MOE_ERR_BAD_SHAPE;
   LayerArgs a{x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, d, I, E, k, clamp};
   a.terms = (flags & MOE_LAYER_MXFP6) ? 1 : 3;
   a.alt = (flags & MOE_LAYER_ALT_ACT) ? 1 : 0;
+  a.packed = (flags & MOE_LAYER_PACKED) ? 1 : 0;
   const bool any = topk_id || topk_w || counts, all = topk_id && topk_w && counts;
   if (any && !all) return MOE_ERR_NULL_PTR;
   if (!all && !out_f32) return forward_owned(a, out, stream);
@@ -553,17 +564,20 @@ int moe_attn_forward(const void* q, const void* k, const void* v, const float* s
   return launch_attention(p, (hipStream_t)stream) ? MOE_ERR_HIP : MOE_OK;
 }
 
-int moe_stack_forward(const void* x0, int n_layers, const void* const* router_w, const float* const* router_b,
-                      const uint8_t* const* w13_codes, const uint8_t* const* w13_scales, const float* const* b13,
-                      const uint8_t* const* w2_codes, const uint8_t* const* w2_scales, const float* const* b2,
-                      int T, int d, int I, int E, int k, float clamp, float eps, void* out, void* stream) {
-  if (n_layers < 1) return MOE_ERR_BAD_SHAPE;
+static int stack_forward(const void* x0, int n_layers, const void* const* router_w, const float* const* router_b,
+                         const uint8_t* const* w13_codes, const uint8_t* const* w13_scales, const float* const* b13,
+                         const uint8_t* const* w2_codes, const uint8_t* const* w2_scales, const float* const* b2,
+                         int T, int d, int I, int E, int k, float clamp, float eps, int flags, void* out,
+                         void* stream) {
+  if (n_layers < 1 || (flags & ~(MOE_LAYER_ALT_ACT | MOE_LAYER_PACKED))) return MOE_ERR_BAD_SHAPE;
   if (!x0 || !out || !router_w || !router_b || !w13_codes || !w13_scales || !b13 || !w2_codes || !w2_scales || !b2)
     return MOE_ERR_NULL_PTR;
   if (!(eps >= 0.0f)) return MOE_ERR_BAD_SHAPE;
   for (int l = 0; l < n_layers; ++l) {
     LayerArgs a{x0, router_w[l], router_b[l], w13_codes[l], w13_scales[l], b13[l], w2_codes[l], w2_scales[l],
                 b2[l], T, d, I, E, k, clamp};
+    a.alt = (flags & MOE_LAYER_ALT_ACT) ? 1 : 0;
+    a.packed = (flags & MOE_LAYER_PACKED) ? 1 : 0;
     if (int st = check_layer(a, out)) return st;
   }
   if (T == 0) return MOE_OK;
@@ -584,6 +598,8 @@ int moe_stack_forward(const void* x0, int n_layers, const void* const* router_w,
   for (int l = 0; l < n_layers; ++l) {
     LayerArgs a{norm, router_w[l], router_b[l], w13_codes[l], w13_scales[l], b13[l], w2_codes[l], w2_scales[l],
                 b2[l], T, d, I, E, k, clamp};
+    a.alt = (flags & MOE_LAYER_ALT_ACT) ? 1 : 0;
+    a.packed = (flags & MOE_LAYER_PACKED) ? 1 : 0;
     uint16_t* dst = bufs[cur];
     const bool last = (l == n_layers - 1);
     if (int st = run_layer(a, L, ws, nullptr, nullptr, nullptr, nullptr, nullptr, false, s, resid, dst,
@@ -593,6 +609,43 @@ int moe_stack_forward(const void* x0, int n_layers, const void* const* router_w,
     cur ^= 1;
   }
   return MOE_OK;
+}
+
+int moe_stack_forward(const void* x0, int n_layers, const void* const* router_w, const float* const* router_b,
+                      const uint8_t* const* w13_codes, const uint8_t* const* w13_scales, const float* const* b13,
+                      const uint8_t* const* w2_codes, const uint8_t* const* w2_scales, const float* const* b2,
+                      int T, int d, int I, int E, int k, float clamp, float eps, void* out, void* stream) {
+  return stack_forward(x0, n_layers, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, d,
+                       I, E, k, clamp, eps, 0, out, stream);
+}
+
+int moe_stack_forward_ex(const void* x0, int n_layers, const void* const* router_w, const float* const* router_b,
+                         const uint8_t* const* w13_codes, const uint8_t* const* w13_scales, const float* const* b13,
+                         const uint8_t* const* w2_codes, const uint8_t* const* w2_scales, const float* const* b2,
+                         int T, int d, int I, int E, int k, float clamp, float eps, int flags, void* out,
+                         void* stream) {
+  return stack_forward(x0, n_layers, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, d,
+                       I, E, k, clamp, eps, flags, out, stream);
+}
+
+size_t moe_packed_scale_bytes(int E, int N, int K) {
+  if (E < 1 || N < 2 || (N & 1) || K < 64 || (K % 64)) return 0;
+  return packed_scale_bytes(E, N, K);
+}
+
+int moe_pack_weights(const uint8_t* codes, const uint8_t* scales, int E, int N, int K, uint8_t* codes_out,
+                     uint8_t* scales_out, void* stream) {
+  if (E < 1 || N < 2 || (N & 1) || K < 64 || (K % 64)) return MOE_ERR_BAD_SHAPE;
+  const size_t nc = (size_t)E * N * (K / 2), ns = (size_t)E * N * (K / 32), nsp = packed_scale_bytes(E, N, K);
+  if (nc >= (1ull << 40)) return MOE_ERR_UNSUPPORTED;
+  if (!codes || !scales || !codes_out || !scales_out) return MOE_ERR_NULL_PTR;
+  if (!aligned(codes, 16) || !aligned(codes_out, 16) || !aligned(scales_out, 4)) return MOE_ERR_MISALIGNED;
+  if (overlap(codes_out, nc, codes, nc) || overlap(codes_out, nc, scales, ns) || overlap(scales_out, nsp, codes, nc) ||
+      overlap(scales_out, nsp, scales, ns) || overlap(codes_out, nc, scales_out, nsp))
+    return MOE_ERR_ALIAS;
+  if (int st = check_device()) return st;
+  return launch_pack_weights(codes, scales, E, N, K, codes_out, scales_out, (hipStream_t)stream) ? MOE_ERR_HIP
+                                                                                                   : MOE_OK;
 }
 
 int moe_timing_enable(int mask) {

@@ -1117,7 +1117,12 @@ static_assert(PW_A_COPIES == 5 && PW_B_COPIES == 4 && PW_S_COPIES == 2, "copy sp
 static_assert(PW_EPI_BYTES >= 16 * (8 * PW_NCB + 4) * 4, "gate/up staging fits");
 static_assert(PW_NW * PW_EPI_BYTES <= 2 * PW_BUF, "epilogue staging fits the operand buffers");
 
-template <bool GATEUP, int TERMS>
+// PACKED: the weights in the packed layout of moe_pack_weights (two weight
+// rows' 64-byte chunk segments share one 128-byte line; each chunk's scale
+// bytes are 4 per row, rows consecutive), so that a chunk's copies touch
+// half the cache lines of the row-major codes and 1/32 of the lines of the
+// row-major scales.  Same LDS contents, same arithmetic, same results.
+template <bool GATEUP, int TERMS, bool PACKED>
 __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmParams p, int spans) {
   // (the body is compiled for the device only: the host pass, which only
   // needs the kernel's signature for its launch stub, cannot type the
@@ -1180,7 +1185,8 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
   const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.b_codes, 0, (int)((uint32_t)p.E * (uint32_t)N * (uint32_t)(K >> 1)), 0x00020000);
   const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)p.b_scales, 0, (int)((uint32_t)p.E * (uint32_t)N * (uint32_t)nblk), 0x00020000);
+      (void*)p.b_scales, 0,
+      (int)((uint32_t)p.E * (uint32_t)N * (uint32_t)(PACKED ? 4 * ((nblk + 3) >> 2) : nblk)), 0x00020000);
   constexpr uint32_t A_OOB = 0x7ffffff0u;  // at or past the A resource's end (it is below 2^31 bytes)
   // A copy k of this wave fills LDS slots u = (5 wave + k) * 64 + lane:
   // tile row u / 20, slot u % 20 holding piece (u % 20) ^ ((row >> 1) & 3)
@@ -1206,13 +1212,18 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
   }
   // B copy k fills slots u = (4 wave + k) * 64 + lane: tile row u / 4,
   // slot u % 4 holding block (u % 4) ^ ((n >> 2) & 3) of the chunk
-  uint32_t b_row[PW_B_COPIES];
+  uint32_t b_row[PW_B_COPIES], b_odd[PW_B_COPIES];
   int b_blk[PW_B_COPIES];
 #pragma unroll
   for (int k = 0; k < PW_B_COPIES; ++k) {
     const int u = (PW_B_COPIES * wave + k) * 64 + lane;
     const int n = u >> 2, slot = u & 3;
-    b_row[k] = ((uint32_t)e * (uint32_t)N + (uint32_t)weight_row(n)) * (uint32_t)(K >> 1);
+    const uint32_t wr = (uint32_t)weight_row(n);
+    // row-major: the row's start; packed: its pair's start, plus 64 bytes
+    // (one chunk segment) for the second row of the pair, scaled per chunk
+    b_row[k] = PACKED ? ((uint32_t)e * (uint32_t)(N >> 1) + (wr >> 1)) * (uint32_t)K
+                      : ((uint32_t)e * (uint32_t)N + wr) * (uint32_t)(K >> 1);
+    b_odd[k] = wr & 1u;
     b_blk[k] = slot ^ ((n >> 2) & 3);
   }
   // scale copy k fills dwords u = (2 wave + k) * 64 + lane: tile row u / 2,
@@ -1225,21 +1236,45 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
     s_row[k] = ((uint32_t)e * (uint32_t)N + (uint32_t)weight_row(u >> 1)) * (uint32_t)nblk;
     s_pair[k] = u & 1;
   }
+  // packed scales: one 4-byte copy per tile row and chunk, lane L of wave w
+  // taking tile row 64 w + L (dword 64 w + L of the chunk's scale region)
+  const int nchk = (nblk + 3) >> 2;
+  const uint32_t sp_row = ((uint32_t)e * (uint32_t)nchk * (uint32_t)N + (uint32_t)weight_row(64 * wave + lane)) * 4u;
+  // A copies whose 3.2 tile rows all lie past the tile's rows are not
+  // issued: those LDS rows keep stale data, which only the MFMA rows of
+  // discarded outputs read (an output row depends on its own A row only)
+  bool a_live[PW_A_COPIES];
+#pragma unroll
+  for (int k = 0; k < PW_A_COPIES; ++k) a_live[k] = (PW_A_COPIES * wave + k) * 64 / 20 < rows;
   auto issue = [&](int c, int buf) {
     uint8_t* base = smem + buf * PW_BUF;
 #pragma unroll
     for (int k = 0; k < PW_A_COPIES; ++k)
-      lds_copy16(arsrc, (lds_void_t*)(base + (PW_A_COPIES * wave + k) * 1024),
-                 (a_src[k] == A_OOB || 4 * c + a_blk[k] >= nblk) ? A_OOB : a_src[k] + (uint32_t)c * MX6_GROUP_BYTES);
+      if (a_live[k])
+        lds_copy16(arsrc, (lds_void_t*)(base + (PW_A_COPIES * wave + k) * 1024),
+                   (a_src[k] == A_OOB || 4 * c + a_blk[k] >= nblk) ? A_OOB : a_src[k] + (uint32_t)c * MX6_GROUP_BYTES);
+    if constexpr (PACKED) {
+      // chunk c of a pair: 128 bytes (64 per row), or 2 x 16 (nblk - 4c)
+      // bytes for a short last chunk; its blocks past K read on into the
+      // next row or pair (finite codes, multiplied by zero A pieces)
+      const uint32_t w = (uint32_t)(4 * c + 4 <= nblk ? 64 : 16 * (nblk - 4 * c));
 #pragma unroll
-    for (int k = 0; k < PW_B_COPIES; ++k)
-      lds_copy16(crsrc, (lds_void_t*)(base + PW_A_BYTES + (PW_B_COPIES * wave + k) * 1024),
-                 b_row[k] + (uint32_t)min(4 * c + b_blk[k], nblk - 1) * 16u);
+      for (int k = 0; k < PW_B_COPIES; ++k)
+        lds_copy16(crsrc, (lds_void_t*)(base + PW_A_BYTES + (PW_B_COPIES * wave + k) * 1024),
+                   b_row[k] + 128u * (uint32_t)c + b_odd[k] * w + (uint32_t)b_blk[k] * 16u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, (lds_void_t*)(base + PW_A_BYTES + PW_B_BYTES + wave * 256), 4,
+                                               sp_row + (uint32_t)c * (uint32_t)N * 4u, 0, 0, 0);
+    } else {
 #pragma unroll
-    for (int k = 0; k < PW_S_COPIES; ++k)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          srsrc, (lds_void_t*)(base + PW_A_BYTES + PW_B_BYTES + (PW_S_COPIES * wave + k) * 256), 2,
-          s_row[k] + (uint32_t)min(4 * c + 2 * s_pair[k], nblk - 2), 0, 0, 0);
+      for (int k = 0; k < PW_B_COPIES; ++k)
+        lds_copy16(crsrc, (lds_void_t*)(base + PW_A_BYTES + (PW_B_COPIES * wave + k) * 1024),
+                   b_row[k] + (uint32_t)min(4 * c + b_blk[k], nblk - 1) * 16u);
+#pragma unroll
+      for (int k = 0; k < PW_S_COPIES; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            srsrc, (lds_void_t*)(base + PW_A_BYTES + PW_B_BYTES + (PW_S_COPIES * wave + k) * 256), 2,
+            s_row[k] + (uint32_t)min(4 * c + 2 * s_pair[k], nblk - 2), 0, 0, 0);
+    }
   };
 
   v4f acc[MB][NCB];
@@ -1257,7 +1292,11 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
   constexpr int WNR = GATEUP ? 8 * NCB : 16 * NCB;  // tile rows per column half
   const uint32_t a_lane = (uint32_t)((32 * wm + r) * MX6_GROUP_BYTES + 16 * (g ^ ((r >> 1) & 3)));
   const uint32_t b_lane = (uint32_t)(PW_A_BYTES + (wn * WNR + r) * 64 + 16 * (g ^ ((r >> 2) & 3)));
-  const uint32_t s_lane = (uint32_t)(PW_A_BYTES + PW_B_BYTES + 8 * (wn * WNR + r) + 4 * (g >> 1) + (g & 1));
+  // scale bytes per tile row in LDS: row-major copies leave two bytes in
+  // each of two dwords (8 per row), packed copies four bytes
+  constexpr int SR = PACKED ? 4 : 8;
+  const uint32_t s_lane = (uint32_t)(PW_A_BYTES + PW_B_BYTES + SR * (wn * WNR + r) +
+                                     (PACKED ? g : 4 * (g >> 1) + (g & 1)));
   // tile row of column block j without the column half's part
   auto jrow = [](auto jc) constexpr {
     constexpr int j = decltype(jc)::value;
@@ -1317,8 +1356,8 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
           "i"(16 * MX6_GROUP_BYTES * 0 + 192), "i"(16 * MX6_GROUP_BYTES * 0 + 256), "i"(16 * MX6_GROUP_BYTES * 1 + 0),
           "i"(16 * MX6_GROUP_BYTES * 1 + 64), "i"(16 * MX6_GROUP_BYTES * 1 + 128), "i"(16 * MX6_GROUP_BYTES * 1 + 192),
           "i"(16 * MX6_GROUP_BYTES * 1 + 256), "i"(64 * jrow(std::integral_constant<int, 0>{})), "i"(64 * jrow(std::integral_constant<int, 1>{})),
-          "i"(64 * jrow(std::integral_constant<int, 2>{})), "i"(64 * jrow(std::integral_constant<int, 3>{})), "i"(8 * jrow(std::integral_constant<int, 0>{})),
-          "i"(8 * jrow(std::integral_constant<int, 1>{})), "i"(8 * jrow(std::integral_constant<int, 2>{})), "i"(8 * jrow(std::integral_constant<int, 3>{})));
+          "i"(64 * jrow(std::integral_constant<int, 2>{})), "i"(64 * jrow(std::integral_constant<int, 3>{})), "i"(SR * jrow(std::integral_constant<int, 0>{})),
+          "i"(SR * jrow(std::integral_constant<int, 1>{})), "i"(SR * jrow(std::integral_constant<int, 2>{})), "i"(SR * jrow(std::integral_constant<int, 3>{})));
     } else {
       asm volatile(
         "ds_read_b128 %0, %14 offset:%17\n\t"
@@ -1344,8 +1383,8 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
           "i"(16 * MX6_GROUP_BYTES * 0 + 0), "i"(16 * MX6_GROUP_BYTES * 0 + 64), "i"(16 * MX6_GROUP_BYTES * 0 + 256),
           "i"(16 * MX6_GROUP_BYTES * 1 + 0), "i"(16 * MX6_GROUP_BYTES * 1 + 64), "i"(16 * MX6_GROUP_BYTES * 1 + 256),
           "i"(64 * jrow(std::integral_constant<int, 0>{})), "i"(64 * jrow(std::integral_constant<int, 1>{})), "i"(64 * jrow(std::integral_constant<int, 2>{})),
-          "i"(64 * jrow(std::integral_constant<int, 3>{})), "i"(8 * jrow(std::integral_constant<int, 0>{})), "i"(8 * jrow(std::integral_constant<int, 1>{})),
-          "i"(8 * jrow(std::integral_constant<int, 2>{})), "i"(8 * jrow(std::integral_constant<int, 3>{})));
+          "i"(64 * jrow(std::integral_constant<int, 3>{})), "i"(SR * jrow(std::integral_constant<int, 0>{})), "i"(SR * jrow(std::integral_constant<int, 1>{})),
+          "i"(SR * jrow(std::integral_constant<int, 2>{})), "i"(SR * jrow(std::integral_constant<int, 3>{})));
       w[0][2] = w[0][3] = w[1][2] = w[1][3] = (v4u){0u, 0u, 0u, 0u};
     }
     v6u a6[MB][TERMS];
@@ -1418,8 +1457,8 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
               "v"(sq[cur][0]), "v"(sq[cur][1]), "v"(sq[cur][2]), "v"(sq[cur][3]), "v"(bb), "v"(sb),
               "i"(64 * jrow(std::integral_constant<int, k0>{})), "i"(64 * jrow(std::integral_constant<int, k0 + 1>{})),
               "i"(64 * jrow(std::integral_constant<int, k0 + 2>{})), "i"(64 * jrow(std::integral_constant<int, k0 + 3>{})),
-              "i"(8 * jrow(std::integral_constant<int, k0>{})), "i"(8 * jrow(std::integral_constant<int, k0 + 1>{})),
-              "i"(8 * jrow(std::integral_constant<int, k0 + 2>{})), "i"(8 * jrow(std::integral_constant<int, k0 + 3>{})));
+              "i"(SR * jrow(std::integral_constant<int, k0>{})), "i"(SR * jrow(std::integral_constant<int, k0 + 1>{})),
+              "i"(SR * jrow(std::integral_constant<int, k0 + 2>{})), "i"(SR * jrow(std::integral_constant<int, k0 + 3>{})));
         } else {
           asm volatile(
             "s_nop 4\n\t"
@@ -1490,8 +1529,8 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
               "v"(sq[cur][0]), "v"(sq[cur][1]), "v"(sq[cur][2]), "v"(sq[cur][3]), "v"(bb), "v"(sb),
               "i"(64 * jrow(std::integral_constant<int, k0>{})), "i"(64 * jrow(std::integral_constant<int, k0 + 1>{})),
               "i"(64 * jrow(std::integral_constant<int, k0 + 2>{})), "i"(64 * jrow(std::integral_constant<int, k0 + 3>{})),
-              "i"(8 * jrow(std::integral_constant<int, k0>{})), "i"(8 * jrow(std::integral_constant<int, k0 + 1>{})),
-              "i"(8 * jrow(std::integral_constant<int, k0 + 2>{})), "i"(8 * jrow(std::integral_constant<int, k0 + 3>{})));
+              "i"(SR * jrow(std::integral_constant<int, k0>{})), "i"(SR * jrow(std::integral_constant<int, k0 + 1>{})),
+              "i"(SR * jrow(std::integral_constant<int, k0 + 2>{})), "i"(SR * jrow(std::integral_constant<int, k0 + 3>{})));
         } else {
           asm volatile(
             "s_nop 4\n\t"
@@ -1589,7 +1628,10 @@ static int launch_gemm(const GemmParams& p, int max_tiles, int mode, hipStream_t
     const long long items = (long long)max_tiles * spans;
     const dim3 g((unsigned)((items + PF_XCD - 1) / PF_XCD * PF_XCD));
     if (wide)
-      hipLaunchKernelGGL((expert_gemm_prefill_wide<GATEUP, TERMS>), g, dim3(PW_NW * 64), 0, s, p, spans);
+      if (p.packed)
+        hipLaunchKernelGGL((expert_gemm_prefill_wide<GATEUP, TERMS, true>), g, dim3(PW_NW * 64), 0, s, p, spans);
+      else
+        hipLaunchKernelGGL((expert_gemm_prefill_wide<GATEUP, TERMS, false>), g, dim3(PW_NW * 64), 0, s, p, spans);
     else
       hipLaunchKernelGGL((expert_gemm_prefill<GATEUP, TERMS>), g, dim3(PF_NW * 64), 0, s, p, spans);
   }

@@ -47,6 +47,7 @@ struct GemmParams {
   float* y;                  // down output: fp32 [P, N]
   int terms;                 // FP6 terms of A taking part: 3 (exact path) or 1 (fast mode)
   int mb;                    // decode only: 16-row A blocks per tile (1, or 2 for 32-row tiles)
+  int packed;                // wide prefill kernel only: 1 = weights in the packed layout (moe_pack_weights)
   int alt;                   // gate/up only: 1 = the variant layout and activation (interleaved rows,
                              // Swish slope 1.702, gate clamped from above only)
   // down, decode only: the combine folded into the epilogue (fold_cnt null: no fold)
@@ -127,5 +128,9 @@ struct AttnParams {
 int launch_attention(const AttnParams& p, hipStream_t s);
 int attn_positions_per_wave(int G);
 int launch_rope(const uint16_t* x, uint16_t* out, int n, int H, int D, int pos0, float theta, hipStream_t s);
+// Packs one stack of MXFP4 matrices ([E, N, K/2] codes, [E, N, K/32] scales)
+// into the layout of the wide prefill kernel (see moe_pack_weights).
+int launch_pack_weights(const uint8_t* codes, const uint8_t* scales, int E, int N, int K, uint8_t* codes_out,
+                        uint8_t* scales_out, hipStream_t s);
 
 }  // namespace moe

@@ -124,3 +124,37 @@ def test_rope_argument_errors(kw, status):
 
 def test_rope_empty_is_a_no_op():
     assert _rope(n=0, x=None, out=None) == 0
+
+
+def _pack(codes=0x100000, scales=0x200000, E=2, N=64, K=128, co=0x300000, so=0x400000):
+    P = ctypes.c_void_p
+    return moe.lib().moe_pack_weights(P(codes), P(scales), E, N, K, P(co), P(so), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=63), -2), (dict(N=0), -2), (dict(K=96), -2), (dict(K=32), -2), (dict(E=0), -2),
+    (dict(codes=None), -1), (dict(so=None), -1), (dict(codes=0x100008), -4), (dict(co=0x300004), -4),
+    (dict(so=0x400002), -4), (dict(co=0x100000), -7), (dict(so=0x200000), -7), (dict(so=0x300010), -7),
+])
+def test_pack_weights_argument_errors(kw, status):
+    assert _pack(**kw) == status
+
+
+def test_packed_scale_bytes():
+    # one 4-byte word per row and chunk of four 32-element blocks
+    assert moe.moe_packed_scale_bytes(128, 5760, 2880) == 128 * 5760 * 4 * 23
+    assert moe.moe_packed_scale_bytes(2, 64, 128) == 2 * 64 * 4
+    assert moe.moe_packed_scale_bytes(2, 63, 128) == 0
+    assert moe.moe_packed_scale_bytes(2, 64, 96) == 0
+
+
+def test_packed_flag_needs_prefill_sizes():
+    P = ctypes.c_void_p
+    # decode sizes (T * k <= 32 E) and K/32 odd are refused before any GPU work
+    f = moe.lib().moe_layer_forward_ex
+    args = [P(0x10000)] * 9
+    assert f(*args, 32, 2880, 2880, 32, 4, 7.0, moe.MOE_LAYER_PACKED, P(0x900000), None, None, None, None,
+             None) == -3
+    assert f(*args, 4096, 2880, 2848, 32, 4, 7.0, moe.MOE_LAYER_PACKED, P(0x900000), None, None, None, None,
+             None) == -3
+    assert f(*args, 4096, 2880, 2880, 32, 4, 7.0, 8, P(0x900000), None, None, None, None, None) == -2
