@@ -135,10 +135,9 @@ enum moe_layer_flags {
    * 替换 GELU); this flag selects the other reading of both. */
   MOE_LAYER_ALT_ACT = 2,
   /* the expert weights (w13_codes, w13_scales, w2_codes, w2_scales) are in
-   * the packed layout written by moe_pack_weights; biases unchanged.  Only
-   * prefill sizes take it (T * k > 32 * E, d and I multiples of 64);
-   * other sizes return MOE_ERR_UNSUPPORTED.  Results are bitwise those of
-   * the row-major weights. */
+   * the packed layout written by moe_pack_weights; biases unchanged.  d and
+   * I must be multiples of 64 (otherwise MOE_ERR_UNSUPPORTED).  Results are
+   * bitwise those of the row-major weights. */
   MOE_LAYER_PACKED = 4
 };
 

@@ -109,10 +109,9 @@ int check_layer(const LayerArgs& a, const void* out) {
       !aligned(a.w13s, 16) || !aligned(a.w2s, 16) ||
       !aligned(a.router_b, 4) || !aligned(a.b13, 4) || !aligned(a.b2, 4))
     return MOE_ERR_MISALIGNED;
-  // the packed layout is read by the 128-row prefill kernel only, which
-  // needs an even number of 32-element blocks in both projections and more
-  // than 32 rows per expert on average
-  if (a.packed && ((a.d % 64) || (a.I % 64) || (long long)a.T * a.k <= 32LL * a.E)) return MOE_ERR_UNSUPPORTED;
+  // the packed layout pairs weight rows and keeps an even number of
+  // 32-element blocks per row: d and I multiples of 64
+  if (a.packed && ((a.d % 64) || (a.I % 64))) return MOE_ERR_UNSUPPORTED;
   if (out) {
     if (!aligned(out, 16)) return MOE_ERR_MISALIGNED;
     const size_t no = (size_t)a.T * a.d * 2;

@@ -235,6 +235,7 @@ struct DecItem {
   __amdgpu_buffer_rsrc_t srsrc;     //   and scales
   int a_off[2];                     // this lane's A row offsets (rows r, r + 16), or past the A resource
   int rs;                           // weight rows between consecutive columns of a block (1, or 2 interleaved)
+  int row0;                         // packed layout: this wave's first weight row within the expert
   float bias[4];                    // this lane's epilogue bias values (gate/up: gate and up of
                                     // columns col0 + r and col0 + 16 + r; down: column col0 + 16j + r)
 };
@@ -248,7 +249,7 @@ typedef __attribute__((address_space(4))) const int cint_t;
 // The head of an item: what its weight copies need (the tile's expert e and
 // first row m0, already loaded, and the item's column span), so that the
 // first copies go out before the row list is read.
-template <bool GATEUP>
+template <bool GATEUP, bool PACKED = false>
 __device__ __forceinline__ void dec_item_head(const GemmParams& p, int e, int m0, int span, int wave, DecItem& it) {
   const int K = p.K, N = p.N, I = p.I, nblk = K >> 5;
   it.e = e;
@@ -269,13 +270,24 @@ __device__ __forceinline__ void dec_item_head(const GemmParams& p, int e, int m0
   const int n = GATEUP ? gu_row(it.col0 + 16 * (cbv & 1), cbv >= 2, I, p.alt) : it.col0 + 16 * cbv;
   it.rs = (GATEUP && p.alt) ? 2 : 1;
   const size_t my_row = (size_t)e * N + n;
-  // resources end at the end of the arrays, so that copies past the last
-  // row return zeros instead of reading past the allocation
-  const size_t rows_left = (size_t)p.E * N - my_row;
-  it.crsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_codes + my_row * (size_t)(K >> 1)), 0,
-                                               (int)(rows_left * (size_t)(K >> 1)), 0x00020000);
-  it.srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_scales + my_row * (size_t)nblk), 0,
-                                               (int)(rows_left * (size_t)nblk), 0x00020000);
+  it.row0 = n;
+  if constexpr (PACKED) {
+    // the pair of my_row onwards (codes), the expert's chunk-major scales
+    // onwards; both end at the end of their arrays
+    const size_t pair = my_row >> 1, nchk = (size_t)((nblk + 3) >> 2);
+    it.crsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_codes + pair * (size_t)K), 0,
+                                                 (int)(((size_t)p.E * (N >> 1) - pair) * (size_t)K), 0x00020000);
+    it.srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_scales + (size_t)e * nchk * N * 4), 0,
+                                                 (int)((size_t)(p.E - e) * nchk * N * 4), 0x00020000);
+  } else {
+    // resources end at the end of the arrays, so that copies past the last
+    // row return zeros instead of reading past the allocation
+    const size_t rows_left = (size_t)p.E * N - my_row;
+    it.crsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_codes + my_row * (size_t)(K >> 1)), 0,
+                                                 (int)(rows_left * (size_t)(K >> 1)), 0x00020000);
+    it.srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_scales + my_row * (size_t)nblk), 0,
+                                                 (int)(rows_left * (size_t)nblk), 0x00020000);
+  }
 }
 
 // The tail of an item: its rows (count, place in the grouped order, the
@@ -334,14 +346,18 @@ __device__ __forceinline__ void dec_null_item(const GemmParams& p, DecItem& it) 
   it.srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.b_scales, 0, 0, 0x00020000);
   it.a_off[0] = it.a_off[1] = 0x7ffffff0;
   it.rs = 1;
+  it.row0 = 0;
   it.bias[0] = it.bias[1] = it.bias[2] = it.bias[3] = 0.f;
 }
 
 // MB = 2: 32-row tiles (two A row blocks per lane), for batches of up to
 // 32 rows per expert, so that an expert's weights are read once.
-template <bool GATEUP, int NPH, bool U16, int TERMS, int MB>
+// PACKED (with U16): the weights in the packed layout of moe_pack_weights;
+// the copies put the same bytes into the same LDS places.
+template <bool GATEUP, int NPH, bool U16, int TERMS, int MB, bool PACKED = false>
 __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) void expert_gemm_decode(GemmParams p,
                                                                                                      int spans) {
+  static_assert(!PACKED || U16, "the packed layout has K/32 even");
   using Cfg = DecCfg<U16>;
   // vector-memory instructions per wave per phase (the fast mode loads two
   // fewer A pieces per row block)
@@ -395,13 +411,38 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
       const int rr = 4 * q + sub;                  // row within the column block
       const int b = min(slot ^ rr, npb - 1);       // logical block stored at `slot`
       const int row_off = (wave * 16 + 4 * q) * DEC_KPH;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(it.crsrc, (lds_void_t*)(s_code[buf] + row_off * 16), 16,
-                                               rr * it.rs * (K >> 1) + b * 16, pb0 * 16, 0, 0);
+      if constexpr (PACKED) {
+        // weight row row0 + rr * rs sits in pair (row0 + rr * rs) / 2 (from
+        // the resource's pair), its chunk c at 128 c + half * w_c there; the
+        // phase's 4 chunks of a pair are 512 bytes (the scalar offset)
+        const int wr = (it.row0 & 1) + rr * it.rs, bb = pb0 + b, c = bb >> 2;
+        const int w = 4 * c + 4 <= nblk ? 64 : 16 * (nblk - 4 * c);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(it.crsrc, (lds_void_t*)(s_code[buf] + row_off * 16), 16,
+                                                 (wr >> 1) * K + 128 * (b >> 2) + (wr & 1) * w + 16 * (b & 3),
+                                                 pb0 * 32, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(it.crsrc, (lds_void_t*)(s_code[buf] + row_off * 16), 16,
+                                                 rr * it.rs * (K >> 1) + b * 16, pb0 * 16, 0, 0);
+      }
       if constexpr (!U16)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(it.srsrc, (lds_void_t*)(s_scl[buf] + row_off), 1,
                                                  rr * it.rs * nblk + min(slot, npb - 1), pb0, 0, 0);
     }
-    if constexpr (U16) {
+    if constexpr (PACKED) {
+      // the same block pairs into the same LDS dwords as below, from the
+      // chunk-major scales: pair 2 uc of the phase is in chunk pb0 / 4 +
+      // uc / 2 (the chunk of pb0 in the scalar offset), bytes 2 (uc & 1)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int rr = 8 * q + (lane >> 3);
+        const int u = (lane & 7) ^ ((rr >> 2) & 3);
+        const int uc = 2 * u < npb ? u : 0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(it.srsrc,
+                                                 (lds_void_t*)(s_scl[buf] + (wave * 16 + 8 * q) * Cfg::SROW), 2,
+                                                 ((uc >> 1) * N + it.row0 + rr * it.rs) * 4 + 2 * (uc & 1), pb0 * N,
+                                                 0, 0);
+      }
+    } else if constexpr (U16) {
       // instruction q moves rows 8q .. 8q+7; lane L holds the block pair
       // (L % 8) ^ ((row >> 2) & 3) of row 8q + L/8, so that the reads of 16
       // rows hit 16 banks; pairs past the phase read pair 0 (never used)
@@ -662,7 +703,7 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
   // The first phase's weight copies go out as soon as the expert is known;
   // the row list, the A offsets and the bias follow.
   DecItem cur, nul;
-  dec_item_head<GATEUP>(p, te_e, te_m0, span, wave, cur);
+  dec_item_head<GATEUP, PACKED>(p, te_e, te_m0, span, wave, cur);
   issue_b(cur, 0, 0);
   dec_item_tail<GATEUP, MB>(p, r, cur);
   dec_null_item(p, nul);
@@ -1581,29 +1622,33 @@ static bool prefill_offsets_fit(const GemmParams& p) {
 }
 
 // Decode kernel instance for the phase count of K (unrolled up to 8 phases).
-template <bool GATEUP, bool U16, int TERMS, int MB>
+template <bool GATEUP, bool U16, int TERMS, int MB, bool PACKED>
 static void launch_decode_u(const GemmParams& p, unsigned grid, int spans, hipStream_t s) {
   const int nph = (p.K / 32 + DEC_KPH - 1) / DEC_KPH;
   const dim3 g(grid), b(DEC_NW * 64);
+#define MOE_DEC(NPH) hipLaunchKernelGGL((expert_gemm_decode<GATEUP, NPH, U16, TERMS, MB, PACKED>), g, b, 0, s, p, spans)
   switch (nph) {
-    case 1: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 1, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
-    case 2: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 2, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
-    case 3: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 3, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
-    case 4: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 4, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
-    case 5: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 5, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
-    case 6: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 6, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
-    case 7: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 7, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
-    case 8: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 8, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
-    default: hipLaunchKernelGGL((expert_gemm_decode<GATEUP, 0, U16, TERMS, MB>), g, b, 0, s, p, spans); break;
+    case 1: MOE_DEC(1); break;
+    case 2: MOE_DEC(2); break;
+    case 3: MOE_DEC(3); break;
+    case 4: MOE_DEC(4); break;
+    case 5: MOE_DEC(5); break;
+    case 6: MOE_DEC(6); break;
+    case 7: MOE_DEC(7); break;
+    case 8: MOE_DEC(8); break;
+    default: MOE_DEC(0); break;
   }
+#undef MOE_DEC
 }
 
 template <bool GATEUP, int TERMS, int MB>
 static void launch_decode_mb(const GemmParams& p, unsigned items, int spans, hipStream_t s) {
-  if ((p.K / 32) % 2 == 0)
-    launch_decode_u<GATEUP, true, TERMS, MB>(p, items, spans, s);
+  if (p.packed)  // (the packed layout has K/32 even)
+    launch_decode_u<GATEUP, true, TERMS, MB, true>(p, items, spans, s);
+  else if ((p.K / 32) % 2 == 0)
+    launch_decode_u<GATEUP, true, TERMS, MB, false>(p, items, spans, s);
   else
-    launch_decode_u<GATEUP, false, TERMS, MB>(p, items, spans, s);
+    launch_decode_u<GATEUP, false, TERMS, MB, false>(p, items, spans, s);
 }
 
 template <bool GATEUP, int TERMS>

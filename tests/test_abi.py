@@ -148,13 +148,14 @@ def test_packed_scale_bytes():
     assert moe.moe_packed_scale_bytes(2, 64, 96) == 0
 
 
-def test_packed_flag_needs_prefill_sizes():
+def test_packed_flag_needs_even_block_counts():
     P = ctypes.c_void_p
-    # decode sizes (T * k <= 32 E) and K/32 odd are refused before any GPU work
+    # d or I not a multiple of 64 (an odd number of 32-element blocks) is
+    # refused before any GPU work
     f = moe.lib().moe_layer_forward_ex
     args = [P(0x10000)] * 9
-    assert f(*args, 32, 2880, 2880, 32, 4, 7.0, moe.MOE_LAYER_PACKED, P(0x900000), None, None, None, None,
+    assert f(*args, 32, 2880, 2848, 32, 4, 7.0, moe.MOE_LAYER_PACKED, P(0x900000), None, None, None, None,
              None) == -3
-    assert f(*args, 4096, 2880, 2848, 32, 4, 7.0, moe.MOE_LAYER_PACKED, P(0x900000), None, None, None, None,
+    assert f(*args, 4096, 2848, 2880, 32, 4, 7.0, moe.MOE_LAYER_PACKED, P(0x900000), None, None, None, None,
              None) == -3
     assert f(*args, 4096, 2880, 2880, 32, 4, 7.0, 8, P(0x900000), None, None, None, None, None) == -2
