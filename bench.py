@@ -19,7 +19,11 @@ combine -- on one batch of synthetic inputs already resident in HBM (for the
 36-layer stack, one pass through all layers with the RMSNorm and residual
 add between them).  Single-layer steps rotate over several independently
 seeded weight sets so that HBM, not the 256 MB Infinity Cache, serves the
-weights.  Every leg times exactly K steps after W warm-up steps.
+weights.  Every leg times exactly K steps after W warm-up steps, on the
+expert weights in the library's packed layout (moe_pack_weights, applied
+once per weight set before timing: the same MXFP4 bytes, two weight rows per
+128-byte line); the same leg on the row-major stored layout is timed beside
+it and reported under config.rowmajor.
 
 Per-kernel durations come from HIP events the library records around its
 launches on the launch stream (moe_timing_enable); the dominant kernel's
@@ -202,63 +206,94 @@ def run_leg(wl, bound, args, torch, moe, want_cpu):
     P = wl.T * wl.k
     x_bytes = wl.T * wl.d * 2
 
-    if nlay == 1:
-        fwd = moe.moe_layer_forward if args.act == "exact" else moe.moe_layer_forward_mx6
-        outs = [torch.empty((wl.T, wl.d), dtype=torch.bfloat16, device="cuda:0") for _ in range(nsets)]
-
-        def step(i):
-            g = sets[i % nsets]
-            return fwd(*[g[k] for k in KEYS], k=wl.k, clamp=wl.clamp, out=outs[i % nsets])
-    else:
-        x0 = sets[0]["x"]
-        out = torch.empty_like(x0)
-        layers = [{k: g[k] for k in LAYER_KEYS} for g in sets]
-
-        def step(i):
-            return moe.moe_stack_forward(x0, layers, k=wl.k, clamp=wl.clamp, eps=1e-5, out=out)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # per-kernel breakdown (diagnostic, untimed): every kernel bracketed by events
-    moe.moe_timing_read(reset=True)
-    moe.moe_timing_enable(True)
-    for i in range(min(args.steps, 20 if nlay == 1 else 2)):
-        step(i)
-    torch.cuda.synchronize()
-    moe.moe_timing_enable(False)
-    kt = moe.moe_timing_read(reset=True)
-
-    # timed region: K steps; in every TIME_EVERY-th step the library brackets
-    # the dominant kernel's launches (gate/up GEMM) with HIP event pairs on
-    # the launch stream.  An event pair costs about 11 us of stream time
-    # around a decode step, so bracketing every step would inflate the step
-    # time it is measured in; the sampled launches run inside the same
-    # stream of steps.
-    torch.cuda.synchronize()
+    # Every leg runs on both weight layouts: the packed layout
+    # (moe_pack_weights, once per weight set before timing) is the primary
+    # record; the row-major layout (the stored format, moe_layer_forward)
+    # is timed the same way beside it.
     t0 = time.perf_counter()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for i in range(args.steps):
-        timed = i % TIME_EVERY == 0
-        if timed:
-            moe.moe_timing_enable(["gateup_gemm"])
-        step(i)
-        if timed:
-            moe.moe_timing_enable(False)
-    ev1.record()
+    psets = []
+    for g in sets:
+        pg = dict(g)
+        pg["w13_codes"], pg["w13_scales"] = moe.moe_pack_weights(g["w13_codes"], g["w13_scales"])
+        pg["w2_codes"], pg["w2_scales"] = moe.moe_pack_weights(g["w2_codes"], g["w2_scales"])
+        psets.append(pg)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kt_live = moe.moe_timing_read(reset=True)
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"weights packed in {time.perf_counter() - t0:.2f} s")
+    mx6 = args.act != "exact"
+
+    def make_step(S, packed):
+        flags = (moe.MOE_LAYER_PACKED if packed else 0) | (moe.MOE_LAYER_MXFP6 if mx6 else 0)
+        if nlay == 1:
+            outs = [torch.empty((wl.T, wl.d), dtype=torch.bfloat16, device="cuda:0") for _ in range(nsets)]
+
+            def step(i):
+                g = S[i % nsets]
+                if flags:
+                    return moe.moe_layer_forward_ex(*[g[k] for k in KEYS], k=wl.k, clamp=wl.clamp, flags=flags,
+                                                    out=outs[i % nsets])
+                return moe.moe_layer_forward(*[g[k] for k in KEYS], k=wl.k, clamp=wl.clamp, out=outs[i % nsets])
+        else:
+            x0 = S[0]["x"]
+            out = torch.empty_like(x0)
+            layers = [{k: g[k] for k in LAYER_KEYS} for g in S]
+
+            def step(i):
+                return moe.moe_stack_forward(x0, layers, k=wl.k, clamp=wl.clamp, eps=1e-5, out=out, flags=flags)
+        return step
+
+    def measure(step, breakdown):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        kt = None
+        if breakdown:
+            # per-kernel breakdown (diagnostic, untimed): every kernel bracketed by events
+            moe.moe_timing_read(reset=True)
+            moe.moe_timing_enable(True)
+            for i in range(min(args.steps, 20 if nlay == 1 else 2)):
+                step(i)
+            torch.cuda.synchronize()
+            moe.moe_timing_enable(False)
+            kt = moe.moe_timing_read(reset=True)
+        # timed region: K steps; in every TIME_EVERY-th step the library
+        # brackets the dominant kernel's launches (gate/up GEMM) with HIP
+        # event pairs on the launch stream.  An event pair costs about 11 us
+        # of stream time around a decode step, so bracketing every step would
+        # inflate the step time it is measured in; the sampled launches run
+        # inside the same stream of steps.
+        moe.moe_timing_read(reset=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(args.steps):
+            timed = i % TIME_EVERY == 0
+            if timed:
+                moe.moe_timing_enable(["gateup_gemm"])
+            step(i)
+            if timed:
+                moe.moe_timing_enable(False)
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kt_live = moe.moe_timing_read(reset=True)
+        ms_step = ev0.elapsed_time(ev1) / args.steps
+        gu_ms, gu_n = kt_live["gateup_gemm"]
+        return ms_step, wall / args.steps, gu_ms / max(gu_n, 1) * 1e3, gu_n, kt
+
+    ms_rm, wall_rm, gu_us_rm, _, kt_rm = measure(make_step(sets, False), breakdown=True)
+    log(f"row-major weights: {ms_rm * 1e3:.1f} us/step (host wall {wall_rm * 1e6:.1f} us/step), "
+        f"gate/up live {gu_us_rm:.1f} us")
+    for kname, (ms, n) in kt_rm.items():
+        if n:
+            log(f"  {kname:12s} {ms / n * 1e3:9.1f} us/launch  x{n}  (separate pass, all kernels timed)")
+    ms_step, wall, gu_us, gu_n, kt = measure(make_step(psets, True), breakdown=True)
     tok_s = wl.T / (ms_step * 1e-3)
-    log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (host wall {wall / args.steps * 1e6:.1f} us/step)")
+    log(f"packed weights: timed {args.steps} steps: {ms_step * 1e3:.1f} us/step "
+        f"(host wall {wall * 1e6:.1f} us/step)")
     for kname, (ms, n) in kt.items():
         if n:
             log(f"  {kname:12s} {ms / n * 1e3:9.1f} us/launch  x{n}  (separate pass, all kernels timed)")
-    gu_ms, gu_n = kt_live["gateup_gemm"]
-    gu_us = gu_ms / max(gu_n, 1) * 1e3
     log(f"  gateup_gemm live in the timed region: {gu_us:.1f} us/launch ({gu_n} sampled launches)")
 
     # algorithmic work
@@ -273,6 +308,7 @@ def run_leg(wl, bound, args, torch, moe, want_cpu):
     gu_bytes = nsel_mean * gu_unit_bytes + x_bytes
     gu_flops = 2.0 * P * wl.d * 2 * wl.I
     traffic = read_traffic("gateup_gemm", wl.name) if args.act == "exact" else None
+    hbm_kernel_rm = gu_bytes / (gu_us_rm * 1e-6)
     hbm_kernel = gu_bytes / (gu_us * 1e-6)
     mfma_kernel = gu_flops / (gu_us * 1e-6)
     if bound == "hbm":
@@ -305,18 +341,23 @@ def run_leg(wl, bound, args, torch, moe, want_cpu):
             "parallelism": "single-gpu",
             "activations": "three-term MX6x3 (each value to about 2^-13 of its 32-block maximum)"
                            if args.act == "exact" else "mxfp6 (activation-quantised fast mode)",
+            "weight_layout": "packed MXFP4 (moe_pack_weights once per weight set before timing; "
+                             "MOE_LAYER_PACKED); the same bytes as the stored format",
+            "rowmajor": {
+                "weight_layout": "row-major MXFP4 as stored (moe_layer_forward / moe_stack_forward)",
+                "ms_per_step": ms_rm, "value": wl.T / (ms_rm * 1e-3),
+                "gateup_gemm_us": gu_us_rm,
+                "kernel_us": {k: (v[0] / v[1] * 1e3 if v[1] else None) for k, v in kt_rm.items()},
+                "gateup_roofline_frac": (hbm_kernel_rm / HBM_PEAK) if bound == "hbm"
+                                        else gu_flops / (gu_us_rm * 1e-6) / MFMA_FP6_FP4_PEAK,
+            },
         },
         "roofline": roof,
         "cpu_baseline": None,
     }
     # free this leg's device memory before the next leg
     sets.clear()
-    if nlay > 1:
-        layers.clear()
-        del x0, out
-    else:
-        outs.clear()
-    del g, step
+    psets.clear()
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     if want_cpu and host0 is not None:
