@@ -88,11 +88,14 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,wl", CASES, ids=[c[0] for c in CASES])
-@pytest.mark.parametrize("alt", [0, moe.MOE_LAYER_ALT_ACT])
+# every case with the stored activation reading, and the variant one (interleaved gate/up rows)
+# on the shapes that exercise each kernel once
+ALT_ON = ("tiny", "20b_decode", "qwen3_decode", "20b_prefill", "ragged", "ragged_k8")
+RUNS = [(n, w, 0) for n, w in CASES] + [(n, w, moe.MOE_LAYER_ALT_ACT) for n, w in CASES if n in ALT_ON]
+
+
+@pytest.mark.parametrize("name,wl,alt", RUNS, ids=[f"{n}-alt{a}" for n, _, a in RUNS])
 def test_packed_layer_equals_row_major_bitwise(torch, name, wl, alt):
-    if alt and name in ("120b_prefill_zipf", "stack_layer", "20b_batch256", "decode_k4160"):
-        pytest.skip("the variant activation is covered on the other shapes")
     wl = wl or WORKLOADS[name]
     say(f"packed vs row-major {name} alt={alt}")
     inp = make_inputs(wl, condition=False)
