@@ -20,9 +20,10 @@
 //                    keys of it in each of the four lane groups;
 //   softmax          scores scaled by log2(e)/sqrt(D), masked, running max and
 //                    sum per column (exchanged between the four lane groups);
-//   O^T += V^T P^T   A = 16 head elements x 32 keys from a transposed copy of
-//                    the value tile in LDS, B = P^T straight from the softmax's
-//                    registers (the MFMA's K order is chosen to match them).
+//   O^T += V^T P^T   A = 16 head elements x 32 keys, read from the value tile
+//                    (stored as it comes, key rows) with gfx950's transposing
+//                    LDS reads, B = P^T straight from the softmax's registers
+//                    (the MFMA's K order is chosen to match them).
 //                    P is fed as two bf16 terms, hi = bf16(p) and
 //                    lo = bf16(p - hi), so the products carry p to about 2^-17.
 // The output O^T has the same one-column-per-lane layout as the softmax
@@ -52,19 +53,30 @@ constexpr int AT_BK = 32;             // keys per tile
 constexpr int AT_NQ = 2;              // 16-column blocks per wave
 constexpr int AT_TILE_BYTES = AT_BK * AT_D * 2;  // 4 KB of keys or of values
 
-// LDS copy of one tile: keys as rows of 128 bytes whose 16-byte chunks are
-// XOR-swizzled by the key's low three bits; values transposed, one row of 64
-// bytes per head element whose 8-byte chunks (four keys each) are swizzled by
-// bits 1..3 of the element index.  Both make the MFMA operand reads free of
-// bank conflicts.
+// LDS copy of one tile: keys and values as rows of 128 bytes (one key each),
+// their 16-byte chunks XOR-swizzled -- keys by the key's bits 0..2, values by
+// bits 1..3 -- so that the 16-byte key reads are conflict-free and the
+// values' transposing 8-byte reads (16 rows at a time) at most two-way.
 struct AttnTile {
   uint8_t k[AT_TILE_BYTES];
-  uint8_t vt[AT_TILE_BYTES];
+  uint8_t v[AT_TILE_BYTES];
 };
 
 __device__ __forceinline__ uint32_t k_lds_off(int key, int chunk) { return key * 128 + ((chunk ^ (key & 7)) << 4); }
-__device__ __forceinline__ uint32_t vt_lds_off(int d, int key) {
-  return d * 64 + (((key >> 2) ^ ((d >> 1) & 7)) << 3) + ((key & 3) << 1);
+// byte offset of the 8-byte group q (head elements 4q .. 4q+3) of key `key`
+__device__ __forceinline__ uint32_t v_lds_off(int key, int q) {
+  return key * 128 + ((((q >> 1) ^ ((key >> 1) & 7))) << 4) + ((q & 1) << 3);
+}
+
+typedef short at_s4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) at_s4 lds_s4;
+
+// gfx950's transposing LDS read (ds_read_b64_tr_b16): within each group of
+// 16 lanes, if lane 4i + s reads the 4 elements D[4i + s][0..3] at its
+// address, lane j receives D[4i + j / 4][j % 4] for i = 0..3.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint8_t* p) {
+  const at_s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(__attribute__((address_space(3))) uint8_t*)p);
+  return __builtin_bit_cast(uint2, v);
 }
 
 // Copies the 16-byte chunks u = first, first + step, ... (< 256) of tile t
@@ -98,10 +110,7 @@ __device__ __forceinline__ void tile_store(AttnTile& s, int first, int step, con
   for (int i = 0; i < NCH; ++i) {
     const int u = first + i * step, key = u >> 3, c = u & 7;
     *(uint4*)(s.k + k_lds_off(key, c)) = r.k[i];
-    const uint32_t w[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *(uint16_t*)(s.vt + vt_lds_off(8 * c + e, key)) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    *(uint4*)(s.v + v_lds_off(key, 2 * c)) = r.v[i];
   }
 }
 
@@ -137,12 +146,13 @@ struct AttnState {
 };
 
 // One tile for the lane's NQ column blocks.  pos[n] is the position of the
-// lane's column in block n (any value for columns past the batch: their keys
-// are all masked).  MASK = false for a tile every column of the wave sees
-// whole (the caller checks that), which skips the masking.
+// lane's column in block n (-1 for columns past the batch, so that all their
+// keys are masked); a column sees key j when 0 <= pos - j < span.  MASK =
+// false for a tile every column of the wave sees whole (the caller checks
+// that), which skips the masking.
 template <bool MASK>
 __device__ __forceinline__ void attn_tile(const AttnTile& s, int t, const v8bf (&qf)[AT_NQ][2],
-                                          const int (&pos)[AT_NQ], const bool (&live)[AT_NQ], int window,
+                                          const int (&pos)[AT_NQ], const bool (&live)[AT_NQ], uint32_t span,
                                           float scale, AttnState& st) {
   const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
   // K fragments: key 16 kb + r, head elements 32 ks + 8 g .. + 7
@@ -152,15 +162,17 @@ __device__ __forceinline__ void attn_tile(const AttnTile& s, int t, const v8bf (
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
       kf[kb][ks] = *(const v8bf*)(s.k + k_lds_off(16 * kb + r, 4 * ks + g));
-  // V^T fragments: head element 16 db + r, keys 4g .. 4g+3 and 16+4g .. 16+4g+3
+  // V^T fragments: head element 16 db + r, keys 4g .. 4g+3 and 16+4g ..
+  // 16+4g+3.  Lane (g, 4i + s) reads elements 16 db + 4s .. + 3 of key
+  // 4g + i (then of key 16 + 4g + i); the transposing read hands lane
+  // (g, r) element 16 db + r of the four keys.
   v8bf vf[AT_D / 16];
+  const int ki = r >> 2, qs = r & 3;
 #pragma unroll
   for (int db = 0; db < AT_D / 16; ++db) {
-    const int d = 16 * db + r;
-    const uint2 a = *(const uint2*)(s.vt + vt_lds_off(d, 4 * g));
-    const uint2 c = *(const uint2*)(s.vt + vt_lds_off(d, 16 + 4 * g));
-    const uint4 w = make_uint4(a.x, a.y, c.x, c.y);
-    vf[db] = __builtin_bit_cast(v8bf, w);
+    const uint2 a = lds_read_tr16(s.v + v_lds_off(4 * g + ki, 4 * db + qs));
+    const uint2 c = lds_read_tr16(s.v + v_lds_off(16 + 4 * g + ki, 4 * db + qs));
+    vf[db] = __builtin_bit_cast(v8bf, make_uint4(a.x, a.y, c.x, c.y));
   }
 #pragma unroll
   for (int n = 0; n < AT_NQ; ++n) {
@@ -183,7 +195,9 @@ __device__ __forceinline__ void attn_tile(const AttnTile& s, int t, const v8bf (
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = AT_BK * t + 16 * kb + 4 * g + e;
-        const bool ok = !MASK || (live[n] && key <= pos[n] && (window == 0 || pos[n] - key < window));
+        // (one unsigned compare: 0 <= pos - key < span, span the band's
+        // width or 2^31 - 1; columns past the batch have pos = -1)
+        const bool ok = !MASK || (uint32_t)(pos[n] - key) < span;
         const float v = ok ? sc[kb][e] : -INFINITY;
         x[4 * kb + e] = v;
         mx = fmaxf(mx, v);
@@ -269,7 +283,7 @@ __global__ __launch_bounds__(AttnShape<KS>::NW * 64) void attn_kernel(AttnParams
   for (int n = 0; n < AT_NQ; ++n) {
     qi[n] = wq0 + n * PPB + r / G;
     live[n] = qi[n] < p.Tq;
-    pos[n] = p.q_pos0 + qi[n];
+    pos[n] = live[n] ? p.q_pos0 + qi[n] : -1;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       uint4 w = make_uint4(0u, 0u, 0u, 0u);
@@ -280,14 +294,15 @@ __global__ __launch_bounds__(AttnShape<KS>::NW * 64) void attn_kernel(AttnParams
   // tiles that every column of the wave sees whole need no mask
   const bool wave_full = wq0 + PPW <= p.Tq;
   const int wp0 = p.q_pos0 + wq0, wp1 = wp0 + PPW - 1;
+  const uint32_t span = p.window > 0 ? (uint32_t)p.window : 0x7fffffffu;
   auto unmasked = [&](int t) {
     return wave_full && AT_BK * t + AT_BK - 1 <= wp0 && (p.window == 0 || wp1 - AT_BK * t < p.window);
   };
   auto tile = [&](const AttnTile& s, int t, AttnState& st) {
     if (unmasked(t))
-      attn_tile<false>(s, t, qf, pos, live, p.window, p.qk_scale, st);
+      attn_tile<false>(s, t, qf, pos, live, span, p.qk_scale, st);
     else
-      attn_tile<true>(s, t, qf, pos, live, p.window, p.qk_scale, st);
+      attn_tile<true>(s, t, qf, pos, live, span, p.qk_scale, st);
   };
   // the sink starts the running state of one wave per column (all in the
   // query split, wave 0 in the key split)
