@@ -31,6 +31,8 @@ struct Layout {
   int max_tiles;
 };
 
+constexpr int kWide64Rows = 48;
+
 int max_tiles_for(int P, int E, int mt) { return (P + mt - 1) / mt + (E < P ? E : P); }
 
 Layout layout(int T, int d, int I, int E, int k) {
@@ -206,11 +208,17 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   // tiles from 33 rows per expert on, partly filled tiles included (20b
   // shapes: 264 tokens 233 vs 256 us, 384 tokens 242 vs 296 us)
   const bool wide = !small_m && (a.d / 32) % 2 == 0 && (a.I / 32) % 2 == 0;
-  const int mode = small_m ? GEMM_DECODE : wide ? GEMM_WIDE : GEMM_PREFILL;
+  // up to kWide64Rows rows per expert on average, 64-row wide tiles with
+  // three weight stages: twice the weight bytes in flight and half the idle
+  // MFMA rows (20b shapes: 288 tokens 177 vs 208 us, 384 tokens 186 vs 211
+  // us; even from 56 rows on, where experts start to need a second 64-row
+  // tile that reads the weights again)
+  const bool wide64 = wide && (long long)P <= (long long)kWide64Rows * a.E;
+  const int mode = small_m ? GEMM_DECODE : wide64 ? GEMM_WIDE64 : wide ? GEMM_WIDE : GEMM_PREFILL;
   // decode sizes above 16 rows per expert: 32-row tiles (two row blocks),
   // which read an expert's weights once
   const bool mb2 = small_m && (long long)P > 16LL * a.E;
-  const int mt = small_m ? (mb2 ? MT_SMALL2 : MT_SMALL) : wide ? MT_WIDE : MT_LARGE;
+  const int mt = small_m ? (mb2 ? MT_SMALL2 : MT_SMALL) : (wide && !wide64) ? MT_WIDE : MT_LARGE;
   const int max_tiles = max_tiles_for(P, a.E, mt);
   int* hdr = (int*)ws;
 

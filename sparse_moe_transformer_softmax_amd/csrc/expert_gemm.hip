@@ -1119,58 +1119,78 @@ __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams 
 }
 
 // The prefill kernel addresses operands with 32-bit byte offsets.
-// Wide prefill kernel: tiles of PW_MT = 128 rows x PW_NT = 512 weight rows
-// (gate/up: 256 gate + the matching 256 up columns), eight waves, one
-// workgroup per CU.  Wave (wm, wn) owns rows 32wm .. 32wm+31 (two 16-row
-// blocks) and 16 column blocks (gate/up: 8 gate + the matching 8 up blocks),
-// so each A fragment feeds 48 MFMAs and each B fragment 6.  With the
-// three-term A operand (80 bytes per 32 elements) the operands of a 64 x 256
-// tile need about as many bytes per MFMA as a CU's L1 can deliver; this
-// tile moves half as many.
+// Wide prefill kernel: tiles of MT = 128 or 64 rows x PW_NT = 512 weight
+// rows (gate/up: 256 gate + the matching 256 up columns), eight waves, one
+// workgroup per CU.  Each wave owns 32 tile rows (two 16-row blocks) and
+// 512 / WN weight rows (gate/up: half gate, half the matching up rows):
+//   MT = 128: 4 x 2 waves, 16 column blocks per wave, so each A fragment
+//     feeds 48 MFMAs and each B fragment 6.  With the three-term A operand
+//     (80 bytes per 32 elements) the operands of a 64 x 256 tile need about
+//     as many bytes per MFMA as a CU's L1 can deliver; this tile moves half
+//     as many.
+//   MT = 64: 2 x 4 waves, 8 column blocks per wave, for experts of fewer
+//     than 64 rows (many experts and few tokens each: an expert's weights
+//     are then read once, and HBM, not the MFMAs, bounds the kernel).  The
+//     smaller A tile leaves room for three weight stages, so each CU keeps
+//     two chunks of weights in flight instead of one.
 //
 // Both operands reach LDS with buffer_load ... lds (no register staging):
-// per 4-block K chunk the A tile is 128 rows x 320 bytes (one piece-
+// per 4-block K chunk the A tile is MT rows x 320 bytes (one piece-
 // interleaved group per row) and the weight tile 512 rows x 64 bytes of
 // codes plus their scale bytes (2-byte copies, one per LDS dword).  Each
 // copy instruction fills 1 KB (256 B for scales) of consecutive LDS, and
 // the lane -> source mapping places the pieces XOR-swizzled (A: piece s of
 // row m at slot s ^ ((m >> 1) & 3); B: piece g of row n at g ^ ((n >> 2) &
-// 3)), so the fragment reads are free of bank conflicts.  Two chunk buffers:
-// the copies of chunk c+1 are issued right after the barrier that opens
-// chunk c and waited for (vmcnt) before the next barrier.  The LDS reads are
-// asm blocks that wait for their own results, so the compiler never waits
-// for the copies in flight.  Offsets include the chunk (no scalar offset):
-// weight blocks past K are clamped to the row's last block, A rows past the
-// tile read past the A resource (zeros, no traffic).
-constexpr int PW_MT = 128;
+// 3)), so the fragment reads are free of bank conflicts.  A ring of two A
+// stages and a ring of SB weight stages: after the barrier that opens
+// chunk c the copies of A for chunk c+1 and of the weights for chunk
+// c+SB-1 are issued, and each wave waits (vmcnt, in issue order) for its
+// copies of chunk c before that barrier.  The LDS reads are asm blocks that
+// wait for their own results, so the compiler never waits for the copies
+// in flight.  Offsets include the chunk (no scalar offset): weight blocks
+// past K are clamped to the row's last block, A rows past the tile read
+// past the A resource (zeros, no traffic).
 constexpr int PW_NT = 512;
 constexpr int PW_NW = 8;
-constexpr int PW_NCB = 16;
-constexpr int PW_A_BYTES = PW_MT * MX6_GROUP_BYTES;   // 40960
 constexpr int PW_B_BYTES = PW_NT * 64;                // 32768
 constexpr int PW_S_BYTES = PW_NT * 2 * 4;             // 4096
-constexpr int PW_BUF = PW_A_BYTES + PW_B_BYTES + PW_S_BYTES;
-constexpr int PW_A_COPIES = PW_A_BYTES / 1024 / PW_NW;  // 5 per wave
+constexpr int PW_B_STAGE = PW_B_BYTES + PW_S_BYTES;
 constexpr int PW_B_COPIES = PW_B_BYTES / 1024 / PW_NW;  // 4 per wave
 constexpr int PW_S_COPIES = PW_NT * 2 / 64 / PW_NW;     // 2 per wave
-constexpr int PW_EPI_BYTES = 16 * (16 * PW_NCB + 4) * 4;
-static_assert(PW_A_COPIES == 5 && PW_B_COPIES == 4 && PW_S_COPIES == 2, "copy split");
-static_assert(PW_EPI_BYTES >= 16 * (8 * PW_NCB + 4) * 4, "gate/up staging fits");
-static_assert(PW_NW * PW_EPI_BYTES <= 2 * PW_BUF, "epilogue staging fits the operand buffers");
+static_assert(PW_B_COPIES == 4 && PW_S_COPIES == 2, "copy split");
+
+template <int MT>
+struct PwCfg {
+  static_assert(MT == 128 || MT == 64, "128- or 64-row tiles");
+  static constexpr int WN = MT == 128 ? 2 : 4;         // waves across the weight rows
+  static constexpr int WM = PW_NW / WN;                // waves down the tile rows, 32 rows each
+  static constexpr int NCB = PW_NT / 16 / WN;          // column blocks per wave
+  static constexpr int A_BYTES = MT * MX6_GROUP_BYTES;  // 40960 or 20480
+  static constexpr int A_COPIES = A_BYTES / 1024;      // 1-KB A copies per chunk (all waves)
+  static constexpr int A_PER = (A_COPIES + PW_NW - 1) / PW_NW;  // per wave, at most
+  static constexpr int SB = MT == 128 ? 2 : 3;         // weight stages
+  static constexpr int SMEM = 2 * A_BYTES + SB * PW_B_STAGE;
+  static constexpr int EPI_BYTES = 16 * (16 * NCB + 4) * 4;  // per-wave epilogue staging
+  static_assert(WM * 32 == MT && NCB % 4 == 0, "wave grid");
+  static_assert(A_BYTES % 1024 == 0, "whole A copies");
+  static_assert(PW_NW * EPI_BYTES <= SMEM, "epilogue staging fits the operand buffers");
+  static_assert(SMEM + PW_NT * 4 <= 160 * 1024, "LDS");
+};
 
 // PACKED: the weights in the packed layout of moe_pack_weights (two weight
 // rows' 64-byte chunk segments share one 128-byte line; each chunk's scale
 // bytes are 4 per row, rows consecutive), so that a chunk's copies touch
 // half the cache lines of the row-major codes and 1/32 of the lines of the
 // row-major scales.  Same LDS contents, same arithmetic, same results.
-template <bool GATEUP, int TERMS, bool PACKED>
+template <bool GATEUP, int TERMS, bool PACKED, int MT>
 __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmParams p, int spans) {
   // (the body is compiled for the device only: the host pass, which only
   // needs the kernel's signature for its launch stub, cannot type the
   // 6-register operands of the asm blocks)
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int MB = 2, NCB = PW_NCB;
-  __shared__ __align__(16) uint8_t smem[2 * PW_BUF];
+  using C = PwCfg<MT>;
+  constexpr int MB = 2, NCB = C::NCB, WN = C::WN;
+  __shared__ __align__(16) uint8_t smem[C::SMEM];
   __shared__ float s_bias[PW_NT];
 
   // ---- work item: dealt to the XCDs in contiguous ranges ----
@@ -1182,10 +1202,10 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
   const int tile = item / spans, span = item - tile * spans;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int2 te = p.tiles[tile];
   const int e = te.x, m0 = te.y;
-  const int rows = min(PW_MT, p.counts[e] - m0);
+  const int rows = min(MT, p.counts[e] - m0);
   const int row_base = p.offsets[e] + m0;
   const int K = p.K, N = p.N, I = p.I, nblk = K >> 5;
   const int g = lane >> 4, r = lane & 15;
@@ -1229,15 +1249,16 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
       (void*)p.b_scales, 0,
       (int)((uint32_t)p.E * (uint32_t)N * (uint32_t)(PACKED ? 4 * ((nblk + 3) >> 2) : nblk)), 0x00020000);
   constexpr uint32_t A_OOB = 0x7ffffff0u;  // at or past the A resource's end (it is below 2^31 bytes)
-  // A copy k of this wave fills LDS slots u = (5 wave + k) * 64 + lane:
-  // tile row u / 20, slot u % 20 holding piece (u % 20) ^ ((row >> 1) & 3)
-  // (pieces of blocks past K are copied from past the resource: zeros, so
-  // that those K positions contribute nothing whatever the weights hold)
-  uint32_t a_src[PW_A_COPIES];
-  int a_blk[PW_A_COPIES];  // block of the piece within its group of four
+  // A copy k of this wave (copy number i = 8k + wave of the chunk, if
+  // below A_COPIES) fills LDS slots u = 64 i + lane: tile row u / 20, slot
+  // u % 20 holding piece (u % 20) ^ ((row >> 1) & 3) (pieces of blocks past
+  // K are copied from past the resource: zeros, so that those K positions
+  // contribute nothing whatever the weights hold)
+  uint32_t a_src[C::A_PER];
+  int a_blk[C::A_PER];  // block of the piece within its group of four
 #pragma unroll
-  for (int k = 0; k < PW_A_COPIES; ++k) {
-    const int u = (PW_A_COPIES * wave + k) * 64 + lane;
+  for (int k = 0; k < C::A_PER; ++k) {
+    const int u = (PW_NW * k + wave) * 64 + lane;
     const int m = u / 20, slot = u - 20 * m;
     const int piece = slot ^ ((m >> 1) & 3);
     uint32_t off = A_OOB;
@@ -1281,19 +1302,27 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
   // taking tile row 64 w + L (dword 64 w + L of the chunk's scale region)
   const int nchk = (nblk + 3) >> 2;
   const uint32_t sp_row = ((uint32_t)e * (uint32_t)nchk * (uint32_t)N + (uint32_t)weight_row(64 * wave + lane)) * 4u;
-  // A copies whose 3.2 tile rows all lie past the tile's rows are not
-  // issued: those LDS rows keep stale data, which only the MFMA rows of
-  // discarded outputs read (an output row depends on its own A row only)
-  bool a_live[PW_A_COPIES];
+  // A copies whose 3.2 tile rows all lie past the tile's rows (or past the
+  // tile) are not issued: those LDS rows keep stale data, which only the
+  // MFMA rows of discarded outputs read (an output row depends on its own A
+  // row only)
+  bool a_live[C::A_PER];
 #pragma unroll
-  for (int k = 0; k < PW_A_COPIES; ++k) a_live[k] = (PW_A_COPIES * wave + k) * 64 / 20 < rows;
-  auto issue = [&](int c, int buf) {
-    uint8_t* base = smem + buf * PW_BUF;
+  for (int k = 0; k < C::A_PER; ++k)
+    a_live[k] = PW_NW * k + wave < C::A_COPIES && (PW_NW * k + wave) * 64 / 20 < rows;
+  auto issue_a = [&](int c, int stage) {
+    uint8_t* base = smem + stage * C::A_BYTES;
 #pragma unroll
-    for (int k = 0; k < PW_A_COPIES; ++k)
+    for (int k = 0; k < C::A_PER; ++k)
       if (a_live[k])
-        lds_copy16(arsrc, (lds_void_t*)(base + (PW_A_COPIES * wave + k) * 1024),
+        lds_copy16(arsrc, (lds_void_t*)(base + (PW_NW * k + wave) * 1024),
                    (a_src[k] == A_OOB || 4 * c + a_blk[k] >= nblk) ? A_OOB : a_src[k] + (uint32_t)c * MX6_GROUP_BYTES);
+  };
+  // the weight copies of a chunk: PW_B_COPIES code copies, then the scale
+  // copies (one packed, PW_S_COPIES row-major) per wave
+  constexpr int B_OPS = PW_B_COPIES + (PACKED ? 1 : PW_S_COPIES);
+  auto issue_b = [&](int c, int stage) {
+    uint8_t* base = smem + 2 * C::A_BYTES + stage * PW_B_STAGE;
     if constexpr (PACKED) {
       // chunk c of a pair: 128 bytes (64 per row), or 2 x 16 (nblk - 4c)
       // bytes for a short last chunk; its blocks past K read on into the
@@ -1301,19 +1330,19 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
       const uint32_t w = (uint32_t)(4 * c + 4 <= nblk ? 64 : 16 * (nblk - 4 * c));
 #pragma unroll
       for (int k = 0; k < PW_B_COPIES; ++k)
-        lds_copy16(crsrc, (lds_void_t*)(base + PW_A_BYTES + (PW_B_COPIES * wave + k) * 1024),
+        lds_copy16(crsrc, (lds_void_t*)(base + (PW_B_COPIES * wave + k) * 1024),
                    b_row[k] + 128u * (uint32_t)c + b_odd[k] * w + (uint32_t)b_blk[k] * 16u);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, (lds_void_t*)(base + PW_A_BYTES + PW_B_BYTES + wave * 256), 4,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, (lds_void_t*)(base + PW_B_BYTES + wave * 256), 4,
                                                sp_row + (uint32_t)c * (uint32_t)N * 4u, 0, 0, 0);
     } else {
 #pragma unroll
       for (int k = 0; k < PW_B_COPIES; ++k)
-        lds_copy16(crsrc, (lds_void_t*)(base + PW_A_BYTES + (PW_B_COPIES * wave + k) * 1024),
+        lds_copy16(crsrc, (lds_void_t*)(base + (PW_B_COPIES * wave + k) * 1024),
                    b_row[k] + (uint32_t)min(4 * c + b_blk[k], nblk - 1) * 16u);
 #pragma unroll
       for (int k = 0; k < PW_S_COPIES; ++k)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            srsrc, (lds_void_t*)(base + PW_A_BYTES + PW_B_BYTES + (PW_S_COPIES * wave + k) * 256), 2,
+            srsrc, (lds_void_t*)(base + PW_B_BYTES + (PW_S_COPIES * wave + k) * 256), 2,
             s_row[k] + (uint32_t)min(4 * c + 2 * s_pair[k], nblk - 2), 0, 0, 0);
     }
   };
@@ -1324,19 +1353,19 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
 #pragma unroll
     for (int j = 0; j < NCB; ++j) acc[mb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  // LDS byte offsets of this lane's fragments inside a chunk buffer: a lane
-  // part here, the row block / piece / column block part as the
-  // instructions' offset fields.  A: row m = 32 wm + 16 mb + r, piece
+  // LDS byte offsets of this lane's fragments inside an A stage (a_lane)
+  // and a weight stage (b_lane, s_lane): a lane part here, the row block /
+  // piece / column block part as the instructions' offset fields.  A: row m = 32 wm + 16 mb + r, piece
   // 4q + g at slot (4q + g) ^ ((m >> 1) & 3) (the same for both row
   // blocks); B: row n = tile_row(j) + r, whose swizzle (n >> 2) & 3 is
   // (r >> 2) & 3; scales: byte g & 1 of dword 2n + g / 2.
   constexpr int WNR = GATEUP ? 8 * NCB : 16 * NCB;  // tile rows per column half
   const uint32_t a_lane = (uint32_t)((32 * wm + r) * MX6_GROUP_BYTES + 16 * (g ^ ((r >> 1) & 3)));
-  const uint32_t b_lane = (uint32_t)(PW_A_BYTES + (wn * WNR + r) * 64 + 16 * (g ^ ((r >> 2) & 3)));
+  const uint32_t b_lane = (uint32_t)((wn * WNR + r) * 64 + 16 * (g ^ ((r >> 2) & 3)));
   // scale bytes per tile row in LDS: row-major copies leave two bytes in
   // each of two dwords (8 per row), packed copies four bytes
   constexpr int SR = PACKED ? 4 : 8;
-  const uint32_t s_lane = (uint32_t)(PW_A_BYTES + PW_B_BYTES + SR * (wn * WNR + r) +
+  const uint32_t s_lane = (uint32_t)(PW_B_BYTES + SR * (wn * WNR + r) +
                                      (PACKED ? g : 4 * (g >> 1) + (g & 1)));
   // tile row of column block j without the column half's part
   auto jrow = [](auto jc) constexpr {
@@ -1344,15 +1373,28 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
     return GATEUP ? (j < NCB / 2 ? 0 : PW_NT / 2) + 16 * (j % (NCB / 2)) : 16 * j;
   };
 
+  constexpr int SB = C::SB;
   const int nchunk = (nblk + 3) >> 2;
-  issue(0, 0);
+  issue_a(0, 0);
+  issue_b(0, 0);
+  if (SB == 3 && nchunk > 1) issue_b(1, 1);
+  int wst = 0;  // weight stage of chunk c (c mod SB)
   for (int c = 0; c < nchunk; ++c) {
-    const int buf = c & 1;
-    const uint32_t bbase = (uint32_t)(uintptr_t)(smem + buf * PW_BUF);
-    wait_vmcnt<0>();  // this wave's copies of chunk c
+    const uint32_t abase = (uint32_t)(uintptr_t)(smem + (c & 1) * C::A_BYTES);
+    const uint32_t bbase = (uint32_t)(uintptr_t)(smem + 2 * C::A_BYTES + wst * PW_B_STAGE);
+    // this wave's copies of chunk c: with three weight stages the weight
+    // copies of chunk c+1, issued after the A copies of chunk c, may stay
+    // in flight (vector memory loads complete in issue order)
+    if (SB == 3 && c + 1 < nchunk)
+      wait_vmcnt<B_OPS>();
+    else
+      wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();  // everyone's copies of chunk c; everyone done with chunk c - 1
     __builtin_amdgcn_sched_barrier(0);
-    if (c + 1 < nchunk) issue(c + 1, buf ^ 1);
+    // into the stages chunk c - 1 used
+    if (c + 1 < nchunk) issue_a(c + 1, (c + 1) & 1);
+    if (c + SB - 1 < nchunk) issue_b(c + SB - 1, wst == 0 ? SB - 1 : wst - 1);
+    wst = wst == SB - 1 ? 0 : wst + 1;
     __builtin_amdgcn_sched_barrier(0);
     // a wave whose 32 rows all lie past the tile's rows (the last tile of
     // an expert) only copies and keeps the barriers: its SIMD's other wave
@@ -1362,7 +1404,7 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
     // block, zeros past K; the fast mode reads pieces 0, 1 and 4 only) and
     // the first group's B fragments, then the FP6 terms of A as 6-register
     // operands
-    const uint32_t ab = bbase + a_lane, bb = bbase + b_lane, sb = bbase + s_lane;
+    const uint32_t ab = abase + a_lane, bb = bbase + b_lane, sb = bbase + s_lane;
     v4u w[MB][5];
     v4u bq[2][4];
     uint32_t sq[2][4];
@@ -1605,7 +1647,7 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
   const int rows_w = rows - 32 * wm;
   const int row_base_w = row_base + 32 * wm;
   const int wcol0 = GATEUP ? tcol0 + wn * (8 * NCB) : tcol0 + wn * (16 * NCB);
-  uint8_t* scratch = smem + wave * PW_EPI_BYTES;
+  uint8_t* scratch = smem + wave * C::EPI_BYTES;
   if (rows_w <= 0) return;
   if (GATEUP)
     pf_epilogue_gateup<NCB>(p, acc, bias, rows_w, row_base_w, wcol0, lane, scratch);
@@ -1667,18 +1709,19 @@ static int launch_gemm(const GemmParams& p, int max_tiles, int mode, hipStream_t
     launch_decode<GATEUP, TERMS>(p, (unsigned)((long long)max_tiles * spans), spans, s);
   } else {
     if (!prefill_offsets_fit(p)) return -1;
-    const bool wide = mode == GEMM_WIDE;
+    const bool wide = mode == GEMM_WIDE || mode == GEMM_WIDE64;
     const int span_cols = wide ? (GATEUP ? PW_NT / 2 : PW_NT) : (GATEUP ? PF_NT / 2 : PF_NT);
     const int spans = (n_out + span_cols - 1) / span_cols;
     const long long items = (long long)max_tiles * spans;
     const dim3 g((unsigned)((items + PF_XCD - 1) / PF_XCD * PF_XCD));
-    if (wide)
-      if (p.packed)
-        hipLaunchKernelGGL((expert_gemm_prefill_wide<GATEUP, TERMS, true>), g, dim3(PW_NW * 64), 0, s, p, spans);
-      else
-        hipLaunchKernelGGL((expert_gemm_prefill_wide<GATEUP, TERMS, false>), g, dim3(PW_NW * 64), 0, s, p, spans);
-    else
+#define MOE_WIDE(PK, MT) hipLaunchKernelGGL((expert_gemm_prefill_wide<GATEUP, TERMS, PK, MT>), g, dim3(PW_NW * 64), 0, s, p, spans)
+    if (mode == GEMM_WIDE64) {
+      if (p.packed) MOE_WIDE(true, 64); else MOE_WIDE(false, 64);
+    } else if (wide) {
+      if (p.packed) MOE_WIDE(true, 128); else MOE_WIDE(false, 128);
+    } else
       hipLaunchKernelGGL((expert_gemm_prefill<GATEUP, TERMS>), g, dim3(PF_NW * 64), 0, s, p, spans);
+#undef MOE_WIDE
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
@@ -1689,7 +1732,9 @@ static int launch_gemm(const GemmParams& p, int max_tiles, int mode, hipStream_t
 //   large-M (prefill): one workgroup per (64-row tile, 256-column span)
 //     work item, 1-D grid dealt to the XCDs in contiguous ranges;
 //   wide (prefill with enough rows per expert and even K/32 for both
-//     projections): one workgroup per (128-row tile, 512-column span).
+//     projections): one workgroup per (128-row tile, 512-column span);
+//   wide64 (the same with 33 to 48 rows per expert on average): one
+//     workgroup per (64-row tile, 512-column span), three weight stages.
 // p.terms: 3 (the exact path) or 1 (the activation-quantised fast mode).
 int launch_gemm_gateup(const GemmParams& p, int max_tiles, int mode, hipStream_t s) {
   if (p.terms == 1) return launch_gemm<true, 1>(p, max_tiles, mode, s);

@@ -78,7 +78,7 @@ struct CombineParams {
 int launch_route(const RouteParams& p, hipStream_t s);
 // GEMM configurations: decode (16-row tiles), prefill (64-row tiles),
 // wide prefill (128-row tiles)
-enum GemmMode { GEMM_DECODE = 0, GEMM_PREFILL = 1, GEMM_WIDE = 2 };
+enum GemmMode { GEMM_DECODE = 0, GEMM_PREFILL = 1, GEMM_WIDE = 2, GEMM_WIDE64 = 3 };
 int launch_gemm_gateup(const GemmParams& p, int max_tiles, int mode, hipStream_t s);
 int launch_gemm_down(const GemmParams& p, int max_tiles, int mode, hipStream_t s);
 int launch_combine(const CombineParams& p, hipStream_t s);

@@ -5,7 +5,7 @@ give bitwise the results of the same call on the row-major weights (the
 kernels copy the same bytes into the same LDS places and do the same
 arithmetic in the same order) -- at decode sizes (16- and 32-row tiles, the
 combine folded into the down projection, more than 8 phases of K) and at
-prefill sizes (128-row tiles)."""
+prefill sizes (64- and 128-row tiles)."""
 import sys
 
 import numpy as np
@@ -85,12 +85,13 @@ CASES = [
     ("stack_layer", Workload("stack_layer", T=2048, d=2880, I=2880, E=128, k=4, seed=0x5EED1007)),
     ("ragged", Workload("ragged", T=333, d=256, I=192, E=8, k=4, seed=0x5EED3001)),
     ("ragged_k8", Workload("ragged_k8", T=1000, d=384, I=320, E=16, k=8, seed=0x5EED3002)),
+    ("wide64_ragged", Workload("wide64_ragged", T=600, d=320, I=384, E=64, k=4, seed=0x5EED3004)),
 ]
 
 
 # every case with the stored activation reading, and the variant one (interleaved gate/up rows)
 # on the shapes that exercise each kernel once
-ALT_ON = ("tiny", "20b_decode", "qwen3_decode", "20b_prefill", "ragged", "ragged_k8")
+ALT_ON = ("tiny", "20b_decode", "qwen3_decode", "20b_prefill", "ragged", "ragged_k8", "wide64_ragged")
 RUNS = [(n, w, 0) for n, w in CASES] + [(n, w, moe.MOE_LAYER_ALT_ACT) for n, w in CASES if n in ALT_ON]
 
 

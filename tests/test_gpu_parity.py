@@ -139,6 +139,13 @@ RAGGED = [
     (256, 128, 96, 32, 4),
     (264, 128, 96, 32, 4),
     (400, 256, 192, 32, 4),
+    # 64-row wide tiles with three weight stages (33 to 48 rows per expert):
+    # one K chunk in each projection, two and one, three with a 2-block last
+    # chunk, and the largest average that still takes them
+    (200, 64, 64, 16, 3),
+    (500, 192, 128, 48, 4),
+    (600, 320, 384, 64, 5),
+    (768, 256, 320, 64, 4),
 ]
 
 
