@@ -1143,9 +1143,9 @@ __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams 
 // row m at slot s ^ ((m >> 1) & 3); B: piece g of row n at g ^ ((n >> 2) &
 // 3)), so the fragment reads are free of bank conflicts.  A ring of two A
 // stages and a ring of SB weight stages: after the barrier that opens
-// chunk c the copies of A for chunk c+1 and of the weights for chunk
-// c+SB-1 are issued, and each wave waits (vmcnt, in issue order) for its
-// copies of chunk c before that barrier.  The LDS reads are asm blocks that
+// chunk c, waves 4..7 issue the copies of A for chunk c+1 and of the
+// weights for chunk c+SB-1, and each of them waits (vmcnt, in issue order)
+// for its copies of chunk c before that barrier.  The LDS reads are asm blocks that
 // wait for their own results, so the compiler never waits for the copies
 // in flight.  Offsets include the chunk (no scalar offset): weight blocks
 // past K are clamped to the row's last block, A rows past the tile read
@@ -1167,7 +1167,6 @@ struct PwCfg {
   static constexpr int NCB = PW_NT / 16 / WN;          // column blocks per wave
   static constexpr int A_BYTES = MT * MX6_GROUP_BYTES;  // 40960 or 20480
   static constexpr int A_COPIES = A_BYTES / 1024;      // 1-KB A copies per chunk (all waves)
-  static constexpr int A_PER = (A_COPIES + PW_NW - 1) / PW_NW;  // per wave, at most
   static constexpr int SB = MT == 128 ? 2 : 3;         // weight stages
   static constexpr int SMEM = 2 * A_BYTES + SB * PW_B_STAGE;
   static constexpr int EPI_BYTES = 16 * (16 * NCB + 4) * 4;  // per-wave epilogue staging
@@ -1249,20 +1248,35 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
       (void*)p.b_scales, 0,
       (int)((uint32_t)p.E * (uint32_t)N * (uint32_t)(PACKED ? 4 * ((nblk + 3) >> 2) : nblk)), 0x00020000);
   constexpr uint32_t A_OOB = 0x7ffffff0u;  // at or past the A resource's end (it is below 2^31 bytes)
-  // A copy k of this wave (copy number i = 8k + wave of the chunk, if
+  // The copies are issued by the last CW waves only.  Issuing a chunk's
+  // copies takes a wave several hundred cycles (the CU's address unit
+  // accepts about 64 bytes a cycle), during which it issues no MFMAs; with
+  // the copies on half the waves, the other wave of each SIMD keeps the
+  // MFMA pipe busy meanwhile.  The copy waves are waves 4..7: the row
+  // blocks that lie past the rows of a partly filled tile (2 and 3 of four
+  // with 128-row tiles, 1 of two with 64-row tiles), so those waves have
+  // nothing else to do there.
+  constexpr int CW = PW_NW / 2;                          // copy waves
+  constexpr int A_PW = (C::A_COPIES + CW - 1) / CW;      // A copies per copy wave
+  constexpr int B_PW = PW_B_COPIES * PW_NW / CW;         // code copies per copy wave
+  constexpr int S_PW = PW_S_COPIES * PW_NW / CW;         // row-major scale copies per copy wave
+  constexpr int SP_PW = PW_NW / CW;                      // packed scale copies per copy wave
+  const bool copier = wave >= PW_NW - CW;
+  const int cw = copier ? wave - (PW_NW - CW) : 0;
+  // A copy k of a copy wave (copy number i = CW k + cw of the chunk, if
   // below A_COPIES) fills LDS slots u = 64 i + lane: tile row u / 20, slot
   // u % 20 holding piece (u % 20) ^ ((row >> 1) & 3) (pieces of blocks past
   // K are copied from past the resource: zeros, so that those K positions
   // contribute nothing whatever the weights hold)
-  uint32_t a_src[C::A_PER];
-  int a_blk[C::A_PER];  // block of the piece within its group of four
+  uint32_t a_src[A_PW];
+  int a_blk[A_PW];  // block of the piece within its group of four
 #pragma unroll
-  for (int k = 0; k < C::A_PER; ++k) {
-    const int u = (PW_NW * k + wave) * 64 + lane;
+  for (int k = 0; k < A_PW; ++k) {
+    const int u = (CW * k + cw) * 64 + lane;
     const int m = u / 20, slot = u - 20 * m;
     const int piece = slot ^ ((m >> 1) & 3);
     uint32_t off = A_OOB;
-    if (m < rows) {
+    if (copier && m < rows) {
       const uint32_t arow = GATEUP ? (uint32_t)(p.expert_rows[(size_t)e * p.T + m0 + m] / p.k)
                                    : (uint32_t)(row_base + m);
       off = arow * a_rowbytes + (uint32_t)piece * 16u;
@@ -1272,13 +1286,14 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
     a_src[k] = (TERMS == 1 && (piece >> 2) >= 2 && (piece >> 2) <= 3) ? A_OOB : off;
     a_blk[k] = piece & 3;
   }
-  // B copy k fills slots u = (4 wave + k) * 64 + lane: tile row u / 4,
-  // slot u % 4 holding block (u % 4) ^ ((n >> 2) & 3) of the chunk
-  uint32_t b_row[PW_B_COPIES], b_odd[PW_B_COPIES];
-  int b_blk[PW_B_COPIES];
+  // B copy k of a copy wave fills slots u = (B_PW cw + k) * 64 + lane:
+  // tile row u / 4, slot u % 4 holding block (u % 4) ^ ((n >> 2) & 3) of
+  // the chunk
+  uint32_t b_row[B_PW], b_odd[B_PW];
+  int b_blk[B_PW];
 #pragma unroll
-  for (int k = 0; k < PW_B_COPIES; ++k) {
-    const int u = (PW_B_COPIES * wave + k) * 64 + lane;
+  for (int k = 0; k < B_PW; ++k) {
+    const int u = (B_PW * cw + k) * 64 + lane;
     const int n = u >> 2, slot = u & 3;
     const uint32_t wr = (uint32_t)weight_row(n);
     // row-major: the row's start; packed: its pair's start, plus 64 bytes
@@ -1288,40 +1303,47 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
     b_odd[k] = wr & 1u;
     b_blk[k] = slot ^ ((n >> 2) & 3);
   }
-  // scale copy k fills dwords u = (2 wave + k) * 64 + lane: tile row u / 2,
-  // block pair u % 2 of the chunk (two bytes, low half of the dword)
-  uint32_t s_row[PW_S_COPIES];
-  int s_pair[PW_S_COPIES];
+  // row-major scale copy k of a copy wave fills dwords u = (S_PW cw + k)
+  // * 64 + lane: tile row u / 2, block pair u % 2 of the chunk (two bytes,
+  // low half of the dword)
+  uint32_t s_row[PACKED ? 1 : S_PW];
+  int s_pair[PACKED ? 1 : S_PW];
 #pragma unroll
-  for (int k = 0; k < PW_S_COPIES; ++k) {
-    const int u = (PW_S_COPIES * wave + k) * 64 + lane;
+  for (int k = 0; k < (PACKED ? 0 : S_PW); ++k) {
+    const int u = (S_PW * cw + k) * 64 + lane;
     s_row[k] = ((uint32_t)e * (uint32_t)N + (uint32_t)weight_row(u >> 1)) * (uint32_t)nblk;
     s_pair[k] = u & 1;
   }
-  // packed scales: one 4-byte copy per tile row and chunk, lane L of wave w
-  // taking tile row 64 w + L (dword 64 w + L of the chunk's scale region)
+  // packed scales: one 4-byte copy per tile row and chunk, lane L of copy
+  // k of a copy wave taking tile row 64 j + L, j = SP_PW cw + k (dword
+  // 64 j + L of the chunk's scale region)
   const int nchk = (nblk + 3) >> 2;
-  const uint32_t sp_row = ((uint32_t)e * (uint32_t)nchk * (uint32_t)N + (uint32_t)weight_row(64 * wave + lane)) * 4u;
+  uint32_t sp_row[SP_PW];
+#pragma unroll
+  for (int k = 0; k < SP_PW; ++k)
+    sp_row[k] = ((uint32_t)e * (uint32_t)nchk * (uint32_t)N + (uint32_t)weight_row(64 * (SP_PW * cw + k) + lane)) * 4u;
   // A copies whose 3.2 tile rows all lie past the tile's rows (or past the
   // tile) are not issued: those LDS rows keep stale data, which only the
   // MFMA rows of discarded outputs read (an output row depends on its own A
   // row only)
-  bool a_live[C::A_PER];
+  bool a_live[A_PW];
 #pragma unroll
-  for (int k = 0; k < C::A_PER; ++k)
-    a_live[k] = PW_NW * k + wave < C::A_COPIES && (PW_NW * k + wave) * 64 / 20 < rows;
+  for (int k = 0; k < A_PW; ++k)
+    a_live[k] = CW * k + cw < C::A_COPIES && (CW * k + cw) * 64 / 20 < rows;
   auto issue_a = [&](int c, int stage) {
+    if (!copier) return;
     uint8_t* base = smem + stage * C::A_BYTES;
 #pragma unroll
-    for (int k = 0; k < C::A_PER; ++k)
+    for (int k = 0; k < A_PW; ++k)
       if (a_live[k])
-        lds_copy16(arsrc, (lds_void_t*)(base + (PW_NW * k + wave) * 1024),
+        lds_copy16(arsrc, (lds_void_t*)(base + (CW * k + cw) * 1024),
                    (a_src[k] == A_OOB || 4 * c + a_blk[k] >= nblk) ? A_OOB : a_src[k] + (uint32_t)c * MX6_GROUP_BYTES);
   };
-  // the weight copies of a chunk: PW_B_COPIES code copies, then the scale
-  // copies (one packed, PW_S_COPIES row-major) per wave
-  constexpr int B_OPS = PW_B_COPIES + (PACKED ? 1 : PW_S_COPIES);
+  // the weight copies of a chunk: B_PW code copies, then the scale copies
+  // (SP_PW packed, S_PW row-major) per copy wave
+  constexpr int B_OPS = B_PW + (PACKED ? SP_PW : S_PW);
   auto issue_b = [&](int c, int stage) {
+    if (!copier) return;
     uint8_t* base = smem + 2 * C::A_BYTES + stage * PW_B_STAGE;
     if constexpr (PACKED) {
       // chunk c of a pair: 128 bytes (64 per row), or 2 x 16 (nblk - 4c)
@@ -1329,20 +1351,22 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
       // next row or pair (finite codes, multiplied by zero A pieces)
       const uint32_t w = (uint32_t)(4 * c + 4 <= nblk ? 64 : 16 * (nblk - 4 * c));
 #pragma unroll
-      for (int k = 0; k < PW_B_COPIES; ++k)
-        lds_copy16(crsrc, (lds_void_t*)(base + (PW_B_COPIES * wave + k) * 1024),
+      for (int k = 0; k < B_PW; ++k)
+        lds_copy16(crsrc, (lds_void_t*)(base + (B_PW * cw + k) * 1024),
                    b_row[k] + 128u * (uint32_t)c + b_odd[k] * w + (uint32_t)b_blk[k] * 16u);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, (lds_void_t*)(base + PW_B_BYTES + wave * 256), 4,
-                                               sp_row + (uint32_t)c * (uint32_t)N * 4u, 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < SP_PW; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, (lds_void_t*)(base + PW_B_BYTES + (SP_PW * cw + k) * 256), 4,
+                                                 sp_row[k] + (uint32_t)c * (uint32_t)N * 4u, 0, 0, 0);
     } else {
 #pragma unroll
-      for (int k = 0; k < PW_B_COPIES; ++k)
-        lds_copy16(crsrc, (lds_void_t*)(base + (PW_B_COPIES * wave + k) * 1024),
+      for (int k = 0; k < B_PW; ++k)
+        lds_copy16(crsrc, (lds_void_t*)(base + (B_PW * cw + k) * 1024),
                    b_row[k] + (uint32_t)min(4 * c + b_blk[k], nblk - 1) * 16u);
 #pragma unroll
-      for (int k = 0; k < PW_S_COPIES; ++k)
+      for (int k = 0; k < S_PW; ++k)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            srsrc, (lds_void_t*)(base + PW_B_BYTES + (PW_S_COPIES * wave + k) * 256), 2,
+            srsrc, (lds_void_t*)(base + PW_B_BYTES + (S_PW * cw + k) * 256), 2,
             s_row[k] + (uint32_t)min(4 * c + 2 * s_pair[k], nblk - 2), 0, 0, 0);
     }
   };
@@ -1382,7 +1406,7 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
   for (int c = 0; c < nchunk; ++c) {
     const uint32_t abase = (uint32_t)(uintptr_t)(smem + (c & 1) * C::A_BYTES);
     const uint32_t bbase = (uint32_t)(uintptr_t)(smem + 2 * C::A_BYTES + wst * PW_B_STAGE);
-    // this wave's copies of chunk c: with three weight stages the weight
+    // a copy wave's copies of chunk c: with three weight stages the weight
     // copies of chunk c+1, issued after the A copies of chunk c, may stay
     // in flight (vector memory loads complete in issue order)
     if (SB == 3 && c + 1 < nchunk)

@@ -27,12 +27,19 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+# sources no MoE-layer kernel is built from (the attention steps beside the
+# layer): a change there leaves the layer's counter summaries valid
+NOT_LAYER_SOURCES = ("attention.hip",)
+
+
 def src_sha() -> str:
-    """Hash of the HIP sources; a counter summary is valid only for these."""
+    """Hash of the MoE layer's HIP sources (kernels, the launch code that
+    picks them, the weight packing); a counter summary is valid only for
+    these."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_moe_transformer_softmax_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if not f.endswith((".hip", ".h")):
+        if not f.endswith((".hip", ".h")) or f in NOT_LAYER_SOURCES:
             continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
