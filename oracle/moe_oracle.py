@@ -191,6 +191,16 @@ def mxfp6_quantize(v: np.ndarray) -> np.ndarray:
     return (e2m3_round(b / s) * s).reshape(shape)
 
 
+def mx6x2_quantize(v: np.ndarray) -> np.ndarray:
+    """Two-term microscaling FP6: the MXFP6 rounding of v (mxfp6_quantize)
+    plus the MXFP6 rounding of what that leaves over, each 32-element block
+    of each term with the scale of its own largest magnitude.  The reduced-
+    precision option feeds x and h through this before the expert GEMMs
+    (the exact path's activations carry a third such term)."""
+    t0 = mxfp6_quantize(v)
+    return t0 + mxfp6_quantize(np.asarray(v, dtype=np.float64) - t0)
+
+
 def expert_ffn(xs: np.ndarray, w13: np.ndarray, b13: np.ndarray,
                w2: np.ndarray, b2: np.ndarray, clamp: float, act_quant=None, alt: bool = False) -> np.ndarray:
     """One expert on rows xs [n, d] with dequantised weights: the three
@@ -255,12 +265,13 @@ def moe_layer(x_bits: np.ndarray, router_w_bits: np.ndarray, router_b: np.ndarra
     Each expert runs only on the tokens routed to it ([B] 2.4.1).  Returns a
     dict with y (float64 [T, d]), logits, ids, w and per-expert counts.
     act = "mxfp6": the activation-quantised fast mode (x and h rounded to
-    MXFP6 before the expert GEMMs, mxfp6_quantize); the router always sees x.
+    MXFP6 before the expert GEMMs, mxfp6_quantize); act = "mx6x2": the
+    two-term option (mx6x2_quantize); the router always sees x.
     alt: the variant weight layout and activation of expert_ffn.
     """
-    if act not in ("exact", "mxfp6"):
+    if act not in ("exact", "mxfp6", "mx6x2"):
         raise ValueError(act)
-    aq = mxfp6_quantize if act == "mxfp6" else None
+    aq = {"exact": None, "mxfp6": mxfp6_quantize, "mx6x2": mx6x2_quantize}[act]
     x = bf16_bits_to_f64(x_bits)
     logits, ids, w = route(x_bits, router_w_bits, router_b, k)
     T = x.shape[0]
