@@ -219,10 +219,10 @@ def run_leg(wl, bound, args, torch, moe, want_cpu):
         psets.append(pg)
     torch.cuda.synchronize()
     log(f"weights packed in {time.perf_counter() - t0:.2f} s")
-    mx6 = args.act != "exact"
+    act_flag = {"exact": 0, "mxfp6": moe.MOE_LAYER_MXFP6, "mx6x2": moe.MOE_LAYER_MX6X2}[args.act]
 
     def make_step(S, packed):
-        flags = (moe.MOE_LAYER_PACKED if packed else 0) | (moe.MOE_LAYER_MXFP6 if mx6 else 0)
+        flags = (moe.MOE_LAYER_PACKED if packed else 0) | act_flag
         if nlay == 1:
             outs = [torch.empty((wl.T, wl.d), dtype=torch.bfloat16, device="cuda:0") for _ in range(nsets)]
 
@@ -339,8 +339,10 @@ def run_leg(wl, bound, args, torch, moe, want_cpu):
             "mxfp4_mfma_frac": step_flops / (ms_step * 1e-3) / MFMA_FP6_FP4_PEAK,
             "kernel_us": {k: (v[0] / v[1] * 1e3 if v[1] else None) for k, v in kt.items()},
             "parallelism": "single-gpu",
-            "activations": "three-term MX6x3 (each value to about 2^-13 of its 32-block maximum)"
-                           if args.act == "exact" else "mxfp6 (activation-quantised fast mode)",
+            "activations": {"exact": "three-term MX6x3 (each value to about 2^-13 of its 32-block maximum)",
+                            "mxfp6": "mxfp6 (activation-quantised fast mode)",
+                            "mx6x2": "two-term MX6 (MOE_LAYER_MX6X2; each value within 1/225 of its 32-block "
+                                     "maximum)"}[args.act],
             "weight_layout": "packed MXFP4 (moe_pack_weights once per weight set before timing; "
                              "MOE_LAYER_PACKED); the same bytes as the stored format",
             "rowmajor": {
@@ -474,9 +476,9 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="weight sets to rotate over (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=16.0, help="seconds of oracle time per leg")
-    ap.add_argument("--act", default="exact", choices=["exact", "mxfp6"],
-                    help="expert-GEMM activations: exact (three FP6 terms) or mxfp6 "
-                         "(the activation-quantised fast mode, moe_layer_forward_mx6)")
+    ap.add_argument("--act", default="exact", choices=["exact", "mxfp6", "mx6x2"],
+                    help="expert-GEMM activations: exact (three FP6 terms), mxfp6 (the "
+                         "activation-quantised fast mode, one term) or mx6x2 (the two-term option)")
     ap.add_argument("--no-attention", action="store_true", help="leave out the attention legs of the default run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 256 MiB bitwise_not kernel (reads and writes 256 MiB: "
@@ -496,7 +498,8 @@ def main():
         if args.workload is None and not args.no_attention:
             legs = [(n, "attn") for n in ATTN_LEGS] + legs
     if args.act != "exact" and any(b != "attn" and WORKLOADS[n].layers > 1 for n, b in legs):
-        print("the fast mode has a single-layer entry point only; pick a single-layer --workload", file=sys.stderr)
+        print("the one- and two-term activation options have single-layer entry points only; pick a "
+              "single-layer --workload", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -138,7 +138,18 @@ enum moe_layer_flags {
    * the packed layout written by moe_pack_weights; biases unchanged.  d and
    * I must be multiples of 64 (otherwise MOE_ERR_UNSUPPORTED).  Results are
    * bitwise those of the row-major weights. */
-  MOE_LAYER_PACKED = 4
+  MOE_LAYER_PACKED = 4,
+  /* the two-term option: the rows entering each expert GEMM are rounded to
+   * two MXFP6 terms -- the MXFP6 rounding of the row (as in the fast mode)
+   * plus the MXFP6 rounding of what it leaves over, each 32-block of each
+   * term with its own power-of-two scale -- instead of the exact path's
+   * three: two block-scaled MFMAs per 128-wide K step instead of three.
+   * Each value is then within 1/225 of its block's largest magnitude; the
+   * layer differs from moe_layer_forward by about 1e-3 of its rms (at most
+   * 5e-3 to 8e-3 in the cases measured, against 0.3-0.4 for the one-term
+   * fast mode).  The router sees x unrounded.  Not together with
+   * MOE_LAYER_MXFP6 (MOE_ERR_BAD_SHAPE). */
+  MOE_LAYER_MX6X2 = 8
 };
 
 /* moe_layer_forward with flags (any OR of moe_layer_flags; unknown bits give

@@ -17,12 +17,13 @@ __all__ = [
     "moe_timing_enable", "moe_timing_read", "KERNELS", "moe_layer_forward_mx6", "moe_layer_forward_mx6_dbg",
     "moe_layer_forward_ex", "MOE_LAYER_MXFP6", "MOE_LAYER_ALT_ACT", "moe_rmsnorm_residual",
     "moe_layer_forward_noalloc", "MOE_NOALLOC_SCRATCH_BYTES", "moe_attn_rope", "moe_attn_forward",
-    "moe_pack_weights", "moe_packed_scale_bytes", "MOE_LAYER_PACKED", "packed_shapes",
+    "moe_pack_weights", "moe_packed_scale_bytes", "MOE_LAYER_PACKED", "packed_shapes", "MOE_LAYER_MX6X2",
 ]
 
 MOE_LAYER_MXFP6 = 1
 MOE_LAYER_ALT_ACT = 2
 MOE_LAYER_PACKED = 4
+MOE_LAYER_MX6X2 = 8
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
@@ -234,7 +235,8 @@ def moe_layer_forward_dbg(x, router_w, router_b, w13_codes, w13_scales, b13, w2_
 def moe_layer_forward_ex(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,
                          k: int = 4, clamp: float = 7.0, flags: int = 0, debug: bool = False, out=None,
                          stream=None):
-    """moe_layer_forward with flags (MOE_LAYER_MXFP6, MOE_LAYER_ALT_ACT, MOE_LAYER_PACKED).
+    """moe_layer_forward with flags (MOE_LAYER_MXFP6, MOE_LAYER_ALT_ACT, MOE_LAYER_PACKED,
+    MOE_LAYER_MX6X2).
     debug=False: returns out; debug=True: (out, out_f32, topk_id, topk_w, counts)."""
     torch = _torch()
     ptrs, T, d, I, E = _layer_ptrs(x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2,

@@ -93,7 +93,7 @@ struct LayerArgs {
   const uint8_t* w13c; const uint8_t* w13s; const float* b13;
   const uint8_t* w2c; const uint8_t* w2s; const float* b2;
   int T, d, I, E, k; float clamp;
-  int terms = 3;  // FP6 terms of the expert GEMMs' activations: 3 (exact path) or 1 (fast mode)
+  int terms = 3;  // FP6 terms of the expert GEMMs' activations: 3 (exact path), 2 or 1 (fast mode)
   int alt = 0;    // 1: the variant gate/up layout and activation
   int packed = 0; // 1: expert weights in the packed layout of moe_pack_weights
 };
@@ -458,9 +458,10 @@ int moe_layer_forward_ex(const void* x, const void* router_w, const float* route
                          const uint8_t* w2_scales, const float* b2, int T, int d, int I, int E, int k, float clamp,
                          int flags, void* out, float* out_f32, int32_t* topk_id, float* topk_w, int32_t* counts,
                          void* stream) {
-  if (flags & ~(MOE_LAYER_MXFP6 | MOE_LAYER_ALT_ACT | MOE_LAYER_PACKED)) return MOE_ERR_BAD_SHAPE;
+  if (flags & ~(MOE_LAYER_MXFP6 | MOE_LAYER_ALT_ACT | MOE_LAYER_PACKED | MOE_LAYER_MX6X2)) return MOE_ERR_BAD_SHAPE;
+  if ((flags & MOE_LAYER_MXFP6) && (flags & MOE_LAYER_MX6X2)) return MOE_ERR_BAD_SHAPE;
   LayerArgs a{x, router_w, router_b, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, T, d, I, E, k, clamp};
-  a.terms = (flags & MOE_LAYER_MXFP6) ? 1 : 3;
+  a.terms = (flags & MOE_LAYER_MXFP6) ? 1 : (flags & MOE_LAYER_MX6X2) ? 2 : 3;
   a.alt = (flags & MOE_LAYER_ALT_ACT) ? 1 : 0;
   a.packed = (flags & MOE_LAYER_PACKED) ? 1 : 0;
   const bool any = topk_id || topk_w || counts, all = topk_id && topk_w && counts;

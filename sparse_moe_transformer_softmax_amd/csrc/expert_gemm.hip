@@ -95,7 +95,7 @@ template <int MB, int NCB>
 __device__ __forceinline__ uint32_t keep_mask(bool in) { return in ? 0xffffffffu : 0u; }
 
 // TERMS = 1 (the activation-quantised fast mode): only the first FP6 term
-// of A takes part.
+// of A takes part; TERMS = 2 (the two-term option): the first two.
 template <int MB, int NCB, int TERMS = 3>
 __device__ __forceinline__ void mma_stage(v4f (&acc)[MB][NCB], const Stage<MB, NCB>& st, uint32_t keep) {
 #pragma unroll
@@ -118,10 +118,12 @@ __device__ __forceinline__ void mma_stage(v4f (&acc)[MB][NCB], const Stage<MB, N
 #pragma unroll
     for (int j = 0; j < NCB; ++j)
       acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, b[j], acc[mb][j], 2, 4, 0, s0, 0, bsc[j]);
-    if constexpr (TERMS == 3) {
+    if constexpr (TERMS >= 2) {
 #pragma unroll
       for (int j = 0; j < NCB; ++j)
         acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, b[j], acc[mb][j], 2, 4, 0, s1, 0, bsc[j]);
+    }
+    if constexpr (TERMS == 3) {
 #pragma unroll
       for (int j = 0; j < NCB; ++j)
         acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a2, b[j], acc[mb][j], 2, 4, 0, s2, 0, bsc[j]);
@@ -359,9 +361,9 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
                                                                                                      int spans) {
   static_assert(!PACKED || U16, "the packed layout has K/32 even");
   using Cfg = DecCfg<U16>;
-  // vector-memory instructions per wave per phase (the fast mode loads two
-  // fewer A pieces per row block)
-  constexpr int VM = Cfg::VM - 5 + MB * (TERMS == 1 ? 3 : 5);
+  // vector-memory instructions per wave per phase (one term loads two
+  // fewer A pieces per row block, two terms one fewer)
+  constexpr int VM = Cfg::VM - 5 + MB * (TERMS == 1 ? 3 : TERMS == 2 ? 4 : 5);
   constexpr int NCB = 4, NW = DEC_NW;
   // readfirstlane: the wave index is uniform, so the buffer resources and
   // LDS bases derived from it live in scalar registers
@@ -470,7 +472,7 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
       const int off = it.a_off[mb] < 0x7ffffff0 ? it.a_off[mb] + mx6_byte_offset(bl, 0) : 0x7ffffff0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (TERMS == 1 && q >= 2) {  // pieces 2 and 3 hold only the other terms' codes
+        if (q > TERMS && q < 4) {  // pieces 2 and 3 hold only the later terms' codes
           av[mb][q] = make_uint4(0u, 0u, 0u, 0u);
           continue;
         }
@@ -982,14 +984,14 @@ __global__ __launch_bounds__(PF_NW * 64, 2) void expert_gemm_prefill(GemmParams 
     s_off[q] = brow * (uint32_t)nblk + (uint32_t)bpiece;
   });
 
-  // (the fast mode loads pieces 0, 1 and 4 only: the first term's codes
-  // and the scale bytes)
+  // (one term loads pieces 0, 1 and 4 only: the first term's codes and the
+  // scale bytes; two terms pieces 0, 1, 2 and 4)
   auto load_a = [&](int c, v4u (&av)[MB][5]) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int q = 0; q < 5; ++q) {
-        if (TERMS == 1 && (q == 2 || q == 3)) {
+        if (q > TERMS && q < 4) {
           av[mb][q] = (v4u){0u, 0u, 0u, 0u};
           continue;
         }
@@ -1281,9 +1283,9 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
                                    : (uint32_t)(row_base + m);
       off = arow * a_rowbytes + (uint32_t)piece * 16u;
     }
-    // (the fast mode copies pieces 0, 1 and 4 only: the first term's codes
-    // and the scale bytes)
-    a_src[k] = (TERMS == 1 && (piece >> 2) >= 2 && (piece >> 2) <= 3) ? A_OOB : off;
+    // (one term copies pieces 0, 1 and 4 only: the first term's codes and
+    // the scale bytes; two terms pieces 0, 1, 2 and 4)
+    a_src[k] = ((piece >> 2) > TERMS && (piece >> 2) < 4) ? A_OOB : off;
     a_blk[k] = piece & 3;
   }
   // B copy k of a copy wave fills slots u = (B_PW cw + k) * 64 + lane:
@@ -1425,7 +1427,8 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
     // then has the MFMA pipe and the LDS port to itself
     if (32 * wm >= rows) continue;
     // A fragments (pieces 0..4 of block g of the lane's row in each row
-    // block, zeros past K; the fast mode reads pieces 0, 1 and 4 only) and
+    // block, zeros past K; one term reads pieces 0, 1 and 4, two terms 0, 1,
+    // 2 and 4) and
     // the first group's B fragments, then the FP6 terms of A as 6-register
     // operands
     const uint32_t ab = abase + a_lane, bb = bbase + b_lane, sb = bbase + s_lane;
@@ -1465,6 +1468,38 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
           "i"(16 * MX6_GROUP_BYTES * 1 + 256), "i"(64 * jrow(std::integral_constant<int, 0>{})), "i"(64 * jrow(std::integral_constant<int, 1>{})),
           "i"(64 * jrow(std::integral_constant<int, 2>{})), "i"(64 * jrow(std::integral_constant<int, 3>{})), "i"(SR * jrow(std::integral_constant<int, 0>{})),
           "i"(SR * jrow(std::integral_constant<int, 1>{})), "i"(SR * jrow(std::integral_constant<int, 2>{})), "i"(SR * jrow(std::integral_constant<int, 3>{})));
+    } else if constexpr (TERMS == 2) {
+      asm volatile(
+        "ds_read_b128 %0, %16 offset:%19\n\t"
+        "ds_read_b128 %1, %16 offset:%20\n\t"
+        "ds_read_b128 %2, %16 offset:%21\n\t"
+        "ds_read_b128 %3, %16 offset:%22\n\t"
+        "ds_read_b128 %4, %16 offset:%23\n\t"
+        "ds_read_b128 %5, %16 offset:%24\n\t"
+        "ds_read_b128 %6, %16 offset:%25\n\t"
+        "ds_read_b128 %7, %16 offset:%26\n\t"
+        "ds_read_b128 %8, %17 offset:%27\n\t"
+        "ds_read_b128 %9, %17 offset:%28\n\t"
+        "ds_read_b128 %10, %17 offset:%29\n\t"
+        "ds_read_b128 %11, %17 offset:%30\n\t"
+        "ds_read_u8 %12, %18 offset:%31\n\t"
+        "ds_read_u8 %13, %18 offset:%32\n\t"
+        "ds_read_u8 %14, %18 offset:%33\n\t"
+        "ds_read_u8 %15, %18 offset:%34\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0][0]), "=&v"(w[0][1]), "=&v"(w[0][2]), "=&v"(w[0][4]), "=&v"(w[1][0]), "=&v"(w[1][1]),
+          "=&v"(w[1][2]), "=&v"(w[1][4]), "=&v"(bq[0][0]), "=&v"(bq[0][1]), "=&v"(bq[0][2]), "=&v"(bq[0][3]),
+          "=&v"(sq[0][0]), "=&v"(sq[0][1]), "=&v"(sq[0][2]), "=&v"(sq[0][3])
+        : "v"(ab), "v"(bb), "v"(sb),
+          "i"(16 * MX6_GROUP_BYTES * 0 + 0), "i"(16 * MX6_GROUP_BYTES * 0 + 64),
+          "i"(16 * MX6_GROUP_BYTES * 0 + 128), "i"(16 * MX6_GROUP_BYTES * 0 + 256),
+          "i"(16 * MX6_GROUP_BYTES * 1 + 0), "i"(16 * MX6_GROUP_BYTES * 1 + 64),
+          "i"(16 * MX6_GROUP_BYTES * 1 + 128), "i"(16 * MX6_GROUP_BYTES * 1 + 256),
+          "i"(64 * jrow(std::integral_constant<int, 0>{})), "i"(64 * jrow(std::integral_constant<int, 1>{})),
+          "i"(64 * jrow(std::integral_constant<int, 2>{})), "i"(64 * jrow(std::integral_constant<int, 3>{})),
+          "i"(SR * jrow(std::integral_constant<int, 0>{})), "i"(SR * jrow(std::integral_constant<int, 1>{})),
+          "i"(SR * jrow(std::integral_constant<int, 2>{})), "i"(SR * jrow(std::integral_constant<int, 3>{})));
+      w[0][3] = w[1][3] = (v4u){0u, 0u, 0u, 0u};
     } else {
       asm volatile(
         "ds_read_b128 %0, %14 offset:%17\n\t"
@@ -1599,6 +1634,78 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
             "+v"(acc[0][4 * jg + 2]), "+v"(acc[1][4 * jg + 2]), "+v"(acc[0][4 * jg + 3]), "+v"(acc[1][4 * jg + 3])
             : "v"(a6[0][0]), "v"(a6[0][1]), "v"(a6[0][2]), "v"(a6[1][0]), "v"(a6[1][1]), "v"(a6[1][2]),
               "v"(as[0][0]), "v"(as[0][1]), "v"(as[0][2]), "v"(as[1][0]), "v"(as[1][1]), "v"(as[1][2]),
+              "v"(bq[cur][0]), "v"(bq[cur][1]), "v"(bq[cur][2]), "v"(bq[cur][3]),
+              "v"(sq[cur][0]), "v"(sq[cur][1]), "v"(sq[cur][2]), "v"(sq[cur][3]));
+        }
+      } else if constexpr (TERMS == 2) {
+        if constexpr (jg + 1 < NCB / 4) {
+          constexpr int k0 = 4 * (jg + 1);
+          asm volatile(
+            "s_nop 4\n\t"
+          "ds_read_b128 %8, %32 offset:%34\n\t"
+          "ds_read_b128 %9, %32 offset:%35\n\t"
+          "ds_read_b128 %10, %32 offset:%36\n\t"
+          "ds_read_b128 %11, %32 offset:%37\n\t"
+          "ds_read_u8 %12, %33 offset:%38\n\t"
+          "ds_read_u8 %13, %33 offset:%39\n\t"
+          "ds_read_u8 %14, %33 offset:%40\n\t"
+          "ds_read_u8 %15, %33 offset:%41\n\t"
+          "s_setprio 1\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %16, %24, %0, %20, %28 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %18, %24, %1, %22, %28 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %16, %25, %2, %20, %29 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %18, %25, %3, %22, %29 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %4, %16, %26, %4, %20, %30 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %5, %18, %26, %5, %22, %30 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %16, %27, %6, %20, %31 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %18, %27, %7, %22, %31 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %17, %24, %0, %21, %28 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %19, %24, %1, %23, %28 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %17, %25, %2, %21, %29 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %19, %25, %3, %23, %29 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %4, %17, %26, %4, %21, %30 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %5, %19, %26, %5, %23, %30 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %17, %27, %6, %21, %31 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %19, %27, %7, %23, %31 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "s_setprio 0\n\t"
+          "s_waitcnt lgkmcnt(0)"
+            : "+v"(acc[0][4 * jg]), "+v"(acc[1][4 * jg]), "+v"(acc[0][4 * jg + 1]), "+v"(acc[1][4 * jg + 1]),
+            "+v"(acc[0][4 * jg + 2]), "+v"(acc[1][4 * jg + 2]), "+v"(acc[0][4 * jg + 3]), "+v"(acc[1][4 * jg + 3]),
+              "=&v"(bq[nxt][0]), "=&v"(bq[nxt][1]), "=&v"(bq[nxt][2]), "=&v"(bq[nxt][3]),
+              "=&v"(sq[nxt][0]), "=&v"(sq[nxt][1]), "=&v"(sq[nxt][2]), "=&v"(sq[nxt][3])
+            : "v"(a6[0][0]), "v"(a6[0][1]), "v"(a6[1][0]), "v"(a6[1][1]),
+              "v"(as[0][0]), "v"(as[0][1]), "v"(as[1][0]), "v"(as[1][1]),
+              "v"(bq[cur][0]), "v"(bq[cur][1]), "v"(bq[cur][2]), "v"(bq[cur][3]),
+              "v"(sq[cur][0]), "v"(sq[cur][1]), "v"(sq[cur][2]), "v"(sq[cur][3]), "v"(bb), "v"(sb),
+              "i"(64 * jrow(std::integral_constant<int, k0>{})), "i"(64 * jrow(std::integral_constant<int, k0 + 1>{})),
+              "i"(64 * jrow(std::integral_constant<int, k0 + 2>{})), "i"(64 * jrow(std::integral_constant<int, k0 + 3>{})),
+              "i"(SR * jrow(std::integral_constant<int, k0>{})), "i"(SR * jrow(std::integral_constant<int, k0 + 1>{})),
+              "i"(SR * jrow(std::integral_constant<int, k0 + 2>{})), "i"(SR * jrow(std::integral_constant<int, k0 + 3>{})));
+        } else {
+          asm volatile(
+            "s_nop 4\n\t"
+          "s_setprio 1\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %8, %16, %0, %12, %20 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %10, %16, %1, %14, %20 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %8, %17, %2, %12, %21 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %10, %17, %3, %14, %21 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %4, %8, %18, %4, %12, %22 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %5, %10, %18, %5, %14, %22 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %8, %19, %6, %12, %23 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %10, %19, %7, %14, %23 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %9, %16, %0, %13, %20 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %1, %11, %16, %1, %15, %20 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %2, %9, %17, %2, %13, %21 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %3, %11, %17, %3, %15, %21 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %4, %9, %18, %4, %13, %22 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %5, %11, %18, %5, %15, %22 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %6, %9, %19, %6, %13, %23 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "v_mfma_scale_f32_16x16x128_f8f6f4 %7, %11, %19, %7, %15, %23 op_sel_hi:[0,0,0] cbsz:2 blgp:4\n\t"
+          "s_setprio 0"
+            : "+v"(acc[0][4 * jg]), "+v"(acc[1][4 * jg]), "+v"(acc[0][4 * jg + 1]), "+v"(acc[1][4 * jg + 1]),
+            "+v"(acc[0][4 * jg + 2]), "+v"(acc[1][4 * jg + 2]), "+v"(acc[0][4 * jg + 3]), "+v"(acc[1][4 * jg + 3])
+            : "v"(a6[0][0]), "v"(a6[0][1]), "v"(a6[1][0]), "v"(a6[1][1]),
+              "v"(as[0][0]), "v"(as[0][1]), "v"(as[1][0]), "v"(as[1][1]),
               "v"(bq[cur][0]), "v"(bq[cur][1]), "v"(bq[cur][2]), "v"(bq[cur][3]),
               "v"(sq[cur][0]), "v"(sq[cur][1]), "v"(sq[cur][2]), "v"(sq[cur][3]));
         }
@@ -1759,15 +1866,18 @@ static int launch_gemm(const GemmParams& p, int max_tiles, int mode, hipStream_t
 //     projections): one workgroup per (128-row tile, 512-column span);
 //   wide64 (the same with 33 to 48 rows per expert on average): one
 //     workgroup per (64-row tile, 512-column span), three weight stages.
-// p.terms: 3 (the exact path) or 1 (the activation-quantised fast mode).
+// p.terms: 3 (the exact path), 2 (the two-term option) or 1 (the
+// activation-quantised fast mode).
 int launch_gemm_gateup(const GemmParams& p, int max_tiles, int mode, hipStream_t s) {
   if (p.terms == 1) return launch_gemm<true, 1>(p, max_tiles, mode, s);
+  if (p.terms == 2) return launch_gemm<true, 2>(p, max_tiles, mode, s);
   if (p.terms == 3) return launch_gemm<true, 3>(p, max_tiles, mode, s);
   return -1;
 }
 
 int launch_gemm_down(const GemmParams& p, int max_tiles, int mode, hipStream_t s) {
   if (p.terms == 1) return launch_gemm<false, 1>(p, max_tiles, mode, s);
+  if (p.terms == 2) return launch_gemm<false, 2>(p, max_tiles, mode, s);
   if (p.terms == 3) return launch_gemm<false, 3>(p, max_tiles, mode, s);
   return -1;
 }

@@ -158,4 +158,12 @@ def test_packed_flag_needs_even_block_counts():
              None) == -3
     assert f(*args, 4096, 2848, 2880, 32, 4, 7.0, moe.MOE_LAYER_PACKED, P(0x900000), None, None, None, None,
              None) == -3
-    assert f(*args, 4096, 2880, 2880, 32, 4, 7.0, 8, P(0x900000), None, None, None, None, None) == -2
+    assert f(*args, 4096, 2880, 2880, 32, 4, 7.0, 16, P(0x900000), None, None, None, None, None) == -2
+
+
+def test_one_and_two_term_flags_exclude_each_other():
+    P = ctypes.c_void_p
+    f = moe.lib().moe_layer_forward_ex
+    args = [P(0x10000)] * 9
+    both = moe.MOE_LAYER_MXFP6 | moe.MOE_LAYER_MX6X2
+    assert f(*args, 32, 2880, 2880, 32, 4, 7.0, both, P(0x900000), None, None, None, None, None) == -2
