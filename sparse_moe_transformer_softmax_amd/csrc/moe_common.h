@@ -132,19 +132,30 @@ __device__ __forceinline__ void pack6x32(const uint8_t* c, uint32_t out[6]) {
 // compiler's builtin lets the result registers overlap the sources, which
 // these instructions do not support.  On return codes[6t .. 6t+5] hold term
 // t's 32 codes packed little-endian (the MX6x3 byte layout), scw the three
-// scale bytes.  A block with a NaN gets scale 0xFF on every term.
+// scale bytes.  A block with a NaN gets scale 0xFF on every term.  The first
+// term's block maximum is the integer maximum of the magnitudes' bit
+// patterns, where a NaN (every pattern above infinity's) shows itself; the
+// later terms' residuals are then finite, and take the float maximum.
 __device__ __forceinline__ void mx6x3_split_lane(v16f& ve, v16f& vo, uint32_t (&codes)[18], uint32_t& scw) {
+  uint32_t mbits = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    mbits = max(mbits, max(__float_as_uint(ve[i]) & 0x7fffffffu, __float_as_uint(vo[i]) & 0x7fffffffu));
+  if (mbits > 0x7f800000u) {
+#pragma unroll
+    for (int w = 0; w < 18; ++w) codes[w] = 0;
+    scw = 0xffffffu;
+    return;
+  }
   scw = 0;
 #pragma unroll
   for (int t = 0; t < 3; ++t) {
-    float amax = 0.0f;
-    bool nan = false;
+    float amax = __uint_as_float(mbits);
+    if (t > 0) {
+      amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      amax = fmaxf(amax, fmaxf(fabsf(ve[i]), fabsf(vo[i])));
-      nan |= (ve[i] != ve[i]) | (vo[i] != vo[i]);
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fmaxf(fabsf(ve[i]), fabsf(vo[i])));
     }
-    if (nan) amax = __builtin_inff();
     int se = mx6_scale_exp(amax);
     // a subnormal maximum takes 2^-126 (one step coarser, still no
     // saturation), so the scale operand is a normal float
