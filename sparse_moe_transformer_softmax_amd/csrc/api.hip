@@ -177,16 +177,20 @@ struct Timing {
   }
 } g_t;
 
+// ext: the events are handed to the one launch inside the region, which
+// records them when its kernel starts and ends; otherwise they are recorded
+// on the stream around the region (and include the dispatch).
 struct Timed {
-  int kind; hipStream_t s; hipEvent_t a = nullptr, b = nullptr;
-  Timed(int k, hipStream_t st) : kind(k), s(st) {
+  int kind; hipStream_t s; bool ext; hipEvent_t a = nullptr, b = nullptr;
+  Timed(int k, hipStream_t st, bool ext_ = false) : kind(k), s(st), ext(ext_) {
     if (!((g_t.mask >> k) & 1)) return;
     a = g_t.get(); b = g_t.get();
-    if (a && b) (void)hipEventRecord(a, s);
+    if (a && b && !ext) (void)hipEventRecord(a, s);
   }
+  LaunchEvents events() const { return ext && a && b ? LaunchEvents{a, b} : LaunchEvents{}; }
   ~Timed() {
     if (!a || !b) return;
-    (void)hipEventRecord(b, s);
+    if (!ext) (void)hipEventRecord(b, s);
     g_t.pending.push_back({kind, a, b});
   }
 };
@@ -275,8 +279,8 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   gp.out = (uint16_t*)out;
   gp.out_f32 = out_f32;
   {
-    Timed tm(1, s);
-    if (launch_gemm_gateup(gp, max_tiles, mode, s)) return MOE_ERR_HIP;
+    Timed tm(1, s, true);
+    if (launch_gemm_gateup(gp, max_tiles, mode, s, tm.events())) return MOE_ERR_HIP;
   }
 
   gp.a = gp.hq;
@@ -287,8 +291,8 @@ int run_layer(const LayerArgs& a, const Layout& L, uint8_t* ws, void* out, float
   gp.alt = 0;  // (the down projection has no gate/up rows)
   gp.fold_cnt = rp.fold_cnt;
   {
-    Timed tm(2, s);
-    if (launch_gemm_down(gp, max_tiles, mode, s)) return MOE_ERR_HIP;
+    Timed tm(2, s, true);
+    if (launch_gemm_down(gp, max_tiles, mode, s, tm.events())) return MOE_ERR_HIP;
   }
 
   if (fold) return MOE_OK;

@@ -25,6 +25,8 @@
 #include <algorithm>
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -1794,12 +1796,22 @@ static bool prefill_offsets_fit(const GemmParams& p) {
   return a_rows * mx6_row_bytes(p.K / 32) < lim && e_rows * (p.K / 2) < lim;
 }
 
+// A launch, optionally with start and stop events that the launch itself
+// records when the kernel starts and ends (no dispatch time between them).
+template <typename K, typename... A>
+static void launch_k(K kernel, dim3 g, dim3 b, hipStream_t s, const LaunchEvents& ev, A... args) {
+  if (ev.start && ev.stop)
+    hipExtLaunchKernelGGL(kernel, g, b, 0, s, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, g, b, 0, s, args...);
+}
+
 // Decode kernel instance for the phase count of K (unrolled up to 8 phases).
 template <bool GATEUP, bool U16, int TERMS, int MB, bool PACKED>
-static void launch_decode_u(const GemmParams& p, unsigned grid, int spans, hipStream_t s) {
+static void launch_decode_u(const GemmParams& p, unsigned grid, int spans, hipStream_t s, const LaunchEvents& ev) {
   const int nph = (p.K / 32 + DEC_KPH - 1) / DEC_KPH;
   const dim3 g(grid), b(DEC_NW * 64);
-#define MOE_DEC(NPH) hipLaunchKernelGGL((expert_gemm_decode<GATEUP, NPH, U16, TERMS, MB, PACKED>), g, b, 0, s, p, spans)
+#define MOE_DEC(NPH) launch_k(expert_gemm_decode<GATEUP, NPH, U16, TERMS, MB, PACKED>, g, b, s, ev, p, spans)
   switch (nph) {
     case 1: MOE_DEC(1); break;
     case 2: MOE_DEC(2); break;
@@ -1815,29 +1827,29 @@ static void launch_decode_u(const GemmParams& p, unsigned grid, int spans, hipSt
 }
 
 template <bool GATEUP, int TERMS, int MB>
-static void launch_decode_mb(const GemmParams& p, unsigned items, int spans, hipStream_t s) {
+static void launch_decode_mb(const GemmParams& p, unsigned items, int spans, hipStream_t s, const LaunchEvents& ev) {
   if (p.packed)  // (the packed layout has K/32 even)
-    launch_decode_u<GATEUP, true, TERMS, MB, true>(p, items, spans, s);
+    launch_decode_u<GATEUP, true, TERMS, MB, true>(p, items, spans, s, ev);
   else if ((p.K / 32) % 2 == 0)
-    launch_decode_u<GATEUP, true, TERMS, MB, false>(p, items, spans, s);
+    launch_decode_u<GATEUP, true, TERMS, MB, false>(p, items, spans, s, ev);
   else
-    launch_decode_u<GATEUP, false, TERMS, MB, false>(p, items, spans, s);
+    launch_decode_u<GATEUP, false, TERMS, MB, false>(p, items, spans, s, ev);
 }
 
 template <bool GATEUP, int TERMS>
-static void launch_decode(const GemmParams& p, unsigned items, int spans, hipStream_t s) {
+static void launch_decode(const GemmParams& p, unsigned items, int spans, hipStream_t s, const LaunchEvents& ev) {
   if (p.mb == 2)
-    launch_decode_mb<GATEUP, TERMS, 2>(p, items, spans, s);
+    launch_decode_mb<GATEUP, TERMS, 2>(p, items, spans, s, ev);
   else
-    launch_decode_mb<GATEUP, TERMS, 1>(p, items, spans, s);
+    launch_decode_mb<GATEUP, TERMS, 1>(p, items, spans, s, ev);
 }
 
 template <bool GATEUP, int TERMS>
-static int launch_gemm(const GemmParams& p, int max_tiles, int mode, hipStream_t s) {
+static int launch_gemm(const GemmParams& p, int max_tiles, int mode, hipStream_t s, const LaunchEvents& ev) {
   const int n_out = GATEUP ? p.I : p.N;  // output columns
   if (mode == GEMM_DECODE) {
     const int spans = GATEUP ? (n_out + 31) / 32 : (n_out + 63) / 64;
-    launch_decode<GATEUP, TERMS>(p, (unsigned)((long long)max_tiles * spans), spans, s);
+    launch_decode<GATEUP, TERMS>(p, (unsigned)((long long)max_tiles * spans), spans, s, ev);
   } else {
     if (!prefill_offsets_fit(p)) return -1;
     const bool wide = mode == GEMM_WIDE || mode == GEMM_WIDE64;
@@ -1845,13 +1857,13 @@ static int launch_gemm(const GemmParams& p, int max_tiles, int mode, hipStream_t
     const int spans = (n_out + span_cols - 1) / span_cols;
     const long long items = (long long)max_tiles * spans;
     const dim3 g((unsigned)((items + PF_XCD - 1) / PF_XCD * PF_XCD));
-#define MOE_WIDE(PK, MT) hipLaunchKernelGGL((expert_gemm_prefill_wide<GATEUP, TERMS, PK, MT>), g, dim3(PW_NW * 64), 0, s, p, spans)
+#define MOE_WIDE(PK, MT) launch_k(expert_gemm_prefill_wide<GATEUP, TERMS, PK, MT>, g, dim3(PW_NW * 64), s, ev, p, spans)
     if (mode == GEMM_WIDE64) {
       if (p.packed) MOE_WIDE(true, 64); else MOE_WIDE(false, 64);
     } else if (wide) {
       if (p.packed) MOE_WIDE(true, 128); else MOE_WIDE(false, 128);
     } else
-      hipLaunchKernelGGL((expert_gemm_prefill<GATEUP, TERMS>), g, dim3(PF_NW * 64), 0, s, p, spans);
+      launch_k(expert_gemm_prefill<GATEUP, TERMS>, g, dim3(PF_NW * 64), s, ev, p, spans);
 #undef MOE_WIDE
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -1868,17 +1880,17 @@ static int launch_gemm(const GemmParams& p, int max_tiles, int mode, hipStream_t
 //     workgroup per (64-row tile, 512-column span), three weight stages.
 // p.terms: 3 (the exact path), 2 (the two-term option) or 1 (the
 // activation-quantised fast mode).
-int launch_gemm_gateup(const GemmParams& p, int max_tiles, int mode, hipStream_t s) {
-  if (p.terms == 1) return launch_gemm<true, 1>(p, max_tiles, mode, s);
-  if (p.terms == 2) return launch_gemm<true, 2>(p, max_tiles, mode, s);
-  if (p.terms == 3) return launch_gemm<true, 3>(p, max_tiles, mode, s);
+int launch_gemm_gateup(const GemmParams& p, int max_tiles, int mode, hipStream_t s, const LaunchEvents& ev) {
+  if (p.terms == 1) return launch_gemm<true, 1>(p, max_tiles, mode, s, ev);
+  if (p.terms == 2) return launch_gemm<true, 2>(p, max_tiles, mode, s, ev);
+  if (p.terms == 3) return launch_gemm<true, 3>(p, max_tiles, mode, s, ev);
   return -1;
 }
 
-int launch_gemm_down(const GemmParams& p, int max_tiles, int mode, hipStream_t s) {
-  if (p.terms == 1) return launch_gemm<false, 1>(p, max_tiles, mode, s);
-  if (p.terms == 2) return launch_gemm<false, 2>(p, max_tiles, mode, s);
-  if (p.terms == 3) return launch_gemm<false, 3>(p, max_tiles, mode, s);
+int launch_gemm_down(const GemmParams& p, int max_tiles, int mode, hipStream_t s, const LaunchEvents& ev) {
+  if (p.terms == 1) return launch_gemm<false, 1>(p, max_tiles, mode, s, ev);
+  if (p.terms == 2) return launch_gemm<false, 2>(p, max_tiles, mode, s, ev);
+  if (p.terms == 3) return launch_gemm<false, 3>(p, max_tiles, mode, s, ev);
   return -1;
 }
 

@@ -79,8 +79,13 @@ int launch_route(const RouteParams& p, hipStream_t s);
 // GEMM configurations: decode (16-row tiles), prefill (64-row tiles),
 // wide prefill (128-row tiles)
 enum GemmMode { GEMM_DECODE = 0, GEMM_PREFILL = 1, GEMM_WIDE = 2, GEMM_WIDE64 = 3 };
-int launch_gemm_gateup(const GemmParams& p, int max_tiles, int mode, hipStream_t s);
-int launch_gemm_down(const GemmParams& p, int max_tiles, int mode, hipStream_t s);
+// Optional events that a launch records itself when its kernel starts and
+// ends (timing of one kernel without the dispatch before it).
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+int launch_gemm_gateup(const GemmParams& p, int max_tiles, int mode, hipStream_t s, const LaunchEvents& ev = {});
+int launch_gemm_down(const GemmParams& p, int max_tiles, int mode, hipStream_t s, const LaunchEvents& ev = {});
 int launch_combine(const CombineParams& p, hipStream_t s);
 int launch_rmsnorm(const uint16_t* x, uint16_t* out, int T, int d, float eps, hipStream_t s);
 int launch_residual_rmsnorm(const uint16_t* x, const void* y, bool y_f32, uint16_t* x_out, uint16_t* n_out, int T,
