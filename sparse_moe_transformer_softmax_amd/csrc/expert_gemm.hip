@@ -55,26 +55,33 @@ struct StaticFor {
 
 // clamp(g) * sigmoid(clamp(g)) * (clamp(u) + 1) with the hardware exp2 and
 // reciprocal (a few ulp; the result is then rounded to 2^-13 of its block
-// maximum by the MX6x3 split).  Without a clamp, large |g| gives the limits
-// 0 and g (exp2 overflows to inf, its reciprocal to 0); a NaN propagates.
-__device__ __forceinline__ float clamped_swiglu(float g, float u, float c) {
-  const float gc = (g != g) ? g : fminf(fmaxf(g, -c), c);
-  const float uc = (u != u) ? u : fminf(fmaxf(u, -c), c);
-  const float e = __builtin_amdgcn_exp2f(-gc * 1.44269504088896341f);
-  return gc * __builtin_amdgcn_rcpf(1.0f + e) * (uc + 1.0f);
+// maximum by the MX6x3 split).  The clamp to [-c, c] (c > 0, +inf allowed)
+// is the median of (v, -c, c), equal to min(max(v, -c), c) for every
+// non-NaN v, signed zeros included; a NaN in g or u (one unordered
+// compare) makes the result NaN.  Without a clamp, large |g| gives the
+// limits 0 and g (exp2 overflows to inf, its reciprocal to 0).
+// The variant activation reading (alt) differs only in two constants: Swish
+// with slope 1.702 on the gate clamped from above only (the median of (g,
+// -inf, c)), times the symmetrically clamped up plus one.  glo and gk are
+// the gate's lower bound and the exponent's factor of either reading
+// (swiglu_consts), so the function has no branch.
+struct SwigluConsts {
+  float glo, gk;
+};
+__device__ __forceinline__ SwigluConsts swiglu_consts(float c, int alt) {
+  return alt ? SwigluConsts{-__builtin_inff(), 1.702f * 1.44269504088896341f}
+             : SwigluConsts{-c, 1.44269504088896341f};
 }
-
-// The variant activation reading: Swish with slope 1.702 on the gate
-// clamped from above only, times the symmetrically clamped up plus one.
-__device__ __forceinline__ float clamped_swiglu_alt(float g, float u, float c) {
-  const float gc = (g != g) ? g : fminf(g, c);
-  const float uc = (u != u) ? u : fminf(fmaxf(u, -c), c);
-  const float e = __builtin_amdgcn_exp2f(-gc * (1.702f * 1.44269504088896341f));
-  return gc * __builtin_amdgcn_rcpf(1.0f + e) * (uc + 1.0f);
+__device__ __forceinline__ float clamped_swiglu(float g, float u, float c, SwigluConsts k) {
+  const float gc = __builtin_amdgcn_fmed3f(g, k.glo, c);
+  const float uc = __builtin_amdgcn_fmed3f(u, -c, c);
+  const float e = __builtin_amdgcn_exp2f(-gc * k.gk);
+  const float h = gc * __builtin_amdgcn_rcpf(1.0f + e) * (uc + 1.0f);
+  return __builtin_isunordered(g, u) ? g + u : h;
 }
 
 __device__ __forceinline__ float swiglu_act(float g, float u, float c, int alt) {
-  return alt ? clamped_swiglu_alt(g, u, c) : clamped_swiglu(g, u, c);
+  return clamped_swiglu(g, u, c, swiglu_consts(c, alt));
 }
 
 // Row of the fused gate/up weight (and index of its bias) that holds output
@@ -819,6 +826,7 @@ __device__ __forceinline__ void pf_epilogue_gateup(const GemmParams& p, const v4
   // column 16j + r of the wave's span lies in block j / 2 at position
   // 16 (j & 1) + r, stored at 16 * (r & 1) + 8 (j & 1) + r / 2
   const int cpos = 16 * (r & 1) + (r >> 1);
+  const SwigluConsts sk = swiglu_consts(p.clamp, p.alt);
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     if (16 * mb >= rows_w) break;
@@ -827,7 +835,7 @@ __device__ __forceinline__ void pf_epilogue_gateup(const GemmParams& p, const v4
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         sh_h[(4 * g + q) * HS + 32 * (j >> 1) + 8 * (j & 1) + cpos] =
-            swiglu_act(acc[mb][j][q] + bias[j], acc[mb][HALF + j][q] + bias[HALF + j], p.clamp, p.alt);
+            clamped_swiglu(acc[mb][j][q] + bias[j], acc[mb][HALF + j][q] + bias[HALF + j], p.clamp, sk);
     lds_wave_sync();
     if (srow < 16) {
       const float* src = sh_h + srow * HS + 32 * sblk;
