@@ -372,7 +372,12 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
   using Cfg = DecCfg<U16>;
   // vector-memory instructions per wave per phase (one term loads two
   // fewer A pieces per row block, two terms one fewer)
-  constexpr int VM = Cfg::VM - 5 + MB * (TERMS == 1 ? 3 : TERMS == 2 ? 4 : 5);
+  // the packed layout's chunk-major scales go to LDS with one 4-byte copy
+  // per wave and phase (four dwords per weight row), the row-major scales
+  // with 2-byte (U16) or 1-byte copies
+  constexpr int SROW = PACKED ? 4 : Cfg::SROW;
+  constexpr int SQ = PACKED ? 1 : Cfg::SQ;
+  constexpr int VM = DEC_Q + SQ + MB * (TERMS == 1 ? 3 : TERMS == 2 ? 4 : 5);
   constexpr int NCB = 4, NW = DEC_NW;
   // readfirstlane: the wave index is uniform, so the buffer resources and
   // LDS bases derived from it live in scalar registers
@@ -390,7 +395,7 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
 
   // two phase buffers: codes [64 rows][16 slots][16 B], scales one per dword
   __shared__ __align__(16) uint8_t s_code[2][64 * DEC_KPH * 16];
-  __shared__ __align__(16) uint32_t s_scl[2][64 * Cfg::SROW];
+  __shared__ __align__(16) uint32_t s_scl[2][64 * SROW];
   __shared__ uint8_t s_codes[16][3][32];
   __shared__ uint32_t s_sc[16];
 
@@ -440,19 +445,17 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
                                                  rr * it.rs * nblk + min(slot, npb - 1), pb0, 0, 0);
     }
     if constexpr (PACKED) {
-      // the same block pairs into the same LDS dwords as below, from the
-      // chunk-major scales: pair 2 uc of the phase is in chunk pb0 / 4 +
-      // uc / 2 (the chunk of pb0 in the scalar offset), bytes 2 (uc & 1)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int rr = 8 * q + (lane >> 3);
-        const int u = (lane & 7) ^ ((rr >> 2) & 3);
-        const int uc = 2 * u < npb ? u : 0;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(it.srsrc,
-                                                 (lds_void_t*)(s_scl[buf] + (wave * 16 + 8 * q) * Cfg::SROW), 2,
-                                                 ((uc >> 1) * N + it.row0 + rr * it.rs) * 4 + 2 * (uc & 1), pb0 * N,
-                                                 0, 0);
-      }
+      // one 4-byte copy: lane L fills dword L of the wave's 16 rows x 4
+      // dwords; row rr = L / 4 keeps chunk (L % 4) ^ ((rr >> 3) & 1) of the
+      // phase (the scale bytes of its blocks 4c .. 4c+3, from chunk pb0 / 4
+      // + c of the chunk-major scales, the chunk of pb0 in the scalar
+      // offset) in slot L % 4, so that the reads of one chunk by 16 rows
+      // hit 16 banks.  Chunks past K read on past the expert's scales (or
+      // past the resource: zeros); their blocks are masked off.
+      const int rr = lane >> 2;
+      const int c = (lane & 3) ^ ((rr >> 3) & 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(it.srsrc, (lds_void_t*)(s_scl[buf] + wave * 16 * SROW), 4,
+                                               (c * N + it.row0 + rr * it.rs) * 4, pb0 * N, 0, 0);
     } else if constexpr (U16) {
       // instruction q moves rows 8q .. 8q+7; lane L holds the block pair
       // (L % 8) ^ ((row >> 2) & 3) of row 8q + L/8, so that the reads of 16
@@ -463,7 +466,7 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
         const int u = (lane & 7) ^ ((rr >> 2) & 3);
         const int uc = 2 * u < npb ? u : 0;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(it.srsrc,
-                                                 (lds_void_t*)(s_scl[buf] + (wave * 16 + 8 * q) * Cfg::SROW), 2,
+                                                 (lds_void_t*)(s_scl[buf] + (wave * 16 + 8 * q) * SROW), 2,
                                                  rr * it.rs * nblk + 2 * uc, pb0, 0, 0);
       }
     }
@@ -517,7 +520,10 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
     const uint32_t cb_addr = (uint32_t)(uintptr_t)(s_code[buf]) + (uint32_t)((r * DEC_KPH + (bl ^ r)) * 16);
     const uint32_t sb_addr =
         (uint32_t)(uintptr_t)(s_scl[buf]) +
-        (uint32_t)((U16 ? r * Cfg::SROW + ((bl >> 1) ^ ((r >> 2) & 3)) : r * DEC_KPH + bl) * 4);
+        (uint32_t)((PACKED ? r * SROW + ((bl >> 2) ^ ((r >> 3) & 1))
+                    : U16  ? r * SROW + ((bl >> 1) ^ ((r >> 2) & 3))
+                           : r * DEC_KPH + bl) *
+                   4);
     v4u b0, b1, b2, b3;
     uint32_t s0, s1, s2, s3;
     asm volatile(
@@ -532,12 +538,13 @@ __global__ __launch_bounds__(DEC_NW * 64, MB == 1 ? DecCfg<U16>::WG_PER_CU : 3) 
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
         : "v"(cb_addr), "v"(sb_addr), "i"(16 * DEC_KPH * 16), "i"(32 * DEC_KPH * 16), "i"(48 * DEC_KPH * 16),
-          "i"(16 * Cfg::SROW * 4), "i"(32 * Cfg::SROW * 4), "i"(48 * Cfg::SROW * 4));
+          "i"(16 * SROW * 4), "i"(32 * SROW * 4), "i"(48 * SROW * 4));
     st.bc[0] = make_uint4(b0.x, b0.y, b0.z, b0.w);
     st.bc[1] = make_uint4(b1.x, b1.y, b1.z, b1.w);
     st.bc[2] = make_uint4(b2.x, b2.y, b2.z, b2.w);
     st.bc[3] = make_uint4(b3.x, b3.y, b3.z, b3.w);
-    const int sh = U16 ? 8 * (bl & 1) : 0;  // byte of the block within its pair
+    // byte of the block within its chunk (packed) or pair (U16)
+    const int sh = PACKED ? 8 * (bl & 3) : U16 ? 8 * (bl & 1) : 0;
     st.bs[0] = (int)((s0 >> sh) & 0xffu);
     st.bs[1] = (int)((s1 >> sh) & 0xffu);
     st.bs[2] = (int)((s2 >> sh) & 0xffu);
