@@ -1332,14 +1332,24 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
     s_row[k] = ((uint32_t)e * (uint32_t)N + (uint32_t)weight_row(u >> 1)) * (uint32_t)nblk;
     s_pair[k] = u & 1;
   }
-  // packed scales: one 4-byte copy per tile row and chunk, lane L of copy
-  // k of a copy wave taking tile row 64 j + L, j = SP_PW cw + k (dword
-  // 64 j + L of the chunk's scale region)
+  // packed scales: tile row n's four scale bytes of a chunk go to dword n
+  // of the chunk's scale region.  Where the 512 tile rows are two runs of
+  // 256 consecutive weight rows (the gate/up weight's gate-then-up layout,
+  // and the down weight), copy waves 0 and 1 each move one run with a
+  // single 16-byte copy (lane L: tile rows 256 cw + 4L .. +3; rows past the
+  // output read on into other rows' scales, which only discarded outputs
+  // use); with the interleaved gate/up layout every copy wave moves its
+  // SP_PW groups of 64 rows with 4-byte copies (lane L of copy k: tile row
+  // 64 j + L, j = SP_PW cw + k).
   const int nchk = (nblk + 3) >> 2;
+  const bool sc16 = PACKED && !(GATEUP && p.alt);
   uint32_t sp_row[SP_PW];
 #pragma unroll
-  for (int k = 0; k < SP_PW; ++k)
-    sp_row[k] = ((uint32_t)e * (uint32_t)nchk * (uint32_t)N + (uint32_t)weight_row(64 * (SP_PW * cw + k) + lane)) * 4u;
+  for (int k = 0; k < SP_PW; ++k) {
+    const uint32_t run = GATEUP ? (uint32_t)(cw == 1 ? I : 0) + (uint32_t)tcol0 : (uint32_t)(tcol0 + 256 * cw);
+    sp_row[k] = sc16 ? ((uint32_t)e * (uint32_t)nchk * (uint32_t)N + run) * 4u + 16u * (uint32_t)lane
+                     : ((uint32_t)e * (uint32_t)nchk * (uint32_t)N + (uint32_t)weight_row(64 * (SP_PW * cw + k) + lane)) * 4u;
+  }
   // A copies whose 3.2 tile rows all lie past the tile's rows (or past the
   // tile) are not issued: those LDS rows keep stale data, which only the
   // MFMA rows of discarded outputs read (an output row depends on its own A
@@ -1358,8 +1368,10 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
                    (a_src[k] == A_OOB || 4 * c + a_blk[k] >= nblk) ? A_OOB : a_src[k] + (uint32_t)c * MX6_GROUP_BYTES);
   };
   // the weight copies of a chunk: B_PW code copies, then the scale copies
-  // (SP_PW packed, S_PW row-major) per copy wave
+  // (packed: one 16-byte copy on copy waves 0 and 1 and none on 2 and 3,
+  // or SP_PW 4-byte copies; row-major: S_PW) per copy wave
   constexpr int B_OPS = B_PW + (PACKED ? SP_PW : S_PW);
+  const int b_ops = sc16 ? B_PW + (cw < 2 ? 1 : 0) : B_OPS;  // (uniform)
   auto issue_b = [&](int c, int stage) {
     if (!copier) return;
     uint8_t* base = smem + 2 * C::A_BYTES + stage * PW_B_STAGE;
@@ -1372,10 +1384,15 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
       for (int k = 0; k < B_PW; ++k)
         lds_copy16(crsrc, (lds_void_t*)(base + (B_PW * cw + k) * 1024),
                    b_row[k] + 128u * (uint32_t)c + b_odd[k] * w + (uint32_t)b_blk[k] * 16u);
+      if (sc16) {
+        if (cw < 2)
+          lds_copy16(srsrc, (lds_void_t*)(base + PW_B_BYTES + cw * 1024), sp_row[0] + (uint32_t)c * (uint32_t)N * 4u);
+      } else {
 #pragma unroll
-      for (int k = 0; k < SP_PW; ++k)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, (lds_void_t*)(base + PW_B_BYTES + (SP_PW * cw + k) * 256), 4,
-                                                 sp_row[k] + (uint32_t)c * (uint32_t)N * 4u, 0, 0, 0);
+        for (int k = 0; k < SP_PW; ++k)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, (lds_void_t*)(base + PW_B_BYTES + (SP_PW * cw + k) * 256),
+                                                   4, sp_row[k] + (uint32_t)c * (uint32_t)N * 4u, 0, 0, 0);
+      }
     } else {
 #pragma unroll
       for (int k = 0; k < B_PW; ++k)
@@ -1427,10 +1444,16 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
     // a copy wave's copies of chunk c: with three weight stages the weight
     // copies of chunk c+1, issued after the A copies of chunk c, may stay
     // in flight (vector memory loads complete in issue order)
-    if (SB == 3 && c + 1 < nchunk)
-      wait_vmcnt<B_OPS>();
-    else
+    if (SB == 3 && c + 1 < nchunk) {
+      if (b_ops == B_OPS)
+        wait_vmcnt<B_OPS>();
+      else if (b_ops == B_PW + 1)
+        wait_vmcnt<B_PW + 1>();
+      else
+        wait_vmcnt<B_PW>();
+    } else {
       wait_vmcnt<0>();
+    }
     __builtin_amdgcn_s_barrier();  // everyone's copies of chunk c; everyone done with chunk c - 1
     __builtin_amdgcn_sched_barrier(0);
     // into the stages chunk c - 1 used
