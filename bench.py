@@ -53,6 +53,7 @@ LEGS = [("20b_decode", "hbm"), ("20b_prefill", "mfma"), ("120b_prefill_zipf", "m
 ATTN_LEGS = ["attn_prefill_band", "attn_prefill_dense", "attn_decode_dense", "attn_decode_band"]
 BF16_MFMA_PEAK = 2.5e15    # MI355X dense bf16 MFMA, FLOP/s
 TIME_EVERY = 10            # every TIME_EVERY-th timed step brackets the dominant kernel with events
+SAMPLE_EXTRA = 200         # single-layer legs: more steps after the K timed ones, sampled the same way
 
 
 def log(*a):
@@ -260,7 +261,10 @@ def run_leg(wl, bound, args, torch, moe, want_cpu):
         # event pairs on the launch stream.  An event pair costs about 11 us
         # of stream time around a decode step, so bracketing every step would
         # inflate the step time it is measured in; the sampled launches run
-        # inside the same stream of steps.
+        # inside the same stream of steps.  A single-layer leg then runs
+        # SAMPLE_EXTRA more steps back to back in the same stream, sampled the
+        # same way, so that the kernel's mean rests on more than K / 10
+        # launches; the step time is that of the K steps alone.
         moe.moe_timing_read(reset=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -274,12 +278,20 @@ def run_leg(wl, bound, args, torch, moe, want_cpu):
             if timed:
                 moe.moe_timing_enable(False)
         ev1.record()
+        extra = SAMPLE_EXTRA if nlay == 1 else 0
+        for i in range(args.steps, args.steps + extra):
+            timed = i % TIME_EVERY == 0
+            if timed:
+                moe.moe_timing_enable(["gateup_gemm"])
+            step(i)
+            if timed:
+                moe.moe_timing_enable(False)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         kt_live = moe.moe_timing_read(reset=True)
         ms_step = ev0.elapsed_time(ev1) / args.steps
         gu_ms, gu_n = kt_live["gateup_gemm"]
-        return ms_step, wall / args.steps, gu_ms / max(gu_n, 1) * 1e3, gu_n, kt
+        return ms_step, wall / (args.steps + extra), gu_ms / max(gu_n, 1) * 1e3, gu_n, kt
 
     ms_rm, wall_rm, gu_us_rm, _, kt_rm = measure(make_step(sets, False), breakdown=True)
     log(f"row-major weights: {ms_rm * 1e3:.1f} us/step (host wall {wall_rm * 1e6:.1f} us/step), "
@@ -299,13 +311,16 @@ def run_leg(wl, bound, args, torch, moe, want_cpu):
     # algorithmic work
     if nlay == 1:
         nsel_mean = float(np.mean([n_sel[i % nsets] for i in range(args.steps)]))
+        # the weight sets of the sampled gate/up launches (every TIME_EVERY-th
+        # step of the K timed and SAMPLE_EXTRA further steps)
+        nsel_gu = float(np.mean([n_sel[i % nsets] for i in range(0, args.steps + SAMPLE_EXTRA, TIME_EVERY)]))
     else:
-        nsel_mean = float(np.mean(n_sel))
+        nsel_mean = nsel_gu = float(np.mean(n_sel))
     layer_bytes = nsel_mean * expert_bytes + wl.E * wl.d * 2 + wl.E * 4 + 2 * x_bytes
     step_bytes = layer_bytes * nlay
     step_flops = 2.0 * P * 3 * wl.d * wl.I * nlay
     gu_unit_bytes = mxfp4_bytes(2 * wl.I, wl.d) + 4 * 2 * wl.I
-    gu_bytes = nsel_mean * gu_unit_bytes + x_bytes
+    gu_bytes = nsel_gu * gu_unit_bytes + x_bytes
     gu_flops = 2.0 * P * wl.d * 2 * wl.I
     traffic = read_traffic("gateup_gemm", wl.name) if args.act == "exact" else None
     hbm_kernel_rm = gu_bytes / (gu_us_rm * 1e-6)
