@@ -1321,6 +1321,13 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
     b_odd[k] = wr & 1u;
     b_blk[k] = slot ^ ((n >> 2) & 3);
   }
+  // A copy wave whose 16 B_PW tile rows all lie past the output (in the
+  // last column span) issues no code copies with two weight stages, whose
+  // wait drains every copy (vmcnt 0); those LDS rows keep stale codes, which
+  // only the MFMA columns of discarded outputs read.  With three stages the
+  // waits count every wave's copies, so all are issued.
+  const int bn0 = 16 * B_PW * cw;
+  const bool b_live = C::SB == 3 || (GATEUP ? tcol0 + (bn0 % (PW_NT / 2)) < I : tcol0 + bn0 < N);
   // row-major scale copy k of a copy wave fills dwords u = (S_PW cw + k)
   // * 64 + lane: tile row u / 2, block pair u % 2 of the chunk (two bytes,
   // low half of the dword)
@@ -1380,10 +1387,12 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
       // bytes for a short last chunk; its blocks past K read on into the
       // next row or pair (finite codes, multiplied by zero A pieces)
       const uint32_t w = (uint32_t)(4 * c + 4 <= nblk ? 64 : 16 * (nblk - 4 * c));
+      if (b_live) {
 #pragma unroll
-      for (int k = 0; k < B_PW; ++k)
-        lds_copy16(crsrc, (lds_void_t*)(base + (B_PW * cw + k) * 1024),
-                   b_row[k] + 128u * (uint32_t)c + b_odd[k] * w + (uint32_t)b_blk[k] * 16u);
+        for (int k = 0; k < B_PW; ++k)
+          lds_copy16(crsrc, (lds_void_t*)(base + (B_PW * cw + k) * 1024),
+                     b_row[k] + 128u * (uint32_t)c + b_odd[k] * w + (uint32_t)b_blk[k] * 16u);
+      }
       if (sc16) {
         if (cw < 2)
           lds_copy16(srsrc, (lds_void_t*)(base + PW_B_BYTES + cw * 1024), sp_row[0] + (uint32_t)c * (uint32_t)N * 4u);
@@ -1394,10 +1403,12 @@ __global__ __launch_bounds__(PW_NW * 64, 1) void expert_gemm_prefill_wide(GemmPa
                                                    4, sp_row[k] + (uint32_t)c * (uint32_t)N * 4u, 0, 0, 0);
       }
     } else {
+      if (b_live) {
 #pragma unroll
-      for (int k = 0; k < B_PW; ++k)
-        lds_copy16(crsrc, (lds_void_t*)(base + (B_PW * cw + k) * 1024),
-                   b_row[k] + (uint32_t)min(4 * c + b_blk[k], nblk - 1) * 16u);
+        for (int k = 0; k < B_PW; ++k)
+          lds_copy16(crsrc, (lds_void_t*)(base + (B_PW * cw + k) * 1024),
+                     b_row[k] + (uint32_t)min(4 * c + b_blk[k], nblk - 1) * 16u);
+      }
 #pragma unroll
       for (int k = 0; k < S_PW; ++k)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
