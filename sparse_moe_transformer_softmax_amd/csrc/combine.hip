@@ -78,13 +78,16 @@ __device__ __forceinline__ void keep(float4 (&xk)[ROW_KEEP], int i, float4 v) {
 
 // Stack variant of the combine, one row per workgroup: the combine sum,
 // x_out = bf16(x + sum) (the add in fp32) and, unless it is the last layer,
-// n_out = bf16(RMSNorm(x_out)).
+// n_out = bf16(RMSNorm(x_out)).  K: the slots per token (a template
+// argument, so that every slot's loads are issued before the first sum).
+template <int K>
 __global__ __launch_bounds__(ROW_THREADS) void combine_kernel(CombineParams p) {
   __shared__ float s_red[ROW_THREADS / 64];
   const int t = blockIdx.x;
-  const int k = p.k, d = p.d, d4 = d >> 2;
-  const float4* rows[8];
-  float w[8];
+  const int k = K, d = p.d, d4 = d >> 2;
+  const float4* rows[K];
+  float w[K];
+#pragma unroll
   for (int j = 0; j < k; ++j) {
     const int pair = t * k + j;
     const int e = p.topk_id[pair];
@@ -97,17 +100,21 @@ __global__ __launch_bounds__(ROW_THREADS) void combine_kernel(CombineParams p) {
   float4 xk[ROW_KEEP];
   int i = 0;
   for (int c = threadIdx.x; c < d4; c += ROW_THREADS, ++i) {
+    const uint2 xr = xi[c];  // (in flight with the rows' loads)
+    float4 v[K];
+#pragma unroll
+    for (int j = 0; j < k; ++j) v[j] = rows[j][c];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
     for (int j = 0; j < k; ++j) {
-      const float4 v = rows[j][c];
-      acc.x = fmaf(w[j], v.x, acc.x);
-      acc.y = fmaf(w[j], v.y, acc.y);
-      acc.z = fmaf(w[j], v.z, acc.z);
-      acc.w = fmaf(w[j], v.w, acc.w);
+      acc.x = fmaf(w[j], v[j].x, acc.x);
+      acc.y = fmaf(w[j], v[j].y, acc.y);
+      acc.z = fmaf(w[j], v[j].z, acc.z);
+      acc.w = fmaf(w[j], v[j].w, acc.w);
     }
     if (p.out_f32) ((float4*)(p.out_f32 + (size_t)t * d))[c] = acc;
     if (p.out) ((uint2*)(p.out + (size_t)t * d))[c] = pack_bf16x4(acc);
-    const float4 x = unpack_bf16x4(xi[c]);
+    const float4 x = unpack_bf16x4(xr);
     const uint2 xb = pack_bf16x4(make_float4(x.x + acc.x, x.y + acc.y, x.z + acc.z, x.w + acc.w));
     xo[c] = xb;
     const float4 xn = unpack_bf16x4(xb);
@@ -150,12 +157,16 @@ __global__ __launch_bounds__(ROW_THREADS) void residual_rmsnorm_kernel(const uin
 
 // Plain combine: one thread per float4 column group of one token, so that a
 // small batch still spreads over many workgroups.
+// K: the slots per token (a template argument, so that every slot's loads
+// are issued before the first sum).
+template <int K>
 __global__ __launch_bounds__(256) void combine_cols_kernel(CombineParams p) {
   const int t = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
-  const int k = p.k, d = p.d;
+  const int k = K, d = p.d;
   if (c >= (d >> 2)) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
   for (int j = 0; j < k; ++j) {
     const int pair = t * k + j;
     const float w = p.topk_w[pair];
@@ -194,11 +205,24 @@ __global__ void zero_ints_kernel(int* p, int n) {
 }
 
 int launch_combine(const CombineParams& p, hipStream_t s) {
-  if (p.resid_out == nullptr) {
-    hipLaunchKernelGGL(combine_cols_kernel, dim3((p.d / 4 + 255) / 256, p.T), dim3(256), 0, s, p);
-  } else {
-    hipLaunchKernelGGL(combine_kernel, dim3(p.T), dim3(ROW_THREADS), 0, s, p);
+  const dim3 gc((p.d / 4 + 255) / 256, p.T), gr(p.T);
+#define MOE_COMB(K)                                                                    \
+  if (p.resid_out == nullptr)                                                          \
+    hipLaunchKernelGGL(combine_cols_kernel<K>, gc, dim3(256), 0, s, p);                \
+  else                                                                                 \
+    hipLaunchKernelGGL(combine_kernel<K>, gr, dim3(ROW_THREADS), 0, s, p);
+  switch (p.k) {
+    case 1: MOE_COMB(1) break;
+    case 2: MOE_COMB(2) break;
+    case 3: MOE_COMB(3) break;
+    case 4: MOE_COMB(4) break;
+    case 5: MOE_COMB(5) break;
+    case 6: MOE_COMB(6) break;
+    case 7: MOE_COMB(7) break;
+    case 8: MOE_COMB(8) break;
+    default: return -1;
   }
+#undef MOE_COMB
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
